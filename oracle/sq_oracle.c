@@ -1,0 +1,374 @@
+/*
+ * sq_oracle.c -- CPU oracle for the SmoothQuant W8A8 quantized linear
+ * Y = X W^T.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The product path
+ * (the HIP library and its binding) never calls it, links it or shares a
+ * line of code with it.
+ *
+ * What it follows: the page "w8a8_smoothquant.py" (BiGRU_T_version,
+ * src/bigru_t/quantization), namely
+ *   - the module docstring: the transform X~ = X / s, W~ = W * s with
+ *     Y = X~ W~^T, and the choice s_j = max|X_j|^alpha / max|W_j|^(1-alpha);
+ *   - calibrate_smoothquant: column maxima of |X| and |W| floored at 1e-8,
+ *     the power quotient, the final floor on s;
+ *   - quantize_per_channel_symmetric / quantize_per_token_symmetric: one
+ *     scale per row, max|row| floored at 1e-8 and divided by 127, codes
+ *     round(v / scale) clamped and stored as int8;
+ *   - SmoothQuantW8A8.calibrate: a running per-channel max of |X|;
+ *   - SmoothQuantW8A8.freeze_quantization: s from the running max, then
+ *     per-output-channel int8 of W * s;
+ *   - SmoothQuantW8A8.forward (quantized branch): X / s, per-token int8,
+ *     the product of the dequantised operands, then + bias. The page notes
+ *     there that real hardware does INT8 x INT8 -> INT32 -> fp32; this file
+ *     computes exactly that integer product.
+ *
+ * Readings where the page is silent or garbled (each one also listed in
+ * the design notes of the repository):
+ *   R1  codes are clamped to [-128, 127]; with a max-abs scale no code
+ *       below -127 can arise, so the page's [-127, 127] gives the same codes.
+ *   R2  round() is round-half-to-even of the fp32 quotient.
+ *   R3  every quotient is one IEEE binary32 division.
+ *   R4  the powers in s are taken through binary64 (see sqo_pow below) so
+ *       that the result does not depend on a math library's fp32 pow.
+ *   R5  the floor 1e-8 is the binary32 number nearest to 1e-8.
+ *   R6  no calibration at all means s = 1 for every channel.
+ *   R9  bf16 inputs are widened exactly to fp32 by the caller; all scale
+ *       and code arithmetic is fp32; the dequantised output is binary64 and
+ *       a bf16 output is that value rounded once, to nearest-even, to bf16.
+ *
+ * Build: gcc -std=c99 -O2 -ffp-contract=off -fno-fast-math (x86-64 SSE2
+ * arithmetic, never x87), optionally -fopenmp for the integer product.
+ * Mutants: -DSQO_MUTANT=n plants one deliberate mistake (see the sites
+ * marked MUTANT) so that the tests can show each pin catches it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifndef SQO_MUTANT
+#define SQO_MUTANT 0
+#endif
+
+/* R5: the page clamps with the Python float 1e-8 on fp32 tensors, i.e. the
+ * binary32 value nearest to 1e-8. */
+static const float SQO_FLOOR = 1e-8f;
+
+/* Largest and smallest int8 codes (R1). 127 is the page's qmax. */
+#define SQO_QMAX 127
+#define SQO_QMIN (-128)
+
+int sqo_mutant(void) { return SQO_MUTANT; }
+
+static float fmax_f(float a, float b) { return a > b ? a : b; }
+
+/* ---------------------------------------------------------------------
+ * SmoothQuantW8A8.calibrate: running per-input-channel max of |X| over
+ * every calibration row. `running` starts at zero (the page's buffer is
+ * created with zeros) and is updated in place. No floor here: the page
+ * floors only when it forms s.
+ * ------------------------------------------------------------------ */
+void sqo_calibrate(const float* x, int64_t rows, int64_t k, float* running)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < k; ++j) {
+#if SQO_MUTANT == 13
+            /* MUTANT 13: forgets the absolute value. */
+            float a = x[r * k + j];
+#else
+            float a = fabsf(x[r * k + j]);
+#endif
+            if (a > running[j]) running[j] = a;
+        }
+}
+
+/* ---------------------------------------------------------------------
+ * calibrate_smoothquant, max_w: per input channel j the max over output
+ * rows o of |W[o, j]|, floored at 1e-8 (one value per input channel).
+ * ------------------------------------------------------------------ */
+void sqo_weight_col_max(const float* w, int64_t n, int64_t k, float* mw)
+{
+    for (int64_t j = 0; j < k; ++j) mw[j] = 0.0f;
+    for (int64_t o = 0; o < n; ++o)
+        for (int64_t j = 0; j < k; ++j) {
+#if SQO_MUTANT == 6
+            /* MUTANT 6: forgets the absolute value. */
+            float a = w[o * k + j];
+#else
+            float a = fabsf(w[o * k + j]);
+#endif
+            if (a > mw[j]) mw[j] = a;
+        }
+    for (int64_t j = 0; j < k; ++j) mw[j] = fmax_f(mw[j], SQO_FLOOR);
+}
+
+/* ---------------------------------------------------------------------
+ * R4: x^a for the exponents the smoothing factor uses. The page writes
+ * torch.pow in fp32, whose last bit depends on the math library. Here:
+ *   a = 0    -> 1
+ *   a = 1    -> x
+ *   a = 1/2  -> sqrt(x)            (binary64 sqrt, correctly rounded)
+ *   a = 1/4  -> sqrt(sqrt(x))      (binary64)
+ *   a = 3/4  -> sqrt(x) * sqrt(sqrt(x))   (binary64 product)
+ *   other a  -> pow(x, a) in binary64
+ * The caller rounds the result to binary32 once.
+ * ------------------------------------------------------------------ */
+static double sqo_pow(double x, double a)
+{
+    if (a == 0.0) return 1.0;
+    if (a == 1.0) return x;
+    if (a == 0.5) return sqrt(x);
+    if (a == 0.25) return sqrt(sqrt(x));
+    if (a == 0.75) return sqrt(x) * sqrt(sqrt(x));
+    return pow(x, a);
+}
+
+/* ---------------------------------------------------------------------
+ * calibrate_smoothquant: s_j = max(|X_j|)^alpha / max(|W_j|)^(1 - alpha),
+ * with both maxima floored at 1e-8 first and s floored at 1e-8 last.
+ *   mx : running max of |X| per channel (from sqo_calibrate), or NULL for
+ *        "never calibrated" (R6: s = 1).
+ *   mw : floored column max of |W| (from sqo_weight_col_max).
+ * 1 - alpha is formed in binary64. The quotient is one binary32 division
+ * of the two binary32-rounded powers.
+ * Returns 1 when mx was NULL (the page warns in that case), else 0.
+ * ------------------------------------------------------------------ */
+int sqo_smoothing_factor(const float* mx, const float* mw, float alpha,
+                         int64_t k, float* s)
+{
+    if (mx == NULL) {
+        for (int64_t j = 0; j < k; ++j) s[j] = 1.0f;
+        return 1;
+    }
+    const double a_x = (double)alpha;
+#if SQO_MUTANT == 4
+    /* MUTANT 4: the weight exponent uses alpha instead of 1 - alpha. */
+    const double a_w = (double)alpha;
+#else
+    const double a_w = 1.0 - (double)alpha;
+#endif
+    for (int64_t j = 0; j < k; ++j) {
+        float mxj = fmax_f(mx[j], SQO_FLOOR);
+        float num = (float)sqo_pow((double)mxj, a_x);
+        float den = (float)sqo_pow((double)mw[j], a_w);
+#if SQO_MUTANT == 12
+        /* MUTANT 12: multiplies the two powers instead of dividing. */
+        float q = num * den;
+#else
+        float q = num / den;
+#endif
+        s[j] = fmax_f(q, SQO_FLOOR);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------
+ * freeze_quantization: W_smooth = weight * s (s broadcast over the input
+ * channel, i.e. column j of every row is multiplied by s_j).
+ * ------------------------------------------------------------------ */
+void sqo_smooth_weight(const float* w, const float* s, int64_t n, int64_t k,
+                       float* w_smooth)
+{
+    for (int64_t o = 0; o < n; ++o)
+        for (int64_t j = 0; j < k; ++j)
+            w_smooth[o * k + j] = w[o * k + j] * s[j];
+}
+
+/* ---------------------------------------------------------------------
+ * forward (quantized branch): X_smooth = X / s, channel j divided by s_j.
+ * ------------------------------------------------------------------ */
+void sqo_smooth_act(const float* x, const float* s, int64_t m, int64_t k,
+                    float* x_smooth)
+{
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t j = 0; j < k; ++j)
+#if SQO_MUTANT == 5
+            /* MUTANT 5: multiplies by s instead of dividing. */
+            x_smooth[t * k + j] = x[t * k + j] * s[j];
+#else
+            x_smooth[t * k + j] = x[t * k + j] / s[j];
+#endif
+}
+
+/* Round-half-to-even of a binary32 value to an integer (R2). rintf under
+ * the default rounding mode is exactly that. */
+static float sqo_round_even(float v)
+{
+#if SQO_MUTANT == 1
+    /* MUTANT 1: rounds halves away from zero. */
+    return roundf(v);
+#else
+    return rintf(v);
+#endif
+}
+
+/* ---------------------------------------------------------------------
+ * quantize_per_channel_symmetric (axis 0) and quantize_per_token_symmetric
+ * are the same operation on a 2-D array: one scale per row,
+ *   scale[r] = max(max_j |v[r, j]|, 1e-8) / 127            (binary32)
+ *   q[r, j]  = clamp(round_even(v[r, j] / scale[r]), -128, 127)
+ * ------------------------------------------------------------------ */
+void sqo_quantize_rows(const float* v, int64_t rows, int64_t k, int8_t* q,
+                       float* scale)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* row = v + r * k;
+        float m = 0.0f;
+        for (int64_t j = 0; j < k; ++j) m = fmax_f(m, fabsf(row[j]));
+#if SQO_MUTANT == 2
+        /* MUTANT 2: no floor; an all-zero row gets scale 1 instead. */
+        float sc = m / (float)SQO_QMAX;
+        if (sc == 0.0f) sc = 1.0f;
+#elif SQO_MUTANT == 10
+        /* MUTANT 10: divides the row max by 128 instead of 127. */
+        float sc = fmax_f(m, SQO_FLOOR) / 128.0f;
+#else
+        float sc = fmax_f(m, SQO_FLOOR) / (float)SQO_QMAX;
+#endif
+        scale[r] = sc;
+        for (int64_t j = 0; j < k; ++j) {
+            float c = sqo_round_even(row[j] / sc);
+            if (c > (float)SQO_QMAX) c = (float)SQO_QMAX;
+            if (c < (float)SQO_QMIN) c = (float)SQO_QMIN;
+            q[r * k + j] = (int8_t)c;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------
+ * The INT8 x INT8 -> INT32 product the page's forward stands in for:
+ *   acc[t, o] = sum_j xq[t, j] * wq[o, j]
+ * accumulated in int64. Returns the number of entries that do not fit in
+ * int32 (0 for every valid input: |acc| <= 128^2 * k).
+ * ------------------------------------------------------------------ */
+int64_t sqo_int_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
+                     int64_t k, int32_t* acc)
+{
+    int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : overflow)
+    for (int64_t t = 0; t < m; ++t) {
+        const int8_t* xr = xq + t * k;
+        for (int64_t o = 0; o < n; ++o) {
+            const int8_t* wr = wq + o * k;
+            int64_t sum = 0;
+            for (int64_t j = 0; j < k; ++j)
+#if SQO_MUTANT == 8
+                /* MUTANT 8: reads the weight operand as if stored k x n. */
+                sum += (int64_t)xr[j] * (int64_t)wq[j * n + o];
+#else
+                sum += (int64_t)xr[j] * (int64_t)wr[j];
+#endif
+            if (sum > INT32_MAX || sum < INT32_MIN) ++overflow;
+            acc[t * n + o] = (int32_t)sum;
+        }
+    }
+    return overflow;
+}
+
+/* ---------------------------------------------------------------------
+ * Dequantisation of the integer product, in binary64:
+ *   y[t, o] = acc[t, o] * scale_x[t] * scale_w[o] + bias[o]
+ * (the page adds the bias after the product). bias may be NULL.
+ * ------------------------------------------------------------------ */
+void sqo_dequant(const int32_t* acc, const float* scale_x, const float* scale_w,
+                 const float* bias, int64_t m, int64_t n, double* y)
+{
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t o = 0; o < n; ++o) {
+#if SQO_MUTANT == 3
+            /* MUTANT 3: the two scales are indexed the wrong way round. */
+            double v = (double)acc[t * n + o] * (double)scale_x[o % m] * (double)scale_w[t % n];
+#else
+            double v = (double)acc[t * n + o] * (double)scale_x[t] * (double)scale_w[o];
+#endif
+#if SQO_MUTANT != 9
+            /* MUTANT 9 drops the bias. */
+            if (bias) v += (double)bias[o];
+#endif
+            y[t * n + o] = v;
+        }
+}
+
+/* ---------------------------------------------------------------------
+ * The page's own formulation of the frozen forward ("simulation"):
+ * dequantise each operand first (code * scale, exact in binary64), then
+ * the product of the dequantised matrices, then + bias. It must agree with
+ * sqo_dequant(sqo_int_gemm(...)) up to binary64 rounding.
+ * ------------------------------------------------------------------ */
+void sqo_simulated_forward(const int8_t* xq, const float* scale_x,
+                           const int8_t* wq, const float* scale_w,
+                           const float* bias, int64_t m, int64_t n, int64_t k,
+                           double* y)
+{
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t o = 0; o < n; ++o) {
+            double sum = 0.0;
+            for (int64_t j = 0; j < k; ++j) {
+                double xd = (double)xq[t * k + j] * (double)scale_x[t];
+                double wd = (double)wq[o * k + j] * (double)scale_w[o];
+                sum += xd * wd;
+            }
+            if (bias) sum += (double)bias[o];
+            y[t * n + o] = sum;
+        }
+}
+
+/* ---------------------------------------------------------------------
+ * Round binary64 values once, to nearest-even, to bfloat16 (8 significant
+ * bits, the binary32 exponent range, subnormals kept). Returns the bf16
+ * bit patterns. Used for the bf16 output of the dequantised product (R9).
+ * ------------------------------------------------------------------ */
+void sqo_f64_to_bf16(const double* v, int64_t count, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        double x = v[i];
+        uint16_t sign = signbit(x) ? 0x8000u : 0u;
+        double a = fabs(x);
+        if (isnan(x)) { out[i] = 0x7FC0u; continue; }
+        if (a == 0.0) { out[i] = sign; continue; }
+        int e;
+        (void)frexp(a, &e);           /* a = f * 2^e, f in [0.5, 1) */
+        int ex = e - 1;               /* a in [2^ex, 2^(ex+1)) */
+        if (ex < -126) ex = -126;     /* bf16 subnormal spacing 2^-133 */
+        /* quantum of bf16 at this binade: 2^(ex - 7) */
+        double units = ldexp(a, 7 - ex);        /* exact scaling */
+        double r = nearbyint(units);            /* ties to even */
+        double rounded = ldexp(r, ex - 7);
+        if (rounded >= ldexp(1.0, 128)) { out[i] = (uint16_t)(sign | 0x7F80u); continue; }
+        float f = (float)rounded;               /* exact: 8 significant bits */
+        uint32_t bits;
+        memcpy(&bits, &f, 4);
+        out[i] = (uint16_t)(sign | ((bits >> 16) & 0x7FFFu));
+    }
+}
+
+/* ---------------------------------------------------------------------
+ * One-call composition of the whole frozen path for convenience of the
+ * tests and the CPU baseline. All arrays are caller-owned.
+ *   x      [m*k]  activations (fp32 values; bf16 inputs widened)
+ *   w      [n*k]  weights
+ *   bias   [n]    or NULL
+ *   calib  [rc*k] calibration rows, or NULL (R6)
+ * Outputs: mx[k], s[k], wq[n*k], sw[n], xq[m*k], sx[m], acc[m*n], y[m*n].
+ * Scratch: ws[max(m,n)*k] fp32.
+ * Returns the int32 overflow count from sqo_int_gemm.
+ * ------------------------------------------------------------------ */
+int64_t sqo_linear(const float* x, const float* w, const float* bias,
+                   const float* calib, int64_t rc, int64_t m, int64_t n,
+                   int64_t k, float alpha, float* mx, float* mw, float* s,
+                   int8_t* wq, float* sw, int8_t* xq, float* sx, int32_t* acc,
+                   double* y, float* ws)
+{
+    for (int64_t j = 0; j < k; ++j) mx[j] = 0.0f;
+    if (calib) sqo_calibrate(calib, rc, k, mx);
+    sqo_weight_col_max(w, n, k, mw);
+    sqo_smoothing_factor(calib ? mx : NULL, mw, alpha, k, s);
+    sqo_smooth_weight(w, s, n, k, ws);
+    sqo_quantize_rows(ws, n, k, wq, sw);
+    sqo_smooth_act(x, s, m, k, ws);
+    sqo_quantize_rows(ws, m, k, xq, sx);
+    int64_t ov = sqo_int_gemm(xq, wq, m, n, k, acc);
+    sqo_dequant(acc, sx, sw, bias, m, n, y);
+    return ov;
+}

@@ -1,0 +1,404 @@
+"""Pins of the CPU oracle against what the page and mathematics fix.
+
+Each pin is a function of an ``oracle.Oracle`` instance that raises
+AssertionError on a mismatch. ``test_oracle_pins.py`` runs them on the
+oracle as built; ``test_oracle_mutants.py`` runs them on copies of the oracle
+with one deliberate mistake planted, and requires every such copy to fail at
+least one pin.
+
+Source of the method: page "w8a8_smoothquant.py" (BiGRU_T_version): module
+docstring (the transform, the choice of s and its alpha limits, the error
+bound), calibrate_smoothquant, quantize_per_channel_symmetric,
+quantize_per_token_symmetric, SmoothQuantW8A8.calibrate /
+freeze_quantization / forward / quantization_error.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from exact import (FLOOR, bf16_bits_of, rn_bf16, rn_f32, rn_f32_root,
+                   round_half_even)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _outlier_acts(rng, m, k, chans=(1,), mult=40.0):
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    x[:, list(chans)] *= np.float32(mult)
+    return x
+
+
+def _with_ties(rng, m, k):
+    """Rows whose max is 127 * 2^e so that scale = 2^e exactly and several
+    entries sit exactly on half-integers after division by the scale."""
+    e = rng.integers(-8, 4, size=m)
+    x = np.empty((m, k), np.float32)
+    for r in range(m):
+        codes = rng.integers(-126, 127, size=k).astype(np.float64)
+        halves = rng.random(k) < 0.5
+        codes[halves] += 0.5 * np.sign(rng.standard_normal(halves.sum()))
+        codes = np.clip(codes, -126.5, 126.5)
+        codes[rng.integers(k)] = 127.0 * (1 if rng.random() < 0.5 else -1)
+        x[r] = (codes * 2.0 ** float(e[r])).astype(np.float32)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# 1. Hand-derived worked example (tests/golden/hand_worked_alpha_half.json).
+# ---------------------------------------------------------------------------
+def pin_golden_hand_example(o):
+    d = json.load(open(os.path.join(GOLDEN, "hand_worked_alpha_half.json")))
+    x = np.array(d["x"], np.float32)
+    w = np.array(d["w"], np.float32)
+    b = np.array(d["bias"], np.float32)
+    ex = {kk: np.array(v) for kk, v in d["expected"].items()}
+    mx = o.calibrate(x)
+    assert np.array_equal(mx, ex["mx"].astype(np.float32)), mx
+    mw = o.weight_col_max(w)
+    assert np.array_equal(mw, ex["mw"].astype(np.float32)), mw
+    s = o.smoothing_factor(mx, mw, d["alpha"])
+    assert np.array_equal(s, ex["s"].astype(np.float32)), s
+    xs = o.smooth_act(x, s)
+    assert np.array_equal(xs, ex["x_smooth"].astype(np.float32))
+    ws = o.smooth_weight(w, s)
+    assert np.array_equal(ws, ex["w_smooth"].astype(np.float32))
+    xq, sx = o.quantize_rows(xs)
+    assert np.array_equal(sx, ex["scale_x"].astype(np.float32))
+    assert np.array_equal(xq, ex["xq"].astype(np.int8)), xq
+    wq, sw = o.quantize_rows(ws)
+    assert np.array_equal(sw, ex["scale_w"].astype(np.float32))
+    assert np.array_equal(wq, ex["wq"].astype(np.int8)), wq
+    acc = o.int_gemm(xq, wq)
+    assert np.array_equal(acc, ex["acc"].astype(np.int32)), acc
+    y = o.dequant(acc, sx, sw, b)
+    assert np.array_equal(y, ex["y"]), y
+    # bf16 output: the exact y rounded once to bf16 (exact rational rounding).
+    yb = o.to_bf16(y)
+    want = np.array([[bf16_bits_of(rn_bf16(Fraction(v))) for v in row] for row in d["expected"]["y"]],
+                    np.uint16)
+    assert np.array_equal(yb, want)
+    # composed helpers agree with the step-by-step route
+    s2, wq2, sw2 = o.prepare_weight(w, mx, d["alpha"])
+    assert np.array_equal(s2, s) and np.array_equal(wq2, wq) and np.array_equal(sw2, sw)
+
+
+# ---------------------------------------------------------------------------
+# 2. The floor 1e-8 and degenerate rows.
+# ---------------------------------------------------------------------------
+def pin_floor_and_zero_rows(o):
+    rng = _rng(11)
+    x = _outlier_acts(rng, 5, 32)
+    x[2] = 0.0                              # an all-zero token
+    q, sc = o.quantize_rows(x)
+    zero_scale = rn_f32(FLOOR / 127)
+    assert Fraction(float(sc[2])) == zero_scale
+    assert np.all(q[2] == 0)
+    # the floor constant itself and the zero-row scale, bit patterns
+    assert int(np.float32(float(FLOOR)).view(np.uint32)) == 0x322BCC77
+    assert int(np.float32(float(zero_scale)).view(np.uint32)) == 0x2EAD26C5
+    # all-zero weight column -> mw floored; all-zero weight row -> zero codes
+    w = rng.standard_normal((6, 32), dtype=np.float32) * np.float32(0.02)
+    w[:, 5] = 0.0
+    w[3] = 0.0
+    mw = o.weight_col_max(w)
+    assert Fraction(float(mw[5])) == FLOOR
+    mx = o.calibrate(x)
+    s, wq, sw = o.prepare_weight(w, mx, 0.5)
+    assert np.all(wq[3] == 0) and Fraction(float(sw[3])) == zero_scale
+    # a never-seen channel (all-zero calibration column) is floored too
+    xc = x.copy()
+    xc[:, 7] = 0.0
+    mx0 = o.calibrate(xc)
+    assert mx0[7] == 0.0
+    s0 = o.smoothing_factor(mx0, mw, 1.0)
+    assert Fraction(float(s0[7])) == FLOOR
+
+
+# ---------------------------------------------------------------------------
+# 3-6. The smoothing factor: closed forms at alpha = 0, 1, 1/2, 1/4, 3/4.
+# ---------------------------------------------------------------------------
+def _layer(seed, m=24, n=20, k=48):
+    rng = _rng(seed)
+    x = _outlier_acts(rng, m, k, chans=(3, 17), mult=50.0)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    return x, w
+
+
+def pin_alpha_zero(o):
+    """alpha = 0: s_j = 1 / mw_j (one binary32 division), and s, W_q and the
+    weight scales do not depend on the calibration data at all."""
+    x, w = _layer(21)
+    mw = o.weight_col_max(w)
+    s = o.smoothing_factor(o.calibrate(x), mw, 0.0)
+    want = np.maximum(np.float32(1.0) / mw, np.float32(float(FLOOR)))
+    assert np.array_equal(s, want)
+    s1, wq1, sw1 = o.prepare_weight(w, o.calibrate(x), 0.0)
+    s2, wq2, sw2 = o.prepare_weight(w, o.calibrate(x * np.float32(7.5) + np.float32(1.0)), 0.0)
+    assert np.array_equal(s1, s2) and np.array_equal(wq1, wq2) and np.array_equal(sw1, sw2)
+
+
+def pin_alpha_one(o):
+    """alpha = 1: s_j = mx_j (independent of W), and on the calibration
+    tokens every smoothed channel has max |X~_j| = 1 exactly."""
+    x, w = _layer(22)
+    mx = o.calibrate(x)
+    s = o.smoothing_factor(mx, o.weight_col_max(w), 1.0)
+    assert np.array_equal(s, mx)
+    s2 = o.smoothing_factor(mx, o.weight_col_max(w * np.float32(3.0) - np.float32(0.5)), 1.0)
+    assert np.array_equal(s, s2)
+    xs = o.smooth_act(x, s)
+    assert np.array_equal(np.abs(xs).max(axis=0), np.ones(x.shape[1], np.float32))
+
+
+def pin_alpha_half(o):
+    """alpha = 1/2: s_j = sqrtf(mx_j) / sqrtf(mw_j) with correctly rounded
+    binary32 square roots (numpy's float32 sqrt) and one division."""
+    x, w = _layer(23)
+    mx = o.calibrate(x)
+    mw = o.weight_col_max(w)
+    s = o.smoothing_factor(mx, mw, 0.5)
+    want = np.sqrt(mx.astype(np.float32)) / np.sqrt(mw.astype(np.float32))
+    assert np.array_equal(s, want.astype(np.float32))
+
+
+def pin_alpha_quarters(o):
+    """alpha in {1/4, 3/4}: the powers are the correctly rounded binary32
+    values of mx^alpha and mw^(1-alpha) (integer-root enclosures)."""
+    x, w = _layer(24)
+    mx = o.calibrate(x)
+    mw = o.weight_col_max(w)
+    for a_num in (1, 3):
+        alpha = a_num / 4
+        s = o.smoothing_factor(mx, mw, alpha)
+        for j in range(len(mx)):
+            num = rn_f32_root(Fraction(float(mx[j])), a_num, 4)
+            den = rn_f32_root(Fraction(float(mw[j])), 4 - a_num, 4)
+            want = max(rn_f32(num / den), FLOOR)
+            assert Fraction(float(s[j])) == want, (alpha, j)
+
+
+# ---------------------------------------------------------------------------
+# 7-8. Maxima: brute force and split invariance.
+# ---------------------------------------------------------------------------
+def pin_calibration_running_max(o):
+    rng = _rng(31)
+    x = _outlier_acts(rng, 40, 24, chans=(2, 9))
+    x[:, 4] = -np.abs(x[:, 4])              # a channel whose max |.| is negative
+    want = np.abs(x).max(axis=0)
+    assert np.array_equal(o.calibrate(x), want)
+    for splits in ([40], [1, 39], [13, 13, 14], [5] * 8):
+        run = np.zeros(24, np.float32)
+        bounds = np.cumsum([0] + splits)
+        for i in reversed(range(len(splits))):      # any batch order
+            o.calibrate(x[bounds[i]:bounds[i + 1]], run)
+        assert np.array_equal(run, want)
+
+
+def pin_weight_col_max(o):
+    rng = _rng(32)
+    w = rng.standard_normal((17, 21), dtype=np.float32)
+    w[:, 6] = -np.abs(w[:, 6])
+    want = np.maximum(np.abs(w).max(axis=0), np.float32(float(FLOOR)))
+    assert np.array_equal(o.weight_col_max(w), want)
+
+
+# ---------------------------------------------------------------------------
+# 9. Codes and scales in exact rational arithmetic.
+# ---------------------------------------------------------------------------
+def _check_rows_exact(v, q, sc):
+    for r in range(v.shape[0]):
+        m = max(Fraction(float(abs(t))) for t in v[r])
+        want_sc = rn_f32(max(m, FLOOR) / 127)
+        assert Fraction(float(sc[r])) == want_sc, r
+        for j in range(v.shape[1]):
+            quo = rn_f32(Fraction(float(v[r, j])) / want_sc)
+            c = min(127, max(-128, round_half_even(quo)))
+            assert int(q[r, j]) == c, (r, j, float(v[r, j]), float(quo), int(q[r, j]), c)
+
+
+def pin_codes_exact(o):
+    rng = _rng(41)
+    for v in (_outlier_acts(rng, 6, 40), _with_ties(rng, 6, 40),
+              rng.standard_normal((5, 33), dtype=np.float32) * np.float32(1e-3)):
+        q, sc = o.quantize_rows(v)
+        _check_rows_exact(v, q, sc)
+
+
+def pin_smoothing_exact(o):
+    """X~ = RN32(X / s) and W~ = RN32(W * s), element by element."""
+    x, w = _layer(42, m=6, n=5, k=20)
+    mx = o.calibrate(x)
+    s = o.smoothing_factor(mx, o.weight_col_max(w), 0.5)
+    xs = o.smooth_act(x, s)
+    ws = o.smooth_weight(w, s)
+    for t in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            assert Fraction(float(xs[t, j])) == rn_f32(Fraction(float(x[t, j])) / Fraction(float(s[j])))
+    for r in range(w.shape[0]):
+        for j in range(w.shape[1]):
+            assert Fraction(float(ws[r, j])) == rn_f32(Fraction(float(w[r, j])) * Fraction(float(s[j])))
+
+
+# ---------------------------------------------------------------------------
+# 10. Invariants of the codes.
+# ---------------------------------------------------------------------------
+def pin_code_invariants(o):
+    rng = _rng(51)
+    x = _outlier_acts(rng, 30, 64, chans=(5, 40), mult=60.0)
+    q, sc = o.quantize_rows(x)
+    assert q.min() >= -127                         # -128 never arises
+    am = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(30), am]) == 127)   # +-127 at the row max
+    assert np.all(np.sign(q[np.arange(30), am]) == np.sign(x[np.arange(30), am]))
+    qn, scn = o.quantize_rows(-x)                  # odd symmetry
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    for e in (-20, -3, 5, 30):                     # exact power-of-two scaling
+        qe, sce = o.quantize_rows(x * np.float32(2.0 ** e))
+        assert np.array_equal(qe, q)
+        assert np.array_equal(sce, sc * np.float32(2.0 ** e))
+    perm = rng.permutation(64)                     # channel permutation
+    qp, scp = o.quantize_rows(x[:, perm])
+    assert np.array_equal(qp, q[:, perm]) and np.array_equal(scp, sc)
+
+
+# ---------------------------------------------------------------------------
+# 11. The integer product.
+# ---------------------------------------------------------------------------
+def pin_int_gemm(o):
+    rng = _rng(61)
+    for m, n, k in ((1, 1, 1), (3, 5, 7), (9, 4, 33)):
+        a = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+        b = rng.integers(-128, 128, size=(n, k)).astype(np.int8)
+        acc = o.int_gemm(a, b)
+        for t in range(m):
+            for u in range(n):
+                assert int(acc[t, u]) == sum(int(a[t, j]) * int(b[u, j]) for j in range(k))
+        perm = rng.permutation(k)
+        assert np.array_equal(o.int_gemm(a[:, perm], b[:, perm]), acc)
+    # extremes: |acc| = 128^2 k with k = 4096 still fits int32
+    a = np.full((2, 4096), -128, np.int8)
+    acc = o.int_gemm(a, a)
+    assert np.all(acc == 128 * 128 * 4096)
+
+
+# ---------------------------------------------------------------------------
+# 12-14. The dequantised output.
+# ---------------------------------------------------------------------------
+def pin_dequant_matches_simulated_forward(o):
+    """The page's own formulation (dequantise both operands, multiply, add
+    bias) equals acc * scale_x * scale_w + bias up to binary64 rounding."""
+    rng = _rng(71)
+    x = _outlier_acts(rng, 7, 96, chans=(4,))
+    w = rng.standard_normal((5, 96), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal(5, dtype=np.float32) * np.float32(0.01)
+    s, wq, sw = o.prepare_weight(w, o.calibrate(x), 0.5)
+    xq, sx, acc, y = o.linear(x, s, wq, sw, b)
+    ysim = o.simulated_forward(xq, sx, wq, sw, b)
+    scale = np.abs(acc.astype(np.float64) * sx[:, None] * sw[None, :]) + np.abs(b)[None, :]
+    assert np.all(np.abs(y - ysim) <= 1e-12 * scale)
+
+
+def pin_dequant_exact(o):
+    rng = _rng(72)
+    acc = rng.integers(-2 ** 30, 2 ** 30, size=(4, 3)).astype(np.int32)
+    sx = (rng.random(4) * 0.1).astype(np.float32)
+    sw = (rng.random(3) * 0.01).astype(np.float32)
+    b = rng.standard_normal(3, dtype=np.float32)
+    y = o.dequant(acc, sx, sw, b)
+    for t in range(4):
+        for u in range(3):
+            exact = Fraction(int(acc[t, u])) * Fraction(float(sx[t])) * Fraction(float(sw[u])) + Fraction(float(b[u]))
+            assert abs(Fraction(float(y[t, u])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
+
+
+def pin_bf16_rounding(o):
+    rng = _rng(73)
+    v = np.concatenate([rng.standard_normal(200) * 10.0 ** rng.integers(-40, 38, 200),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2.0 ** -133,
+                                  3 * 2.0 ** -134, 2.0 ** -140, 0.0, -0.0, 65504.0])])
+    got = o.to_bf16(v)
+    for i, val in enumerate(v):
+        r = rn_bf16(Fraction(float(val)))
+        if r == 0:
+            want = 0x8000 if np.signbit(val) else 0
+        else:
+            want = bf16_bits_of(r)
+        assert int(got[i]) == want, (val, hex(int(got[i])), hex(want))
+
+
+# ---------------------------------------------------------------------------
+# 15-16. The transform is an identity; the error bound.
+# ---------------------------------------------------------------------------
+def pin_smoothing_identity(o):
+    """(X / s)(W * s)^T = X W^T up to the binary32 rounding of X~ and W~:
+    each term has relative error <= 2^-23, so per entry
+    |X~ W~^T - X W^T| <= 2^-22 * sum_j |X_tj W_oj|."""
+    x, w = _layer(81, m=12, n=10, k=64)
+    for alpha in (0.25, 0.5, 0.75):
+        s = o.smoothing_factor(o.calibrate(x), o.weight_col_max(w), alpha)
+        xs = o.smooth_act(x, s).astype(np.float64)
+        ws = o.smooth_weight(w, s).astype(np.float64)
+        x64, w64 = x.astype(np.float64), w.astype(np.float64)
+        diff = np.abs(xs @ ws.T - x64 @ w64.T)
+        bound = 2.0 ** -22 * (np.abs(x64) @ np.abs(w64).T) + 1e-300
+        assert np.all(diff <= bound)
+        # and the smoothing really moves the outlier: max|X~| over max|X| shrinks
+        assert np.abs(xs).max() < np.abs(x64).max()
+
+
+def error_bound_terms(o, x, w, b, alpha):
+    """Returns (err, literal_bound, provable_bound) for the docstring's
+    error statement, Frobenius norms as quantization_error measures them."""
+    s, wq, sw = o.prepare_weight(w, o.calibrate(x), alpha)
+    xq, sx, acc, y = o.linear(x, s, wq, sw, b)
+    x64, w64 = x.astype(np.float64), w.astype(np.float64)
+    yfp = x64 @ w64.T + b.astype(np.float64)
+    err = np.linalg.norm(yfp - y)
+    eps = 2.0 ** -7
+    literal = eps * np.linalg.norm(w64) * np.linalg.norm(x64) + eps * np.linalg.norm(x64) * np.linalg.norm(w64)
+    xs = o.smooth_act(x, s).astype(np.float64)
+    ws = o.smooth_weight(w, s).astype(np.float64)
+    xd = xq.astype(np.float64) * sx[:, None]
+    wd = wq.astype(np.float64) * sw[:, None]
+    ex = np.linalg.norm(xs - xd) / np.linalg.norm(xs)
+    ew = np.linalg.norm(ws - wd) / np.linalg.norm(ws)
+    resid = np.linalg.norm(xs @ ws.T - x64 @ w64.T)
+    provable = (ex + ew + ex * ew) * np.linalg.norm(xs) * np.linalg.norm(ws) + resid
+    return err, literal, provable
+
+
+def pin_error_bound(o):
+    rng = _rng(91)
+    x = _outlier_acts(rng, 16, 256, chans=(3, 77, 200), mult=40.0)
+    w = rng.standard_normal((128, 256), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal(128, dtype=np.float32) * np.float32(0.01)
+    for alpha in (0.0, 0.25, 0.5, 0.75, 1.0):
+        err, literal, provable = error_bound_terms(o, x, w, b, alpha)
+        assert err <= literal, (alpha, err, literal)
+        assert err <= provable * (1 + 1e-9), (alpha, err, provable)
+
+
+# ---------------------------------------------------------------------------
+# 17. Never calibrated: s = 1, plain per-token / per-channel int8.
+# ---------------------------------------------------------------------------
+def pin_uncalibrated(o):
+    x, w = _layer(101, m=8, n=6, k=32)
+    s = o.smoothing_factor(None, o.weight_col_max(w), 0.5)
+    assert np.all(s == 1.0)
+    s2, wq, sw = o.prepare_weight(w, None, 0.5)
+    q_plain, sc_plain = o.quantize_rows(w)
+    assert np.array_equal(wq, q_plain) and np.array_equal(sw, sc_plain)
+    xq, sx = o.quantize_act(x, s2)
+    qx, scx = o.quantize_rows(x)
+    assert np.array_equal(xq, qx) and np.array_equal(sx, scx)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

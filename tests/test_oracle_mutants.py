@@ -1,0 +1,33 @@
+"""Each deliberate mistake planted in a copy of the oracle (the MUTANT sites
+of oracle/sq_oracle.c) must be caught by at least one pin (CPU only)."""
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    1: "rounds halves away from zero",
+    2: "no 1e-8 floor on the row max",
+    3: "token and channel scales swapped in the dequant",
+    4: "weight exponent alpha instead of 1 - alpha",
+    5: "multiplies activations by s",
+    6: "weight column max without abs",
+    8: "weight operand read transposed",
+    9: "bias dropped",
+    10: "row max divided by 128",
+    12: "powers multiplied instead of divided",
+    13: "calibration max without abs",
+}
+
+
+@pytest.mark.parametrize("n", sorted(MUTANTS), ids=lambda n: f"m{n}")
+def test_mutant_is_caught(n, tmp_path):
+    o = oracle.mutant(n, str(tmp_path))
+    assert o.mutant == n
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, OverflowError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {n} ({MUTANTS[n]}) passes every pin"
