@@ -1,0 +1,175 @@
+/*
+ * sq.h -- C ABI of libsq.so: the SmoothQuant W8A8 quantized linear
+ * Y = X W^T on MI355X (gfx950).
+ *
+ * The method is the one of the page "w8a8_smoothquant.py" (BiGRU_T_version,
+ * src/bigru_t/quantization): activations X (M x K) and weights W (N x K, the
+ * nn.Linear layout) are rebalanced per input channel j by a smoothing factor
+ *     s_j = max|X_j|^alpha / max|W_j|^(1 - alpha)        (module docstring,
+ *                                                        calibrate_smoothquant)
+ * so that X~ = X / s and W~ = W * s give the same product. W~ is quantised
+ * to int8 once with one scale per output channel, X~ is quantised to int8 per
+ * token on every call, and the integer product is scaled back:
+ *     y[t, o] = acc[t, o] * scale_x[t] * scale_w[o] + bias[o],
+ *     acc[t, o] = sum_j xq[t, j] * wq[o, j]  (int32).
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers owned by the caller. The
+ *     library allocates nothing, frees nothing and never synchronises: work
+ *     is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     the call returns at once. Outputs are valid when the stream reaches
+ *     that point. Calls on different streams that write the same buffer race.
+ *   - Row-major, dense: X is [m][k], W and wq are [n][k], Y is [m][n].
+ *   - k must be a positive multiple of 16. Every pointer to a [.][k] array
+ *     must be 16-byte aligned. m and n may be any size >= 1 (a call with
+ *     m == 0 is a no-op that touches nothing).
+ *   - Floating-point input types: SQ_F32 or SQ_BF16 (widened exactly to
+ *     fp32). All scale and code arithmetic is IEEE binary32 with
+ *     round-to-nearest-even, every quotient one correctly rounded division
+ *     (or a scheme proven to give the same result); codes are
+ *     round-half-to-even of that quotient, clamped to [-128, 127].
+ *   - The floor 1e-8 (the binary32 value 0x322BCC77) is applied to every
+ *     maximum that is divided by, and to s.
+ *   - Errors: arguments are checked before anything is enqueued; a negative
+ *     status means nothing was enqueued. SQ_ERR_HIP means a launch failed
+ *     (earlier launches of the same call may have run). No exception or
+ *     abort ever crosses this ABI.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_WARN_UNCALIBRATED = 1, /* success; s was set to 1 (no calibration data) */
+    SQ_ERR_ARG = -1,          /* null pointer, alpha outside [0, 1], bad enum */
+    SQ_ERR_SHAPE = -2,        /* negative / zero size where one is required, or too large */
+    SQ_ERR_DTYPE = -3,        /* unsupported input or output type */
+    SQ_ERR_ALIGN = -4,        /* k not a multiple of 16, or a pointer not 16-byte aligned */
+    SQ_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+    SQ_ERR_HIP = -6           /* a HIP launch reported an error */
+} sq_status;
+
+typedef enum {
+    SQ_F32 = 0,   /* IEEE binary32 */
+    SQ_BF16 = 1,  /* bfloat16 */
+    SQ_I32 = 2    /* int32: output only, the raw integer accumulators */
+} sq_dtype;
+
+/* Largest k the kernels accept (one token row of X~ is held on chip). */
+#define SQ_MAX_K 16384
+
+/*
+ * sq_calibrate -- running per-input-channel max of |X| over calibration rows.
+ * Follows SmoothQuantW8A8.calibrate (page "w8a8_smoothquant.py"): the buffer
+ * starts at zero once and every batch folds max_r |x[r][j]| into it; the
+ * result is independent of how the rows are split into batches or ordered.
+ *   x               [rows][k] in xt (F32 or BF16), 16-byte aligned
+ *   running_max_abs [k] fp32, in/out; caller zero-fills it before the first
+ *                   batch; values stay non-negative (no floor is applied here)
+ * Returns SQ_OK, or SQ_ERR_* before launching. rows == 0 is a no-op.
+ */
+sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k,
+                       float* running_max_abs, void* stream);
+
+/*
+ * sq_prepare_weight -- the smoothing factor s and the int8 weights.
+ * Follows calibrate_smoothquant + SmoothQuantW8A8.freeze_quantization
+ * (page "w8a8_smoothquant.py"); calling it again with another alpha is
+ * recompute_smooth_scale.
+ *   mw_j     = max(max_o |w[o][j]|, 1e-8)
+ *   mx_j     = max(x_max_abs[j], 1e-8)
+ *   s_j      = max(f32(P(mx_j, alpha)) / f32(P(mw_j, 1 - alpha)), 1e-8)
+ *              with P(x, a) = x^a through binary64 (exact sqrt-based forms
+ *              for a in {0, 1/4, 1/2, 3/4, 1}, binary64 pow otherwise) and
+ *              1 - alpha formed in binary64
+ *   w~[o][j] = f32(w[o][j] * s_j)
+ *   w_scale[o] = max(max_j |w~[o][j]|, 1e-8) / 127
+ *   w_q[o][j]  = clamp(round_half_even(w~[o][j] / w_scale[o]), -128, 127)
+ *   w         [n][k] in wt (F32 or BF16), 16-byte aligned
+ *   x_max_abs [k] fp32 from sq_calibrate, or NULL: never calibrated, s = 1
+ *             and the call returns SQ_WARN_UNCALIBRATED (the page warns
+ *             "using s = 1" in that case)
+ *   alpha     in [0, 1]
+ *   smooth    [k] fp32 out (also used as scratch during the call)
+ *   w_q       [n][k] int8 out, 16-byte aligned
+ *   w_scale   [n] fp32 out
+ * n must be >= 1.
+ */
+sq_status sq_prepare_weight(const void* w, sq_dtype wt, int64_t n, int64_t k,
+                            const float* x_max_abs, float alpha, float* smooth,
+                            int8_t* w_q, float* w_scale, void* stream);
+
+/*
+ * sq_quantize_act -- dynamic per-token int8 of X / s.
+ * Follows SmoothQuantW8A8.forward (X_smooth = X / s, then
+ * quantize_per_token_symmetric), page "w8a8_smoothquant.py":
+ *   x~[t][j]   = f32(x[t][j] / smooth[j])
+ *   x_scale[t] = max(max_j |x~[t][j]|, 1e-8) / 127
+ *   x_q[t][j]  = clamp(round_half_even(x~[t][j] / x_scale[t]), -128, 127)
+ *   x       [m][k] in xt (F32 or BF16), 16-byte aligned
+ *   smooth  [k] fp32 from sq_prepare_weight (every s_j > 0)
+ *   x_q     [m][k] int8 out, 16-byte aligned
+ *   x_scale [m] fp32 out
+ */
+sq_status sq_quantize_act(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                          const float* smooth, int8_t* x_q, float* x_scale,
+                          void* stream);
+
+/*
+ * sq_w8a8_gemm -- the INT8 x INT8 -> INT32 product and its dequantisation.
+ * The page's forward multiplies the dequantised operands in fp32 and notes
+ * that real hardware does INT8 x INT8 -> INT32 -> fp32; this is that route:
+ *   acc[t][o] = sum_j x_q[t][j] * w_q[o][j]          (exact, int32)
+ *   y[t][o]   = acc[t][o] * x_scale[t] * w_scale[o] + bias[o]   (fp32, then
+ *               rounded to yt); the bias is added after the product
+ *   x_q     [m][k] int8, w_q [n][k] int8 (both 16-byte aligned)
+ *   x_scale [m] fp32, w_scale [n] fp32 (ignored when yt == SQ_I32)
+ *   bias    [n] in bias_t (F32 or BF16), or NULL for none
+ *   y       [m][n] in yt: SQ_F32, SQ_BF16 (round to nearest even) or SQ_I32
+ *           (raw acc; scales and bias are not applied), 16-byte aligned
+ */
+sq_status sq_w8a8_gemm(const int8_t* x_q, const float* x_scale, int64_t m,
+                       const int8_t* w_q, const float* w_scale, int64_t n,
+                       int64_t k, const void* bias, sq_dtype bias_t, void* y,
+                       sq_dtype yt, void* stream);
+
+/*
+ * sq_w8a8_linear -- one frozen forward: sq_quantize_act then sq_w8a8_gemm.
+ * Follows SmoothQuantW8A8.forward, quantized branch (page
+ * "w8a8_smoothquant.py"). The activation codes and scales are written to
+ * the caller's workspace, laid out as
+ *   [0, m*k)                      x_q  int8 [m][k]
+ *   [round_up(m*k, 256), +4*m)    x_scale fp32 [m]
+ * so they can be inspected after the call.
+ *   x         [m][k] in xt; bias [n] in xt or NULL; y [m][n] in yt
+ *   workspace device memory of at least sq_w8a8_linear_workspace_bytes(m, k)
+ *             bytes, 256-byte aligned
+ */
+sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                         const float* smooth, const int8_t* w_q,
+                         const float* w_scale, int64_t n, const void* bias,
+                         void* y, sq_dtype yt, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
+size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);
+
+/* A static, human-readable name for a status code. */
+const char* sq_status_string(sq_status status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define SQ_ABI_VERSION 1
+int sq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

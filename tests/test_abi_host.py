@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/sq.h declares, and every argument error returns its status
+before anything is launched."""
+import ctypes
+import subprocess
+
+import pytest
+
+from w8a8_quantized_linear_sq_amd import binding as B
+
+BAD = 0x1001          # a misaligned fake address (never dereferenced)
+OK_PTR = 0x10000      # an aligned fake address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    declared = B.header_functions()
+    assert set(declared) >= {"sq_calibrate", "sq_prepare_weight", "sq_quantize_act", "sq_w8a8_gemm",
+                             "sq_w8a8_linear", "sq_w8a8_linear_workspace_bytes", "sq_status_string",
+                             "sq_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        getattr(L, f)
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.sq_abi_version() == 1
+    for code in (0, 1, -1, -2, -3, -4, -5, -6):
+        s = B.status_string(code)
+        assert s.startswith("SQ_"), s
+    assert "unknown" in B.status_string(42)
+
+
+def test_workspace_bytes(L):
+    assert L.sq_w8a8_linear_workspace_bytes(0, 64) == 0
+    assert L.sq_w8a8_linear_workspace_bytes(3, 16) == 256 + 12
+    assert L.sq_w8a8_linear_workspace_bytes(4096, 4096) == 4096 * 4096 + 4 * 4096
+
+
+def test_calibrate_errors(L):
+    f = L.sq_calibrate
+    assert f(OK_PTR, 7, 4, 64, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_I32, 4, 64, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, -1, 64, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 0, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, B.SQ_MAX_K + 16, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 24, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(None, B.SQ_BF16, 4, 64, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, None, None) == B.SQ_ERR_ARG
+    assert f(BAD, B.SQ_BF16, 4, 64, OK_PTR, None) == B.SQ_ERR_ALIGN
+    # empty batch: a no-op that needs no pointer at all
+    assert f(None, B.SQ_BF16, 0, 64, None, None) == B.SQ_OK
+
+
+def test_prepare_weight_errors(L):
+    f = L.sq_prepare_weight
+    args = dict(w=OK_PTR, wt=B.SQ_BF16, n=8, k=64, mx=OK_PTR, alpha=0.5, s=OK_PTR, wq=OK_PTR, ws=OK_PTR)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["w"], a["wt"], a["n"], a["k"], a["mx"], a["alpha"], a["s"], a["wq"], a["ws"], None)
+
+    assert call(wt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=-16) == B.SQ_ERR_SHAPE
+    assert call(k=40) == B.SQ_ERR_ALIGN
+    for a in (-0.01, 1.01, float("nan"), float("inf")):
+        assert call(alpha=a) == B.SQ_ERR_ARG
+    for key in ("w", "s", "wq", "ws"):
+        assert call(**{key: None}) == B.SQ_ERR_ARG
+    for key in ("w", "s", "wq", "mx"):
+        assert call(**{key: BAD}) == B.SQ_ERR_ALIGN
+
+
+def test_quantize_act_errors(L):
+    f = L.sq_quantize_act
+    assert f(OK_PTR, 5, 4, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, -3, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 48 + 8, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(None, B.SQ_BF16, 0, 64, None, None, None, None) == B.SQ_OK
+
+
+def test_gemm_errors(L):
+    f = L.sq_w8a8_gemm
+
+    def call(xq=OK_PTR, sx=OK_PTR, m=4, wq=OK_PTR, sw=OK_PTR, n=8, k=64, bias=None, bt=B.SQ_F32, y=OK_PTR,
+             yt=B.SQ_BF16):
+        return f(xq, sx, m, wq, sw, n, k, bias, bt, y, yt, None)
+
+    assert call(yt=9) == B.SQ_ERR_DTYPE
+    assert call(bias=OK_PTR, bt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(m=-1) == B.SQ_ERR_SHAPE
+    assert call(k=8) == B.SQ_ERR_ALIGN
+    assert call(xq=None) == B.SQ_ERR_ARG
+    assert call(sx=None) == B.SQ_ERR_ARG
+    assert call(y=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0, xq=None, y=None) == B.SQ_OK
+
+
+def test_linear_errors(L):
+    f = L.sq_w8a8_linear
+    need = L.sq_w8a8_linear_workspace_bytes(4, 64)
+
+    def call(x=OK_PTR, xt=B.SQ_BF16, m=4, k=64, s=OK_PTR, wq=OK_PTR, sw=OK_PTR, n=8, bias=None, y=OK_PTR,
+             yt=B.SQ_BF16, ws=OK_PTR, wsb=need):
+        return f(x, xt, m, k, s, wq, sw, n, bias, y, yt, ws, wsb, None)
+
+    assert call(xt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=-2) == B.SQ_ERR_SHAPE
+    assert call(k=72) == B.SQ_ERR_ALIGN
+    assert call(x=None) == B.SQ_ERR_ARG
+    assert call(s=None) == B.SQ_ERR_ARG
+    assert call(ws=None) == B.SQ_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.SQ_ERR_WORKSPACE
+    assert call(ws=OK_PTR + 16) == B.SQ_ERR_ALIGN
+    assert call(x=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0, x=None, y=None, ws=None, wsb=0) == B.SQ_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

@@ -1,0 +1,272 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the
+C ABI, on seeded inputs. Bit-exact for maxima, s, scales, int8 codes and
+int32 accumulators; fp32 outputs within 1e-6 of |acc sx sw| + |bias|; bf16
+outputs within 1 bf16 ulp of the oracle's binary64 result rounded once."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (DEV, assert_bf16_within_one_ulp, assert_equal, assert_f32_rel, down,
+                      require_gpu, up)
+from w8a8_quantized_linear_sq_amd import binding as B
+from w8a8_quantized_linear_sq_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+# (m, n, k): single elements, ragged tails of every tile, K tails of 16/32/48,
+# several tiles, the widest K the block uses.
+SMALL = [(1, 1, 16), (3, 5, 32), (7, 17, 48), (17, 33, 272), (33, 7, 16), (130, 260, 528),
+         (257, 300, 1040), (64, 512, 4096), (5, 40, 11008), (300, 129, 2064)]
+ALPHAS = [0.0, 0.25, 0.5, 0.75, 1.0, 0.3, None]
+
+
+def _id(s):
+    return "x".join(map(str, s))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    B.lib()
+
+
+def _case(shape, dtype, seed=7, bias=True):
+    m, n, k = shape
+    return inputs.small(m, n, k, seed=seed + m + 3 * n + k, dtype=dtype, bias=bias)
+
+
+def upo(t):
+    return None if t is None else up(t)
+
+
+def _zeros(shape, dtype):
+    return torch.zeros(shape, dtype=dtype, device=DEV)
+
+
+# ---------------------------------------------------------------------------
+# a1: running column max of |X|
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_calibrate(orc, shape, dtype):
+    c = _case(shape, dtype)
+    x = up(c.x)
+    run = _zeros(c.k, torch.float32)
+    # three uneven batches, last one first
+    m = c.m
+    cuts = sorted({0, m, max(0, m // 3), max(0, (2 * m) // 3)})
+    for a, b in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        B.sq_calibrate(x[a:b], run)
+    B.sq_calibrate(x[:0], run)  # empty batch: no-op
+    torch.cuda.synchronize()
+    assert_equal(down(run), orc.calibrate(c.x.f32), "running max")
+
+
+# ---------------------------------------------------------------------------
+# a2-a5: s, int8 weights, weight scales
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("alpha", ALPHAS, ids=lambda a: f"a{a}")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SMALL[::2] + [(64, 512, 4096)], ids=_id)
+def test_prepare_weight(orc, shape, dtype, alpha):
+    c = _case(shape, dtype)
+    w = up(c.w)
+    w_np = c.w.f32.copy()
+    mx = orc.calibrate(c.x.f32)
+    smooth = _zeros(c.k, torch.float32)
+    wq = _zeros((c.n, c.k), torch.int8)
+    ws = _zeros(c.n, torch.float32)
+    st = B.sq_prepare_weight(w, None if alpha is None else up(mx), 0.5 if alpha is None else alpha,
+                             smooth, wq, ws)
+    torch.cuda.synchronize()
+    assert st == (B.SQ_WARN_UNCALIBRATED if alpha is None else B.SQ_OK)
+    s_gpu = down(smooth)
+    s_ref = orc.smoothing_factor(None if alpha is None else mx, orc.weight_col_max(w_np),
+                                 0.5 if alpha is None else alpha)
+    if alpha in (None, 0.0, 0.25, 0.5, 0.75, 1.0):
+        assert_equal(s_gpu, s_ref, "s")
+    else:
+        # alpha outside the exact forms: binary64 pow from two math libraries;
+        # s may differ in the last bit, and everything after s must follow it
+        ulps = np.abs(s_gpu.view(np.int32).astype(np.int64) - s_ref.view(np.int32))
+        assert ulps.max() <= 1
+    wq_ref, ws_ref = orc.quantize_rows(orc.smooth_weight(w_np, s_gpu))
+    assert_equal(down(ws), ws_ref, "w_scale")
+    assert_equal(down(wq), wq_ref, "w_q")
+
+
+# ---------------------------------------------------------------------------
+# a6-a7: per-token int8 of X / s
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_quantize_act(orc, shape, dtype):
+    c = _case(shape, dtype)
+    xf = c.x.f32.copy()
+    if c.m > 2:
+        xf[1] = 0.0  # an all-zero token: the floor decides its scale
+    xt = inputs.Tensor(xf, None if c.x.bits is None else inputs.bf16_bits(xf))
+    s, _, _ = orc.prepare_weight(c.w.f32, orc.calibrate(xf), 0.5)
+    xq = _zeros((c.m, c.k), torch.int8)
+    xs = _zeros(c.m, torch.float32)
+    B.sq_quantize_act(up(xt), up(s), xq, xs)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = orc.quantize_act(xf, s)
+    assert_equal(down(xs), xs_ref, "x_scale")
+    assert_equal(down(xq), xq_ref, "x_q")
+
+
+# ---------------------------------------------------------------------------
+# a8-a9: int8 GEMM, raw int32 and dequantised
+# ---------------------------------------------------------------------------
+def _codes(rng, r, k):
+    q = rng.integers(-127, 128, size=(r, k)).astype(np.int8)
+    if r > 1:
+        q[0] = -128  # extremes: |acc| = 128^2 k
+    return q
+
+
+GEMM_SHAPES = SMALL + [(256, 256, 64), (384, 640, 1024), (1000, 1000, 336)]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=_id)
+def test_gemm_int32(orc, shape):
+    m, n, k = shape
+    rng = np.random.default_rng(m * 7 + n * 13 + k)
+    a, b = _codes(rng, m, k), _codes(rng, n, k)
+    y = _zeros((m, n), torch.int32)
+    B.sq_w8a8_gemm(up(a), None, up(b), None, None, y)
+    torch.cuda.synchronize()
+    assert_equal(down(y), orc.int_gemm(a, b), "acc")
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 5, 32), (130, 260, 528), (257, 300, 1040), (1000, 1000, 336)], ids=_id)
+def test_gemm_dequant(orc, shape, out, bias):
+    m, n, k = shape
+    rng = np.random.default_rng(m + n + k)
+    a, b = _codes(rng, m, k), _codes(rng, n, k)
+    sx = (rng.random(m, dtype=np.float32) * np.float32(0.05)).astype(np.float32)
+    sw = (rng.random(n, dtype=np.float32) * np.float32(0.001)).astype(np.float32)
+    bias_t = bias_f = None
+    if bias is not None:
+        bf = rng.standard_normal(n, dtype=np.float32) * np.float32(3.0)
+        if bias == "bf16":
+            bits = inputs.bf16_bits(bf)
+            bias_f, bias_t = inputs.bf16_to_f32(bits), up(bits)
+        else:
+            bias_f, bias_t = bf, up(bf)
+    y = _zeros((m, n), torch.float32 if out == "f32" else torch.bfloat16)
+    B.sq_w8a8_gemm(up(a), up(sx), up(b), up(sw), bias_t, y)
+    torch.cuda.synchronize()
+    acc = orc.int_gemm(a, b)
+    yref = orc.dequant(acc, sx, sw, bias_f)
+    scale = np.abs(acc.astype(np.float64) * sx[:, None] * sw[None, :])
+    if bias_f is not None:
+        scale = scale + np.abs(bias_f)[None, :]
+    if out == "f32":
+        assert_f32_rel(down(y), yref, scale)
+    else:
+        assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
+
+
+# ---------------------------------------------------------------------------
+# a6-a9 in one call, with the workspace codes checked too
+# ---------------------------------------------------------------------------
+def _check_linear(orc, c, s, wq, sw, x_dev, bias_dev, out_dtype, rows=None):
+    m, n, k = c.m, c.n, c.k
+    y = _zeros((m, n), out_dtype)
+    ws = torch.empty(B.sq_w8a8_linear_workspace_bytes(m, k), dtype=torch.uint8, device=DEV)
+    B.sq_w8a8_linear(x_dev, up(s), up(wq), up(sw), bias_dev, y, ws)
+    torch.cuda.synchronize()
+    xq_gpu, xs_gpu = (down(t) for t in B.workspace_views(ws, m, k))
+    xq_ref, xs_ref = orc.quantize_act(c.x.f32, s)
+    assert_equal(xs_gpu, xs_ref, "x_scale (linear)")
+    assert_equal(xq_gpu, xq_ref, "x_q (linear)")
+    sel = np.arange(m) if rows is None else rows
+    acc = orc.int_gemm(xq_ref[sel], wq)
+    bias_f = None if c.bias is None else c.bias.f32
+    yref = orc.dequant(acc, xs_ref[sel], sw, bias_f)
+    ysel = down(y[torch.from_numpy(sel).to(DEV)])
+    scale = np.abs(acc.astype(np.float64) * xs_ref[sel][:, None] * sw[None, :])
+    if bias_f is not None:
+        scale = scale + np.abs(bias_f)[None, :]
+    if out_dtype == torch.float32:
+        assert_f32_rel(ysel, yref, scale)
+    else:
+        # without a bias nothing cancels: the strict 1-ulp bar applies
+        if bias_f is None:
+            assert_bf16_within_one_ulp(ysel, orc.to_bf16(yref))
+        else:
+            assert_bf16_within_one_ulp(ysel, orc.to_bf16(yref), yref, scale)
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_linear(orc, shape, dtype):
+    c = _case(shape, dtype)
+    s, wq, sw = orc.prepare_weight(c.w.f32, orc.calibrate(c.x.f32), 0.5)
+    out = torch.float32 if dtype == "f32" else torch.bfloat16
+    y1 = _check_linear(orc, c, s, wq, sw, up(c.x), upo(c.bias), out)
+    y2 = _check_linear(orc, c, s, wq, sw, up(c.x), upo(c.bias), out)
+    assert torch.equal(y1.view(torch.int16 if out == torch.bfloat16 else torch.int32),
+                       y2.view(torch.int16 if out == torch.bfloat16 else torch.int32)), "not deterministic"
+
+
+def test_golden_hand_example_on_gpu():
+    """The hand-derived example (ties included), padded to k = 16 with zero
+    channels (floored: s = 1 there, codes 0), through the whole GPU path."""
+    d = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_alpha_half.json")))
+    ex = d["expected"]
+    for dtype in ("f32", "bf16"):
+        x = np.zeros((3, 16), np.float32)
+        x[:, :4] = d["x"]
+        w = np.zeros((2, 16), np.float32)
+        w[:, :4] = d["w"]
+        b = np.array(d["bias"], np.float32)
+        xt = inputs.Tensor(x, inputs.bf16_bits(x) if dtype == "bf16" else None)
+        wt = inputs.Tensor(w, inputs.bf16_bits(w) if dtype == "bf16" else None)
+        bt = inputs.Tensor(b, inputs.bf16_bits(b) if dtype == "bf16" else None)
+        run = _zeros(16, torch.float32)
+        B.sq_calibrate(up(xt), run)
+        smooth, wq, ws = _zeros(16, torch.float32), _zeros((2, 16), torch.int8), _zeros(2, torch.float32)
+        B.sq_prepare_weight(up(wt), run, d["alpha"], smooth, wq, ws)
+        y = _zeros((3, 2), torch.float32)
+        wsp = torch.empty(B.sq_w8a8_linear_workspace_bytes(3, 16), dtype=torch.uint8, device=DEV)
+        B.sq_w8a8_linear(up(xt), smooth, wq, ws, up(bt), y, wsp)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(run)[:4], np.array(ex["mx"], np.float32))
+        assert np.array_equal(down(smooth), np.array(ex["s"] + [1.0] * 12, np.float32))
+        assert np.array_equal(down(wq)[:, :4], np.array(ex["wq"])) and not down(wq)[:, 4:].any()
+        xq, xs = (down(t) for t in B.workspace_views(wsp, 3, 16))
+        assert np.array_equal(xq[:, :4], np.array(ex["xq"])) and not xq[:, 4:].any()
+        assert np.array_equal(xs, np.array(ex["scale_x"], np.float32))
+        assert np.array_equal(down(y), np.array(ex["y"], np.float32))
+        yi = _zeros((3, 2), torch.int32)
+        B.sq_w8a8_gemm(up(xq), None, wq, None, None, yi)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(yi), np.array(ex["acc"]))
+
+
+def test_layer_lifecycle():
+    """The page's state machine on top of the ABI: calibrate -> freeze ->
+    forward; calibrating after the freeze raises."""
+    c = _case((40, 24, 64), "bf16")
+    layer = B.SmoothQuantLinear(up(c.w), upo(c.bias), alpha=0.5)
+    layer.calibrate(up(c.x)[:20])
+    layer.calibrate(up(c.x)[20:])
+    assert layer.freeze() == B.SQ_OK
+    with pytest.raises(RuntimeError):
+        layer.calibrate(up(c.x))
+    y = layer.forward(up(c.x))
+    assert y.shape == (40, 24) and y.dtype == torch.bfloat16
+    fresh = B.SmoothQuantLinear(up(c.w), None)
+    assert fresh.freeze() == B.SQ_WARN_UNCALIBRATED
+    assert torch.all(fresh.smooth == 1.0)

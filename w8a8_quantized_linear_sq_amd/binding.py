@@ -1,0 +1,243 @@
+"""ctypes binding of libsq.so (the C ABI in include/sq.h).
+
+Argument marshalling only: every step of the SmoothQuant W8A8 path runs in
+the HIP kernels behind the ABI. torch supplies device memory (``data_ptr``)
+and the stream (``torch.cuda.current_stream().cuda_stream``). The functions
+keep the ABI's names; sizes are read from the tensors' shapes.
+
+If libsq.so is missing this module raises at first use: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsq.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "sq.h")
+
+SQ_OK, SQ_WARN_UNCALIBRATED = 0, 1
+SQ_ERR_ARG, SQ_ERR_SHAPE, SQ_ERR_DTYPE, SQ_ERR_ALIGN, SQ_ERR_WORKSPACE, SQ_ERR_HIP = -1, -2, -3, -4, -5, -6
+SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
+SQ_MAX_K = 16384
+
+
+class SQError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+_P, _I64, _SZ, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_int
+
+_SIGNATURES = {
+    "sq_calibrate": ([_P, _E, _I64, _I64, _P, _P], _E),
+    "sq_prepare_weight": ([_P, _E, _I64, _I64, _P, _F, _P, _P, _P, _P], _E),
+    "sq_quantize_act": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
+    "sq_w8a8_gemm": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_w8a8_linear": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P, _SZ, _P], _E),
+    "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
+    "sq_status_string": ([_E], ctypes.c_char_p),
+    "sq_abi_version": ([], _E),
+}
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m w8a8_quantized_linear_sq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/sq.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().sq_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> int:
+    if status < 0:
+        raise SQError(fn, status, status_string(status))
+    return status
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SQ_F32
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    if t.dtype == torch.int32:
+        return SQ_I32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libsq must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream, t: torch.Tensor):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _need_dtype(t: torch.Tensor, dt, what):
+    if t.dtype != dt:
+        raise TypeError(f"{what} must be {dt}, got {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# the ABI, one wrapper per entry point
+# ---------------------------------------------------------------------------
+def sq_calibrate(x: torch.Tensor, running_max_abs: torch.Tensor, stream=None) -> int:
+    """running_max_abs[j] = max(running_max_abs[j], max_r |x[r, j]|)."""
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    _need_dtype(running_max_abs, torch.float32, "running_max_abs")
+    return _check("sq_calibrate", lib().sq_calibrate(_ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
+                                                     _stream(stream, x)))
+
+
+def sq_prepare_weight(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: float, smooth: torch.Tensor,
+                      w_q: torch.Tensor, w_scale: torch.Tensor, stream=None) -> int:
+    """s, int8 weights and per-output-channel scales (SQ_WARN_UNCALIBRATED
+    when x_max_abs is None)."""
+    n, k = w.shape
+    _need_dtype(smooth, torch.float32, "smooth")
+    _need_dtype(w_q, torch.int8, "w_q")
+    _need_dtype(w_scale, torch.float32, "w_scale")
+    if x_max_abs is not None:
+        _need_dtype(x_max_abs, torch.float32, "x_max_abs")
+    return _check("sq_prepare_weight",
+                  lib().sq_prepare_weight(_ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), float(alpha),
+                                          _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w)))
+
+
+def sq_quantize_act(x: torch.Tensor, smooth: torch.Tensor, x_q: torch.Tensor, x_scale: torch.Tensor,
+                    stream=None) -> int:
+    """Per-token int8 codes and scales of x / smooth."""
+    m, k = x.shape
+    _need_dtype(x_q, torch.int8, "x_q")
+    _need_dtype(x_scale, torch.float32, "x_scale")
+    return _check("sq_quantize_act",
+                  lib().sq_quantize_act(_ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(x_q), _ptr(x_scale),
+                                        _stream(stream, x)))
+
+
+def sq_w8a8_gemm(x_q: torch.Tensor, x_scale: torch.Tensor | None, w_q: torch.Tensor,
+                 w_scale: torch.Tensor | None, bias: torch.Tensor | None, y: torch.Tensor, stream=None) -> int:
+    """y = x_q w_q^T (int32), dequantised unless y is int32."""
+    m, k = x_q.shape
+    n = w_q.shape[0]
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _check("sq_w8a8_gemm",
+                  lib().sq_w8a8_gemm(_ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
+                                     _ptr(y), _dtype_code(y), _stream(stream, x_q)))
+
+
+def sq_w8a8_linear_workspace_bytes(m: int, k: int) -> int:
+    return lib().sq_w8a8_linear_workspace_bytes(m, k)
+
+
+def workspace_views(workspace: torch.Tensor, m: int, k: int):
+    """(x_q [m, k] int8, x_scale [m] fp32) views of a linear's workspace."""
+    off = (m * k + 255) // 256 * 256
+    xq = workspace[: m * k].view(torch.int8).view(m, k)
+    xs = workspace[off: off + 4 * m].view(torch.float32)
+    return xq, xs
+
+
+def sq_w8a8_linear(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                   bias: torch.Tensor | None, y: torch.Tensor, workspace: torch.Tensor, stream=None) -> int:
+    """One frozen forward (activation quantisation + int8 GEMM + dequant)."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    if bias is not None:
+        _need_dtype(bias, x.dtype, "bias")
+    nbytes = workspace.numel() * workspace.element_size()
+    return _check("sq_w8a8_linear",
+                  lib().sq_w8a8_linear(_ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale), n,
+                                       _ptr(bias), _ptr(y), _dtype_code(y), _ptr(workspace), nbytes,
+                                       _stream(stream, x)))
+
+
+# ---------------------------------------------------------------------------
+# The page's layer lifecycle on top of the ABI: calibrate -> freeze -> forward
+# (SmoothQuantW8A8 in "w8a8_smoothquant.py"). Buffers only; no arithmetic.
+# ---------------------------------------------------------------------------
+class SmoothQuantLinear:
+    """Holds a layer's buffers and drives the ABI in the page's order."""
+
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, alpha: float = 0.5):
+        if not weight.is_cuda:
+            raise ValueError("weight must be a device tensor")
+        self.weight = weight.contiguous()
+        self.bias = None if bias is None else bias.contiguous()
+        self.alpha = float(alpha)
+        n, k = self.weight.shape
+        dev = self.weight.device
+        self.calib_max_abs = torch.zeros(k, dtype=torch.float32, device=dev)
+        self.calib_count = 0
+        self.smooth = torch.ones(k, dtype=torch.float32, device=dev)
+        self.weight_int8 = torch.zeros((n, k), dtype=torch.int8, device=dev)
+        self.weight_scale = torch.ones(n, dtype=torch.float32, device=dev)
+        self.is_quantized = False
+
+    def calibrate(self, x: torch.Tensor) -> None:
+        if self.is_quantized:
+            raise RuntimeError("calibration after freeze is not allowed")
+        x2 = x.reshape(-1, x.shape[-1])
+        sq_calibrate(x2, self.calib_max_abs)
+        self.calib_count += x2.shape[0]
+
+    def freeze(self) -> int:
+        """Returns SQ_OK, or SQ_WARN_UNCALIBRATED when no batch was seen."""
+        mx = self.calib_max_abs if self.calib_count else None
+        st = sq_prepare_weight(self.weight, mx, self.alpha, self.smooth, self.weight_int8, self.weight_scale)
+        self.is_quantized = True
+        return st
+
+    def recompute(self, alpha: float) -> int:
+        """Re-smooth and re-quantise the weights for a new alpha."""
+        if not self.is_quantized:
+            raise RuntimeError("recompute before freeze")
+        self.alpha = float(alpha)
+        mx = self.calib_max_abs if self.calib_count else None
+        return sq_prepare_weight(self.weight, mx, self.alpha, self.smooth, self.weight_int8, self.weight_scale)
+
+    def forward(self, x: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+        if not self.is_quantized:
+            raise RuntimeError("forward before freeze")
+        shape = x.shape
+        x2 = x.reshape(-1, shape[-1]).contiguous()
+        m, k = x2.shape
+        n = self.weight_int8.shape[0]
+        y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+        ws = torch.empty(max(sq_w8a8_linear_workspace_bytes(m, k), 1), dtype=torch.uint8, device=x.device)
+        sq_w8a8_linear(x2, self.smooth, self.weight_int8, self.weight_scale, self.bias, y, ws)
+        return y.reshape(*shape[:-1], n)

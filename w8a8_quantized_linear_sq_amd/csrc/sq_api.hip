@@ -1,0 +1,155 @@
+// sq_api.hip -- the C ABI of libsq.so (declared in include/sq.h): argument
+// checks, then the kernel launches on the caller's stream. Nothing here
+// allocates, frees or synchronises.
+#include "../../include/sq.h"
+#include "sq_device.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool fp_in(sq_dtype t) { return t == SQ_F32 || t == SQ_BF16; }
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // m, n, rows: int32 tile indexing
+
+sq_status launched(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+// shared checks on k and a [.][k] pointer
+sq_status check_k(int64_t k) {
+    if (k <= 0 || k > SQ_MAX_K) return SQ_ERR_SHAPE;
+    if (k % 16) return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int sq_abi_version(void) { return SQ_ABI_VERSION; }
+
+const char* sq_status_string(sq_status s) {
+    switch (s) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_WARN_UNCALIBRATED: return "SQ_WARN_UNCALIBRATED: no calibration data, s = 1";
+        case SQ_ERR_ARG: return "SQ_ERR_ARG: null pointer, alpha outside [0, 1] or bad enum";
+        case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: size out of range";
+        case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: unsupported type";
+        case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: k not a multiple of 16 or pointer not 16-byte aligned";
+        case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP: a kernel launch failed";
+    }
+    return "unknown sq_status";
+}
+
+sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k, float* running_max_abs,
+                       void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (rows < 0 || rows > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (rows == 0) return SQ_OK;
+    if (!x || !running_max_abs) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(running_max_abs)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_colmax(x, xt == SQ_BF16, rows, k, running_max_abs, as_stream(stream)));
+}
+
+sq_status sq_prepare_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* x_max_abs,
+                            float alpha, float* smooth, int8_t* w_q, float* w_scale, void* stream) {
+    if (!fp_in(wt)) return SQ_ERR_DTYPE;
+    if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (!w || !smooth || !w_q || !w_scale) return SQ_ERR_ARG;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    if (x_max_abs && !aligned16(x_max_abs)) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    const int bf16 = wt == SQ_BF16;
+    hipError_t e;
+    if (!x_max_abs) {
+        e = sq_launch_fill(smooth, 1.0f, k, s);
+    } else {
+        // smooth <- column max of |W| (integer atomic max from zero), then s in place
+        e = sq_launch_fill(smooth, 0.0f, k, s);
+        if (e == hipSuccess) e = sq_launch_colmax(w, bf16, n, k, smooth, s);
+        if (e == hipSuccess) {
+            const double a_x = (double)alpha;
+            const double a_w = 1.0 - (double)alpha;
+            e = sq_launch_smooth_factor(x_max_abs, smooth, a_x, a_w, k, s);
+        }
+    }
+    if (e == hipSuccess) e = sq_launch_quantize_weight(w, bf16, smooth, n, k, w_q, w_scale, s);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
+}
+
+sq_status sq_quantize_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                          int8_t* x_q, float* x_scale, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (m == 0) return SQ_OK;
+    if (!x || !smooth || !x_q || !x_scale) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(smooth) || !aligned16(x_q)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_quantize_act(x, xt == SQ_BF16, smooth, m, k, x_q, x_scale, as_stream(stream)));
+}
+
+static sq_status check_gemm(const int8_t* x_q, const float* x_scale, int64_t m, const int8_t* w_q,
+                            const float* w_scale, int64_t n, int64_t k, const void* bias,
+                            sq_dtype bias_t, const void* y, sq_dtype yt) {
+    if (!(yt == SQ_F32 || yt == SQ_BF16 || yt == SQ_I32)) return SQ_ERR_DTYPE;
+    if (bias && !fp_in(bias_t)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (m == 0) return SQ_OK;
+    if (!x_q || !w_q || !y) return SQ_ERR_ARG;
+    if (yt != SQ_I32 && (!x_scale || !w_scale)) return SQ_ERR_ARG;
+    if (!aligned16(x_q) || !aligned16(w_q) || !aligned16(y)) return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+static int out_kind(sq_dtype yt) { return yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : 2; }
+static int bias_kind(const void* bias, sq_dtype bt) { return !bias ? 0 : bt == SQ_F32 ? 1 : 2; }
+
+sq_status sq_w8a8_gemm(const int8_t* x_q, const float* x_scale, int64_t m, const int8_t* w_q,
+                       const float* w_scale, int64_t n, int64_t k, const void* bias, sq_dtype bias_t,
+                       void* y, sq_dtype yt, void* stream) {
+    sq_status st = check_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    return launched(sq_launch_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
+                                   out_kind(yt), as_stream(stream)));
+}
+
+size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k) {
+    if (m <= 0 || k <= 0) return 0;
+    return round_up((size_t)m * (size_t)k, 256) + 4 * (size_t)m;
+}
+
+sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                         const int8_t* w_q, const float* w_scale, int64_t n, const void* bias, void* y,
+                         sq_dtype yt, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    // the workspace holds the codes, so check it as the gemm's x_q
+    int8_t* xq = (int8_t*)workspace;
+    float* xs = workspace ? (float*)((char*)workspace + round_up((size_t)(m > 0 ? m : 0) * (size_t)(k > 0 ? k : 0), 256))
+                          : nullptr;
+    sq_status st = check_gemm(xq ? xq : (const int8_t*)w_q, w_scale, m, w_q, w_scale, n, k, bias, xt, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    if (!x || !smooth) return SQ_ERR_ARG;
+    if (!workspace || workspace_bytes < sq_w8a8_linear_workspace_bytes(m, k)) return SQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return SQ_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = sq_launch_quantize_act(x, xt == SQ_BF16, smooth, m, k, xq, xs, s);
+    if (e == hipSuccess)
+        e = sq_launch_gemm(xq, xs, m, w_q, w_scale, n, k, bias, bias_kind(bias, xt), y, out_kind(yt), s);
+    return launched(e);
+}
+
+}  // extern "C"
