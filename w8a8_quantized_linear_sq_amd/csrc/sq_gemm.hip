@@ -8,51 +8,92 @@
 //   y[t][o]   = f32(acc) * sx[t] * sw[o] (+ bias[o])       (fp32 -> out type)
 //
 // Design (gfx950):
-//   * one 256-thread workgroup (4 wavefronts in a 2 x 2 grid) per BM x BN
-//     output tile; each wavefront owns a (BM/2) x (BN/2) block held in
-//     accumulation registers as 32 x 32 tiles of v_mfma_i32_32x32x32_i8;
-//   * K is walked in BK = 64-byte steps. A and B tiles go global -> registers
-//     -> LDS, double-buffered: the loads of step k+1 are in flight while the
-//     MFMAs of step k run, and one barrier per step separates the buffers;
-//   * LDS rows are padded to 80 bytes so that the 16-byte operand reads of
-//     a wavefront hit distinct banks;
+//   * one workgroup per BM x BN output tile; its wavefronts form a WGM x WGN
+//     grid and each owns a (BM/WGM) x (BN/WGN) block held in registers as
+//     32 x 32 tiles of v_mfma_i32_32x32x32_i8 (the 16x16x64 int8 form
+//     measures at half the rate on this chip). The 256 x 256 tile uses
+//     8 wavefronts (2 per SIMD) so that one can issue MFMAs while the other
+//     waits on LDS;
+//   * K advances in BK = 64-byte steps through a ring of 4 LDS stages filled
+//     by direct global -> LDS loads (global_load_lds_dwordx4: no VGPR
+//     staging, no LDS store instructions), issued three steps ahead;
+//   * a DMA load writes 64 lanes x 16 bytes contiguously, so the LDS rows
+//     (64 bytes) cannot be padded; instead chunk c of row r is stored at
+//     position c ^ swz(r), swz(r) = (r >> 2) & 3, under which the 16-byte
+//     operand reads of a wavefront (32 rows x 2 chunks) measure free of LDS
+//     bank conflicts on gfx950;
+//   * one barrier per step, placed between the two 32-byte k slices: after
+//     it every wavefront has a whole slice of MFMAs to issue (fragments
+//     already in registers) while the next stage's first fragments are read
+//     and the DMA of a later stage is issued;
 //   * rows past m or n are clamped for loading (their results are never
-//     stored); K-chunks past k are zero-filled;
+//     stored); a last partial K step goes through registers, zero-filled;
 //   * the 1-D grid is remapped so that the tiles dispatched to one XCD (the
 //     hardware deals workgroups round-robin over the 8 XCDs) form a compact
-//     block sharing A rows and B columns in that XCD's L2.
+//     block sharing A rows and B columns in that XCD's L2;
+//   * the epilogue stages each 32-row slab through LDS and writes whole
+//     16-byte row chunks.
 #include "sq_device.h"
+
+#include <type_traits>
 
 using namespace sq;
 
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 16;  // padded LDS row, bytes
+constexpr int kBK = 64;            // bytes of K per step
+constexpr int kStages = 4;         // LDS ring depth
 constexpr int kXcds = 8;
+constexpr int kSlices = kBK / 32;  // 32-byte k slices per step (one MFMA depth each)
+
+// Scheduling-group masks (instruction classes) of sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and does not wait on the other counters.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// Groups for one k slice: MF MFMAs with R LDS reads and V global loads
+// spread evenly between them (group I is MFMA number I).
+template <int I, int MF, int R, int V>
+__device__ __forceinline__ void sched_slice() {
+    constexpr int r = (I + 1) * R / MF - I * R / MF;
+    constexpr int v = (I + 1) * V / MF - I * V / MF;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, v, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (I + 1 < MF) sched_slice<I + 1, MF, R, V>();
+}
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // MFMA 32x32x32 i8 operand: lane l holds 16 k-consecutive bytes of row
 // (l % 32) at k offset 16 * (l / 32) of a 32-wide k slice; A and B use the
 // same mapping, so the hardware's pairing of bytes is the same for both.
 // Result: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 
-template <int BM, int BN, int OUT>
-__global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
+template <int BM, int BN, int WGM, int WGN, int OUT>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
     int bias_kind, void* __restrict__ Y, int grid_m, int grid_n) {
-    constexpr int WM = BM / 2, WN = BN / 2;  // per-wavefront block
+    constexpr int NW = WGM * WGN;                 // wavefronts (WGM x WGN grid)
+    constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wavefront block
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_CHUNKS = BM * (kBK / 16) / 256;  // 16-byte chunks per thread
-    constexpr int B_CHUNKS = BN * (kBK / 16) / 256;
-    __shared__ __attribute__((aligned(16))) int8_t smem[2 * (BM + BN) * kLdsRow];
-    int8_t* As = smem;                              // [2][BM][kLdsRow]
-    int8_t* Bs = smem + 2 * BM * kLdsRow;           // [2][BN][kLdsRow]
+    constexpr int STAGE = (BM + BN) * kBK;          // bytes of one LDS stage (A rows, then B rows)
+    constexpr int BLOCKS = (BM + BN) / 16;          // 1 KB DMA blocks per stage (16 rows each)
+    constexpr int LOADS = BLOCKS / NW;              // DMA loads per thread per stage
+    static_assert(BLOCKS % NW == 0, "stage must split evenly over the wavefronts");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     // ---- tile order: XCD-compact, then grouped along m --------------------
     const int total = grid_m * grid_n;
@@ -66,41 +107,42 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
     const int tile_n = (pid % group_size) / gm;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-    // ---- global -> register mapping: chunk c of row r ---------------------
-    const int ld_c = tid & 3;   // 16-byte chunk inside the 64-byte k step
-    const int ld_r = tid >> 2;  // first row; rows step by 64
-    const int8_t* a_ptr[A_CHUNKS];
-    const int8_t* b_ptr[B_CHUNKS];
+    // ---- DMA mapping: wave w fills blocks w, w + 4, ...; lane i of a block
+    // ---- writes LDS granule i = (row i / 4, position i % 4) and reads the
+    // ---- global chunk that position holds.
+    const int8_t* src[LOADS];
+    int dst[LOADS];
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        int r = min(m0 + ld_r + 64 * i, m - 1);
-        a_ptr[i] = A + (int64_t)r * k + ld_c * 16;
+    for (int q = 0; q < LOADS; ++q) {
+        const int blk = wave + NW * q;
+        const int row = blk * 16 + (lane >> 2);      // row in the A|B stage space
+        const int pos = lane & 3;
+        const int chunk = pos ^ swz(row);
+        const int8_t* g;
+        if (row < BM) g = A + (int64_t)min(m0 + row, m - 1) * k;
+        else g = B + (int64_t)min(n0 + row - BM, n - 1) * k;
+        src[q] = g + chunk * 16;
+        dst[q] = blk * 1024;
     }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-        int r = min(n0 + ld_r + 64 * i, n - 1);
-        b_ptr[i] = B + (int64_t)r * k + ld_c * 16;
-    }
-    i32x4 ra[A_CHUNKS], rb[B_CHUNKS];
-    auto load_tile = [&](int kt) {
+    auto issue_stage = [&](int kt, int buf) {
         const int kb = kt * kBK;
-        const bool ok = kb + ld_c * 16 < k;
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i)
-            ra[i] = ok ? *(const i32x4*)(a_ptr[i] + kb) : i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i)
-            rb[i] = ok ? *(const i32x4*)(b_ptr[i] + kb) : i32x4{0, 0, 0, 0};
+        for (int q = 0; q < LOADS; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(src[q] + kb), (lds_ptr_t)(smem + buf * STAGE + dst[q]),
+                                             16, 0, 0);
     };
-    auto store_tile = [&](int buf) {
-        int8_t* as = As + buf * BM * kLdsRow;
-        int8_t* bs = Bs + buf * BN * kLdsRow;
+    // a last partial step: the same layout through registers, chunks past k
+    // zero-filled
+    auto tail_stage = [&](int kt, int buf) {
+        const int kb = kt * kBK;
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i)
-            *(i32x4*)(as + (ld_r + 64 * i) * kLdsRow + ld_c * 16) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i)
-            *(i32x4*)(bs + (ld_r + 64 * i) * kLdsRow + ld_c * 16) = rb[i];
+        for (int q = 0; q < LOADS; ++q) {
+            const int row = (wave + NW * q) * 16 + (lane >> 2);
+            const int chunk = (lane & 3) ^ swz(row);
+            i32x4 v = {0, 0, 0, 0};
+            if (kb + chunk * 16 < k) v = *(const i32x4*)(src[q] + kb);
+            *(i32x4*)(smem + buf * STAGE + dst[q] + lane * 16) = v;
+        }
     };
 
     i32x16 acc[TM][TN];
@@ -109,48 +151,162 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = i32x16{};
 
-    const int KT = (k + kBK - 1) / kBK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // fragment offsets inside a stage: row (.. + fr), k chunk 2 s + lane / 32
+    const int fr = lane & 31;
+    int foff[kSlices];
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) foff[s] = fr * kBK + (((2 * s + (lane >> 5)) ^ swz(fr)) * 16);
+    static_assert(kSlices == 2, "the step below is written for two k slices");
 
-    const int fr = lane & 31;          // operand row inside a 32-row slice
-    const int fk = (lane >> 5) * 16;   // operand k offset inside a 32-wide slice
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_tile(kt + 1);
-        const int8_t* as = As + cur * BM * kLdsRow + (wm * WM + fr) * kLdsRow + fk;
-        const int8_t* bs = Bs + cur * BN * kLdsRow + (wn * WN + fr) * kLdsRow + fk;
+    i32x4 f0a[TM], f0b[TN], f1a[TM], f1b[TN];  // fragments of slice 0 / slice 1
+    auto read_frags = [&](int buf, int s, i32x4 (&fa)[TM], i32x4 (&fb)[TN]) {
+        const int8_t* as = smem + buf * STAGE + (wm * WM) * kBK + foff[s];
+        const int8_t* bs = smem + buf * STAGE + (BM + wn * WN) * kBK + foff[s];
 #pragma unroll
-        for (int ks = 0; ks < kBK; ks += 32) {
-            i32x4 fa[TM], fb[TN];
+        for (int i = 0; i < TM; ++i) fa[i] = *(const i32x4*)(as + i * 32 * kBK);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i] = *(const i32x4*)(as + i * 32 * kLdsRow + ks);
+        for (int j = 0; j < TN; ++j) fb[j] = *(const i32x4*)(bs + j * 32 * kBK);
+    };
+    auto mfmas = [&](const i32x4 (&fa)[TM], const i32x4 (&fb)[TN]) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = *(const i32x4*)(bs + j * 32 * kLdsRow + ks);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    constexpr int MF = TM * TN, R = TM + TN;
+    // wait until at most n DMA loads per thread are outstanding, then the
+    // workgroup barrier (a bare s_barrier: __syncthreads would also drain
+    // every later stage)
+    auto wait_barrier = [&](int n_later_stages) {
+        if (n_later_stages >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+        else if (n_later_stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // ---- main loop -----------------------------------------------------------
+    // Step kt, with the slice-0 fragments of stage kt already in registers:
+    //   phase 1: MFMAs of slice 0, while slice 1 of stage kt is read;
+    //   barrier: stage kt+1 is complete and visible, and every wavefront has
+    //            finished reading stage kt-1's buffer;
+    //   phase 2: MFMAs of slice 1, while slice 0 of stage kt+1 is read and
+    //            the DMA of stage kt+3 into stage kt-1's buffer is issued.
+    // Right after the barrier every wavefront has a full slice of MFMAs to
+    // issue, which covers the LDS latency of the next fragments.
+    const int KF = k / kBK;  // whole steps
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int st = 0; st < kStages - 1; ++st)
+        if (st < KF) issue_stage(st, st);
+    if (KF > 0) {
+        wait_barrier(min(KF - 1, kStages - 2));
+        read_frags(0, 0, f0a, f0b);
+    }
+    int kt = 0;
+    for (; kt + kStages - 1 < KF; ++kt) {
+        const int buf = kt % kStages;
+        read_frags(buf, 1, f1a, f1b);
+        mfmas(f0a, f0b);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+        sched_slice<0, MF, 0, 0>();
+        wait_barrier(1);
+        read_frags((kt + 1) % kStages, 0, f0a, f0b);
+        issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        mfmas(f1a, f1b);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+        sched_slice<0, MF, 0, LOADS>();
+    }
+    for (; kt < KF; ++kt) {
+        const int buf = kt % kStages;
+        read_frags(buf, 1, f1a, f1b);
+        mfmas(f0a, f0b);
+        if (kt + 1 < KF) {
+            wait_barrier(KF - 2 - kt);
+            read_frags((kt + 1) % kStages, 0, f0a, f0b);
         }
-        if (kt + 1 < KT) store_tile(cur ^ 1);
+        mfmas(f1a, f1b);
+    }
+    if (k % kBK) {
+        // a last partial step: its buffer was last read kStages steps ago
         __syncthreads();
+        tail_stage(KF, KF % kStages);
+        __syncthreads();
+        read_frags(KF % kStages, 0, f0a, f0b);
+        read_frags(KF % kStages, 1, f1a, f1b);
+        mfmas(f0a, f0b);
+        mfmas(f1a, f1b);
     }
 
     // ---- epilogue ---------------------------------------------------------
+    // y = f32(acc) * sa[row] * sb[col] (+ bias[col]) in the MFMA layout, then
+    // (whole tiles) staged per 32-row slab through this wavefront's own LDS
+    // region and written as 16-byte row chunks.
     const int ecol = lane & 31;
     const int erow = (lane >> 5) * 4;
+    float swc[TN], bc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int col = min(n0 + wn * WN + j * 32 + ecol, n - 1);
+        swc[j] = 0.0f;
+        bc[j] = 0.0f;
+        if constexpr (OUT != 2) {
+            swc[j] = sb[col];
+            if (bias_kind == 1) bc[j] = ((const float*)bias)[col];
+            else if (bias_kind == 2) bc[j] = __uint_as_float((uint32_t)((const uint16_t*)bias)[col] << 16);
+        }
+    }
+    auto value = [&](int i, int j, int r, float sar) -> float {
+        float y = (float)acc[i][j][r] * sar * swc[j];
+        if (bias_kind) y = y + bc[j];
+        return y;
+    };
+    constexpr int OB = OUT == 1 ? 2 : 4;            // output bytes per element
+    constexpr int PITCH = WN * OB + 32;             // staged row, bytes (bank-spread)
+    constexpr int ROW_CHUNKS = WN * OB / 16;        // 16-byte chunks per staged row
+    constexpr int SLAB_CHUNKS = 32 * ROW_CHUNKS;
+    static_assert(NW * 32 * PITCH <= (int)sizeof(smem), "epilogue staging exceeds LDS");
+    const bool whole = (m0 + BM <= m) && (n0 + BN <= n) && (n % (16 / OB) == 0) &&
+                       (((uintptr_t)sa & 15) == 0) && (((uintptr_t)Y & 15) == 0);
+    if (whole) {
+        __syncthreads();  // every wavefront is done with the operand buffers
+        int8_t* stage = smem + wave * 32 * PITCH;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int rbase = m0 + wm * WM + i * 32;
+            float sar[4][4];
+            if constexpr (OUT != 2) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *(const float4*)(sa + rbase + q * 8 + erow);
+                    sar[q][0] = v.x; sar[q][1] = v.y; sar[q][2] = v.z; sar[q][3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = (r >> 2) * 8 + erow + (r & 3);
+                    int8_t* dst = stage + lr * PITCH + (j * 32 + ecol) * OB;
+                    if constexpr (OUT == 2) *(int*)dst = acc[i][j][r];
+                    else if constexpr (OUT == 0) *(float*)dst = value(i, j, r, sar[r >> 2][r & 3]);
+                    else *(__bf16*)dst = (__bf16)value(i, j, r, sar[r >> 2][r & 3]);
+                }
+            }
+            // the same wavefront reads back what it wrote: LDS keeps its order
+#pragma unroll
+            for (int c = lane; c < SLAB_CHUNKS; c += 64) {
+                const int lr = c / ROW_CHUNKS, cc = c % ROW_CHUNKS;
+                const i32x4 v = *(const i32x4*)(stage + lr * PITCH + cc * 16);
+                int8_t* out = (int8_t*)Y + ((int64_t)(rbase + lr) * n + n0 + wn * WN) * OB + cc * 16;
+                *(i32x4*)out = v;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int col = n0 + wn * WN + j * 32 + ecol;
         if (col >= n) continue;
-        float swc = 0.0f, bc = 0.0f;
-        if constexpr (OUT != 2) {
-            swc = sb[col];
-            if (bias_kind == 1) bc = ((const float*)bias)[col];
-            else if (bias_kind == 2) bc = __uint_as_float((uint32_t)((const uint16_t*)bias)[col] << 16);
-        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -158,12 +314,10 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
                 const int row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + erow + (r & 3);
                 if (row >= m) continue;
                 const int64_t off = (int64_t)row * n + col;
-                const int a = acc[i][j][r];
                 if constexpr (OUT == 2) {
-                    ((int*)Y)[off] = a;
+                    ((int*)Y)[off] = acc[i][j][r];
                 } else {
-                    float y = (float)a * sa[row] * swc;
-                    if (bias_kind) y = y + bc;
+                    const float y = value(i, j, r, sa[row]);
                     if constexpr (OUT == 0) ((float*)Y)[off] = y;
                     else ((__bf16*)Y)[off] = (__bf16)y;
                 }
@@ -172,23 +326,23 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
                        int n, int k, const void* bias, int bias_kind, void* y, int out_kind,
                        hipStream_t st) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
-    dim3 grid(gm * gn), block(256);
+    dim3 grid(gm * gn), block(64 * WGM * WGN);
     switch (out_kind) {
         case 0:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, 0>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
+            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 0>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
                                bias, bias_kind, y, gm, gn);
             break;
         case 1:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, 1>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
+            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 1>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
                                bias, bias_kind, y, gm, gn);
             break;
         default:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, 2>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
+            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 2>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
                                bias, bias_kind, y, gm, gn);
             break;
     }
@@ -219,8 +373,8 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
     }
     const int mi = (int)m, ni = (int)n, ki = (int)k;
     switch (best) {
-        case 0: return launch_tile<256, 256>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        case 1: return launch_tile<128, 256>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        default: return launch_tile<128, 128>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
+        case 0: return launch_tile<256, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
+        case 1: return launch_tile<128, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
+        default: return launch_tile<128, 128, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
     }
 }
