@@ -98,7 +98,8 @@ sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k,
  *             "using s = 1" in that case)
  *   alpha     in [0, 1]
  *   smooth    [k] fp32 out (also used as scratch during the call)
- *   w_q       [n][k] int8 out, 16-byte aligned
+ *   w_q       [n][k] int8 out, 16-byte aligned (also used as scratch for
+ *             the per-row-group column maxima before the codes are written)
  *   w_scale   [n] fp32 out
  * n must be >= 1.
  */
@@ -157,6 +158,32 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k,
                          const float* w_scale, int64_t n, const void* bias,
                          void* y, sq_dtype yt, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * sq_selfcheck_reciprocal -- device self-check behind the activation path.
+ * For bf16 activations, sq_quantize_act / sq_w8a8_linear form x / s as
+ * fma(fma(-q0, s, x), y, q0) with q0 = x * y and y the correctly rounded
+ * 1/s, obtained from the hardware reciprocal and one Newton step. This call
+ * counts, over every binary32 s in [2^-100, 2^100), the values for which
+ * that y differs from the IEEE quotient 1/s, and adds the count to
+ * *mismatches (a device uint64 the caller zeroes). 0 on the running device
+ * is the precondition of the fast path's exactness.
+ */
+sq_status sq_selfcheck_reciprocal(unsigned long long* mismatches, void* stream);
+
+/*
+ * sq_selfcheck_division -- device self-check behind every binary32 quotient
+ * of the quantisation kernels. They divide a by b as q0 = RN(a * y),
+ * q1 = fma(fma(-q0, b, a), y, q0) with y = RN(1/b). For the divisor
+ * significands m in [b_begin, b_end) (b = 1 + m * 2^-23, m < 2^23) and
+ * every numerator significand a in [1, 2), this call adds to *mismatches
+ * the count of pairs where q1 differs from the IEEE quotient a / b (the
+ * whole range, 2^46 pairs, takes some tens of seconds). Powers of two scale
+ * every step exactly, so 0 over the whole range makes the scheme exact for
+ * all operands whose steps stay in the normal range.
+ */
+sq_status sq_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
+                                void* stream);
 
 /* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);

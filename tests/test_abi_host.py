@@ -21,7 +21,7 @@ def test_exports_every_declared_function(L):
     declared = B.header_functions()
     assert set(declared) >= {"sq_calibrate", "sq_prepare_weight", "sq_quantize_act", "sq_w8a8_gemm",
                              "sq_w8a8_linear", "sq_w8a8_linear_workspace_bytes", "sq_status_string",
-                             "sq_abi_version"}
+                             "sq_abi_version", "sq_selfcheck_reciprocal", "sq_selfcheck_division"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -126,6 +126,15 @@ def test_linear_errors(L):
     assert call(ws=OK_PTR + 16) == B.SQ_ERR_ALIGN
     assert call(x=BAD) == B.SQ_ERR_ALIGN
     assert call(m=0, x=None, y=None, ws=None, wsb=0) == B.SQ_OK
+
+
+def test_selfcheck_errors(L):
+    assert L.sq_selfcheck_reciprocal(None, None) == B.SQ_ERR_ARG
+    assert L.sq_selfcheck_reciprocal(OK_PTR + 4, None) == B.SQ_ERR_ALIGN
+    assert L.sq_selfcheck_division(0, 16, None, None) == B.SQ_ERR_ARG
+    assert L.sq_selfcheck_division(0, 16, OK_PTR + 4, None) == B.SQ_ERR_ALIGN
+    assert L.sq_selfcheck_division(8, 4, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert L.sq_selfcheck_division(0, (1 << 23) + 1, OK_PTR, None) == B.SQ_ERR_SHAPE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

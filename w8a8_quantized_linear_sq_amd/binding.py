@@ -42,6 +42,8 @@ _SIGNATURES = {
     "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
     "sq_status_string": ([_E], ctypes.c_char_p),
     "sq_abi_version": ([], _E),
+    "sq_selfcheck_reciprocal": ([_P, _P], _E),
+    "sq_selfcheck_division": ([ctypes.c_uint, ctypes.c_uint, _P, _P], _E),
 }
 
 _lib: ctypes.CDLL | None = None
@@ -158,6 +160,22 @@ def sq_w8a8_gemm(x_q: torch.Tensor, x_scale: torch.Tensor | None, w_q: torch.Ten
     return _check("sq_w8a8_gemm",
                   lib().sq_w8a8_gemm(_ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
                                      _ptr(y), _dtype_code(y), _stream(stream, x_q)))
+
+
+def sq_selfcheck_reciprocal(mismatches: torch.Tensor, stream=None) -> int:
+    """Adds to mismatches[0] (int64, device) the count of s in [2^-100, 2^100)
+    whose kernel reciprocal differs from the IEEE 1/s."""
+    _need_dtype(mismatches, torch.int64, "mismatches")
+    return _check("sq_selfcheck_reciprocal",
+                  lib().sq_selfcheck_reciprocal(_ptr(mismatches), _stream(stream, mismatches)))
+
+
+def sq_selfcheck_division(b_begin: int, b_end: int, mismatches: torch.Tensor, stream=None) -> int:
+    """Adds to mismatches[0] (int64, device) the count of significand pairs
+    (divisors [b_begin, b_end)) whose kernel quotient differs from IEEE a/b."""
+    _need_dtype(mismatches, torch.int64, "mismatches")
+    return _check("sq_selfcheck_division",
+                  lib().sq_selfcheck_division(b_begin, b_end, _ptr(mismatches), _stream(stream, mismatches)))
 
 
 def sq_w8a8_linear_workspace_bytes(m: int, k: int) -> int:

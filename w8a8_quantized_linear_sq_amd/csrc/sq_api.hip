@@ -73,13 +73,15 @@ sq_status sq_prepare_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, co
     if (!x_max_abs) {
         e = sq_launch_fill(smooth, 1.0f, k, s);
     } else {
-        // smooth <- column max of |W| (integer atomic max from zero), then s in place
-        e = sq_launch_fill(smooth, 0.0f, k, s);
-        if (e == hipSuccess) e = sq_launch_colmax(w, bf16, n, k, smooth, s);
+        // column max of |W| per row group into a buffer the call overwrites
+        // later anyway (w_q, or smooth itself for a single group), then s
+        const int64_t groups = sq_colmax_partial_groups(n, k, bf16, n * k);
+        unsigned* partial = groups == 1 ? (unsigned*)smooth : (unsigned*)w_q;
+        e = sq_launch_colmax_partial(w, bf16, n, k, groups, partial, s);
         if (e == hipSuccess) {
             const double a_x = (double)alpha;
             const double a_w = 1.0 - (double)alpha;
-            e = sq_launch_smooth_factor(x_max_abs, smooth, a_x, a_w, k, s);
+            e = sq_launch_smooth_factor(x_max_abs, partial, groups, a_x, a_w, k, smooth, s);
         }
     }
     if (e == hipSuccess) e = sq_launch_quantize_weight(w, bf16, smooth, n, k, w_q, w_scale, s);
@@ -124,6 +126,20 @@ sq_status sq_w8a8_gemm(const int8_t* x_q, const float* x_scale, int64_t m, const
     if (st != SQ_OK || m == 0) return st;
     return launched(sq_launch_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
                                    out_kind(yt), as_stream(stream)));
+}
+
+sq_status sq_selfcheck_reciprocal(unsigned long long* mismatches, void* stream) {
+    if (!mismatches) return SQ_ERR_ARG;
+    if (((uintptr_t)mismatches & 7u) != 0) return SQ_ERR_ALIGN;
+    return launched(sq_launch_selfcheck_reciprocal(mismatches, as_stream(stream)));
+}
+
+sq_status sq_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
+                                void* stream) {
+    if (!mismatches) return SQ_ERR_ARG;
+    if (((uintptr_t)mismatches & 7u) != 0) return SQ_ERR_ALIGN;
+    if (b_begin > b_end || b_end > (1u << 23)) return SQ_ERR_SHAPE;
+    return launched(sq_launch_selfcheck_division(b_begin, b_end, mismatches, as_stream(stream)));
 }
 
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k) {

@@ -27,40 +27,34 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// round_half_even(v / scale) clamped to [-128, 127], where rs = RN(1/scale).
-// RN(v * rs) is within 2^-15.9 of v / scale for |v / scale| <= 127.00002
-// (two binary32 roundings of a quotient below 2^7). When that approximation
-// lies more than 2^-14 away from every half-integer, the correctly rounded
-// quotient lies on the same side of the same half-integers and rounds to
-// the same integer; otherwise the exact IEEE quotient decides.
-__device__ __forceinline__ float code_of(float v, float scale, float rs) {
-    float q = v * rs;
-    float c = __builtin_rintf(q);
-    float d = q - c;  // exact (Sterbenz)
-    if (__builtin_fabsf(d) >= 0.5f - 0x1p-14f) c = __builtin_rintf(v / scale);
-    return __builtin_fminf(__builtin_fmaxf(c, -128.0f), 127.0f);
-}
-
-// Four codes (already integral floats in [-128, 127]) -> one packed dword.
-__device__ __forceinline__ uint32_t pack4(float c0, float c1, float c2, float c3) {
-    uint32_t b0 = (uint32_t)(int)c0 & 0xffu, b1 = (uint32_t)(int)c1 & 0xffu;
-    uint32_t b2 = (uint32_t)(int)c2 & 0xffu, b3 = (uint32_t)(int)c3 & 0xffu;
-    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-}
-
 }  // namespace sq
 
 // ---- launchers (host side), one per kernel family; each returns the
 // ---- hipError_t of its launch.
 hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st);
-hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k,
-                            float* out_max, hipStream_t st);
-hipError_t sq_launch_smooth_factor(const float* x_max, float* io, double a_x, double a_w,
-                                   int64_t k, hipStream_t st);
+// running column max of |x| folded into running_max (calibration)
+hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
+                            hipStream_t st);
+// row groups for a partial column max whose [groups][k] uint32 result must
+// fit in scratch_bytes (at least 1)
+int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes);
+// partial[g][j] = max over row group g of |x[.][j]| (binary32 bit patterns)
+hipError_t sq_launch_colmax_partial(const void* x, int bf16, int64_t rows, int64_t k, int64_t groups,
+                                    unsigned* partial, hipStream_t st);
+// s[j] from x_max[j] and the max over groups of partial[.][j]; partial may
+// alias s when groups == 1
+hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, int64_t groups, double a_x,
+                                   double a_w, int64_t k, float* s, hipStream_t st);
 hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, int64_t n,
                                      int64_t k, int8_t* wq, float* w_scale, hipStream_t st);
 hipError_t sq_launch_quantize_act(const void* x, int bf16, const float* s, int64_t m, int64_t k,
                                   int8_t* xq, float* x_scale, hipStream_t st);
+// counts s in [2^-100, 2^100) whose kernel reciprocal differs from IEEE 1/s
+hipError_t sq_launch_selfcheck_reciprocal(unsigned long long* mismatches, hipStream_t st);
+// counts significand pairs (divisors [b_begin, b_end)) where the kernels'
+// quotient differs from IEEE a / b
+hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
+                                        hipStream_t st);
 // out_kind: 0 fp32, 1 bf16, 2 int32; bias_kind: 0 none, 1 fp32, 2 bf16
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,

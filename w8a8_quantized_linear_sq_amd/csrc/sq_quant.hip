@@ -2,14 +2,23 @@
 // (page "w8a8_smoothquant.py", BiGRU_T_version):
 //   * column max-abs reduction (SmoothQuantW8A8.calibrate's running max, and
 //     calibrate_smoothquant's max over output rows of |W|);
-//   * the smoothing factor s (calibrate_smoothquant);
-//   * smoothing + per-output-channel int8 of the weights
-//     (freeze_quantization -> quantize_per_channel_symmetric);
-//   * smoothing + per-token int8 of the activations
-//     (forward -> X / s -> quantize_per_token_symmetric).
+//   * the smoothing factor s (calibrate_smoothquant), fused into the last
+//     stage of the weight column max;
+//   * smoothing + symmetric int8 of rows: weights W * s with one scale per
+//     output channel (freeze_quantization -> quantize_per_channel_symmetric)
+//     and activations X / s with one scale per token (forward ->
+//     quantize_per_token_symmetric).
 #include "sq_device.h"
 
 using namespace sq;
+
+// max of the two 16-bit halves of a and b, independently (magnitudes of
+// bf16 pairs: integer order is value order)
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    const uint32_t lo = max(a & 0xffffu, b & 0xffffu);
+    const uint32_t hi = max(a >> 16, b >> 16);
+    return lo | (hi << 16);
+}
 
 // ---------------------------------------------------------------------------
 // fill
@@ -27,100 +36,150 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Column max of |x| over rows, folded into out[] with an integer atomic max.
-// |x| is non-negative, so the order of the binary32 bit patterns as unsigned
-// integers is the order of the values: the fold is exact and independent of
-// the order in which blocks run.
-// Each thread owns one 16-byte column chunk (8 bf16 or 4 fp32 columns) and
-// walks `rows_per_block` rows; a block is 256 chunks wide.
+// Column max of |x| over a group of rows.
+// Block = 4 wavefronts over one strip of 64 16-byte column chunks (512 bf16
+// or 256 fp32 columns); wavefront w takes rows w, w+4, ... of the group with
+// 8 loads in flight; the 4 partial maxima meet in LDS. |x| >= 0, so the
+// order of the binary32 bit patterns as unsigned integers is the order of
+// the values: every max is an exact integer max, independent of order.
+//   FOLD:    out[j] = max(out[j], max) -- one row group: the owning thread
+//            updates in place; several: integer atomicMax (the running max of
+//            calibration keeps its value across calls);
+//   PARTIAL: out[g * k + j] = max over row group g (plain stores).
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x, int64_t rows,
-                                                     int64_t kvec, int rows_per_block,
+template <bool BF16, bool FOLD>
+__global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
+                                                     int64_t rows_per_group, int64_t k,
                                                      unsigned* __restrict__ out) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= kvec) return;
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-    int64_t r1 = r0 + rows_per_block;
-    if (r1 > rows) r1 = rows;
+    constexpr int U = 8;
+    __shared__ u32x4 red[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_group;
+    const int64_t r1 = min(r0 + rows_per_group, rows);
     constexpr uint32_t kMask = BF16 ? 0x7fff7fffu : 0x7fffffffu;
-    u32x4 m0 = {0, 0, 0, 0}, m1 = {0, 0, 0, 0};
-    int64_t r = r0;
-    // four rows in flight per thread
-    for (; r + 4 <= r1; r += 4) {
-        u32x4 v0 = x[(r + 0) * kvec + c];
-        u32x4 v1 = x[(r + 1) * kvec + c];
-        u32x4 v2 = x[(r + 2) * kvec + c];
-        u32x4 v3 = x[(r + 3) * kvec + c];
-        if constexpr (BF16) {
+    u32x4 m = {0, 0, 0, 0};
+    auto fold = [&](u32x4 v) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t a0 = v0[i] & kMask, a1 = v1[i] & kMask, a2 = v2[i] & kMask, a3 = v3[i] & kMask;
-                uint32_t lo = max(max(a0 & 0xffffu, a1 & 0xffffu), max(a2 & 0xffffu, a3 & 0xffffu));
-                uint32_t hi = max(max(a0 >> 16, a1 >> 16), max(a2 >> 16, a3 >> 16));
-                m0[i] = max(m0[i], lo);
-                m1[i] = max(m1[i], hi);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a = v[i] & kMask;
+            if constexpr (BF16) m[i] = max_u16x2(m[i], a);
+            else m[i] = max(m[i], a);
+        }
+    };
+    if (c < kvec) {
+        int64_t r = r0 + wave;
+        for (; r + 4 * (U - 1) < r1; r += 4 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = x[(r + 4 * u) * kvec + c];
+#pragma unroll
+            for (int u = 0; u < U; ++u) fold(v[u]);
+        }
+        for (; r < r1; r += 4) fold(x[r * kvec + c]);
+    }
+    red[wave][lane] = m;
+    __syncthreads();
+    if (wave != 0 || c >= kvec) return;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        const u32x4 o = red[w][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BF16) m[i] = max_u16x2(m[i], o[i]);
+            else m[i] = max(m[i], o[i]);
+        }
+    }
+    // the chunk's columns as binary32 bit patterns
+    constexpr int NC = BF16 ? 8 : 4;
+    uint32_t val[NC];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+            val[2 * i] = m[i] << 16;
+            val[2 * i + 1] = m[i] & 0xffff0000u;
+        } else {
+            val[i] = m[i];
+        }
+    }
+    const int64_t col0 = c * NC;
+    if constexpr (FOLD) {
+        if (gridDim.y == 1) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) out[col0 + i] = max(out[col0 + i], val[i]);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                m0[i] = max(m0[i], max(max(v0[i] & kMask, v1[i] & kMask), max(v2[i] & kMask, v3[i] & kMask)));
-        }
-    }
-    for (; r < r1; ++r) {
-        u32x4 v0 = x[r * kvec + c];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t a0 = v0[i] & kMask;
-            if constexpr (BF16) {
-                m0[i] = max(m0[i], a0 & 0xffffu);
-                m1[i] = max(m1[i], a0 >> 16);
-            } else {
-                m0[i] = max(m0[i], a0);
-            }
-        }
-    }
-    if constexpr (BF16) {
-        unsigned* o = out + c * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            atomicMax(o + 2 * i, m0[i] << 16);
-            atomicMax(o + 2 * i + 1, m1[i] << 16);
+            for (int i = 0; i < NC; ++i) atomicMax(out + col0 + i, val[i]);
         }
     } else {
-        unsigned* o = out + c * 4;
+        unsigned* o = out + (int64_t)blockIdx.y * k + col0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicMax(o + i, m0[i]);
+        for (int i = 0; i < NC; i += 4) *(u32x4*)(o + i) = u32x4{val[i], val[i + 1], val[i + 2], val[i + 3]};
     }
 }
 
-hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, float* out_max,
-                            hipStream_t st) {
-    if (rows <= 0) return hipSuccess;
+// Row groups for a column max over `rows` rows: enough blocks to keep HBM
+// busy (about 1024) but at least 128 rows per group, so that a column gets
+// few partial maxima (atomics when folding, partials when reducing).
+static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups, int64_t& rpg) {
+    gx = (kvec + 63) / 64;
+    int64_t want = 1024 / gx;
+    if (want < 1) want = 1;
+    groups = (rows + 127) / 128;
+    if (groups > want) groups = want;
+    if (groups < 1) groups = 1;
+    rpg = (rows + groups - 1) / groups;
+    groups = (rows + rpg - 1) / rpg;
+}
+
+template <bool FOLD>
+static hipError_t launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, unsigned* out, int64_t groups,
+                                int64_t rpg, hipStream_t st) {
     const int64_t kvec = bf16 ? k / 8 : k / 4;
-    const int64_t gx = (kvec + 255) / 256;
-    // about 1024 blocks in all, at least 4 rows each
-    int64_t gy = 1024 / gx;
-    if (gy < 1) gy = 1;
-    int64_t rpb = (rows + gy - 1) / gy;
-    if (rpb < 4) rpb = 4;
-    gy = (rows + rpb - 1) / rpb;
-    dim3 grid((unsigned)gx, (unsigned)gy);
+    const int64_t gx = (kvec + 63) / 64;
+    dim3 grid((unsigned)gx, (unsigned)groups);
     if (bf16)
-        hipLaunchKernelGGL(colmax_kernel<true>, grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec,
-                           (int)rpb, (unsigned*)out_max);
+        hipLaunchKernelGGL((colmax_kernel<true, FOLD>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg, k,
+                           out);
     else
-        hipLaunchKernelGGL(colmax_kernel<false>, grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec,
-                           (int)rpb, (unsigned*)out_max);
+        hipLaunchKernelGGL((colmax_kernel<false, FOLD>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg, k,
+                           out);
     return hipGetLastError();
 }
 
+hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
+                            hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    int64_t gx, groups, rpg;
+    colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg);
+    return launch_colmax<true>(x, bf16, rows, k, (unsigned*)running_max, groups, rpg, st);
+}
+
+int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes) {
+    int64_t gx, groups, rpg;
+    colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg);
+    const int64_t fit = scratch_bytes / (4 * k);
+    if (groups > fit) groups = fit < 1 ? 1 : fit;
+    return groups;
+}
+
+hipError_t sq_launch_colmax_partial(const void* x, int bf16, int64_t rows, int64_t k, int64_t groups,
+                                    unsigned* partial, hipStream_t st) {
+    // exactly `groups` row groups are written (a trailing group past the
+    // last row writes zeros, neutral for the max of non-negative values)
+    const int64_t rpg = (rows + groups - 1) / groups;
+    return launch_colmax<false>(x, bf16, rows, k, partial, groups, rpg, st);
+}
+
 // ---------------------------------------------------------------------------
-// Smoothing factor, per input channel j (calibrate_smoothquant):
-//   s_j = max(f32(P(max(mx_j, floor), a_x)) / f32(P(max(mw_j, floor), a_w)), floor)
+// Smoothing factor, per input channel j (calibrate_smoothquant), from the
+// per-row-group column maxima of |W|:
+//   mw_j = max(max_g partial[g][j], floor),  mx_j = max(x_max[j], floor)
+//   s_j  = max(f32(P(mx_j, a_x)) / f32(P(mw_j, a_w)), floor)
 // P(x, a) = x^a through binary64: exact forms built from correctly rounded
-// sqrt for a in {0, 1/4, 1/2, 3/4, 1}, pow otherwise. `io` holds the raw
-// column max of |W| on entry and s on exit.
+// sqrt for a in {0, 1/4, 1/2, 3/4, 1}, pow otherwise.
+// A block owns 64 channels; its 4 wavefronts split the row groups (8 loads
+// in flight each) and meet in LDS.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double pow64(double x, double a) {
     if (a == 0.0) return 1.0;
@@ -132,141 +191,177 @@ __device__ __forceinline__ double pow64(double x, double a) {
 }
 
 __global__ __launch_bounds__(256) void smooth_factor_kernel(const float* __restrict__ x_max,
-                                                            float* __restrict__ io, double a_x,
-                                                            double a_w, int64_t k) {
-    int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= k) return;
-    float mx = fmaxf(x_max[j], kFloor);
-    float mw = fmaxf(io[j], kFloor);
-    float num = (float)pow64((double)mx, a_x);
-    float den = (float)pow64((double)mw, a_w);
-    io[j] = fmaxf(num / den, kFloor);
+                                                            const unsigned* partial, int64_t groups, double a_x,
+                                                            double a_w, int64_t k, float* s) {
+    __shared__ unsigned red[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    unsigned mwb = 0;
+    if (j < k) {
+        int64_t g = wave;
+        for (; g + 28 < groups; g += 32) {
+            unsigned v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = partial[(g + 4 * u) * k + j];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mwb = max(mwb, v[u]);
+        }
+        for (; g < groups; g += 4) mwb = max(mwb, partial[g * k + j]);
+    }
+    red[wave][lane] = mwb;
+    __syncthreads();  // every partial is read before s (which may alias it) is written
+    if (wave != 0 || j >= k) return;
+    mwb = max(max(red[0][lane], red[1][lane]), max(red[2][lane], red[3][lane]));
+    const float mw = fmaxf(__uint_as_float(mwb), kFloor);
+    const float mx = fmaxf(x_max[j], kFloor);
+    const float num = (float)pow64((double)mx, a_x);
+    const float den = (float)pow64((double)mw, a_w);
+    s[j] = fmaxf(num / den, kFloor);
 }
 
-hipError_t sq_launch_smooth_factor(const float* x_max, float* io, double a_x, double a_w,
-                                   int64_t k, hipStream_t st) {
-    unsigned blocks = (unsigned)((k + 255) / 256);
-    hipLaunchKernelGGL(smooth_factor_kernel, dim3(blocks), dim3(256), 0, st, x_max, io, a_x, a_w, k);
+hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, int64_t groups, double a_x,
+                                   double a_w, int64_t k, float* s, hipStream_t st) {
+    unsigned blocks = (unsigned)((k + 63) / 64);
+    hipLaunchKernelGGL(smooth_factor_kernel, dim3(blocks), dim3(256), 0, st, x_max, partial, groups, a_x, a_w, k,
+                       s);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Loads of 8 consecutive elements as fp32 (bf16: one 16-byte load; fp32: two).
+// Rows -> int8 codes with one scale per row, for both sides of the product:
+//   weights (DIV = false):     v[j] = f32(w[j] * s_j)
+//   activations (DIV = true):  v[j] = f32(x[j] / s_j)
+//   scale = max(max_j |v[j]|, floor) / 127
+//   q[j]  = round_half_even(v[j] / scale)
+//
+// Division. For a binary32 quotient a / b the kernels use y = RN(1/b),
+// q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0). On gfx950 q1 equals the
+// IEEE quotient RN(a/b) for every pair of binary32 significands (2^46
+// pairs, checked on the device by sq_selfcheck_division); as every step is
+// one correctly rounded operation, powers of two scale it exactly, so it
+// holds for all operands as long as no step under- or overflows.
+//   * x / s_j: y_j = RN(1/s_j) comes from recip_rn (also checked against
+//     IEEE 1/s on the device, sq_selfcheck_reciprocal) for s_j in
+//     [2^-40, 2^40), else NaN. The quotient is taken when 2^-50 <= |q0| <=
+//     2^120 or q0 = 0 (then |x| >= 2^-90: no step leaves the normal range);
+//     otherwise, once per row and only if needed, the IEEE division.
+//   * v / scale: scale is in [2^-34, 2^122] (floor / 127 up to max / 127)
+//     and |v / scale| <= 127.00002, so no step overflows; a step can only
+//     underflow when |v| < 2^-90, where the quotient is below 2^-50 and its
+//     code is 0 either way. The code is then rint(quotient), computed by
+//     adding 1.5 * 2^23 (round to nearest even into the low mantissa bits,
+//     whose low byte is the two's complement code); |quotient| <= 127.00002
+//     rounds into [-127, 127].
+//
+// Layout. A block of T threads owns a row at a time and walks a few rows
+// with a grid stride. Thread t owns the 8-channel chunks t, t + T, ... (C
+// of them) and keeps their s (and y) in registers; the row stays in
+// registers between the max and the codes, so the input is read once; a
+// further row's loads are issued before the current row is finished. One
+// barrier per row (the block max goes through a double-buffered LDS slot).
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t elem, float (&v)[8]) {
-    if constexpr (BF16) {
-        u32x4 u = *(const u32x4*)((const uint16_t*)base + elem);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_lo(u[i]);
-            v[2 * i + 1] = bf16_hi(u[i]);
-        }
-    } else {
-        const float* f = (const float*)base + elem;
-        u32x4 a = *(const u32x4*)f;
-        u32x4 b = *(const u32x4*)(f + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(a[i]);
-            v[4 + i] = __uint_as_float(b[i]);
-        }
-    }
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+// RN(1/s) for s in [2^-40, 2^40): the hardware reciprocal refined by one
+// Newton step; on gfx950 it equals the IEEE quotient 1/s for every binary32
+// s in [2^-100, 2^100) (sq_selfcheck_reciprocal). Elsewhere NaN, which fails
+// every guard below.
+__device__ __forceinline__ float recip_rn(float s) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    return (s >= 0x1p-40f && s < 0x1p40f) ? y : __builtin_nanf("");
 }
 
-__device__ __forceinline__ void load8_f32(const float* __restrict__ p, float (&v)[8]) {
-    u32x4 a = *(const u32x4*)p;
-    u32x4 b = *(const u32x4*)(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = __uint_as_float(a[i]);
-        v[4 + i] = __uint_as_float(b[i]);
-    }
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+    const float q0 = a * y;
+    return __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
 }
 
-// ---------------------------------------------------------------------------
-// Weights: one wavefront per output row o.
-//   pass 1: m = max_j |f32(w[o][j] * s_j)|
-//   scale  = max(m, floor) / 127
-//   pass 2: codes of f32(w[o][j] * s_j) (the row is re-read from L2)
-// ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(256) void quantize_weight_kernel(const void* __restrict__ w,
-                                                              const float* __restrict__ s, int64_t n,
-                                                              int64_t k, int8_t* __restrict__ wq,
-                                                              float* __restrict__ w_scale) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= n) return;
-    const int64_t k8 = k >> 3;
-    const int64_t base = row * k;
-    float m = 0.0f;
-    for (int64_t j8 = lane; j8 < k8; j8 += 64) {
-        float v[8], sv[8];
-        load8<BF16>(w, base + j8 * 8, v);
-        load8_f32(s + j8 * 8, sv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i] * sv[i]));
-    }
-    m = wave_max(m);
-    const float scale = fmaxf(m, kFloor) / kQmax;
-    const float rs = 1.0f / scale;
-    for (int64_t j8 = lane; j8 < k8; j8 += 64) {
-        float v[8], sv[8];
-        load8<BF16>(w, base + j8 * 8, v);
-        load8_f32(s + j8 * 8, sv);
-        float c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = code_of(v[i] * sv[i], scale, rs);
-        u32x2 packed = {pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
-        *(u32x2*)(wq + base + j8 * 8) = packed;
-    }
-    if (lane == 0) w_scale[row] = scale;
+__global__ __launch_bounds__(256) void selfcheck_reciprocal_kernel(unsigned long long* mismatches) {
+    const unsigned long long idx = (unsigned long long)blockIdx.x * 256 + threadIdx.x;
+    const unsigned e = (unsigned)(idx >> 23), mant = (unsigned)(idx & 0x7fffffu);
+    if (e >= 200) return;
+    const float s = __uint_as_float(((e + 27u) << 23) | mant);  // 2^-100 .. 2^100
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    if (__float_as_uint(y) != __float_as_uint(1.0f / s)) atomicAdd(mismatches, 1ull);
 }
 
-hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, int64_t n, int64_t k,
-                                     int8_t* wq, float* w_scale, hipStream_t st) {
-    unsigned blocks = (unsigned)((n + 3) / 4);
-    if (bf16)
-        hipLaunchKernelGGL(quantize_weight_kernel<true>, dim3(blocks), dim3(256), 0, st, w, s, n, k, wq,
-                           w_scale);
-    else
-        hipLaunchKernelGGL(quantize_weight_kernel<false>, dim3(blocks), dim3(256), 0, st, w, s, n, k, wq,
-                           w_scale);
+hipError_t sq_launch_selfcheck_reciprocal(unsigned long long* mismatches, hipStream_t st) {
+    const unsigned long long total = 200ull << 23;
+    hipLaunchKernelGGL(selfcheck_reciprocal_kernel, dim3((unsigned)(total / 256)), dim3(256), 0, st, mismatches);
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Activations: a team of W wavefronts per token row; each lane holds C steps
-// of 8 consecutive channels of x~ = f32(x / s) in registers, so the row is
-// read once and x / s is formed once.
-//   m = max_j |x~_j| (lane -> wave -> team), scale = max(m, floor) / 127,
-//   codes of x~_j.
-// Teams walk rows with a grid stride; the block's loop count is uniform so
-// the team barrier is reached by every thread.
-// ---------------------------------------------------------------------------
-template <bool BF16, int W, int C>
-__global__ __launch_bounds__(256) void quantize_act_kernel(const void* __restrict__ x,
-                                                           const float* __restrict__ s, int64_t m,
-                                                           int64_t k, int8_t* __restrict__ xq,
-                                                           float* __restrict__ x_scale) {
-    constexpr int kTeams = 4 / W;
-    __shared__ float red[4];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int team = wave / W;
-    const int wit = wave % W;  // wave index inside its team
+// divisor significands [b_begin, b_end) against every numerator significand
+__global__ __launch_bounds__(256) void selfcheck_division_kernel(unsigned b_begin, unsigned b_end,
+                                                                 unsigned long long* mismatches) {
+    const unsigned bm = b_begin + blockIdx.x * 256 + threadIdx.x;
+    if (bm >= b_end) return;
+    const float b = __uint_as_float(0x3f800000u | bm);
+    const float y = 1.0f / b;
+    unsigned long long bad = 0;
+    for (unsigned am = 0; am < (1u << 23); ++am) {
+        const float a = __uint_as_float(0x3f800000u | am);
+        if (__float_as_uint(div_rn(a, b, y)) != __float_as_uint(a / b)) ++bad;
+    }
+    if (bad) atomicAdd(mismatches, bad);
+}
+
+hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
+                                        hipStream_t st) {
+    if (b_end <= b_begin) return hipSuccess;
+    hipLaunchKernelGGL(selfcheck_division_kernel, dim3((b_end - b_begin + 255) / 256), dim3(256), 0, st, b_begin,
+                       b_end, mismatches);
+    return hipGetLastError();
+}
+
+// low bytes of four words -> one word
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // [a.b0, b.b0, 0, 0]
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // [a, b, c, d]
+}
+
+template <bool BF16, bool DIV, int T, int C>
+__global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict__ x, const float* __restrict__ s,
+                                                          int64_t m, int64_t k, int8_t* __restrict__ q,
+                                                          float* __restrict__ scale_out) {
+    constexpr int NW = T / 64;
+    constexpr int kV = BF16 ? 1 : 2;  // 16-byte loads per 8 channels
+    __shared__ float red[2][NW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t k8 = k >> 3;
-    for (int64_t rbase = (int64_t)blockIdx.x * kTeams; rbase < m; rbase += (int64_t)gridDim.x * kTeams) {
-        const int64_t row = rbase + team;
-        const bool active = row < m;
-        // issue every load of the row first, then compute
-        constexpr int kV = BF16 ? 1 : 2;
-        u32x4 raw[C][kV];
+
+    float sv[C][8], yv[DIV ? C : 1][8];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int64_t j8 = (int64_t)c * T + tid;
+        if (j8 < k8) {
+            const u32x4 a = *(const u32x4*)(s + j8 * 8);
+            const u32x4 b = *(const u32x4*)(s + j8 * 8 + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sv[c][i] = __uint_as_float(a[i]);
+                sv[c][4 + i] = __uint_as_float(b[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sv[c][i] = 1.0f;
+        }
+        if constexpr (DIV) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[c][i] = recip_rn(sv[c][i]);
+        }
+    }
+
+    u32x4 raw[C][kV];
+    auto load_row = [&](int64_t row) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int64_t j8 = (int64_t)(c * W + wit) * 64 + lane;
-            if (active && j8 < k8) {
+            const int64_t j8 = (int64_t)c * T + tid;
+            if (row < m && j8 < k8) {
                 const u32x4* p = BF16 ? (const u32x4*)((const uint16_t*)x + row * k + j8 * 8)
                                       : (const u32x4*)((const float*)x + row * k + j8 * 8);
 #pragma unroll
@@ -276,101 +371,125 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const void* __restric
                 for (int v = 0; v < kV; ++v) raw[c][v] = u32x4{0, 0, 0, 0};
             }
         }
+    };
+    auto unpack = [&](int c, float (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BF16) {
+                v[2 * i] = bf16_lo(raw[c][0][i]);
+                v[2 * i + 1] = bf16_hi(raw[c][0][i]);
+            } else {
+                v[i] = __uint_as_float(raw[c][0][i]);
+                v[4 + i] = __uint_as_float(raw[c][1][i]);
+            }
+        }
+    };
+    // the fast quotient's proven range; q0 = 0 (x = 0) is exact as well but is
+    // left to the rare path, which skips it element by element
+    auto in_range = [](float q0) {
+        const float a0 = __builtin_fabsf(q0);
+        return a0 >= 0x1p-50f && a0 <= 0x1p120f;
+    };
+
+    int64_t row = blockIdx.x;
+    load_row(row);
+    for (int parity = 0; row < m; row += gridDim.x, parity ^= 1) {
         float xs[C][8];
-        float mx = 0.0f;
+        bool exact_needed = false;  // one branch per row, never taken for sane inputs
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int64_t j8 = (int64_t)(c * W + wit) * 64 + lane;
-            float v[8], sv[8];
-            if constexpr (BF16) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[2 * i] = bf16_lo(raw[c][0][i]);
-                    v[2 * i + 1] = bf16_hi(raw[c][0][i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = __uint_as_float(raw[c][0][i]);
-                    v[4 + i] = __uint_as_float(raw[c][1][i]);
-                }
-            }
-            if (j8 < k8) {
-                load8_f32(s + j8 * 8, sv);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
-            }
+            float v[8];
+            unpack(c, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                xs[c][i] = v[i] / sv[i];
-                mx = fmaxf(mx, fabsf(xs[c][i]));
-            }
-        }
-        mx = wave_max(mx);
-        if constexpr (W > 1) {
-            if (lane == 0) red[wave] = mx;
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < W; ++i) mx = fmaxf(mx, red[team * W + i]);
-            __syncthreads();
-        }
-        const float scale = fmaxf(mx, kFloor) / kQmax;
-        const float rs = 1.0f / scale;
-        if (active) {
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const int64_t j8 = (int64_t)(c * W + wit) * 64 + lane;
-                if (j8 < k8) {
-                    float q[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = code_of(xs[c][i], scale, rs);
-                    u32x2 packed = {pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])};
-                    *(u32x2*)(xq + row * k + j8 * 8) = packed;
+                if constexpr (DIV) {
+                    xs[c][i] = div_rn(v[i], sv[c][i], yv[c][i]);
+                    exact_needed |= !in_range(v[i] * yv[c][i]);
+                } else {
+                    xs[c][i] = v[i] * sv[c][i];
                 }
             }
-            if (wit == 0 && lane == 0) x_scale[row] = scale;
         }
+        if constexpr (DIV) {
+            if (exact_needed) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    float v[8];
+                    unpack(c, v);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float q0 = v[i] * yv[c][i];
+                        if (!in_range(q0) && q0 != 0.0f) xs[c][i] = v[i] / sv[c][i];
+                    }
+                }
+            }
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mx = fmaxf(mx, __builtin_fabsf(xs[c][i]));
+        // the next row's loads are in flight while this row finishes
+        load_row(row + gridDim.x);
+        mx = wave_max(mx);
+        if (lane == 0) red[parity][wave] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[parity][w]);
+        const float scale = fmaxf(mx, kFloor) / kQmax;
+        const float rs = 1.0f / scale;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t j8 = (int64_t)c * T + tid;
+            uint32_t b[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(div_rn(xs[c][i], scale, rs) + kMagic);
+            if (j8 < k8)
+                *(u32x2*)(q + row * k + j8 * 8) =
+                    u32x2{pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7])};
+        }
+        if (tid == 0) scale_out[row] = scale;
     }
 }
 
-template <bool BF16>
-static hipError_t launch_act(const void* x, const float* s, int64_t m, int64_t k, int8_t* xq,
-                             float* x_scale, hipStream_t st) {
-    // team width W and steps per lane C such that 512 * W * C >= k
-    int W, C;
-    const int64_t steps = (k + 511) / 512;  // 8-channel steps per lane for one wave
-    if (steps <= 8) {
-        W = 1;
-        C = (int)steps;
-    } else if (steps <= 16) {
-        W = 2;
-        C = (int)((steps + 1) / 2);
-    } else {
-        W = 4;
-        C = (int)((steps + 3) / 4);
+template <bool BF16, bool DIV>
+static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t k, int8_t* q, float* scale,
+                              hipStream_t st) {
+    // threads per row T and 8-channel chunks per thread C, with T * C * 8 >= k
+    const int64_t k8 = k / 8;
+    int T, C;
+    if (k8 <= 512) { T = 256; C = k8 <= 256 ? 1 : 2; }
+    else if (k8 <= 1024) { T = 512; C = 2; }
+    else if (k8 <= 1536) { T = 512; C = 3; }
+    else if (k8 <= 2048) { T = 1024; C = 2; }
+    else return hipErrorInvalidValue;
+    // a few rows per block (walked with a grid stride) so that the next
+    // row's loads overlap the current row's arithmetic: 2 for rows up to
+    // 4096 channels, 4 beyond (measured best on MI355X)
+    const int64_t rows_per_block = k8 <= 512 ? 2 : 4;
+    int64_t blocks = (m + rows_per_block - 1) / rows_per_block;
+    if (blocks > 16384) blocks = 16384;
+    dim3 grid((unsigned)blocks), block(T);
+#define SQ_ROWS_CASE(TT, CC)                                                                                  \
+    if (T == TT && C == CC) {                                                                                 \
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, DIV, TT, CC>), grid, block, 0, st, x, s, m, k, q, scale); \
+        return hipGetLastError();                                                                             \
     }
-    // round C up to an instantiated value
-    C = C <= 1 ? 1 : C <= 2 ? 2 : C <= 4 ? 4 : C <= 6 ? 6 : 8;
-    const int teams = 4 / W;
-    int64_t blocks = (m + teams - 1) / teams;
-    if (blocks > 8192) blocks = 8192;
-    dim3 grid((unsigned)blocks), block(256);
-#define SQ_ACT_CASE(WW, CC)                                                                      \
-    if (W == WW && C == CC) {                                                                    \
-        hipLaunchKernelGGL((quantize_act_kernel<BF16, WW, CC>), grid, block, 0, st, x, s, m, k, xq, \
-                           x_scale);                                                             \
-        return hipGetLastError();                                                                \
-    }
-    SQ_ACT_CASE(1, 1) SQ_ACT_CASE(1, 2) SQ_ACT_CASE(1, 4) SQ_ACT_CASE(1, 6) SQ_ACT_CASE(1, 8)
-    SQ_ACT_CASE(2, 6) SQ_ACT_CASE(2, 8) SQ_ACT_CASE(4, 6) SQ_ACT_CASE(4, 8)
-#undef SQ_ACT_CASE
+    SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
+#undef SQ_ROWS_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t sq_launch_quantize_act(const void* x, int bf16, const float* s, int64_t m, int64_t k,
-                                  int8_t* xq, float* x_scale, hipStream_t st) {
+hipError_t sq_launch_quantize_act(const void* x, int bf16, const float* s, int64_t m, int64_t k, int8_t* xq,
+                                  float* x_scale, hipStream_t st) {
     if (m <= 0) return hipSuccess;
-    return bf16 ? launch_act<true>(x, s, m, k, xq, x_scale, st)
-                : launch_act<false>(x, s, m, k, xq, x_scale, st);
+    return bf16 ? launch_rows<true, true>(x, s, m, k, xq, x_scale, st)
+                : launch_rows<false, true>(x, s, m, k, xq, x_scale, st);
+}
+
+hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, int64_t n, int64_t k, int8_t* wq,
+                                     float* w_scale, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    return bf16 ? launch_rows<true, false>(w, s, n, k, wq, w_scale, st)
+                : launch_rows<false, false>(w, s, n, k, wq, w_scale, st);
 }
