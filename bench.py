@@ -10,8 +10,10 @@ alpha = 0.5, calibrated on 512 separate tokens fed as 4 batches of 128):
   sq_quantize_act -> sq_w8a8_gemm (int8 GEMM + fused dequant).
 Inputs are resident in HBM before the timed region; 4 copies of every buffer
 are rotated so that each step's data is not left in the 256 MB Infinity
-Cache by the previous step. HIP events on the launch stream bracket every
-stage of every timed step. Prints one JSON line.
+Cache by the previous step. HIP events on the launch stream bracket the
+timed region and every GEMM launch in it; a second pass of the same steps
+with an event between stages gives the per-stage breakdown. Prints one JSON
+line.
 
 The CPU baseline times the CPU oracle (test infrastructure) on a bounded
 sample of the same workload on this host.
@@ -44,6 +46,9 @@ def _args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--counter-pass", action="store_true",
+                   help="run only a 256 MiB fp32 copy (known bytes) and the GEMM, 3 times each, for "
+                        "rocprofv3 --pmc passes; prints no JSON line")
     return p.parse_args()
 
 
@@ -109,6 +114,25 @@ def cpu_baseline(case, budget_s: float):
     }
 
 
+def counter_pass(torch, B, s, dev, stream):
+    """A copy of known size (reads and writes 256 MiB: torch.neg over 2^26
+    fp32) gives the factor between the HBM counters and real bytes; then the
+    GEMM of the benchmark step on prepared operands."""
+    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    B.sq_calibrate(s["calib"][0], s["run"], stream)
+    B.sq_prepare_weight(s["w"], s["run"], 0.5, s["smooth"], s["wq"], s["ws"], stream)
+    B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], None, s["y"], stream)
+    torch.cuda.synchronize()
+    print("counter pass done", flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -153,9 +177,12 @@ def main():
             y=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
     del x0, w0, c0
     stream = torch.cuda.current_stream(dev)
+    if args.counter_pass:
+        counter_pass(torch, B, sets[0], dev, stream)
+        return
     n_stage = 5  # reset+calibrate, prepare, act quant, gemm
 
-    def step(i, ev=None):
+    def step(i, ev=None, gemm_ev=None):
         s = sets[i % ROTATE]
         if ev is not None:
             ev[0].record(stream)
@@ -170,24 +197,44 @@ def main():
         B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
         if ev is not None:
             ev[3].record(stream)
+        if gemm_ev is not None:
+            gemm_ev[0].record(stream)
         B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], None, s["y"], stream)
         if ev is not None:
             ev[4].record(stream)
+        if gemm_ev is not None:
+            gemm_ev[1].record(stream)
+
+    def new_events(count, per):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(count)]
 
     for i in range(args.warmup):
         step(i)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage)] for _ in range(args.steps)]
+    # timed region: K steps; HIP events on the launch stream bracket the
+    # region and every GEMM launch (the GEMM's live average duration)
+    region = new_events(1, 2)[0]
+    gemm_events = new_events(args.steps, 2)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, gemm_ev=gemm_events[i])
+    region[1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
+    ms_per_step = region[0].elapsed_time(region[1]) / args.steps
+    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in gemm_events) / args.steps
 
-    total_ms = events[0][0].elapsed_time(events[-1][-1])
-    ms_per_step = total_ms / args.steps
+    # stage breakdown: a second pass of K steps with an event between stages
+    # (every event adds a few microseconds between kernels, so this pass is
+    # not the throughput figure)
+    events = new_events(args.steps, n_stage)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, ev=events[i])
+    torch.cuda.synchronize()
     stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(n_stage - 1)]
-    calib_ms, prep_ms, act_ms, gemm_ms = stage_ms
+    calib_ms, prep_ms, act_ms, gemm_stage_ms = stage_ms
     ops = 2.0 * m * n * k
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -219,8 +266,10 @@ def main():
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": None if traffic is None else round(traffic)},
+        "gemm_us": round(gemm_ms * 1e3, 2),
         "stages_us": {"reset+calibrate": round(calib_ms * 1e3, 2), "prepare_weight": round(prep_ms * 1e3, 2),
-                      "quantize_act": round(act_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)},
+                      "quantize_act": round(act_ms * 1e3, 2), "gemm": round(gemm_stage_ms * 1e3, 2),
+                      "note": "second pass of the same K steps with an event between stages"},
         "stage_rooflines": {
             "quantize_act": {"bound": "hbm", "achieved": round(act_bytes / (act_ms * 1e-3) / 1e9, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
