@@ -11,9 +11,7 @@
 //   * one workgroup per BM x BN output tile; its wavefronts form a WGM x WGN
 //     grid and each owns a (BM/WGM) x (BN/WGN) block held in registers as
 //     32 x 32 tiles of v_mfma_i32_32x32x32_i8 (the 16x16x64 int8 form
-//     measures at half the rate on this chip). The 256 x 256 tile uses
-//     8 wavefronts (2 per SIMD) so that one can issue MFMAs while the other
-//     waits on LDS;
+//     measures at half the rate on this chip);
 //   * K advances in BK = 64-byte steps through a ring of 4 LDS stages filled
 //     by direct global -> LDS loads (global_load_lds_dwordx4: no VGPR
 //     staging, no LDS store instructions), issued three steps ahead;
@@ -22,10 +20,16 @@
 //     position c ^ swz(r), swz(r) = (r >> 2) & 3, under which the 16-byte
 //     operand reads of a wavefront (32 rows x 2 chunks) measure free of LDS
 //     bank conflicts on gfx950;
-//   * one barrier per step, placed between the two 32-byte k slices: after
-//     it every wavefront has a whole slice of MFMAs to issue (fragments
-//     already in registers) while the next stage's first fragments are read
-//     and the DMA of a later stage is issued;
+//   * the 256 x 256 and 128 x 256 tiles run 8 wavefronts, two per SIMD
+//     (waves w and w + 4 share one), in ping-pong: the two groups of four
+//     alternate between a run of 16 (8) MFMAs on fragments already in
+//     registers and the memory work of their next step (LDS fragment reads,
+//     their share of a later stage's DMA, the waits), with a workgroup
+//     barrier between phases. Interleaving the memory instructions into the
+//     MFMA stream of the same wavefronts measured slower;
+//   * the 128 x 128 tile (4 wavefronts, one per SIMD) interleaves instead:
+//     one barrier per step between the two 32-byte k slices, the next
+//     slice's fragments read right after each slice's first MFMA;
 //   * rows past m or n are clamped for loading (their results are never
 //     stored); a last partial K step goes through registers, zero-filled;
 //   * the 1-D grid is remapped so that the tiles dispatched to one XCD (the
@@ -33,6 +37,11 @@
 //     block sharing A rows and B columns in that XCD's L2;
 //   * the epilogue stages each 32-row slab through LDS and writes whole
 //     16-byte row chunks.
+//
+// Measured at M = N = K = 4096 (bf16 out): the clock under this load is
+// power-limited to about 1.7 GHz (int8 MFMA at 32 busy cycles per
+// instruction per SIMD), and the main loop keeps the MFMA units about 70%
+// busy; HBM traffic is the per-XCD minimum of the tile order.
 #include "sq_device.h"
 
 #include <type_traits>
@@ -43,6 +52,8 @@ namespace {
 
 constexpr int kBK = 64;            // bytes of K per step
 constexpr int kStages = 4;         // LDS ring depth
+constexpr int kRowLanes = kBK / 16;        // lanes of one DMA load per row
+constexpr int kBlockRows = 64 / kRowLanes; // rows per 1 KiB DMA load
 constexpr int kXcds = 8;
 constexpr int kSlices = kBK / 32;  // 32-byte k slices per step (one MFMA depth each)
 
@@ -51,20 +62,29 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
-// memory operations are outstanding and does not wait on the other counters.
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
+// operations are outstanding (vmcnt_imm), and in addition every LDS
+// operation has completed (vm_lgkm_imm).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int vm_lgkm_imm(int n) { return vmcnt_imm(n) & ~(15 << 8); }
 
-// Groups for one k slice: MF MFMAs with R LDS reads and V global loads
-// spread evenly between them (group I is MFMA number I).
-template <int I, int MF, int R, int V>
-__device__ __forceinline__ void sched_slice() {
-    constexpr int r = (I + 1) * R / MF - I * R / MF;
-    constexpr int v = (I + 1) * V / MF - I * V / MF;
-    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, v, 0);
-    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
+// V global loads spread evenly between MFMAs I .. MF-1.
+template <int I, int MF, int V>
+__device__ __forceinline__ void sched_spread() {
+    constexpr int n = MF - 1;
+    constexpr int v = I * V / n - (I - 1) * V / n;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if constexpr (I + 1 < MF) sched_slice<I + 1, MF, R, V>();
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, v, 0);
+    if constexpr (I + 1 < MF) sched_spread<I + 1, MF, V>();
+}
+// Order of one k slice: its first MFMA, then all R LDS reads of the next
+// slice's fragments (as early as possible: they have the rest of the slice
+// to land), then the remaining MFMAs with V global loads spread between them.
+template <int MF, int R, int V>
+__device__ __forceinline__ void sched_slice() {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+    sched_spread<1, MF, V>();
 }
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
@@ -85,14 +105,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wavefront block
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int STAGE = (BM + BN) * kBK;          // bytes of one LDS stage (A rows, then B rows)
-    constexpr int BLOCKS = (BM + BN) / 16;          // 1 KB DMA blocks per stage (16 rows each)
+    constexpr int BLOCKS = (BM + BN) / kBlockRows;  // 1 KiB DMA blocks per stage
     constexpr int LOADS = BLOCKS / NW;              // DMA loads per thread per stage
     static_assert(BLOCKS % NW == 0, "stage must split evenly over the wavefronts");
     __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
     const int wm = wave / WGN, wn = wave % WGN;
 
     // ---- tile order: XCD-compact, then grouped along m --------------------
@@ -115,8 +135,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
         const int blk = wave + NW * q;
-        const int row = blk * 16 + (lane >> 2);      // row in the A|B stage space
-        const int pos = lane & 3;
+        const int row = blk * kBlockRows + lane / kRowLanes;  // row in the A|B stage space
+        const int pos = lane % kRowLanes;
         const int chunk = pos ^ swz(row);
         const int8_t* g;
         if (row < BM) g = A + (int64_t)min(m0 + row, m - 1) * k;
@@ -137,8 +157,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
         const int kb = kt * kBK;
 #pragma unroll
         for (int q = 0; q < LOADS; ++q) {
-            const int row = (wave + NW * q) * 16 + (lane >> 2);
-            const int chunk = (lane & 3) ^ swz(row);
+            const int row = (wave + NW * q) * kBlockRows + lane / kRowLanes;
+            const int chunk = (lane % kRowLanes) ^ swz(row);
             i32x4 v = {0, 0, 0, 0};
             if (kb + chunk * 16 < k) v = *(const i32x4*)(src[q] + kb);
             *(i32x4*)(smem + buf * STAGE + dst[q] + lane * 16) = v;
@@ -156,85 +176,140 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     int foff[kSlices];
 #pragma unroll
     for (int s = 0; s < kSlices; ++s) foff[s] = fr * kBK + (((2 * s + (lane >> 5)) ^ swz(fr)) * 16);
-    static_assert(kSlices == 2, "the step below is written for two k slices");
 
-    i32x4 f0a[TM], f0b[TN], f1a[TM], f1b[TN];  // fragments of slice 0 / slice 1
-    auto read_frags = [&](int buf, int s, i32x4 (&fa)[TM], i32x4 (&fb)[TN]) {
+    static_assert(kSlices == 2, "the loops below are written for two k slices per step");
+
+    i32x4 fa[TM], fb[TN], ga[TM], gb[TN];  // fragments of slice 0 / slice 1
+    auto read_frags = [&](int buf, int s, i32x4 (&xa)[TM], i32x4 (&xb)[TN]) {
         const int8_t* as = smem + buf * STAGE + (wm * WM) * kBK + foff[s];
         const int8_t* bs = smem + buf * STAGE + (BM + wn * WN) * kBK + foff[s];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i] = *(const i32x4*)(as + i * 32 * kBK);
+        for (int i = 0; i < TM; ++i) xa[i] = *(const i32x4*)(as + i * 32 * kBK);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[j] = *(const i32x4*)(bs + j * 32 * kBK);
+        for (int j = 0; j < TN; ++j) xb[j] = *(const i32x4*)(bs + j * 32 * kBK);
     };
-    auto mfmas = [&](const i32x4 (&fa)[TM], const i32x4 (&fb)[TN]) {
+    auto mfmas = [&](const i32x4 (&xa)[TM], const i32x4 (&xb)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+    };
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
     };
     constexpr int MF = TM * TN, R = TM + TN;
-    // wait until at most n DMA loads per thread are outstanding, then the
-    // workgroup barrier (a bare s_barrier: __syncthreads would also drain
-    // every later stage)
-    auto wait_barrier = [&](int n_later_stages) {
-        if (n_later_stages >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
-        else if (n_later_stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_s_barrier();
-    };
 
-    // ---- main loop -----------------------------------------------------------
-    // Step kt, with the slice-0 fragments of stage kt already in registers:
-    //   phase 1: MFMAs of slice 0, while slice 1 of stage kt is read;
-    //   barrier: stage kt+1 is complete and visible, and every wavefront has
-    //            finished reading stage kt-1's buffer;
-    //   phase 2: MFMAs of slice 1, while slice 0 of stage kt+1 is read and
-    //            the DMA of stage kt+3 into stage kt-1's buffer is issued.
-    // Right after the barrier every wavefront has a full slice of MFMAs to
-    // issue, which covers the LDS latency of the next fragments.
     const int KF = k / kBK;  // whole steps
+    // The epilogue's kernel arguments arrive by scalar loads; scalar loads
+    // share the LDS wait counter and may return out of order, so while one
+    // is outstanding every LDS wait in the loop would have to drain all LDS
+    // reads. Consume them here, before the loop.
+    asm volatile("" ::"s"(sa), "s"(sb), "s"(bias), "s"(Y), "s"(bias_kind));
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
         if (st < KF) issue_stage(st, st);
     if (KF > 0) {
-        wait_barrier(min(KF - 1, kStages - 2));
-        read_frags(0, 0, f0a, f0b);
+        // stage 0 landed (later ones may be in flight), visible to all
+        if (KF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+        else if (KF > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        barrier();
     }
-    int kt = 0;
-    for (; kt + kStages - 1 < KF; ++kt) {
-        const int buf = kt % kStages;
-        read_frags(buf, 1, f1a, f1b);
-        mfmas(f0a, f0b);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
-        sched_slice<0, MF, 0, 0>();
-        wait_barrier(1);
-        read_frags((kt + 1) % kStages, 0, f0a, f0b);
-        issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
-        mfmas(f1a, f1b);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
-        sched_slice<0, MF, 0, LOADS>();
-    }
-    for (; kt < KF; ++kt) {
-        const int buf = kt % kStages;
-        read_frags(buf, 1, f1a, f1b);
-        mfmas(f0a, f0b);
-        if (kt + 1 < KF) {
-            wait_barrier(KF - 2 - kt);
-            read_frags((kt + 1) % kStages, 0, f0a, f0b);
+
+    if constexpr (NW == 8) {
+        // ---- ping-pong: waves w and w + 4 share a SIMD. Group 0 (waves
+        // ---- 0-3) and group 1 (waves 4-7) take turns, one phase each,
+        // ---- separated by workgroup barriers: while one group issues an
+        // ---- uninterrupted run of MFMAs on fragments already in registers,
+        // ---- the other reads its next fragments from LDS and issues its
+        // ---- share of the DMA of a later stage, so on every SIMD the matrix
+        // ---- unit is fed by one wave while the other does the memory work.
+        //   group 0: M(0) C(0) M(1) C(1) ... M(KF-1) C(KF-1) | extra barrier
+        //   group 1: barrier | M(0) C(0) ... M(KF-1) C(KF-1)
+        // M(kt): read both slices of stage kt; issue this wave's loads of
+        //        stage kt+3 into the buffer of stage kt-1 (whose last reads,
+        //        by group 1 in the previous phase, completed before that
+        //        phase's barrier); wait for own LDS reads and own loads of
+        //        stage kt+1, which the next M phase (by either group) reads.
+        // C(kt): the MFMAs of both slices.
+        const bool second = wave >= NW / 2;
+        if (second) barrier();
+        int kt = 0;
+        for (; kt + kStages - 1 < KF; ++kt) {
+            const int buf = kt % kStages;
+            read_frags(buf, 0, fa, fb);
+            read_frags(buf, 1, ga, gb);
+            issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
+            __builtin_amdgcn_s_waitcnt(vm_lgkm_imm((kStages - 2) * LOADS));
+            barrier();
+            mfmas(fa, fb);
+            mfmas(ga, gb);
+            barrier();
         }
-        mfmas(f1a, f1b);
+        for (; kt < KF; ++kt) {
+            const int buf = kt % kStages;
+            read_frags(buf, 0, fa, fb);
+            read_frags(buf, 1, ga, gb);
+            __builtin_amdgcn_s_waitcnt(vm_lgkm_imm(0));
+            barrier();
+            mfmas(fa, fb);
+            mfmas(ga, gb);
+            barrier();
+        }
+        if (!second) barrier();
+    } else {
+        // ---- interleaved (one wave per SIMD): step kt, with the slice-0
+        // ---- fragments of stage kt in registers:
+        //   phase 1: MFMAs of slice 0, while slice 1 of stage kt is read;
+        //   barrier: stage kt+1 is complete and visible, and every wavefront
+        //            has finished reading stage kt-1's buffer;
+        //   phase 2: MFMAs of slice 1, while slice 0 of stage kt+1 is read
+        //            and the DMA of stage kt+3 into stage kt-1's buffer is
+        //            issued.
+        auto wait_barrier = [&](int n_later_stages) {
+            if (n_later_stages >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+            else if (n_later_stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            barrier();
+        };
+        if (KF > 0) read_frags(0, 0, fa, fb);
+        int kt = 0;
+        for (; kt + kStages - 1 < KF; ++kt) {
+            const int buf = kt % kStages;
+            read_frags(buf, 1, ga, gb);
+            mfmas(fa, fb);
+            sched_slice<MF, R, 0>();
+            wait_barrier(1);
+            read_frags((kt + 1) % kStages, 0, fa, fb);
+            issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
+            mfmas(ga, gb);
+            sched_slice<MF, R, LOADS>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (; kt < KF; ++kt) {
+            const int buf = kt % kStages;
+            read_frags(buf, 1, ga, gb);
+            mfmas(fa, fb);
+            if (kt + 1 < KF) {
+                wait_barrier(KF - 2 - kt);
+                read_frags((kt + 1) % kStages, 0, fa, fb);
+            }
+            mfmas(ga, gb);
+        }
     }
     if (k % kBK) {
-        // a last partial step: its buffer was last read kStages steps ago
+        // a last partial step through registers: its buffer was last read
+        // kStages steps ago
         __syncthreads();
         tail_stage(KF, KF % kStages);
         __syncthreads();
-        read_frags(KF % kStages, 0, f0a, f0b);
-        read_frags(KF % kStages, 1, f1a, f1b);
-        mfmas(f0a, f0b);
-        mfmas(f1a, f1b);
+        read_frags(KF % kStages, 0, fa, fb);
+        read_frags(KF % kStages, 1, ga, gb);
+        mfmas(fa, fb);
+        mfmas(ga, gb);
     }
 
     // ---- epilogue ---------------------------------------------------------
