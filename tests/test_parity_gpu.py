@@ -292,3 +292,32 @@ def test_division_scheme_is_correctly_rounded():
         torch.cuda.synchronize()
         print(f"divisor significands [{b0}, {b0 + step}): {int(cnt.item())} mismatches so far", flush=True)
     assert int(cnt.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# a8-a9 for few tokens (m <= 64: the weight-streaming kernel): token counts
+# around every 16-row group, weight rows around every 16-row block, K tails
+# of 16/32/48 bytes and K long enough for several rounds of every wavefront;
+# m = 65 and 80 cross over to the tiled kernel.
+# ---------------------------------------------------------------------------
+SKINNY = [(1, 1, 16), (2, 17, 48), (15, 16, 64), (16, 100, 208), (17, 31, 4096), (31, 15, 1040),
+          (32, 33, 11008), (33, 64, 80), (48, 47, 336), (49, 200, 2048), (63, 65, 4112),
+          (64, 129, 4096), (65, 70, 272), (80, 33, 4096)]
+
+
+@pytest.mark.parametrize("shape", SKINNY, ids=_id)
+def test_skinny_int32(orc, shape):
+    m, n, k = shape
+    rng = np.random.default_rng(m * 31 + n * 17 + k)
+    a, b = _codes(rng, m, k), _codes(rng, n, k)
+    y = _zeros((m, n), torch.int32)
+    B.sq_w8a8_gemm(up(a), None, up(b), None, None, y)
+    torch.cuda.synchronize()
+    assert_equal(down(y), orc.int_gemm(a, b), "acc")
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 33, 64), (16, 200, 4096), (37, 129, 1040), (64, 100, 528)], ids=_id)
+def test_skinny_dequant(orc, shape, out, bias):
+    test_gemm_dequant(orc, shape, out, bias)

@@ -59,3 +59,8 @@ hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsign
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                           void* y, int out_kind, hipStream_t st);
+// the same product for m <= 64 tokens (weight-streaming kernel)
+constexpr int64_t kSkinnyMaxM = 64;
+hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
+                                 const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
+                                 void* y, int out_kind, hipStream_t st);

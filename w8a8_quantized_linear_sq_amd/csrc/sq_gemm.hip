@@ -433,6 +433,9 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                           void* y, int out_kind, hipStream_t st) {
     if (m <= 0 || n <= 0) return hipSuccess;
+    // few tokens: the product streams the weights; the tiled kernel would
+    // leave most CUs idle
+    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, st);
     struct Cfg { int bm, bn; };
     const Cfg cfgs[] = {{256, 256}, {128, 256}, {128, 128}};
     int best = 0;
