@@ -1,0 +1,135 @@
+"""GPU parity at the workloads' full sizes, the path run as the benchmark
+runs it: the running max over the calibration batches (sq_calibrate), the
+smoothing factor and int8 weights (sq_prepare_weight), then the activation
+codes (sq_quantize_act) and the int8 product with its dequantisation
+(sq_w8a8_gemm), or the last two in one call (sq_w8a8_linear).
+
+Every maximum, smoothing factor, scale and int8 code is compared with the
+oracle in full, bit for bit. Outputs are compared in full where the oracle's
+integer product takes seconds (tiny, prefill, decode), else on seeded row
+samples that always include the first and last token (block linears, MLP
+up-projection): fp32 within 1e-6 of |acc sx sw| + |bias|, bf16 within one
+bf16 ulp of the oracle's binary64 result rounded once (with the bias
+cancellation allowance where a bias is added)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, assert_bf16_within_one_ulp, assert_equal, assert_f32_rel, down, require_gpu, up
+from w8a8_quantized_linear_sq_amd import binding as B
+from w8a8_quantized_linear_sq_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    B.lib()
+
+
+def _empty(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device=DEV)
+
+
+def _calibrate(case):
+    run = torch.zeros(case.k, dtype=torch.float32, device=DEV)
+    for cb in case.calib:
+        B.sq_calibrate(up(cb), run)
+    return run
+
+
+def _prepare(w_dev, run, alpha, n, k):
+    s = _empty(k, torch.float32)
+    wq = _empty((n, k), torch.int8)
+    sw = _empty(n, torch.float32)
+    B.sq_prepare_weight(w_dev, run, alpha, s, wq, sw)
+    return s, wq, sw
+
+
+def _rows(m, count, seed):
+    if count is None or count >= m:
+        return np.arange(m)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, m - 1), size=count - 2, replace=False)
+    return np.unique(np.concatenate([[0, m - 1], mid]))
+
+
+def _check_y(orc, y_dev, xq_ref, xs_ref, wq_ref, sw_ref, bias_f, rows):
+    acc = orc.int_gemm(np.ascontiguousarray(xq_ref[rows]), wq_ref)
+    yref = orc.dequant(acc, xs_ref[rows], sw_ref, bias_f)
+    got = down(y_dev[torch.from_numpy(rows).to(DEV)])
+    scale = np.abs(acc.astype(np.float64) * xs_ref[rows][:, None] * sw_ref[None, :])
+    if bias_f is not None:
+        scale = scale + np.abs(bias_f)[None, :]
+    if y_dev.dtype == torch.float32:
+        assert_f32_rel(got, yref, scale)
+    elif bias_f is None:
+        assert_bf16_within_one_ulp(got, orc.to_bf16(yref))
+    else:
+        assert_bf16_within_one_ulp(got, orc.to_bf16(yref), yref, scale)
+
+
+def _run_and_check(orc, case, alphas, sample_rows, out_dtype, fused=False):
+    m, n, k = case.m, case.n, case.k
+    print(f"config {case.name}: m={m} n={n} k={k} alphas={alphas} fused={fused}", flush=True)
+    x_dev, w_dev = up(case.x), up(case.w)
+    bias_dev = None if case.bias is None else up(case.bias)
+    bias_f = None if case.bias is None else case.bias.f32
+
+    run = _calibrate(case)
+    torch.cuda.synchronize()
+    run_ref = np.zeros(k, np.float32)
+    for cb in case.calib:
+        orc.calibrate(cb.f32, run_ref)
+    assert_equal(down(run), run_ref, "running max")
+
+    rows = _rows(m, sample_rows, seed=m + n + k)
+    for alpha in alphas:
+        s, wq, sw = _prepare(w_dev, run, alpha, n, k)
+        y = _empty((m, n), out_dtype)
+        if fused:
+            ws = _empty(B.sq_w8a8_linear_workspace_bytes(m, k), torch.uint8)
+            B.sq_w8a8_linear(x_dev, s, wq, sw, bias_dev, y, ws)
+            xq, xs = B.workspace_views(ws, m, k)
+        else:
+            xq, xs = _empty((m, k), torch.int8), _empty(m, torch.float32)
+            B.sq_quantize_act(x_dev, s, xq, xs)
+            B.sq_w8a8_gemm(xq, xs, wq, sw, bias_dev, y)
+        torch.cuda.synchronize()
+
+        s_ref, wq_ref, sw_ref = orc.prepare_weight(case.w.f32, run_ref, alpha)
+        assert_equal(down(s), s_ref, f"smooth (alpha {alpha})")
+        assert_equal(down(sw), sw_ref, f"w_scale (alpha {alpha})")
+        assert_equal(down(wq), wq_ref, f"w_q (alpha {alpha})")
+        xq_ref, xs_ref = orc.quantize_act(case.x.f32, s_ref)
+        assert_equal(down(xs), xs_ref, f"x_scale (alpha {alpha})")
+        assert_equal(down(xq), xq_ref, f"x_q (alpha {alpha})")
+        _check_y(orc, y, xq_ref, xs_ref, wq_ref, sw_ref, bias_f, rows)
+        del s, wq, sw, y, xq, xs
+
+
+def test_tiny_f32(orc):
+    _run_and_check(orc, inputs.tiny(), (0.5,), None, torch.float32)
+
+
+def test_prefill_2048x4096x4096(orc):
+    _run_and_check(orc, inputs.prefill(), (0.5,), None, torch.bfloat16)
+
+
+def test_decode_16x4096x11008(orc):
+    # the per-call path: activation codes and the product in one call
+    _run_and_check(orc, inputs.decode(), (0.5,), None, torch.bfloat16, fused=True)
+
+
+@pytest.mark.parametrize("layer", range(len(inputs.BLOCK_LINEARS)),
+                         ids=[f"{nm}_{n}x{k}" for nm, n, k in inputs.BLOCK_LINEARS])
+def test_block_linear(orc, layer):
+    _run_and_check(orc, inputs.block_linear(layer), (0.5,), 96, torch.bfloat16)
+
+
+def test_mlp_up_8192x8192x28672_alpha_sweep(orc):
+    case = inputs.mlp_up()
+    _run_and_check(orc, case, case.alphas, 40, torch.bfloat16)

@@ -19,9 +19,9 @@ from w8a8_quantized_linear_sq_amd import inputs
 pytestmark = pytest.mark.gpu
 
 # (m, n, k): single elements, ragged tails of every tile, K tails of 16/32/48,
-# several tiles, the widest K the block uses.
+# several tiles, the largest K accepted (16384).
 SMALL = [(1, 1, 16), (3, 5, 32), (7, 17, 48), (17, 33, 272), (33, 7, 16), (130, 260, 528),
-         (257, 300, 1040), (64, 512, 4096), (5, 40, 11008), (300, 129, 2064)]
+         (257, 300, 1040), (64, 512, 4096), (5, 40, 11008), (300, 129, 2064), (70, 33, 16384)]
 ALPHAS = [0.0, 0.25, 0.5, 0.75, 1.0, 0.3, None]
 
 
