@@ -37,59 +37,64 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Column max of |x| over a group of rows.
-// Block = 4 wavefronts over one strip of 64 16-byte column chunks (512 bf16
-// or 256 fp32 columns); wavefront w takes rows w, w+4, ... of the group with
-// 8 loads in flight; the 4 partial maxima meet in LDS. |x| >= 0, so the
-// order of the binary32 bit patterns as unsigned integers is the order of
-// the values: every max is an exact integer max, independent of order.
+// Block = 4 wavefronts over one strip of 64 / L 16-byte column chunks; a
+// load instruction of a wavefront covers L rows of the strip (64 / L lanes
+// per row), and wavefront w takes row steps w, w+4, ... of the group with 8
+// loads in flight (L > 1 spreads a short batch over more blocks); the
+// partial maxima meet in LDS. |x| >= 0, so the order of the binary32 bit
+// patterns as unsigned integers is the order of the values: every max is an
+// exact integer max, independent of order.
 //   FOLD:    out[j] = max(out[j], max) -- one row group: the owning thread
 //            updates in place; several: integer atomicMax (the running max of
 //            calibration keeps its value across calls);
 //   PARTIAL: out[g * k + j] = max over row group g (plain stores).
 // ---------------------------------------------------------------------------
-template <bool BF16, bool FOLD>
+template <bool BF16, bool FOLD, int L>
 __global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
                                                      int64_t rows_per_group, int64_t k,
                                                      unsigned* __restrict__ out) {
     constexpr int U = 8;
+    constexpr int W = 64 / L;  // chunks per strip
     __shared__ u32x4 red[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t c = (int64_t)blockIdx.x * W + lane % W;
+    const int sub = lane / W;  // row within the instruction's L rows
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_group;
     const int64_t r1 = min(r0 + rows_per_group, rows);
     constexpr uint32_t kMask = BF16 ? 0x7fff7fffu : 0x7fffffffu;
     u32x4 m = {0, 0, 0, 0};
-    auto fold = [&](u32x4 v) {
+    auto merge = [&](u32x4& acc, u32x4 v) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t a = v[i] & kMask;
-            if constexpr (BF16) m[i] = max_u16x2(m[i], a);
-            else m[i] = max(m[i], a);
+            if constexpr (BF16) acc[i] = max_u16x2(acc[i], v[i]);
+            else acc[i] = max(acc[i], v[i]);
         }
     };
+    auto fold = [&](u32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] &= kMask;
+        merge(m, v);
+    };
     if (c < kvec) {
-        int64_t r = r0 + wave;
-        for (; r + 4 * (U - 1) < r1; r += 4 * U) {
+        constexpr int STEP = 4 * L;  // rows per round of the 4 wavefronts
+        int64_t r = r0 + wave * L + sub;
+        for (; r + STEP * (U - 1) < r1; r += STEP * U) {
             u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = x[(r + 4 * u) * kvec + c];
+            for (int u = 0; u < U; ++u) v[u] = x[(r + STEP * u) * kvec + c];
 #pragma unroll
             for (int u = 0; u < U; ++u) fold(v[u]);
         }
-        for (; r < r1; r += 4) fold(x[r * kvec + c]);
+        for (; r < r1; r += STEP) fold(x[r * kvec + c]);
     }
     red[wave][lane] = m;
     __syncthreads();
-    if (wave != 0 || c >= kvec) return;
+    if (wave != 0 || lane >= W || c >= kvec) return;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        const u32x4 o = red[w][lane];
+    for (int w = 0; w < 4; ++w)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (BF16) m[i] = max_u16x2(m[i], o[i]);
-            else m[i] = max(m[i], o[i]);
-        }
-    }
+        for (int j = 0; j < L; ++j)
+            if (w | j) merge(m, red[w][lane + j * W]);
     // the chunk's columns as binary32 bit patterns
     constexpr int NC = BF16 ? 8 : 4;
     uint32_t val[NC];
@@ -121,8 +126,13 @@ __global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x
 // Row groups for a column max over `rows` rows: enough blocks to keep HBM
 // busy (about 1024) but at least 128 rows per group, so that a column gets
 // few partial maxima (atomics when folding, partials when reducing).
+// rows per load instruction: 4 for a batch of up to 2048 rows (four times
+// the blocks, a short batch in flight at once), 1 otherwise (measured best)
+static int colmax_l(int64_t rows) { return rows <= 2048 ? 4 : 1; }
+
 static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups, int64_t& rpg) {
-    gx = (kvec + 63) / 64;
+    const int L = colmax_l(rows);
+    gx = (kvec + 64 / L - 1) / (64 / L);
     int64_t want = 1024 / gx;
     if (want < 1) want = 1;
     groups = (rows + 127) / 128;
@@ -132,18 +142,26 @@ static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups
     groups = (rows + rpg - 1) / rpg;
 }
 
+template <bool FOLD, int L>
+static void launch_colmax_l(const void* x, int bf16, int64_t rows, int64_t kvec, int64_t k, unsigned* out,
+                            int64_t groups, int64_t rpg, hipStream_t st) {
+    dim3 grid((unsigned)((kvec + 64 / L - 1) / (64 / L)), (unsigned)groups);
+    if (bf16)
+        hipLaunchKernelGGL((colmax_kernel<true, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
+                           k, out);
+    else
+        hipLaunchKernelGGL((colmax_kernel<false, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
+                           k, out);
+}
+
 template <bool FOLD>
 static hipError_t launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, unsigned* out, int64_t groups,
                                 int64_t rpg, hipStream_t st) {
     const int64_t kvec = bf16 ? k / 8 : k / 4;
-    const int64_t gx = (kvec + 63) / 64;
-    dim3 grid((unsigned)gx, (unsigned)groups);
-    if (bf16)
-        hipLaunchKernelGGL((colmax_kernel<true, FOLD>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg, k,
-                           out);
-    else
-        hipLaunchKernelGGL((colmax_kernel<false, FOLD>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg, k,
-                           out);
+    switch (colmax_l(rows)) {
+        case 1: launch_colmax_l<FOLD, 1>(x, bf16, rows, kvec, k, out, groups, rpg, st); break;
+        default: launch_colmax_l<FOLD, 4>(x, bf16, rows, kvec, k, out, groups, rpg, st); break;
+    }
     return hipGetLastError();
 }
 
@@ -460,13 +478,17 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
     int T, C;
     if (k8 <= 512) { T = 256; C = k8 <= 256 ? 1 : 2; }
     else if (k8 <= 1024) { T = 512; C = 2; }
+    else if (k8 <= 1408) { T = 704; C = 2; }
     else if (k8 <= 1536) { T = 512; C = 3; }
     else if (k8 <= 2048) { T = 1024; C = 2; }
     else return hipErrorInvalidValue;
-    // a few rows per block (walked with a grid stride) so that the next
-    // row's loads overlap the current row's arithmetic: 2 for rows up to
-    // 4096 channels, 4 beyond (measured best on MI355X)
-    const int64_t rows_per_block = k8 <= 512 ? 2 : 4;
+    // several rows per block (walked with a grid stride): the next row's
+    // loads overlap the current row's arithmetic, and the smoothing factors
+    // are loaded once per block. Rows up to 4096 channels: 2 per block; longer
+    // rows: up to 16 (the factors' load stays well below the rows' own
+    // bytes), but no fewer blocks than CUs. Measured best on MI355X.
+    int64_t rows_per_block = 2;
+    if (k8 > 512) rows_per_block = m >= 16 * 256 ? 16 : (m >= 256 ? m / 256 : 1);
     int64_t blocks = (m + rows_per_block - 1) / rows_per_block;
     if (blocks > 16384) blocks = 16384;
     dim3 grid((unsigned)blocks), block(T);
@@ -475,7 +497,7 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
         hipLaunchKernelGGL((quantize_rows_kernel<BF16, DIV, TT, CC>), grid, block, 0, st, x, s, m, k, q, scale); \
         return hipGetLastError();                                                                             \
     }
-    SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
+    SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(704, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
 #undef SQ_ROWS_CASE
     return hipErrorInvalidValue;
 }
