@@ -1,19 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the SmoothQuant W8A8 linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the whole path over one batch of synthetic input, on
-the transformer block's O projection (M = N = K = 4096, bf16 in and out,
-alpha = 0.5, calibrated on 512 separate tokens fed as 4 batches of 128):
+Default workload (the headline): the transformer block's O projection
+(M = N = K = 4096, bf16 in and out, alpha = 0.5, calibrated on 512 separate
+tokens fed as 4 batches of 128). One step is one pass of the whole path
+over one batch of synthetic input:
   reset the running max -> 4 x sq_calibrate -> sq_prepare_weight ->
   sq_quantize_act -> sq_w8a8_gemm (int8 GEMM + fused dequant).
-Inputs are resident in HBM before the timed region; 4 copies of every buffer
-are rotated so that each step's data is not left in the 256 MB Infinity
-Cache by the previous step. HIP events on the launch stream bracket the
-timed region and every GEMM launch in it; a second pass of the same steps
-with an event between stages gives the per-stage breakdown. Prints one JSON
-line.
+Other workloads (--workload) are the remaining shapes of the method's
+workloads: prefill, the block's qkv / up / down linears and the MLP
+up-projection run the same full step; decode times the per-call path
+(sq_quantize_act + sq_w8a8_gemm) on weights prepared once, as a decode
+step uses them.
+
+Inputs are resident in HBM before the timed region; enough copies of every
+buffer a step reads are rotated (at least 512 MiB per cycle, 2 to 12
+copies) that a step does not find its inputs in the 256 MB Infinity Cache
+left there by the previous step. HIP events on the launch stream bracket
+the timed region and every product launch in it; a second pass of the same
+steps with an event between stages gives the per-stage breakdown. Prints
+one JSON line.
 
 The CPU baseline times the CPU oracle (test infrastructure) on a bounded
 sample of the same workload on this host.
@@ -23,6 +31,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -34,9 +43,27 @@ sys.path.insert(0, ROOT)
 METRIC = "W8A8 SmoothQuant linear TOPS at M=N=K=4096; % of INT8 MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-ROTATE = 4
+ROTATE_BYTES = 512 << 20     # bytes read per rotation cycle, at least
 GEMM_SOURCE = os.path.join(ROOT, "w8a8_quantized_linear_sq_amd", "csrc", "sq_gemm.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_o_proj_4096_traffic.md")
+
+# name -> (description, case factory and arguments, mode)
+WORKLOADS = {
+    "o_proj": ("block O projection, M=N=K=4096, bf16 in/out, alpha=0.5, 512-token calibration in 4 batches",
+               ("block_linear", 1), "full"),
+    "prefill": ("prefill linear, 2048 tokens x 4096 -> 4096, bf16 in/out, alpha=0.5, calibrated on the same tokens",
+                ("prefill",), "full"),
+    "decode": ("decode linear, 16 tokens x 4096 -> 11008, bf16 in/out, alpha=0.5, int8 weights prepared once; "
+               "per call: activation codes + int8 product + dequant", ("decode",), "per_call"),
+    "qkv": ("block QKV projection, 4096 tokens x 4096 -> 12288, bf16, alpha=0.5, 512-token calibration",
+            ("block_linear", 0), "full"),
+    "up": ("block up projection, 4096 tokens x 4096 -> 11008, bf16, alpha=0.5, 512-token calibration",
+           ("block_linear", 2), "full"),
+    "down": ("block down projection, 4096 tokens x 11008 -> 4096, bf16, alpha=0.5, 512-token calibration",
+             ("block_linear", 3), "full"),
+    "mlp_up": ("MLP up-projection, 8192 tokens x 8192 -> 28672, bf16, bias, alpha=0.5 (of the 0.25/0.5/0.75 "
+               "sweep), calibrated on the same tokens", ("mlp_up",), "full"),
+}
 
 
 def _args():
@@ -44,6 +71,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="o_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--counter-pass", action="store_true",
@@ -52,9 +80,10 @@ def _args():
     return p.parse_args()
 
 
-def _gemm_traffic(gemm_launch_count_bytes=None):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    or None when the GEMM source changed since the counters were taken."""
+def _gemm_traffic():
+    """HBM bytes per GEMM launch of the O projection from the committed
+    rocprofv3 counter summary, or None when the GEMM source changed since
+    the counters were taken."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
@@ -68,16 +97,24 @@ def _gemm_traffic(gemm_launch_count_bytes=None):
     return float(m_b.group(1))
 
 
-def cpu_baseline(case, budget_s: float):
-    """The oracle on this host's cores: calibration and weight preparation in
-    full, then activation quantisation + integer GEMM + dequant on as many
-    token rows as fit the time budget; the step time is extrapolated to all
-    M rows (those stages are linear in the rows)."""
+def _make_case(inputs, spec):
+    return getattr(inputs, spec[0])(*spec[1:])
+
+
+def cpu_baseline(case, mode: str, budget_s: float):
+    """The oracle on this host's cores. Full step: calibration and weight
+    preparation in full, then activation quantisation + integer product +
+    dequant on as many token rows as fit the time budget, the step time
+    extrapolated to all M rows (those stages are linear in the rows).
+    Per-call step: activation quantisation + product + dequant of all M rows,
+    repeated while the budget lasts."""
     import numpy as np
     import oracle
 
     o = oracle.get()
     m, n, k = case.m, case.n, case.k
+    bias = None if case.bias is None else case.bias.f32
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
     run = np.zeros(k, np.float32)
     for cb in case.calib:
@@ -85,40 +122,51 @@ def cpu_baseline(case, budget_s: float):
     t1 = time.perf_counter()
     s, wq, sw = o.prepare_weight(case.w.f32, run, 0.5)
     t2 = time.perf_counter()
-    # probe 64 rows to size the sample
-    rows = 64
-    tp = time.perf_counter()
-    xq, sx = o.quantize_act(case.x.f32[:rows], s)
-    acc = o.int_gemm(xq, wq)
-    o.dequant(acc, sx, sw, None)
-    per_row = (time.perf_counter() - tp) / rows
-    left = max(budget_s - (t2 - t0), 1.0)
-    rows = int(min(m, max(64, left / per_row)))
-    tp = time.perf_counter()
-    xq, sx = o.quantize_act(case.x.f32[:rows], s)
-    acc = o.int_gemm(xq, wq)
-    o.dequant(acc, sx, sw, None)
-    t_rows = time.perf_counter() - tp
-    step_s = (t1 - t0) + (t2 - t1) + t_rows * (m / rows)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def rows_pass(rows):
+        tp = time.perf_counter()
+        xq, sx = o.quantize_act(case.x.f32[:rows], s)
+        acc = o.int_gemm(xq, wq)
+        o.dequant(acc, sx, sw, bias)
+        return time.perf_counter() - tp
+
+    if mode == "per_call":
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < budget_s and reps < 50):
+            spent += rows_pass(m)
+            reps += 1
+        step_s = spent / reps
+        sample = (f"weights prepared once ({n}x{k}, not timed, as on the GPU); {reps} per-call passes of "
+                  f"all {m} tokens through activation quantisation, the int8 product (OpenMP over rows) "
+                  f"and dequant: {step_s:.4f} s per call")
+        measured = spent
+    else:
+        probe = min(m, 16)
+        per_row = rows_pass(probe) / probe
+        left = max(budget_s - (t2 - t0), 1.0)
+        rows = int(min(m, max(16, left / per_row)))
+        t_rows = rows_pass(rows)
+        step_s = (t1 - t0) + (t2 - t1) + t_rows * (m / rows)
+        calib_rows = sum(int(c.f32.shape[0]) for c in case.calib)
+        sample = (f"calibration ({calib_rows} tokens) and weight preparation ({n}x{k}) in full, then "
+                  f"{rows} of {m} token rows through activation quantisation, the int8 product (OpenMP "
+                  f"over rows) and dequant; step time extrapolated to {m} rows: {step_s:.2f} s")
+        measured = (t2 - t0) + t_rows
     return {
         "value": round(2.0 * m * n * k / step_s / 1e12, 6),
         "unit": "TOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"calibration (512 tokens) and weight preparation ({n}x{k}) in full, then "
-                   f"{rows} of {m} token rows through activation quantisation, the int8 product "
-                   f"(OpenMP over rows) and dequant; step time extrapolated to {m} rows: "
-                   f"{step_s:.2f} s"),
-        "seconds_measured": round((t2 - t0) + t_rows, 3),
+        "sample": sample,
+        "seconds_measured": round(measured, 3),
     }
 
 
-def counter_pass(torch, B, s, dev, stream):
+def counter_pass(torch, B, s, stream):
     """A copy of known size (reads and writes 256 MiB: torch.neg over 2^26
     fp32) gives the factor between the HBM counters and real bytes; then the
-    GEMM of the benchmark step on prepared operands."""
-    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    product of the benchmark step on prepared operands."""
+    src = torch.ones(1 << 26, dtype=torch.float32, device=s["x"].device)
     dst = torch.empty_like(src)
     B.sq_calibrate(s["calib"][0], s["run"], stream)
     B.sq_prepare_weight(s["w"], s["run"], 0.5, s["smooth"], s["wq"], s["ws"], stream)
@@ -128,7 +176,7 @@ def counter_pass(torch, B, s, dev, stream):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     for _ in range(3):
-        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], None, s["y"], stream)
+        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], s["y"], stream)
     torch.cuda.synchronize()
     print("counter pass done", flush=True)
 
@@ -143,6 +191,7 @@ def main():
         print("bench.py does not run under a multi-rank launcher", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     from w8a8_quantized_linear_sq_amd import binding as B
     from w8a8_quantized_linear_sq_amd import inputs
@@ -154,20 +203,29 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    case = inputs.o_proj()
+    desc, spec, mode = WORKLOADS[args.workload]
+    case = _make_case(inputs, spec)
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
 
     def bf16(t):
-        import numpy as np
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     x0, w0 = bf16(case.x), bf16(case.w)
+    b0 = None if case.bias is None else bf16(case.bias)
     c0 = [bf16(c) for c in case.calib]
+    calib_rows = sum(int(c.shape[0]) for c in c0)
+    # bytes one step reads and writes (the rotated part)
+    if mode == "per_call":
+        set_bytes = m * k * 2 + n * k + 4 * n + 4 * k + m * k + m * n * 2
+    else:
+        set_bytes = m * k * 2 + n * k * 2 + calib_rows * k * 2 + n * k + m * k + m * n * 2
+    rotate = max(2, min(12, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = []
-    for r in range(ROTATE):
+    for _ in range(rotate):
         sets.append(dict(
             x=x0.clone(), w=w0.clone(), calib=[c.clone() for c in c0],
+            bias=None if b0 is None else b0.clone(),
             run=torch.zeros(k, dtype=torch.float32, device=dev),
             smooth=torch.empty(k, dtype=torch.float32, device=dev),
             wq=torch.empty((n, k), dtype=torch.int8, device=dev),
@@ -178,30 +236,45 @@ def main():
     del x0, w0, c0
     stream = torch.cuda.current_stream(dev)
     if args.counter_pass:
-        counter_pass(torch, B, sets[0], dev, stream)
+        counter_pass(torch, B, sets[0], stream)
         return
-    n_stage = 5  # reset+calibrate, prepare, act quant, gemm
+    if mode == "per_call":
+        # weights prepared once per copy, outside the timed region; the bf16
+        # weights are then released
+        for s in sets:
+            for cb in s["calib"]:
+                B.sq_calibrate(cb, s["run"], stream)
+            B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
+        torch.cuda.synchronize()
+        for s in sets:
+            s["w"] = None
+        torch.cuda.empty_cache()
+        stage_names = ["quantize_act", "gemm"]
+    else:
+        stage_names = ["reset+calibrate", "prepare_weight", "quantize_act", "gemm"]
 
     def step(i, ev=None, gemm_ev=None):
-        s = sets[i % ROTATE]
-        if ev is not None:
-            ev[0].record(stream)
-        s["run"].zero_()
-        for cb in s["calib"]:
-            B.sq_calibrate(cb, s["run"], stream)
-        if ev is not None:
-            ev[1].record(stream)
-        B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
-        if ev is not None:
-            ev[2].record(stream)
+        s = sets[i % rotate]
+        marks = iter(ev) if ev is not None else None
+
+        def mark():
+            if marks is not None:
+                next(marks).record(stream)
+
+        mark()
+        if mode == "full":
+            s["run"].zero_()
+            for cb in s["calib"]:
+                B.sq_calibrate(cb, s["run"], stream)
+            mark()
+            B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
+            mark()
         B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
-        if ev is not None:
-            ev[3].record(stream)
+        mark()
         if gemm_ev is not None:
             gemm_ev[0].record(stream)
-        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], None, s["y"], stream)
-        if ev is not None:
-            ev[4].record(stream)
+        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], s["y"], stream)
+        mark()
         if gemm_ev is not None:
             gemm_ev[1].record(stream)
 
@@ -211,7 +284,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     # timed region: K steps; HIP events on the launch stream bracket the
-    # region and every GEMM launch (the GEMM's live average duration)
+    # region and every product launch (its live average duration)
     region = new_events(1, 2)[0]
     gemm_events = new_events(args.steps, 2)
     torch.cuda.synchronize()
@@ -228,25 +301,51 @@ def main():
     # stage breakdown: a second pass of K steps with an event between stages
     # (every event adds a few microseconds between kernels, so this pass is
     # not the throughput figure)
-    events = new_events(args.steps, n_stage)
+    events = new_events(args.steps, len(stage_names) + 1)
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, ev=events[i])
     torch.cuda.synchronize()
-    stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(n_stage - 1)]
-    calib_ms, prep_ms, act_ms, gemm_stage_ms = stage_ms
+    stage_ms = {nm: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
+                for j, nm in enumerate(stage_names)}
+
     ops = 2.0 * m * n * k
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    act_ms = stage_ms["quantize_act"]
     linear_tops = ops / ((act_ms + gemm_ms) * 1e-3) / 1e12
-    # algorithmic bytes of the HBM-bound stages
-    act_bytes = m * k * 2 + m * k + 4 * m + 4 * k
-    prep_bytes = 2 * n * k * 2 + n * k + 4 * n + 8 * k
-    calib_bytes = 512 * k * 2 + 8 * k
-    traffic = _gemm_traffic()
 
+    def hbm(bytes_, ms):
+        gbs = bytes_ / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    # algorithmic bytes of the HBM-bound stages
+    stage_roof = {"quantize_act": hbm(m * k * 2 + m * k + 4 * m + 4 * k, act_ms)}
+    if mode == "full":
+        stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_ms["prepare_weight"])
+        stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_ms["reset+calibrate"])
+    if m <= 64:
+        # the weight-streaming product: bound by reading the int8 weights
+        gbs = (n * k + m * k + 2 * m * n + 4 * (m + n)) / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "weight-streaming int8 product + fused dequant (sq_w8a8_gemm, m <= 64)",
+                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        traffic = _gemm_traffic() if args.workload == "o_proj" else None
+        roof = {"bound": "mfma", "kernel": "int8 GEMM + fused dequant (sq_w8a8_gemm)",
+                "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                "traffic": None if traffic is None else round(traffic)}
+
+    config = {"workload": desc, "m": m, "n": n, "k": k, "alpha": alpha, "in_dtype": "bf16",
+              "out_dtype": "bf16", "bias": case.bias is not None, "rotated_buffer_sets": rotate}
+    if mode == "full":
+        config["calib_tokens"] = calib_rows
+    stages = {nm: round(v * 1e3, 2) for nm, v in stage_ms.items()}
+    stages["note"] = "second pass of the same K steps with an event between stages"
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "o_proj" else f"W8A8 SmoothQuant linear TOPS at M={m} N={n} K={k}",
         "value": round(value, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -257,35 +356,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
-        "data": "synthetic (seeded; 1% outlier input channels x50, W ~ N(0, 0.02), bf16)",
-        "config": {"workload": "block O projection, M=N=K=4096, bf16 in/out, alpha=0.5, "
-                               "512-token calibration in 4 batches",
-                   "m": m, "n": n, "k": k, "alpha": alpha, "in_dtype": "bf16", "out_dtype": "bf16",
-                   "calib_tokens": 512, "rotated_buffer_sets": ROTATE},
-        "roofline": {"bound": "mfma", "kernel": "int8 GEMM + fused dequant (sq_w8a8_gemm)",
-                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": None if traffic is None else round(traffic)},
+        "data": "synthetic (seeded; outlier input channels, W ~ N(0, sigma), bf16)",
+        "config": config,
+        "roofline": roof,
         "gemm_us": round(gemm_ms * 1e3, 2),
-        "stages_us": {"reset+calibrate": round(calib_ms * 1e3, 2), "prepare_weight": round(prep_ms * 1e3, 2),
-                      "quantize_act": round(act_ms * 1e3, 2), "gemm": round(gemm_stage_ms * 1e3, 2),
-                      "note": "second pass of the same K steps with an event between stages"},
-        "stage_rooflines": {
-            "quantize_act": {"bound": "hbm", "achieved": round(act_bytes / (act_ms * 1e-3) / 1e9, 1),
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(act_bytes / (act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "prepare_weight": {"bound": "hbm", "achieved": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1),
-                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(prep_bytes / (prep_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "reset+calibrate": {"bound": "hbm", "achieved": round(calib_bytes / (calib_ms * 1e-3) / 1e9, 1),
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s"},
-        },
+        "stages_us": stages,
+        "stage_rooflines": stage_roof,
         "linear_tops": round(linear_tops, 2),
         "gemm_tops": round(gemm_tops, 2),
         "wall_s_timed": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(case, mode, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 

@@ -426,9 +426,10 @@ hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* w
 
 }  // namespace
 
-// Tile choice: the configuration whose tiles cover m x n with the fewest
-// idle MFMA slots over whole waves of 256 workgroups (one per CU), larger
-// tiles first on ties.
+// Tile choice: the configuration with the least estimated time, whole waves
+// of 256 workgroups (one per CU) times the time of one tile, which is its
+// area over the configuration's measured speed per unit area on MI355X
+// (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs).
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                           void* y, int out_kind, hipStream_t st) {
@@ -436,16 +437,16 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
     // few tokens: the product streams the weights; the tiled kernel would
     // leave most CUs idle
     if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, st);
-    struct Cfg { int bm, bn; };
-    const Cfg cfgs[] = {{256, 256}, {128, 256}, {128, 128}};
+    struct Cfg { int bm, bn; double speed; };
+    const Cfg cfgs[] = {{256, 256, 1.0}, {128, 256, 0.80}, {128, 128, 0.73}};
     int best = 0;
-    double best_eff = -1.0;
+    double best_cost = 0.0;
     for (int i = 0; i < 3; ++i) {
         const int64_t tiles = ((m + cfgs[i].bm - 1) / cfgs[i].bm) * ((n + cfgs[i].bn - 1) / cfgs[i].bn);
         const int64_t waves = (tiles + 255) / 256;
-        const double eff = (double)(m * n) / ((double)waves * 256.0 * cfgs[i].bm * cfgs[i].bn);
-        if (eff > best_eff * 1.05) {
-            best_eff = eff;
+        const double cost = (double)waves * cfgs[i].bm * cfgs[i].bn / cfgs[i].speed;
+        if (i == 0 || cost < best_cost) {
+            best_cost = cost;
             best = i;
         }
     }
