@@ -358,13 +358,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
+                if constexpr (OUT == 1) {
+                    // bf16: lanes 2c and 2c+1 hold columns 2c, 2c+1 of the same
+                    // rows; one DPP swap of one value per row pair lets the
+                    // even lane write (row r, both columns) and the odd lane
+                    // (row r+1, both columns) as one 4-byte store each
+                    const bool odd = lane & 1;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int lr = (r >> 2) * 8 + erow + (r & 3);
-                    int8_t* dst = stage + lr * PITCH + (j * 32 + ecol) * OB;
-                    if constexpr (OUT == 2) *(int*)dst = acc[i][j][r];
-                    else if constexpr (OUT == 0) *(float*)dst = value(i, j, r, sar[r >> 2][r & 3]);
-                    else *(__bf16*)dst = (__bf16)value(i, j, r, sar[r >> 2][r & 3]);
+                    for (int r = 0; r < 16; r += 2) {
+                        const float a0 = value(i, j, r, sar[r >> 2][r & 3]);
+                        const float a1 = value(i, j, r + 1, sar[r >> 2][(r & 3) + 1]);
+                        const float send = odd ? a0 : a1;
+                        const float recv = __int_as_float(
+                            __builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
+                        const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
+                        const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+                                                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+                        const int lr = (r >> 2) * 8 + erow + (r & 3) + (odd ? 1 : 0);
+                        *(uint32_t*)(stage + lr * PITCH + (j * 32 + (ecol & ~1)) * OB) = packed;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lr = (r >> 2) * 8 + erow + (r & 3);
+                        int8_t* dst = stage + lr * PITCH + (j * 32 + ecol) * OB;
+                        if constexpr (OUT == 2) *(int*)dst = acc[i][j][r];
+                        else *(float*)dst = value(i, j, r, sar[r >> 2][r & 3]);
+                    }
                 }
             }
             // the same wavefront reads back what it wrote: LDS keeps its order
