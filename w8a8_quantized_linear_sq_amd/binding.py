@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import threading
 
 import torch
 
@@ -82,6 +83,45 @@ def _check(fn: str, status: int) -> int:
     return status
 
 
+class _Capture(threading.local):
+    on = False
+    call = None
+
+
+_capture = _Capture()
+
+
+def _invoke(name: str, *args):
+    """Calls the C entry point, or records the marshalled call for prepared()."""
+    if _capture.on:
+        _capture.call = (name, args)
+        return SQ_OK
+    return _check(name, getattr(lib(), name)(*args))
+
+
+def prepared(fn, *args, **kwargs):
+    """Marshals one call of a wrapper below once and returns a zero-argument
+    callable that repeats exactly that C call (same pointers, sizes and
+    stream) and checks its status: for launch loops where the per-call
+    Python work would otherwise be paced against the GPU."""
+    _capture.on = True
+    try:
+        fn(*args, **kwargs)
+        name, cargs = _capture.call
+    finally:
+        _capture.on = False
+        _capture.call = None
+    cfn = getattr(lib(), name)
+
+    def call():
+        status = cfn(*cargs)
+        if status < 0:
+            raise SQError(name, status, status_string(status))
+        return status
+
+    return call
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return SQ_F32
@@ -121,8 +161,8 @@ def sq_calibrate(x: torch.Tensor, running_max_abs: torch.Tensor, stream=None) ->
     k = x.shape[-1]
     rows = x.numel() // k if k else 0
     _need_dtype(running_max_abs, torch.float32, "running_max_abs")
-    return _check("sq_calibrate", lib().sq_calibrate(_ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
-                                                     _stream(stream, x)))
+    return _invoke("sq_calibrate", _ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
+                   _stream(stream, x))
 
 
 def sq_prepare_weight(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: float, smooth: torch.Tensor,
@@ -135,9 +175,8 @@ def sq_prepare_weight(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: fl
     _need_dtype(w_scale, torch.float32, "w_scale")
     if x_max_abs is not None:
         _need_dtype(x_max_abs, torch.float32, "x_max_abs")
-    return _check("sq_prepare_weight",
-                  lib().sq_prepare_weight(_ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), float(alpha),
-                                          _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w)))
+    return _invoke("sq_prepare_weight", _ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), float(alpha),
+                   _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w))
 
 
 def sq_quantize_act(x: torch.Tensor, smooth: torch.Tensor, x_q: torch.Tensor, x_scale: torch.Tensor,
@@ -146,9 +185,8 @@ def sq_quantize_act(x: torch.Tensor, smooth: torch.Tensor, x_q: torch.Tensor, x_
     m, k = x.shape
     _need_dtype(x_q, torch.int8, "x_q")
     _need_dtype(x_scale, torch.float32, "x_scale")
-    return _check("sq_quantize_act",
-                  lib().sq_quantize_act(_ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(x_q), _ptr(x_scale),
-                                        _stream(stream, x)))
+    return _invoke("sq_quantize_act", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(x_q), _ptr(x_scale),
+                   _stream(stream, x))
 
 
 def sq_w8a8_gemm(x_q: torch.Tensor, x_scale: torch.Tensor | None, w_q: torch.Tensor,
@@ -157,25 +195,22 @@ def sq_w8a8_gemm(x_q: torch.Tensor, x_scale: torch.Tensor | None, w_q: torch.Ten
     m, k = x_q.shape
     n = w_q.shape[0]
     bt = _dtype_code(bias) if bias is not None else SQ_F32
-    return _check("sq_w8a8_gemm",
-                  lib().sq_w8a8_gemm(_ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
-                                     _ptr(y), _dtype_code(y), _stream(stream, x_q)))
+    return _invoke("sq_w8a8_gemm", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
+                   _ptr(y), _dtype_code(y), _stream(stream, x_q))
 
 
 def sq_selfcheck_reciprocal(mismatches: torch.Tensor, stream=None) -> int:
     """Adds to mismatches[0] (int64, device) the count of s in [2^-100, 2^100)
     whose kernel reciprocal differs from the IEEE 1/s."""
     _need_dtype(mismatches, torch.int64, "mismatches")
-    return _check("sq_selfcheck_reciprocal",
-                  lib().sq_selfcheck_reciprocal(_ptr(mismatches), _stream(stream, mismatches)))
+    return _invoke("sq_selfcheck_reciprocal", _ptr(mismatches), _stream(stream, mismatches))
 
 
 def sq_selfcheck_division(b_begin: int, b_end: int, mismatches: torch.Tensor, stream=None) -> int:
     """Adds to mismatches[0] (int64, device) the count of significand pairs
     (divisors [b_begin, b_end)) whose kernel quotient differs from IEEE a/b."""
     _need_dtype(mismatches, torch.int64, "mismatches")
-    return _check("sq_selfcheck_division",
-                  lib().sq_selfcheck_division(b_begin, b_end, _ptr(mismatches), _stream(stream, mismatches)))
+    return _invoke("sq_selfcheck_division", b_begin, b_end, _ptr(mismatches), _stream(stream, mismatches))
 
 
 def sq_w8a8_linear_workspace_bytes(m: int, k: int) -> int:
@@ -198,10 +233,8 @@ def sq_w8a8_linear(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_s
     if bias is not None:
         _need_dtype(bias, x.dtype, "bias")
     nbytes = workspace.numel() * workspace.element_size()
-    return _check("sq_w8a8_linear",
-                  lib().sq_w8a8_linear(_ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale), n,
-                                       _ptr(bias), _ptr(y), _dtype_code(y), _ptr(workspace), nbytes,
-                                       _stream(stream, x)))
+    return _invoke("sq_w8a8_linear", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale), n,
+                   _ptr(bias), _ptr(y), _dtype_code(y), _ptr(workspace), nbytes, _stream(stream, x))
 
 
 # ---------------------------------------------------------------------------

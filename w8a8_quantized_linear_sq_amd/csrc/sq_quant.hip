@@ -484,10 +484,11 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
     else return hipErrorInvalidValue;
     // several rows per block (walked with a grid stride): the next row's
     // loads overlap the current row's arithmetic, and the smoothing factors
-    // are loaded once per block. Rows up to 4096 channels: 2 per block; longer
+    // are loaded once per block. Rows up to 4096 channels: 2 per block (1 for
+    // fewer than 1024 rows, which are latency-bound); longer
     // rows: up to 16 (the factors' load stays well below the rows' own
     // bytes), but no fewer blocks than CUs. Measured best on MI355X.
-    int64_t rows_per_block = 2;
+    int64_t rows_per_block = m >= 1024 ? 2 : 1;  // few rows: one block each
     if (k8 > 512) rows_per_block = m >= 16 * 256 ? 16 : (m >= 256 ? m / 256 : 1);
     int64_t blocks = (m + rows_per_block - 1) / rows_per_block;
     if (blocks > 16384) blocks = 16384;
