@@ -53,6 +53,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "sqo_smooth_weight": ([_P, _P, _I64, _I64, _P], None),
         "sqo_smooth_act": ([_P, _P, _I64, _I64, _P], None),
         "sqo_quantize_rows": ([_P, _I64, _I64, _P, _P], None),
+        "sqo_quantize_tensor": ([_P, _I64, _P, _P], None),
         "sqo_int_gemm": ([_P, _P, _I64, _I64, _I64, _P], _I64),
         "sqo_dequant": ([_P, _P, _P, _P, _I64, _I64, _P], None),
         "sqo_simulated_forward": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], None),
@@ -142,6 +143,27 @@ class Oracle:
         sc = np.empty(r, np.float32)
         self.lib.sqo_quantize_rows(self._ptr(v), r, k, self._ptr(q), self._ptr(sc))
         return q, sc
+
+    def quantize_tensor(self, v):
+        """quantize_tensor of the page "quantized_linear.py" (8 bits): one
+        scale for the whole array; returns (int8 codes of v's shape, the
+        float32 scale)."""
+        v = self._f32(v)
+        q = np.empty(v.shape, np.int8)
+        sc = np.empty(1, np.float32)
+        self.lib.sqo_quantize_tensor(self._ptr(v), v.size, self._ptr(q), self._ptr(sc))
+        return q, np.float32(sc[0])
+
+    def linear_per_tensor(self, x, w, bias=None):
+        """QuantizedLinear of the page "quantized_linear.py" on the integer
+        route: per-tensor codes of x and w, the int32 product, then
+        acc * sx * sw + bias in binary64. Returns (xq, sx, wq, sw, acc, y)."""
+        xq, sx = self.quantize_tensor(x)
+        wq, sw = self.quantize_tensor(w)
+        acc = self.int_gemm(xq, wq)
+        m, n = acc.shape
+        y = self.dequant(acc, np.full(m, sx, np.float32), np.full(n, sw, np.float32), bias)
+        return xq, sx, wq, sw, acc, y
 
     def int_gemm(self, xq, wq) -> np.ndarray:
         """INT8 x INT8 -> INT32: acc[t, o] = sum_j xq[t, j] wq[o, j]."""

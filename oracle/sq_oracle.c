@@ -23,6 +23,8 @@
  *     the product of the dequantised operands, then + bias. The page notes
  *     there that real hardware does INT8 x INT8 -> INT32 -> fp32; this file
  *     computes exactly that integer product.
+ * and, for the per-tensor variant, the page "quantized_linear.py"
+ * (quantize_tensor, QuantizedLinear).
  *
  * Readings where the page is silent or garbled (each one also listed in
  * the design notes of the repository):
@@ -233,6 +235,41 @@ void sqo_quantize_rows(const float* v, int64_t rows, int64_t k, int8_t* q,
             if (c < (float)SQO_QMIN) c = (float)SQO_QMIN;
             q[r * k + j] = (int8_t)c;
         }
+    }
+}
+
+/* ---------------------------------------------------------------------
+ * Per-tensor variant, page "quantized_linear.py", quantize_tensor with
+ * num_bits = 8 (range [-128, 127]): one scale for the whole tensor,
+ *   scale = max_i |x_i| / 127                               (binary32)
+ *   scale = 1 when that value is below 1e-8 (the page's replacement)
+ *   q_i   = clamp(round_even(x_i / scale), -128, 127)
+ * The page returns the dequantised q * scale; its QuantizedLinear
+ * multiplies the two dequantised operands and adds the bias, which is the
+ * integer product (sqo_int_gemm) times the two scalars plus the bias, up to
+ * rounding. bf16 tensors are widened to fp32 by the caller (R9).
+ * ------------------------------------------------------------------ */
+void sqo_quantize_tensor(const float* x, int64_t count, int8_t* q, float* scale_out)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < count; ++i) m = fmax_f(m, fabsf(x[i]));
+#if SQO_MUTANT == 14
+    /* MUTANT 14: the per-row floor rule instead of the replacement by 1. */
+    float sc = fmax_f(m, SQO_FLOOR) / (float)SQO_QMAX;
+#elif SQO_MUTANT == 15
+    /* MUTANT 15: divides the tensor max by 128 instead of 127. */
+    float sc = m / 128.0f;
+    if (sc < SQO_FLOOR) sc = 1.0f;
+#else
+    float sc = m / (float)SQO_QMAX;
+    if (sc < SQO_FLOOR) sc = 1.0f;
+#endif
+    *scale_out = sc;
+    for (int64_t i = 0; i < count; ++i) {
+        float c = sqo_round_even(x[i] / sc);
+        if (c > (float)SQO_QMAX) c = (float)SQO_QMAX;
+        if (c < (float)SQO_QMIN) c = (float)SQO_QMIN;
+        q[i] = (int8_t)c;
     }
 }
 

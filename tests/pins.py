@@ -401,4 +401,74 @@ def pin_uncalibrated(o):
     assert np.array_equal(xq, qx) and np.array_equal(sx, scx)
 
 
+# ---------------------------------------------------------------------------
+# Per-tensor variant: page "quantized_linear.py", quantize_tensor (8 bits,
+# range [-128, 127], one scale max|x| / 127, replaced by 1 below 1e-8) and
+# QuantizedLinear (the dequantised operands multiplied, then + bias).
+# ---------------------------------------------------------------------------
+def _check_tensor_exact(v, q, sc):
+    m = max(Fraction(float(abs(t))) for t in v.ravel())
+    want = rn_f32(m / 127)
+    if want < FLOOR:
+        want = Fraction(1)
+    assert Fraction(float(sc)) == want
+    for idx, val in np.ndenumerate(v):
+        quo = rn_f32(Fraction(float(val)) / want)
+        c = min(127, max(-128, round_half_even(quo)))
+        assert int(q[idx]) == c, (idx, float(val), int(q[idx]), c)
+
+
+def pin_per_tensor_codes_exact(o):
+    rng = _rng(91)
+    for v in (_outlier_acts(rng, 5, 24), _with_ties(rng, 4, 16),
+              rng.standard_normal((3, 7), dtype=np.float32) * np.float32(1e-3)):
+        q, sc = o.quantize_tensor(v)
+        _check_tensor_exact(v, q, sc)
+
+
+def pin_per_tensor_replacement(o):
+    """Below 1e-8 the scale is 1 (not a floored value); just above, it is
+    max / 127 itself."""
+    q, sc = o.quantize_tensor(np.zeros((3, 4), np.float32))
+    assert sc == np.float32(1.0) and not q.any()
+    v = np.array([1e-7, -5e-7, 1.2e-6], np.float32)      # 1.2e-6 / 127 < 1e-8
+    q, sc = o.quantize_tensor(v)
+    assert sc == np.float32(1.0) and not q.any()
+    v = np.array([2e-6, -1e-6, 0.0], np.float32)          # 2e-6 / 127 > 1e-8
+    q, sc = o.quantize_tensor(v)
+    assert Fraction(float(sc)) == rn_f32(Fraction(float(np.float32(2e-6))) / 127)
+    assert q[0] == 127 and q[2] == 0
+    _check_tensor_exact(v, q, sc)
+
+
+def pin_per_tensor_is_one_row(o):
+    """One scale for the whole tensor: the flattened tensor quantised as a
+    single row (max/127 above 1e-8, so the floor and the replacement agree);
+    reshaping and permuting the tensor moves the codes with the values."""
+    rng = _rng(92)
+    v = _outlier_acts(rng, 6, 20, chans=(3,), mult=30.0)
+    q, sc = o.quantize_tensor(v)
+    qr, scr = o.quantize_rows(v.reshape(1, -1))
+    assert sc == scr[0] and np.array_equal(q.reshape(1, -1), qr)
+    perm = rng.permutation(v.size)
+    qp, scp = o.quantize_tensor(v.ravel()[perm].reshape(10, 12))
+    assert scp == sc and np.array_equal(qp.ravel(), q.ravel()[perm])
+    assert np.abs(q).max() == 127 and q.min() >= -127
+
+
+def pin_per_tensor_linear(o):
+    """acc * sx * sw + bias equals the page's QuantizedLinear route (the
+    dequantised operands multiplied, then + bias) up to binary64 rounding,
+    and the integer product is the brute-force one."""
+    rng = _rng(93)
+    x = _outlier_acts(rng, 5, 40, chans=(2,))
+    w = rng.standard_normal((6, 40), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal(6, dtype=np.float32) * np.float32(0.01)
+    xq, sx, wq, sw, acc, y = o.linear_per_tensor(x, w, b)
+    assert np.array_equal(acc, xq.astype(np.int64) @ wq.astype(np.int64).T)
+    ysim = o.simulated_forward(xq, np.full(5, sx, np.float32), wq, np.full(6, sw, np.float32), b)
+    scale = np.abs(acc.astype(np.float64) * float(sx) * float(sw)) + np.abs(b)[None, :]
+    assert np.all(np.abs(y - ysim) <= 1e-12 * scale)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -17,6 +17,8 @@ MUTANTS = {
     10: "row max divided by 128",
     12: "powers multiplied instead of divided",
     13: "calibration max without abs",
+    14: "per-tensor scale floored instead of replaced by 1",
+    15: "per-tensor max divided by 128",
 }
 
 
