@@ -160,6 +160,36 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * sq_quantize_tensor -- per-tensor symmetric int8 (the per-tensor variant).
+ * Follows quantize_tensor (num_bits = 8) of the page "quantized_linear.py":
+ * one scale for the whole tensor,
+ *   scale = f32(max_i |x_i| / 127), replaced by 1 when below 1e-8
+ *   q_i   = clamp(round_half_even(f32(x_i / scale)), -128, 127)
+ * (the page returns q * scale; the codes and the scale are returned here).
+ *   x      [count] in xt (F32 or BF16), 16-byte aligned
+ *   count  >= 1, a multiple of 16
+ *   q      [count] int8 out, 16-byte aligned (also scratch during the call:
+ *          it holds per-block maxima until the codes overwrite them)
+ *   scale  [1] fp32 out, device memory
+ */
+sq_status sq_quantize_tensor(const void* x, sq_dtype xt, int64_t count, int8_t* q,
+                             float* scale, void* stream);
+
+/*
+ * sq_w8a8_gemm_per_tensor -- sq_w8a8_gemm with one activation scale and one
+ * weight scale (the per-tensor variant): the page "quantized_linear.py",
+ * QuantizedLinear.forward, multiplies the per-tensor dequantised input and
+ * weight and adds the bias; on the integer route that is
+ *   y[t][o] = f32(acc[t][o]) * x_scale[0] * w_scale[0] + bias[o].
+ * Arguments as sq_w8a8_gemm, except x_scale and w_scale point to a single
+ * fp32 value each (device memory, e.g. from sq_quantize_tensor).
+ */
+sq_status sq_w8a8_gemm_per_tensor(const int8_t* x_q, const float* x_scale, int64_t m,
+                                  const int8_t* w_q, const float* w_scale, int64_t n,
+                                  int64_t k, const void* bias, sq_dtype bias_t, void* y,
+                                  sq_dtype yt, void* stream);
+
+/*
  * sq_selfcheck_reciprocal -- device self-check behind the activation path.
  * For bf16 activations, sq_quantize_act / sq_w8a8_linear form x / s as
  * fma(fma(-q0, s, x), y, q0) with q0 = x * y and y the correctly rounded

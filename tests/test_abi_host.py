@@ -142,3 +142,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_quantize_tensor_errors(L):
+    f = L.sq_quantize_tensor
+    assert f(OK_PTR, B.SQ_I32, 64, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, 0, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, -16, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 40, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(None, B.SQ_BF16, 64, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 64, None, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 64, OK_PTR, None, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 64, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN
+
+
+def test_gemm_per_tensor_errors(L):
+    f = L.sq_w8a8_gemm_per_tensor
+    args = dict(xq=OK_PTR, sx=OK_PTR, m=4, wq=OK_PTR, sw=OK_PTR, n=8, k=64, bias=None, bt=B.SQ_F32, y=OK_PTR,
+                yt=B.SQ_F32)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["xq"], a["sx"], a["m"], a["wq"], a["sw"], a["n"], a["k"], a["bias"], a["bt"], a["y"], a["yt"], None)
+
+    assert call(yt=9) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=8) == B.SQ_ERR_ALIGN
+    assert call(sw=None) == B.SQ_ERR_ARG
+    assert call(y=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0) == B.SQ_OK  # nothing to do, nothing launched

@@ -133,3 +133,27 @@ def test_block_linear(orc, layer):
 def test_mlp_up_8192x8192x28672_alpha_sweep(orc):
     case = inputs.mlp_up()
     _run_and_check(orc, case, case.alphas, 40, torch.bfloat16)
+
+
+def test_per_tensor_o_proj_4096(orc):
+    """The per-tensor variant (page "quantized_linear.py") at the O
+    projection's size: codes and scales of X and W in full, the output on
+    sampled rows."""
+    case = inputs.o_proj()
+    m, n, k = case.m, case.n, case.k
+    print(f"per-tensor {case.name}", flush=True)
+    xq, sx = _empty((m, k), torch.int8), _empty(1, torch.float32)
+    wq, sw = _empty((n, k), torch.int8), _empty(1, torch.float32)
+    B.sq_quantize_tensor(up(case.x), xq, sx)
+    B.sq_quantize_tensor(up(case.w), wq, sw)
+    y = _empty((m, n), torch.bfloat16)
+    B.sq_w8a8_gemm_per_tensor(xq, sx, wq, sw, None, y)
+    torch.cuda.synchronize()
+    xq_ref, sx_ref = orc.quantize_tensor(case.x.f32)
+    wq_ref, sw_ref = orc.quantize_tensor(case.w.f32)
+    assert_equal(down(sx)[0], sx_ref, "x scale")
+    assert_equal(down(sw)[0], sw_ref, "w scale")
+    assert_equal(down(xq), xq_ref, "x codes")
+    assert_equal(down(wq), wq_ref, "w codes")
+    rows = _rows(m, 64, seed=17)
+    _check_y(orc, y, xq_ref, np.full(m, sx_ref, np.float32), wq_ref, np.full(n, sw_ref, np.float32), None, rows)

@@ -321,3 +321,80 @@ def test_skinny_int32(orc, shape):
 @pytest.mark.parametrize("shape", [(1, 33, 64), (16, 200, 4096), (37, 129, 1040), (64, 100, 528)], ids=_id)
 def test_skinny_dequant(orc, shape, out, bias):
     test_gemm_dequant(orc, shape, out, bias)
+
+
+# ---------------------------------------------------------------------------
+# Per-tensor variant (page "quantized_linear.py": quantize_tensor,
+# QuantizedLinear): one scale per tensor, replaced by 1 below 1e-8
+# ---------------------------------------------------------------------------
+TENSOR_SHAPES = [(1, 16), (3, 48), (130, 528), (257, 1040), (1000, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", TENSOR_SHAPES, ids=_id)
+def test_quantize_tensor(orc, shape, dtype):
+    m, k = shape
+    c = inputs.small(m, 8, k, seed=11 + m + k, dtype=dtype, bias=False)
+    q = _zeros((m, k), torch.int8)
+    sc = _zeros(1, torch.float32)
+    B.sq_quantize_tensor(up(c.x), q, sc)
+    torch.cuda.synchronize()
+    q_ref, sc_ref = orc.quantize_tensor(c.x.f32)
+    assert_equal(down(sc)[0], sc_ref, "scale")
+    assert_equal(down(q), q_ref, "codes")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_tensor_replacement(orc, dtype):
+    """An all-zero tensor and one whose max / 127 is below 1e-8 both get the
+    scale 1 (and zero codes); just above, the scale is max / 127."""
+    for v in (np.zeros((4, 32), np.float32),
+              np.full((2, 16), 1e-6, np.float32) * np.linspace(-1, 1, 32, dtype=np.float32).reshape(2, 16),
+              np.full((2, 16), 2e-6, np.float32) * np.linspace(-1, 1, 32, dtype=np.float32).reshape(2, 16)):
+        if dtype == "bf16":
+            bits = inputs.bf16_bits(v)
+            v, x_dev = inputs.bf16_to_f32(bits), up(bits)
+        else:
+            x_dev = up(v)
+        q = _zeros(v.shape, torch.int8)
+        sc = _zeros(1, torch.float32)
+        B.sq_quantize_tensor(x_dev, q, sc)
+        torch.cuda.synchronize()
+        q_ref, sc_ref = orc.quantize_tensor(v)
+        assert_equal(down(sc)[0], sc_ref, "scale")
+        assert_equal(down(q), q_ref, "codes")
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 5, 32), (16, 200, 4096), (64, 129, 528), (130, 260, 528),
+                                   (257, 300, 1040)], ids=_id)
+def test_gemm_per_tensor(orc, shape, out, bias):
+    """Codes and scales from sq_quantize_tensor, then the per-tensor product
+    (both kernels: m <= 64 streams the weights, larger m is tiled)."""
+    m, n, k = shape
+    c = inputs.small(m, n, k, seed=5 + m + n + k, dtype="bf16", bias=bias is not None)
+    x_dev, w_dev = up(c.x), up(c.w)
+    xq, sx = _zeros((m, k), torch.int8), _zeros(1, torch.float32)
+    wq, sw = _zeros((n, k), torch.int8), _zeros(1, torch.float32)
+    B.sq_quantize_tensor(x_dev, xq, sx)
+    B.sq_quantize_tensor(w_dev, wq, sw)
+    bias_f = bias_t = None
+    if bias == "f32":
+        bias_f = c.bias.f32
+        bias_t = up(bias_f)
+    elif bias == "bf16":
+        bias_f, bias_t = c.bias.f32, up(c.bias)
+    y = _zeros((m, n), torch.float32 if out == "f32" else torch.bfloat16)
+    B.sq_w8a8_gemm_per_tensor(xq, sx, wq, sw, bias_t, y)
+    torch.cuda.synchronize()
+    xq_ref, sx_ref, wq_ref, sw_ref, acc, yref = orc.linear_per_tensor(c.x.f32, c.w.f32, bias_f)
+    assert_equal(down(xq), xq_ref, "x codes")
+    assert_equal(down(wq), wq_ref, "w codes")
+    scale = np.abs(acc.astype(np.float64) * float(sx_ref) * float(sw_ref))
+    if bias_f is not None:
+        scale = scale + np.abs(bias_f)[None, :]
+    if out == "f32":
+        assert_f32_rel(down(y), yref, scale)
+    else:
+        assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)

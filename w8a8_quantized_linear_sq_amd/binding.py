@@ -43,6 +43,8 @@ _SIGNATURES = {
     "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
     "sq_status_string": ([_E], ctypes.c_char_p),
     "sq_abi_version": ([], _E),
+    "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
+    "sq_w8a8_gemm_per_tensor": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_selfcheck_reciprocal": ([_P, _P], _E),
     "sq_selfcheck_division": ([ctypes.c_uint, ctypes.c_uint, _P, _P], _E),
 }
@@ -197,6 +199,26 @@ def sq_w8a8_gemm(x_q: torch.Tensor, x_scale: torch.Tensor | None, w_q: torch.Ten
     bt = _dtype_code(bias) if bias is not None else SQ_F32
     return _invoke("sq_w8a8_gemm", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
                    _ptr(y), _dtype_code(y), _stream(stream, x_q))
+
+
+def sq_quantize_tensor(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None) -> int:
+    """Per-tensor int8 codes of x (any shape, contiguous) and its one scale."""
+    _need_dtype(q, torch.int8, "q")
+    _need_dtype(scale, torch.float32, "scale")
+    if q.numel() != x.numel() or scale.numel() < 1:
+        raise ValueError("q must have x's size and scale at least one element")
+    return _invoke("sq_quantize_tensor", _ptr(x), _dtype_code(x), x.numel(), _ptr(q), _ptr(scale),
+                   _stream(stream, x))
+
+
+def sq_w8a8_gemm_per_tensor(x_q: torch.Tensor, x_scale: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                            bias: torch.Tensor | None, y: torch.Tensor, stream=None) -> int:
+    """y = x_q w_q^T * x_scale[0] * w_scale[0] (+ bias)."""
+    m, k = x_q.shape
+    n = w_q.shape[0]
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_w8a8_gemm_per_tensor", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k,
+                   _ptr(bias), bt, _ptr(y), _dtype_code(y), _stream(stream, x_q))
 
 
 def sq_selfcheck_reciprocal(mismatches: torch.Tensor, stream=None) -> int:

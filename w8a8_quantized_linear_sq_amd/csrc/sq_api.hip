@@ -125,7 +125,25 @@ sq_status sq_w8a8_gemm(const int8_t* x_q, const float* x_scale, int64_t m, const
     sq_status st = check_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
     if (st != SQ_OK || m == 0) return st;
     return launched(sq_launch_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
-                                   out_kind(yt), as_stream(stream)));
+                                   out_kind(yt), 0, as_stream(stream)));
+}
+
+sq_status sq_quantize_tensor(const void* x, sq_dtype xt, int64_t count, int8_t* q, float* scale, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (count <= 0 || count > ((int64_t)1 << 40)) return SQ_ERR_SHAPE;
+    if (count % 16) return SQ_ERR_ALIGN;
+    if (!x || !q || !scale) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scale & 3u) != 0) return SQ_ERR_ALIGN;
+    return launched(sq_launch_quantize_tensor(x, xt == SQ_BF16, count, q, scale, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_per_tensor(const int8_t* x_q, const float* x_scale, int64_t m, const int8_t* w_q,
+                                  const float* w_scale, int64_t n, int64_t k, const void* bias, sq_dtype bias_t,
+                                  void* y, sq_dtype yt, void* stream) {
+    sq_status st = check_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    return launched(sq_launch_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
+                                   out_kind(yt), 1, as_stream(stream)));
 }
 
 sq_status sq_selfcheck_reciprocal(unsigned long long* mismatches, void* stream) {
@@ -164,7 +182,7 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const
     hipStream_t s = as_stream(stream);
     hipError_t e = sq_launch_quantize_act(x, xt == SQ_BF16, smooth, m, k, xq, xs, s);
     if (e == hipSuccess)
-        e = sq_launch_gemm(xq, xs, m, w_q, w_scale, n, k, bias, bias_kind(bias, xt), y, out_kind(yt), s);
+        e = sq_launch_gemm(xq, xs, m, w_q, w_scale, n, k, bias, bias_kind(bias, xt), y, out_kind(yt), 0, s);
     return launched(e);
 }
 

@@ -49,18 +49,23 @@ hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, in
                                      int64_t k, int8_t* wq, float* w_scale, hipStream_t st);
 hipError_t sq_launch_quantize_act(const void* x, int bf16, const float* s, int64_t m, int64_t k,
                                   int8_t* xq, float* x_scale, hipStream_t st);
+// per-tensor codes and scale of x[count] (count a multiple of 16; q 16-byte
+// aligned, also holds the block maxima until the codes overwrite them)
+hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int8_t* q, float* scale,
+                                     hipStream_t st);
 // counts s in [2^-100, 2^100) whose kernel reciprocal differs from IEEE 1/s
 hipError_t sq_launch_selfcheck_reciprocal(unsigned long long* mismatches, hipStream_t st);
 // counts significand pairs (divisors [b_begin, b_end)) where the kernels'
 // quotient differs from IEEE a / b
 hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
                                         hipStream_t st);
-// out_kind: 0 fp32, 1 bf16, 2 int32; bias_kind: 0 none, 1 fp32, 2 bf16
+// out_kind: 0 fp32, 1 bf16, 2 int32; bias_kind: 0 none, 1 fp32, 2 bf16;
+// scalar_scales: sx and sw are single values (per-tensor) instead of [m], [n]
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
-                          void* y, int out_kind, hipStream_t st);
+                          void* y, int out_kind, int scalar_scales, hipStream_t st);
 // the same product for m <= 64 tokens (weight-streaming kernel)
 constexpr int64_t kSkinnyMaxM = 64;
 hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                                  const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
-                                 void* y, int out_kind, hipStream_t st);
+                                 void* y, int out_kind, int scalar_scales, hipStream_t st);

@@ -100,7 +100,7 @@ template <int BM, int BN, int WGM, int WGN, int OUT>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
-    int bias_kind, void* __restrict__ Y, int grid_m, int grid_n) {
+    int bias_kind, void* __restrict__ Y, int grid_m, int grid_n, int scalar_scales) {
     constexpr int NW = WGM * WGN;                 // wavefronts (WGM x WGN grid)
     constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wavefront block
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     // share the LDS wait counter and may return out of order, so while one
     // is outstanding every LDS wait in the loop would have to drain all LDS
     // reads. Consume them here, before the loop.
-    asm volatile("" ::"s"(sa), "s"(sb), "s"(bias), "s"(Y), "s"(bias_kind));
+    asm volatile("" ::"s"(sa), "s"(sb), "s"(bias), "s"(Y), "s"(bias_kind), "s"(scalar_scales));
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
         if (st < KF) issue_stage(st, st);
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
         swc[j] = 0.0f;
         bc[j] = 0.0f;
         if constexpr (OUT != 2) {
-            swc[j] = sb[col];
+            swc[j] = sb[scalar_scales ? 0 : col];
             if (bias_kind == 1) bc[j] = ((const float*)bias)[col];
             else if (bias_kind == 2) bc[j] = __uint_as_float((uint32_t)((const uint16_t*)bias)[col] << 16);
         }
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     constexpr int SLAB_CHUNKS = 32 * ROW_CHUNKS;
     static_assert(NW * 32 * PITCH <= (int)sizeof(smem), "epilogue staging exceeds LDS");
     const bool whole = (m0 + BM <= m) && (n0 + BN <= n) && (n % (16 / OB) == 0) &&
-                       (((uintptr_t)sa & 15) == 0) && (((uintptr_t)Y & 15) == 0);
+                       (scalar_scales || ((uintptr_t)sa & 15) == 0) && (((uintptr_t)Y & 15) == 0);
     if (whole) {
         __syncthreads();  // every wavefront is done with the operand buffers
         int8_t* stage = smem + wave * 32 * PITCH;
@@ -352,7 +352,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
             if constexpr (OUT != 2) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 v = *(const float4*)(sa + rbase + q * 8 + erow);
+                    const float4 v = scalar_scales ? make_float4(sa[0], sa[0], sa[0], sa[0])
+                                                   : *(const float4*)(sa + rbase + q * 8 + erow);
                     sar[q][0] = v.x; sar[q][1] = v.y; sar[q][2] = v.z; sar[q][3] = v.w;
                 }
             }
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
                 if constexpr (OUT == 2) {
                     ((int*)Y)[off] = acc[i][j][r];
                 } else {
-                    const float y = value(i, j, r, sa[row]);
+                    const float y = value(i, j, r, sa[scalar_scales ? 0 : row]);
                     if constexpr (OUT == 0) ((float*)Y)[off] = y;
                     else ((__bf16*)Y)[off] = (__bf16)y;
                 }
@@ -423,22 +424,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
 
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
-                       int n, int k, const void* bias, int bias_kind, void* y, int out_kind,
+                       int n, int k, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
                        hipStream_t st) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
     dim3 grid(gm * gn), block(64 * WGM * WGN);
     switch (out_kind) {
         case 0:
             hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 0>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn);
+                               bias, bias_kind, y, gm, gn, scalar_scales);
             break;
         case 1:
             hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 1>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn);
+                               bias, bias_kind, y, gm, gn, scalar_scales);
             break;
         default:
             hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 2>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn);
+                               bias, bias_kind, y, gm, gn, scalar_scales);
             break;
     }
     return hipGetLastError();
@@ -452,11 +453,12 @@ hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* w
 // (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs).
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
-                          void* y, int out_kind, hipStream_t st) {
+                          void* y, int out_kind, int scalar_scales, hipStream_t st) {
     if (m <= 0 || n <= 0) return hipSuccess;
     // few tokens: the product streams the weights; the tiled kernel would
     // leave most CUs idle
-    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, st);
+    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales,
+                                                          st);
     struct Cfg { int bm, bn; double speed; };
     const Cfg cfgs[] = {{256, 256, 1.0}, {128, 256, 0.80}, {128, 128, 0.73}};
     int best = 0;
@@ -472,8 +474,8 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
     }
     const int mi = (int)m, ni = (int)n, ki = (int)k;
     switch (best) {
-        case 0: return launch_tile<256, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        case 1: return launch_tile<128, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        default: return launch_tile<128, 128, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
+        case 0: return launch_tile<256, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 1: return launch_tile<128, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        default: return launch_tile<128, 128, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
     }
 }

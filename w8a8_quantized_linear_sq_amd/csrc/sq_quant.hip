@@ -516,3 +516,133 @@ hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, in
     return bf16 ? launch_rows<true, false>(w, s, n, k, wq, w_scale, st)
                 : launch_rows<false, false>(w, s, n, k, wq, w_scale, st);
 }
+
+// ---------------------------------------------------------------------------
+// Per-tensor variant (page "quantized_linear.py", quantize_tensor, 8 bits):
+//   scale = max_i |x_i| / 127, replaced by 1 when below 1e-8
+//   q_i   = clamp(round_half_even(x_i / scale), -128, 127)
+// Three launches and no scratch: the block maxima of |x| (bit patterns) go
+// to the first bytes of the code buffer, one block folds them into the
+// scale, then every element's code (the same exact quotient and rounding as
+// the row quantiser above; the scale is >= 1e-8 or exactly 1).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void tensor_max_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                         unsigned* __restrict__ partial) {
+    constexpr int U = 4;
+    constexpr uint32_t kMask = BF16 ? 0x7fff7fffu : 0x7fffffffu;
+    __shared__ float red[4];
+    u32x4 m = {0, 0, 0, 0};
+    auto fold = [&](u32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a = v[i] & kMask;
+            if constexpr (BF16) m[i] = max_u16x2(m[i], a);
+            else m[i] = max(m[i], a);
+        }
+    };
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + stride * (U - 1) < nvec; i += stride * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = x[i + stride * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) fold(v[u]);
+    }
+    for (; i < nvec; i += stride) fold(x[i]);
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (BF16) mx = fmaxf(mx, fmaxf(bf16_lo(m[j]), bf16_hi(m[j])));
+        else mx = fmaxf(mx, __uint_as_float(m[j]));
+    }
+    mx = wave_max(mx);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        partial[blockIdx.x] = __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+}
+
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const unsigned* __restrict__ partial, int blocks,
+                                                           float* __restrict__ scale) {
+    __shared__ float red[4];
+    unsigned m = 0;
+    for (int i = threadIdx.x; i < blocks; i += 256) m = max(m, partial[i]);
+    float mx = wave_max(__uint_as_float(m));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        float sc = mx / kQmax;
+        if (sc < kFloor) sc = 1.0f;  // the page's replacement (not a floor)
+        *scale = sc;
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void tensor_codes_kernel(const u32x4* __restrict__ x, int64_t groups,
+                                                           const float* __restrict__ scale, int8_t* __restrict__ q) {
+    constexpr int kV = BF16 ? 1 : 2;  // 16-byte loads per 8 elements
+    const float sc = *scale;
+    const float rs = 1.0f / sc;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += (int64_t)gridDim.x * 256) {
+        float v[8];
+        if constexpr (BF16) {
+            const u32x4 a = x[g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_lo(a[i]);
+                v[2 * i + 1] = bf16_hi(a[i]);
+            }
+        } else {
+            const u32x4 a = x[g * kV], b = x[g * kV + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = __uint_as_float(a[i]);
+                v[4 + i] = __uint_as_float(b[i]);
+            }
+        }
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = __float_as_uint(div_rn(v[i], sc, rs) + kMagic);
+        *(u32x2*)(q + g * 8) = u32x2{pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7])};
+    }
+}
+
+int64_t sq_tensor_max_blocks(int64_t count) {
+    int64_t b = count / 8192;  // about 8 KiB of input per block
+    if (b < 1) b = 1;
+    if (b > 1024) b = 1024;
+    return b;  // the partials (4 bytes each) fit in the count-byte code buffer
+}
+
+hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int8_t* q, float* scale,
+                                     hipStream_t st) {
+    const int64_t nvec = bf16 ? count / 8 : count / 4;
+    const int64_t blocks = sq_tensor_max_blocks(count);
+    unsigned* partial = (unsigned*)q;
+    if (bf16)
+        hipLaunchKernelGGL(tensor_max_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, (const u32x4*)x, nvec,
+                           partial);
+    else
+        hipLaunchKernelGGL(tensor_max_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, (const u32x4*)x, nvec,
+                           partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, st, (const unsigned*)partial, (int)blocks, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t groups = count / 8;
+    int64_t cb = (groups + 255) / 256;
+    if (cb > 4096) cb = 4096;
+    if (bf16)
+        hipLaunchKernelGGL(tensor_codes_kernel<true>, dim3((unsigned)cb), dim3(256), 0, st, (const u32x4*)x, groups,
+                           (const float*)scale, q);
+    else
+        hipLaunchKernelGGL(tensor_codes_kernel<false>, dim3((unsigned)cb), dim3(256), 0, st, (const u32x4*)x, groups,
+                           (const float*)scale, q);
+    return hipGetLastError();
+}

@@ -60,7 +60,7 @@ template <int TM, int NG, int D, int kWaves, int OUT>
 __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
-    int bias_kind, void* __restrict__ Y) {
+    int bias_kind, void* __restrict__ Y, int scalar_scales) {
     constexpr int kRows = 16 * NG;            // weight rows per workgroup
     constexpr int TILES = NG + TM;            // weight groups, then token groups
     constexpr int STAGE = TILES * kTile;      // one wavefront's LDS stage
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(
     if (o >= n) continue;
     float swo = 0.0f, bo = 0.0f;
     if constexpr (OUT != 2) {
-        swo = sb[o];
+        swo = sb[scalar_scales ? 0 : o];
         if (bias_kind == 1) bo = ((const float*)bias)[o];
         else if (bias_kind == 2) bo = __uint_as_float((uint32_t)((const uint16_t*)bias)[o] << 16);
     }
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(
             if constexpr (OUT == 2) {
                 ((int*)Y)[off] = acc[t][g][r];
             } else {
-                float y = (float)acc[t][g][r] * sa[row] * swo;
+                float y = (float)acc[t][g][r] * sa[scalar_scales ? 0 : row] * swo;
                 if (bias_kind) y = y + bo;
                 if constexpr (OUT == 0) ((float*)Y)[off] = y;
                 else ((__bf16*)Y)[off] = (__bf16)y;
@@ -224,20 +224,21 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_kernel(
 
 template <int TM, int NG, int D, int W>
 hipError_t launch_tm(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw, int n, int k,
-                     const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+                     const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
+                     hipStream_t st) {
     const dim3 grid((n + 16 * NG - 1) / (16 * NG)), block(64 * W);
     switch (out_kind) {
         case 0:
             hipLaunchKernelGGL((skinny_kernel<TM, NG, D, W, 0>), grid, block, 0, st, xq, wq, m, n, k, sx, sw, bias,
-                               bias_kind, y);
+                               bias_kind, y, scalar_scales);
             break;
         case 1:
             hipLaunchKernelGGL((skinny_kernel<TM, NG, D, W, 1>), grid, block, 0, st, xq, wq, m, n, k, sx, sw, bias,
-                               bias_kind, y);
+                               bias_kind, y, scalar_scales);
             break;
         default:
             hipLaunchKernelGGL((skinny_kernel<TM, NG, D, W, 2>), grid, block, 0, st, xq, wq, m, n, k, sx, sw, bias,
-                               bias_kind, y);
+                               bias_kind, y, scalar_scales);
             break;
     }
     return hipGetLastError();
@@ -253,14 +254,14 @@ hipError_t launch_tm(const int8_t* xq, const float* sx, int m, const int8_t* wq,
 // per workgroup keep that traffic down for 33-64 tokens.
 hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq, const float* sw,
                                  int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
-                                 hipStream_t st) {
+                                 int scalar_scales, hipStream_t st) {
     if (m <= 0 || n <= 0) return hipSuccess;
     const int mi = (int)m, ni = (int)n, ki = (int)k;
     switch ((mi + 15) / 16) {
-        case 1: return launch_tm<1, 2, 3, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        case 2: return launch_tm<2, 2, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        case 3: return launch_tm<3, 4, 1, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
-        case 4: return launch_tm<4, 4, 1, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, st);
+        case 1: return launch_tm<1, 2, 3, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 2: return launch_tm<2, 2, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 3: return launch_tm<3, 4, 1, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 4: return launch_tm<4, 4, 1, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
         default: return hipErrorInvalidValue;
     }
 }
