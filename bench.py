@@ -13,7 +13,8 @@ Other workloads (--workload) are the remaining shapes of the method's
 workloads: prefill, the block's qkv / up / down linears and the MLP
 up-projection run the same full step; decode times the per-call path
 (sq_quantize_act + sq_w8a8_gemm) on weights prepared once, as a decode
-step uses them.
+step uses them; o_proj_per_tensor times the per-tensor variant as its
+layer runs it (sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor).
 
 Inputs are resident in HBM before the timed region; enough copies of every
 buffer a step reads are rotated (at least 512 MiB per cycle, 2 to 12
@@ -65,6 +66,9 @@ WORKLOADS = {
              ("block_linear", 3), "full"),
     "mlp_up": ("MLP up-projection, 8192 tokens x 8192 -> 28672, bf16, bias, alpha=0.5 (of the 0.25/0.5/0.75 "
                "sweep), calibrated on the same tokens", ("mlp_up",), "full"),
+    "o_proj_per_tensor": ("per-tensor variant on the O projection shape, M=N=K=4096, bf16 in/out: per call the "
+                          "weight and the input quantised with one scale each, then the int8 product",
+                          ("block_linear", 1), "per_tensor"),
 }
 
 
@@ -117,6 +121,28 @@ def cpu_baseline(case, mode: str, budget_s: float):
     m, n, k = case.m, case.n, case.k
     bias = None if case.bias is None else case.bias.f32
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if mode == "per_tensor":
+        # both per-tensor quantisations in full (a per-tensor scale needs the
+        # whole tensor), then the integer product and dequant on a row sample
+        t0 = time.perf_counter()
+        wq, sw = o.quantize_tensor(case.w.f32)
+        xq, sx = o.quantize_tensor(case.x.f32)
+        t1 = time.perf_counter()
+        probe = min(m, 16)
+        tp = time.perf_counter()
+        o.dequant(o.int_gemm(xq[:probe], wq), np.full(probe, sx, np.float32), np.full(n, sw, np.float32), bias)
+        per_row = (time.perf_counter() - tp) / probe
+        rows = int(min(m, max(16, max(budget_s - (t1 - t0), 1.0) / per_row)))
+        tp = time.perf_counter()
+        o.dequant(o.int_gemm(xq[:rows], wq), np.full(rows, sx, np.float32), np.full(n, sw, np.float32), bias)
+        t_rows = time.perf_counter() - tp
+        step_s = (t1 - t0) + t_rows * (m / rows)
+        return {"value": round(2.0 * m * n * k / step_s / 1e12, 6), "unit": "TOPS", "cores": threads,
+                "kind": "oracle",
+                "sample": (f"per-tensor quantisation of W ({n}x{k}) and X ({m}x{k}) in full, then {rows} of {m} "
+                           f"token rows through the int8 product (OpenMP over rows) and dequant; step time "
+                           f"extrapolated to {m} rows: {step_s:.2f} s"),
+                "seconds_measured": round((t1 - t0) + t_rows, 3)}
     t0 = time.perf_counter()
     run = np.zeros(k, np.float32)
     for cb in case.calib:
@@ -220,6 +246,8 @@ def main():
     # bytes one step reads and writes (the rotated part)
     if mode == "per_call":
         set_bytes = m * k * 2 + n * k + 4 * n + 4 * k + m * k + m * n * 2
+    elif mode == "per_tensor":
+        set_bytes = m * k * 2 + n * k * 2 + n * k + m * k + m * n * 2
     else:
         set_bytes = m * k * 2 + n * k * 2 + calib_rows * k * 2 + n * k + m * k + m * n * 2
     rotate = max(2, min(12, math.ceil(ROTATE_BYTES / set_bytes)))
@@ -234,7 +262,9 @@ def main():
             ws=torch.empty(n, dtype=torch.float32, device=dev),
             xq=torch.empty((m, k), dtype=torch.int8, device=dev),
             xs=torch.empty(m, dtype=torch.float32, device=dev),
-            y=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
+            y=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+            tsx=torch.empty(1, dtype=torch.float32, device=dev),
+            tsw=torch.empty(1, dtype=torch.float32, device=dev)))
     del x0, w0, c0
     stream = torch.cuda.current_stream(dev)
     if args.counter_pass:
@@ -252,12 +282,20 @@ def main():
             s["w"] = None
         torch.cuda.empty_cache()
         stage_names = ["quantize_act", "gemm"]
+    elif mode == "per_tensor":
+        stage_names = ["quantize_weight", "quantize_act", "gemm"]
     else:
         stage_names = ["reset+calibrate", "prepare_weight", "quantize_act", "gemm"]
 
     # every call of a step marshalled once per buffer set (binding.prepared):
     # the timed loop then only repeats the C calls
     for s in sets:
+        if mode == "per_tensor":
+            s["call_prep"] = B.prepared(B.sq_quantize_tensor, s["w"], s["wq"], s["tsw"], stream)
+            s["call_act"] = B.prepared(B.sq_quantize_tensor, s["x"], s["xq"], s["tsx"], stream)
+            s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_per_tensor, s["xq"], s["tsx"], s["wq"], s["tsw"], s["bias"],
+                                        s["y"], stream)
+            continue
         if mode == "full":
             s["calls_calib"] = [B.prepared(B.sq_calibrate, cb, s["run"], stream) for cb in s["calib"]]
             s["call_prep"] = B.prepared(B.sq_prepare_weight, s["w"], s["run"], alpha, s["smooth"], s["wq"],
@@ -279,6 +317,9 @@ def main():
             for call in s["calls_calib"]:
                 call()
             mark()
+            s["call_prep"]()
+            mark()
+        elif mode == "per_tensor":
             s["call_prep"]()
             mark()
         s["call_act"]()
@@ -335,11 +376,18 @@ def main():
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
-    # algorithmic bytes of the HBM-bound stages
-    stage_roof = {"quantize_act": hbm(m * k * 2 + m * k + 4 * m + 4 * k, act_ms)}
+    # algorithmic bytes of the HBM-bound stages (a per-tensor scale needs a
+    # whole pass over the tensor before its first code: two reads)
+    if mode == "per_tensor":
+        stage_roof = {"quantize_act": hbm(2 * m * k * 2 + m * k, act_ms),
+                      "quantize_weight": hbm(2 * n * k * 2 + n * k, stage_ms["quantize_weight"])}
+    else:
+        stage_roof = {"quantize_act": hbm(m * k * 2 + m * k + 4 * m + 4 * k, act_ms)}
     if mode == "full":
         stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_ms["prepare_weight"])
         stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_ms["reset+calibrate"])
+    kernel_name = ("int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)" if mode == "per_tensor"
+                   else "int8 GEMM + fused dequant (sq_w8a8_gemm)")
     if m <= 64:
         # the weight-streaming product: bound by reading the int8 weights
         gbs = (n * k + m * k + 2 * m * n + 4 * (m + n)) / (gemm_ms * 1e-3) / 1e9
@@ -348,7 +396,7 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         traffic = _gemm_traffic() if args.workload == "o_proj" else None
-        roof = {"bound": "mfma", "kernel": "int8 GEMM + fused dequant (sq_w8a8_gemm)",
+        roof = {"bound": "mfma", "kernel": kernel_name,
                 "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                 "traffic": None if traffic is None else round(traffic)}
