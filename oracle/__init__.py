@@ -54,6 +54,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "sqo_smooth_act": ([_P, _P, _I64, _I64, _P], None),
         "sqo_quantize_rows": ([_P, _I64, _I64, _P, _P], None),
         "sqo_quantize_tensor": ([_P, _I64, _P, _P], None),
+        "sqo_wo_linear": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], None),
         "sqo_int_gemm": ([_P, _P, _I64, _I64, _I64, _P], _I64),
         "sqo_dequant": ([_P, _P, _P, _P, _I64, _I64, _P], None),
         "sqo_simulated_forward": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], None),
@@ -164,6 +165,19 @@ class Oracle:
         m, n = acc.shape
         y = self.dequant(acc, np.full(m, sx, np.float32), np.full(n, sw, np.float32), bias)
         return xq, sx, wq, sw, acc, y
+
+    def wo_linear(self, x, wq, sw, bias=None) -> np.ndarray:
+        """Weight-only int8 linear (torchao Int8WeightOnlyQuantizedLinearWeight):
+        (x @ wq^T) * scale_w[o] + bias[o] in binary64; x float32 [m, k]."""
+        x = self._f32(x)
+        wq = np.ascontiguousarray(wq, np.int8)
+        sw = self._f32(sw)
+        m, k = x.shape
+        n = wq.shape[0]
+        b = None if bias is None else self._f32(bias)
+        y = np.empty((m, n), np.float64)
+        self.lib.sqo_wo_linear(self._ptr(x), self._ptr(wq), self._ptr(sw), self._ptr(b), m, n, k, self._ptr(y))
+        return y
 
     def int_gemm(self, xq, wq) -> np.ndarray:
         """INT8 x INT8 -> INT32: acc[t, o] = sum_j xq[t, j] wq[o, j]."""

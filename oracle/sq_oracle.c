@@ -24,7 +24,8 @@
  *     there that real hardware does INT8 x INT8 -> INT32 -> fp32; this file
  *     computes exactly that integer product.
  * and, for the per-tensor variant, the page "quantized_linear.py"
- * (quantize_tensor, QuantizedLinear).
+ * (quantize_tensor, QuantizedLinear); for the weight-only linear, the
+ * torchao page "quantization/subclass.py" (Int8WeightOnlyQuantizedLinearWeight).
  *
  * Readings where the page is silent or garbled (each one also listed in
  * the design notes of the repository):
@@ -271,6 +272,39 @@ void sqo_quantize_tensor(const float* x, int64_t count, int8_t* q, float* scale_
         if (c < (float)SQO_QMIN) c = (float)SQO_QMIN;
         q[i] = (int8_t)c;
     }
+}
+
+/* ---------------------------------------------------------------------
+ * Weight-only int8 linear, the torchao page's
+ * Int8WeightOnlyQuantizedLinearWeight._quantized_op: the activations stay
+ * in floating point, the int8 weights are converted to the activations'
+ * type, multiplied, scaled per output channel, then the bias is added:
+ *   y[t][o] = (sum_j x[t][j] * wq[o][j]) * scale_w[o] + bias[o]
+ * in binary64 (for bf16 activations, widened to fp32 by the caller, every
+ * product is exact and the sum is nearly exact; the caller rounds once).
+ * ------------------------------------------------------------------ */
+void sqo_wo_linear(const float* x, const int8_t* wq, const float* scale_w,
+                   const float* bias, int64_t m, int64_t n, int64_t k, double* y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t o = 0; o < n; ++o) {
+            double sum = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                sum += (double)x[t * k + j] * (double)wq[o * k + j];
+#if SQO_MUTANT == 16
+            /* MUTANT 16: scales by the token index instead of the output
+             * channel (reads scale_w[t]). */
+            double v = sum * (double)scale_w[t < n ? t : n - 1];
+#else
+            double v = sum * (double)scale_w[o];
+#endif
+#if SQO_MUTANT != 17
+            /* MUTANT 17 (when defined): the bias is dropped. */
+            if (bias) v += (double)bias[o];
+#endif
+            y[t * n + o] = v;
+        }
 }
 
 /* ---------------------------------------------------------------------

@@ -471,4 +471,69 @@ def pin_per_tensor_linear(o):
     assert np.all(np.abs(y - ysim) <= 1e-12 * scale)
 
 
+# ---------------------------------------------------------------------------
+# Weight-only int8 linear: torchao page "quantization/subclass.py",
+# Int8WeightOnlyQuantizedLinearWeight (x @ int8 weights in x's type, times
+# the per-output-channel scales, plus the bias).
+# ---------------------------------------------------------------------------
+def pin_wo_linear_exact(o):
+    """Brute force in exact rational arithmetic on bf16 activations: every
+    product is exact, so the binary64 sum is within 2^-50 of the exact one."""
+    rng = _rng(101)
+    x = _bf16_round(rng.standard_normal((3, 24), dtype=np.float32))
+    wq = rng.integers(-128, 128, size=(4, 24)).astype(np.int8)
+    sw = (rng.random(4, dtype=np.float32) * np.float32(0.01)).astype(np.float32)
+    b = rng.standard_normal(4, dtype=np.float32)
+    y = o.wo_linear(x, wq, sw, b)
+    for t in range(3):
+        for u in range(4):
+            s = sum(Fraction(float(x[t, j])) * int(wq[u, j]) for j in range(24))
+            exact = s * Fraction(float(sw[u])) + Fraction(float(b[u]))
+            mag = sum(abs(Fraction(float(x[t, j])) * int(wq[u, j])) for j in range(24)) * Fraction(float(sw[u]))
+            assert abs(Fraction(float(y[t, u])) - exact) <= (mag + abs(Fraction(float(b[u])))) * Fraction(1, 2 ** 50)
+
+
+def pin_wo_linear_matches_integer_route(o):
+    """Activations already on an int8 grid (x = xq * sx): the weight-only
+    product equals the integer product scaled back, acc * sx * sw + bias."""
+    rng = _rng(102)
+    xq = rng.integers(-127, 128, size=(5, 40)).astype(np.int8)
+    sx = np.float32(2.0 ** -7)                       # exact products and sums
+    x = xq.astype(np.float32) * sx
+    wq = rng.integers(-127, 128, size=(6, 40)).astype(np.int8)
+    sw = (rng.random(6, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    b = rng.standard_normal(6, dtype=np.float32) * np.float32(0.1)
+    y = o.wo_linear(x, wq, sw, b)
+    acc = o.int_gemm(xq, wq)
+    want = o.dequant(acc, np.full(5, sx, np.float32), sw, b)
+    assert np.allclose(y, want, rtol=1e-13, atol=1e-13)
+
+
+def pin_wo_linear_structure(o):
+    """Invariant under a common permutation of K; a zero weight row gives the
+    bias; scaling one output channel's scale scales only that column."""
+    rng = _rng(103)
+    x = _bf16_round(rng.standard_normal((4, 32), dtype=np.float32))
+    wq = rng.integers(-128, 128, size=(5, 32)).astype(np.int8)
+    wq[2] = 0
+    sw = (rng.random(5, dtype=np.float32) * np.float32(0.01) + np.float32(0.001)).astype(np.float32)
+    b = rng.standard_normal(5, dtype=np.float32)
+    y = o.wo_linear(x, wq, sw, b)
+    perm = rng.permutation(32)
+    assert np.allclose(o.wo_linear(x[:, perm], wq[:, perm], sw, b), y, rtol=1e-14, atol=1e-14)
+    assert np.all(y[:, 2] == np.float64(b[2]))
+    sw2 = sw.copy()
+    sw2[4] *= np.float32(2.0)
+    y2 = o.wo_linear(x, wq, sw2, b)
+    assert np.array_equal(y2[:, :4], y[:, :4])
+    assert np.allclose(y2[:, 4] - b[4], 2 * (y[:, 4] - b[4]), rtol=1e-14, atol=1e-14)
+
+
+def _bf16_round(v):
+    """Round float32 values to the nearest bf16 (ties to even), as float32."""
+    bits = np.ascontiguousarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    r = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return (r.astype(np.uint32) << 16).view(np.float32)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -19,6 +19,8 @@ MUTANTS = {
     13: "calibration max without abs",
     14: "per-tensor scale floored instead of replaced by 1",
     15: "per-tensor max divided by 128",
+    16: "weight-only linear scaled by the token index",
+    17: "weight-only linear drops the bias",
 }
 
 
