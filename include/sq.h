@@ -190,6 +190,31 @@ sq_status sq_w8a8_gemm_per_tensor(const int8_t* x_q, const float* x_scale, int64
                                   sq_dtype yt, void* stream);
 
 /*
+ * sq_wo_linear -- weight-only int8 linear: bf16 activations, int8 weights.
+ * Follows Int8WeightOnlyQuantizedLinearWeight._quantized_op of the torchao
+ * page "quantization/subclass.py": the int8 weights are converted to the
+ * activations' type, multiplied with them, scaled per output channel, and
+ * the bias is added:
+ *   y[t][o] = f32(sum_j x[t][j] * w_q[o][j]) * w_scale[o] + bias[o]
+ * with every bf16 x int8 product exact and the sum accumulated in fp32
+ * (order unspecified), then rounded to yt. The weights are those of
+ * sq_prepare_weight; with SmoothQuant weights (W * s) the activations must be
+ * the smoothed X / s (as when s is folded into the preceding layer), with
+ * uncalibrated weights (s = 1) they are plain per-channel int8 weights.
+ * Built for the decode shape: tokens are processed in chunks of 64, each
+ * chunk streaming the weights once.
+ *   x       [m][k] bf16 (SQ_BF16 only), 16-byte aligned
+ *   w_q     [n][k] int8, 16-byte aligned; w_scale [n] fp32
+ *   bias    [n] in bias_t (F32 or BF16), or NULL
+ *   y       [m][n] in yt (SQ_F32 or SQ_BF16, round to nearest even),
+ *           4-byte aligned
+ */
+sq_status sq_wo_linear(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                       const int8_t* w_q, const float* w_scale, int64_t n,
+                       const void* bias, sq_dtype bias_t, void* y, sq_dtype yt,
+                       void* stream);
+
+/*
  * sq_selfcheck_reciprocal -- device self-check behind the activation path.
  * For bf16 activations, sq_quantize_act / sq_w8a8_linear form x / s as
  * fma(fma(-q0, s, x), y, q0) with q0 = x * y and y the correctly rounded

@@ -171,3 +171,20 @@ def test_gemm_per_tensor_errors(L):
     assert call(sw=None) == B.SQ_ERR_ARG
     assert call(y=BAD) == B.SQ_ERR_ALIGN
     assert call(m=0) == B.SQ_OK  # nothing to do, nothing launched
+
+
+def test_wo_linear_errors(L):
+    f = L.sq_wo_linear
+
+    def call(x=OK_PTR, xt=B.SQ_BF16, m=4, k=64, wq=OK_PTR, sw=OK_PTR, n=8, bias=None, bt=B.SQ_F32, y=OK_PTR,
+             yt=B.SQ_BF16):
+        return f(x, xt, m, k, wq, sw, n, bias, bt, y, yt, None)
+
+    assert call(xt=B.SQ_F32) == B.SQ_ERR_DTYPE   # bf16 activations only
+    assert call(yt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(bias=OK_PTR, bt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=40) == B.SQ_ERR_ALIGN
+    assert call(sw=None) == B.SQ_ERR_ARG
+    assert call(x=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0, x=None) == B.SQ_OK

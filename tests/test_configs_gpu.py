@@ -157,3 +157,45 @@ def test_per_tensor_o_proj_4096(orc):
     assert_equal(down(wq), wq_ref, "w codes")
     rows = _rows(m, 64, seed=17)
     _check_y(orc, y, xq_ref, np.full(m, sx_ref, np.float32), wq_ref, np.full(n, sw_ref, np.float32), None, rows)
+
+
+def _wo_case(orc, case, sample_rows):
+    """Weight-only int8 linear (torchao page "quantization/subclass.py") on
+    a full-size case: plain per-channel int8 weights (sq_prepare_weight never
+    calibrated, s = 1), compared bit for bit; the bf16 output on sampled rows
+    against the oracle's binary64 result, within the fp32 summation bound
+    K 2^-24 sum|x w| sw plus the scale and bias roundings and half a bf16 ulp."""
+    m, n, k = case.m, case.n, case.k
+    print(f"weight-only {case.name}", flush=True)
+    s, wq, sw = _empty(k, torch.float32), _empty((n, k), torch.int8), _empty(n, torch.float32)
+    assert B.sq_prepare_weight(up(case.w), None, 0.5, s, wq, sw) == B.SQ_WARN_UNCALIBRATED
+    bias_dev = None if case.bias is None else up(case.bias)
+    bias_f = None if case.bias is None else case.bias.f32
+    y = _empty((m, n), torch.bfloat16)
+    B.sq_wo_linear(up(case.x), wq, sw, bias_dev, y)
+    torch.cuda.synchronize()
+    s_ref, wq_ref, sw_ref = orc.prepare_weight(case.w.f32, None, 0.5)
+    assert (s_ref == 1.0).all()
+    assert_equal(down(s), s_ref, "smooth")
+    assert_equal(down(sw), sw_ref, "w_scale")
+    assert_equal(down(wq), wq_ref, "w_q")
+    rows = _rows(m, sample_rows, seed=m + 7 * n)
+    x_rows = np.ascontiguousarray(case.x.f32[rows])
+    yref = orc.wo_linear(x_rows, wq_ref, sw_ref, bias_f)
+    mag = (np.abs(x_rows.astype(np.float64)) @ np.abs(wq_ref.astype(np.float64)).T) * sw_ref[None, :]
+    if bias_f is not None:
+        mag = mag + np.abs(bias_f)[None, :]
+    got = down(y[torch.from_numpy(rows).to(DEV)])
+    got = (got.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(yref), 2.0 ** -126)))
+    bound = k * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(yref) + 2.0 ** (e - 8)
+    err = np.abs(got - yref)
+    assert (err <= bound).all(), (int((err > bound).sum()), float((err / bound).max()))
+
+
+def test_weight_only_decode_16x4096x11008(orc):
+    _wo_case(orc, inputs.decode(), None)
+
+
+def test_weight_only_prefill_2048x4096x4096(orc):
+    _wo_case(orc, inputs.prefill(), 64)

@@ -398,3 +398,52 @@ def test_gemm_per_tensor(orc, shape, out, bias):
         assert_f32_rel(down(y), yref, scale)
     else:
         assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
+
+
+# ---------------------------------------------------------------------------
+# Weight-only int8 linear (torchao page "quantization/subclass.py",
+# Int8WeightOnlyQuantizedLinearWeight): bf16 activations x int8 weights.
+# Tolerance from the arithmetic: the products are exact in fp32 and the sum
+# of K of them, in any order, is within K * 2^-24 * sum |x w| of the exact
+# sum; the scale multiply and the bias add round once each (2^-24 of their
+# result each), and a bf16 output adds half a bf16 ulp.
+# ---------------------------------------------------------------------------
+def _assert_wo_close(got_bits_or_f32, yref, mag, k, out):
+    if out == "f32":
+        got = got_bits_or_f32.astype(np.float64)
+        half_ulp = 0.0
+    else:
+        got = (got_bits_or_f32.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        e = np.floor(np.log2(np.maximum(np.abs(yref), 2.0 ** -126)))
+        half_ulp = 2.0 ** (e - 8)
+    bound = k * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(yref) + half_ulp + 1e-30
+    err = np.abs(got - yref)
+    bad = err > bound
+    assert not bad.any(), (int(bad.sum()), float((err / bound).max()))
+
+
+WO_SHAPES = [(1, 1, 16), (3, 17, 48), (16, 100, 272), (16, 200, 4096), (33, 64, 528), (64, 129, 1040),
+             (80, 70, 256), (130, 40, 4112)]
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WO_SHAPES, ids=_id)
+def test_wo_linear(orc, shape, out, bias):
+    m, n, k = shape
+    rng = np.random.default_rng(m * 3 + n * 5 + k)
+    c = inputs.small(m, n, k, seed=21 + m + n + k, dtype="bf16", bias=bias is not None)
+    wq = _codes(rng, n, k)
+    sw = (rng.random(n, dtype=np.float32) * np.float32(0.002) + np.float32(1e-4)).astype(np.float32)
+    bias_f = bias_t = None
+    if bias == "f32":
+        bias_f = c.bias.f32
+        bias_t = up(bias_f)
+    elif bias == "bf16":
+        bias_f, bias_t = c.bias.f32, up(c.bias)
+    y = _zeros((m, n), torch.float32 if out == "f32" else torch.bfloat16)
+    B.sq_wo_linear(up(c.x), up(wq), up(sw), bias_t, y)
+    torch.cuda.synchronize()
+    yref = orc.wo_linear(c.x.f32, wq, sw, bias_f)
+    mag = (np.abs(c.x.f32.astype(np.float64)) @ np.abs(wq.astype(np.float64)).T) * sw[None, :].astype(np.float64)
+    _assert_wo_close(down(y), yref, mag, k, out)

@@ -45,6 +45,7 @@ _SIGNATURES = {
     "sq_abi_version": ([], _E),
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
     "sq_w8a8_gemm_per_tensor": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_wo_linear": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_selfcheck_reciprocal": ([_P, _P], _E),
     "sq_selfcheck_division": ([ctypes.c_uint, ctypes.c_uint, _P, _P], _E),
 }
@@ -219,6 +220,16 @@ def sq_w8a8_gemm_per_tensor(x_q: torch.Tensor, x_scale: torch.Tensor, w_q: torch
     bt = _dtype_code(bias) if bias is not None else SQ_F32
     return _invoke("sq_w8a8_gemm_per_tensor", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k,
                    _ptr(bias), bt, _ptr(y), _dtype_code(y), _stream(stream, x_q))
+
+
+def sq_wo_linear(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None,
+                 y: torch.Tensor, stream=None) -> int:
+    """Weight-only int8 linear: y = (x @ w_q^T) * w_scale + bias, x bf16."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_wo_linear", _ptr(x), _dtype_code(x), m, k, _ptr(w_q), _ptr(w_scale), n, _ptr(bias), bt,
+                   _ptr(y), _dtype_code(y), _stream(stream, x))
 
 
 def sq_selfcheck_reciprocal(mismatches: torch.Tensor, stream=None) -> int:

@@ -69,3 +69,7 @@ constexpr int64_t kSkinnyMaxM = 64;
 hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                                  const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                                  void* y, int out_kind, int scalar_scales, hipStream_t st);
+// weight-only int8 linear: bf16 x [m][k] times int8 wq [n][k] with fp32
+// scales sw [n]; out_kind 0 fp32, 1 bf16; bias_kind as above
+hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw, int64_t n,
+                               const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st);
