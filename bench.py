@@ -14,16 +14,19 @@ workloads: prefill, the block's qkv / up / down linears and the MLP
 up-projection run the same full step; decode times the per-call path
 (sq_quantize_act + sq_w8a8_gemm) on weights prepared once, as a decode
 step uses them; o_proj_per_tensor times the per-tensor variant as its
-layer runs it (sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor).
+layer runs it (sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor);
+decode_weight_only times the weight-only int8 linear (sq_wo_linear) on the
+decode shape.
 
 Inputs are resident in HBM before the timed region; enough copies of every
 buffer a step reads are rotated (at least 512 MiB per cycle, 2 to 12
 copies) that a step does not find its inputs in the 256 MB Infinity Cache
-left there by the previous step. HIP events on the launch stream bracket
-the timed region and every 4th product launch in it (an event between
-kernels costs a few microseconds, which would otherwise land in the step
-time); a second pass of the same steps with an event between stages gives
-the per-stage breakdown. Prints one JSON line.
+left there by the previous step. The K timed steps are captured into one
+HIP graph on the launch stream and replayed once between two HIP events
+(no host launch cost between kernels); a second graph of 64 product
+launches over the same buffer sets, replayed between events, gives the
+product kernel's average duration; an eager pass of the same steps with an
+event between stages gives the per-stage breakdown. Prints one JSON line.
 
 The CPU baseline times the CPU oracle (test infrastructure) on a bounded
 sample of the same workload on this host.
@@ -46,7 +49,7 @@ METRIC = "W8A8 SmoothQuant linear TOPS at M=N=K=4096; % of INT8 MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20     # bytes read per rotation cycle, at least
-EVENT_STRIDE = 4             # every 4th product launch of the timed region is bracketed by events
+GEMM_LAUNCHES = 64           # product launches in the graph that times the product kernel
 GEMM_SOURCE = os.path.join(ROOT, "w8a8_quantized_linear_sq_amd", "csrc", "sq_gemm.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_o_proj_4096_traffic.md")
 
@@ -69,6 +72,9 @@ WORKLOADS = {
     "o_proj_per_tensor": ("per-tensor variant on the O projection shape, M=N=K=4096, bf16 in/out: per call the "
                           "weight and the input quantised with one scale each, then the int8 product",
                           ("block_linear", 1), "per_tensor"),
+    "decode_weight_only": ("weight-only int8 linear on the decode shape, 16 tokens x 4096 -> 11008, bf16 "
+                           "activations and output, per-channel int8 weights prepared once (never calibrated, "
+                           "s = 1); per call: the bf16 x int8 product + scale", ("decode",), "weight_only"),
 }
 
 
@@ -121,6 +127,21 @@ def cpu_baseline(case, mode: str, budget_s: float):
     m, n, k = case.m, case.n, case.k
     bias = None if case.bias is None else case.bias.f32
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if mode == "weight_only":
+        wq, sw = o.quantize_rows(case.w.f32)
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < budget_s and reps < 50):
+            tp = time.perf_counter()
+            o.wo_linear(case.x.f32, wq, sw, bias)
+            spent += time.perf_counter() - tp
+            reps += 1
+        step_s = spent / reps
+        return {"value": round(2.0 * m * n * k / step_s / 1e12, 6), "unit": "TOPS", "cores": threads,
+                "kind": "oracle",
+                "sample": (f"per-channel int8 weights ({n}x{k}) prepared once, not timed; {reps} calls of all "
+                           f"{m} tokens through the weight-only product in binary64 (OpenMP over rows): "
+                           f"{step_s:.4f} s per call"),
+                "seconds_measured": round(spent, 3)}
     if mode == "per_tensor":
         # both per-tensor quantisations in full (a per-tensor scale needs the
         # whole tensor), then the integer product and dequant on a row sample
@@ -246,6 +267,8 @@ def main():
     # bytes one step reads and writes (the rotated part)
     if mode == "per_call":
         set_bytes = m * k * 2 + n * k + 4 * n + 4 * k + m * k + m * n * 2
+    elif mode == "weight_only":
+        set_bytes = m * k * 2 + n * k + 4 * n + m * n * 2
     elif mode == "per_tensor":
         set_bytes = m * k * 2 + n * k * 2 + n * k + m * k + m * n * 2
     else:
@@ -266,14 +289,20 @@ def main():
             tsx=torch.empty(1, dtype=torch.float32, device=dev),
             tsw=torch.empty(1, dtype=torch.float32, device=dev)))
     del x0, w0, c0
-    stream = torch.cuda.current_stream(dev)
+    # one stream of our own (default priority) for every call, so that the
+    # steps can be captured into a graph on it
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
     if args.counter_pass:
         counter_pass(torch, B, sets[0], stream)
         return
-    if mode == "per_call":
+    if mode in ("per_call", "weight_only"):
         # weights prepared once per copy, outside the timed region; the bf16
-        # weights are then released
+        # weights are then released (weight-only: never calibrated, s = 1)
         for s in sets:
+            if mode == "weight_only":
+                B.sq_prepare_weight(s["w"], None, alpha, s["smooth"], s["wq"], s["ws"], stream)
+                continue
             for cb in s["calib"]:
                 B.sq_calibrate(cb, s["run"], stream)
             B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
@@ -281,7 +310,7 @@ def main():
         for s in sets:
             s["w"] = None
         torch.cuda.empty_cache()
-        stage_names = ["quantize_act", "gemm"]
+        stage_names = ["quantize_act", "gemm"] if mode == "per_call" else ["wo_linear"]
     elif mode == "per_tensor":
         stage_names = ["quantize_weight", "quantize_act", "gemm"]
     else:
@@ -296,6 +325,10 @@ def main():
             s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_per_tensor, s["xq"], s["tsx"], s["wq"], s["tsw"], s["bias"],
                                         s["y"], stream)
             continue
+        if mode == "weight_only":
+            s["call_act"] = None
+            s["call_gemm"] = B.prepared(B.sq_wo_linear, s["x"], s["wq"], s["ws"], s["bias"], s["y"], stream)
+            continue
         if mode == "full":
             s["calls_calib"] = [B.prepared(B.sq_calibrate, cb, s["run"], stream) for cb in s["calib"]]
             s["call_prep"] = B.prepared(B.sq_prepare_weight, s["w"], s["run"], alpha, s["smooth"], s["wq"],
@@ -303,7 +336,7 @@ def main():
         s["call_act"] = B.prepared(B.sq_quantize_act, s["x"], s["smooth"], s["xq"], s["xs"], stream)
         s["call_gemm"] = B.prepared(B.sq_w8a8_gemm, s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], s["y"], stream)
 
-    def step(i, ev=None, gemm_ev=None):
+    def step(i, ev=None):
         s = sets[i % rotate]
         marks = iter(ev) if ev is not None else None
 
@@ -322,37 +355,50 @@ def main():
         elif mode == "per_tensor":
             s["call_prep"]()
             mark()
-        s["call_act"]()
-        mark()
-        if gemm_ev is not None:
-            gemm_ev[0].record(stream)
+        if s["call_act"] is not None:
+            s["call_act"]()
+            mark()
         s["call_gemm"]()
         mark()
-        if gemm_ev is not None:
-            gemm_ev[1].record(stream)
 
     def new_events(count, per):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(count)]
 
     for i in range(args.warmup):
         step(i)
-    # timed region: K steps; HIP events on the launch stream bracket the
-    # region and every EVENT_STRIDE-th product launch (its live average
-    # duration; each event between two kernels costs a few microseconds, so
-    # not every launch carries a pair)
+    torch.cuda.synchronize()
+    # the K steps are captured into one HIP graph on the launch stream and
+    # replayed once as the timed region (no host launch cost between
+    # kernels: microsecond-scale steps would otherwise be paced by the host)
+    steps_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(steps_graph, stream=stream):
+        for i in range(args.steps):
+            step(i)
     region = new_events(1, 2)[0]
-    sampled = list(range(0, args.steps, EVENT_STRIDE))
-    gemm_events = {i: ev for i, ev in zip(sampled, new_events(len(sampled), 2))}
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     region[0].record(stream)
-    for i in range(args.steps):
-        step(i, gemm_ev=gemm_events.get(i))
+    steps_graph.replay()
     region[1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms_per_step = region[0].elapsed_time(region[1]) / args.steps
-    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in gemm_events.values()) / len(gemm_events)
+
+    # the product kernel's average duration: a graph of GEMM_LAUNCHES product
+    # launches over the rotated buffer sets, as in the steps, replayed once
+    # untimed and once between events on the launch stream
+    gemm_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gemm_graph, stream=stream):
+        for i in range(GEMM_LAUNCHES):
+            sets[i % rotate]["call_gemm"]()
+    gemm_graph.replay()
+    gev = new_events(1, 2)[0]
+    torch.cuda.synchronize()
+    gev[0].record(stream)
+    gemm_graph.replay()
+    gev[1].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
     # stage breakdown: a second pass of K steps with an event between stages
     # (every event adds a few microseconds between kernels, so this pass is
@@ -368,7 +414,7 @@ def main():
     ops = 2.0 * m * n * k
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    act_ms = stage_ms["quantize_act"]
+    act_ms = stage_ms.get("quantize_act", 0.0)
     linear_tops = ops / ((act_ms + gemm_ms) * 1e-3) / 1e12
 
     def hbm(bytes_, ms):
@@ -378,7 +424,10 @@ def main():
 
     # algorithmic bytes of the HBM-bound stages (a per-tensor scale needs a
     # whole pass over the tensor before its first code: two reads)
-    if mode == "per_tensor":
+    wo_bytes = n * k + m * k * 2 + 2 * m * n + 4 * n
+    if mode == "weight_only":
+        stage_roof = {"wo_linear": hbm(wo_bytes, stage_ms["wo_linear"])}
+    elif mode == "per_tensor":
         stage_roof = {"quantize_act": hbm(2 * m * k * 2 + m * k, act_ms),
                       "quantize_weight": hbm(2 * n * k * 2 + n * k, stage_ms["quantize_weight"])}
     else:
@@ -388,7 +437,14 @@ def main():
         stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_ms["reset+calibrate"])
     kernel_name = ("int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)" if mode == "per_tensor"
                    else "int8 GEMM + fused dequant (sq_w8a8_gemm)")
-    if m <= 64:
+    if mode == "weight_only":
+        # the weight-only product on the decode shape: bound by reading the
+        # int8 weights once
+        gbs = wo_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "weight-only int8 linear, bf16 MFMA (sq_wo_linear)",
+                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    elif m <= 64:
         # the weight-streaming product: bound by reading the int8 weights
         gbs = (n * k + m * k + 2 * m * n + 4 * (m + n)) / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "weight-streaming int8 product + fused dequant (sq_w8a8_gemm, m <= 64)",
@@ -408,7 +464,9 @@ def main():
     stages = {nm: round(v * 1e3, 2) for nm, v in stage_ms.items()}
     stages["note"] = "second pass of the same K steps with an event between stages"
     line = {
-        "metric": METRIC if args.workload == "o_proj" else f"W8A8 SmoothQuant linear TOPS at M={m} N={n} K={k}",
+        "metric": (METRIC if args.workload == "o_proj" else
+                   f"weight-only int8 linear TOPS at M={m} N={n} K={k}" if mode == "weight_only" else
+                   f"W8A8 SmoothQuant linear TOPS at M={m} N={n} K={k}"),
         "value": round(value, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -418,12 +476,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "bf16" if mode == "weight_only" else "int8",
         "data": "synthetic (seeded; outlier input channels, W ~ N(0, sigma), bf16)",
         "config": config,
         "roofline": roof,
         "gemm_us": round(gemm_ms * 1e3, 2),
-        "gemm_launches_timed": len(gemm_events),
+        "gemm_launches_timed": GEMM_LAUNCHES,
         "stages_us": stages,
         "stage_rooflines": stage_roof,
         "linear_tops": round(linear_tops, 2),

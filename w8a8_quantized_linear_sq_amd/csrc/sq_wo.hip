@@ -9,23 +9,38 @@
 // Every bf16 x int8 product is exact in fp32; the sum is accumulated in fp32
 // by the matrix units.
 //
-// Design (gfx950): the weight-streaming structure of the W8A8 product for
-// few tokens (sq_skinny.hip), with bf16 token fragments:
-//   * one workgroup of 2 wavefronts per 32 weight rows; K is split over the
-//     wavefronts in 256-element segments dealt alternately, each wavefront
-//     staging its segments of the weight rows (256 bytes per row) and of
-//     the token rows (512 bytes per row) through its own LDS ring with
-//     direct global -> LDS loads (one load covers 4 weight rows x 256 bytes
-//     or 2 token rows x 512 bytes, contiguous per row);
-//   * 16-byte chunk c of row r sits at slot c ^ (r & 15) within its LDS row,
-//     so the 16-row fragment reads spread over every bank;
-//   * v_mfma_f32_16x16x32_bf16 with the tokens as the 16-row operand; the
-//     weight fragment (8 int8 per lane) is widened to bf16 in registers
-//     (every int8 is a bf16 exactly);
-//   * the K tail past the last whole segment goes through registers in
-//     32-element blocks, a last partial block zero-filled;
-//   * the partial sums of the two wavefronts meet in LDS in a fixed order,
-//     and wavefront 0 applies the scale and the bias.
+// Design (gfx950). With few tokens every weight byte is used by one
+// workgroup only, so the kernel is a stream over the weights and nothing
+// needs staging for reuse:
+//   * one workgroup of 8 wavefronts per R weight rows, R = ceil(n / 256)
+//     (at most 48, more rounds beyond 256 x 48 rows), so that for the decode
+//     shapes every compute unit holds one workgroup and streams the same
+//     number of rows: no tail round. R need not be a multiple of 16: the
+//     last 16-row group of a workgroup is partly masked;
+//   * K is cut into 64-element chunks dealt round-robin to the wavefronts;
+//     per chunk a lane loads 16 bytes of its weight row (row l % 16, bytes
+//     16 (l / 16) .. +16 of the chunk) straight into registers, 64 bytes
+//     contiguous per row and instruction, and the 32 bytes of bf16
+//     activations at the same k;
+//   * the order of the k sum is free, so the chunk's 16 bytes feed two
+//     v_mfma_f32_16x16x32_bf16, bytes 0-7 and 8-15 of every lane, the
+//     activations split the same way: each lane's k positions map to the
+//     same physical k in both operands;
+//   * batches of CB chunks (weights and activations) stream through NB
+//     register buffers, no LDS; a batch's activations are loaded before its
+//     weights, so the in-order memory counter never holds them behind
+//     weights that are not needed yet;
+//   * loads past the rows or past K read an address another lane of the
+//     same instruction reads (no extra memory traffic), so every load is
+//     unconditional and the waits are exact; rows past the workgroup's rows
+//     and tokens past m only feed outputs that are not stored, and the
+//     activations of pieces past K are zeroed where they are used (a zero
+//     times a finite int8 adds nothing);
+//   * the 8 partial sums of a 16 x 16 output fragment meet in LDS and are
+//     added in wavefront order by one wavefront, which applies the scale and
+//     the bias.
+#include <atomic>
+
 #include "sq_device.h"
 
 using namespace sq;
@@ -34,23 +49,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kSegK = 256;                  // K elements per staged segment
-constexpr int kWTile = 16 * kSegK;          // 16 weight rows x 256 bytes
-constexpr int kXTile = 16 * kSegK * 2;      // 16 token rows x 512 bytes
-constexpr int kLgkm0 = 0xc07f;              // s_waitcnt lgkmcnt(0) only
+constexpr int kChunk = 64;    // K elements per chunk
+constexpr int kWaves = 8;     // wavefronts per workgroup
+constexpr int kMaxRows = 48;  // weight rows per workgroup, at most
 
-constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
-
-__device__ __forceinline__ int slot(int r, int c) { return c ^ (r & 15); }
-
-// 8 int8 (two dwords) -> 8 bf16, exactly
-__device__ __forceinline__ bf16x8 widen(u32x2 w) {
+// 8 int8 (two dwords) -> 8 bf16, exactly (every int8 is a bf16)
+__device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi) {
     bf16x8 out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t word = i < 4 ? w[0] : w[1];
+        const uint32_t word = i < 4 ? lo : hi;
         const int v = (int)(int8_t)(word >> (8 * (i & 3)));
         out[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint((float)v) >> 16));
     }
@@ -59,192 +68,227 @@ __device__ __forceinline__ bf16x8 widen(u32x2 w) {
 
 // v_mfma_f32_16x16x32_bf16 operands: lane l holds 8 k-consecutive bf16 of
 // row (l % 16) at k offset 8 * (l / 16); result lane l, register r -> row
-// 4 * (l / 16) + r, column l % 16.
-template <int TM, int NG, int D, int W, int OUT>
-__global__ __launch_bounds__(64 * W) void wo_kernel(const uint16_t* __restrict__ X, const int8_t* __restrict__ Bw,
-                                                    int m, int n, int k, const float* __restrict__ sb,
-                                                    const void* __restrict__ bias, int bias_kind,
-                                                    void* __restrict__ Y) {
-    constexpr int STAGE = NG * kWTile + TM * kXTile;
-    constexpr int LOADS = NG * 4 + TM * 8;  // DMA loads per stage
-    static_assert(W * D * STAGE >= (W - 1) * TM * NG * 64 * 16, "reduction must fit the staging area");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[W * D * STAGE];
+// 4 * (l / 16) + r (token), column l % 16 (weight row).
+template <int TM, int G, int CB, int NB, int OUT>
+__global__ __launch_bounds__(64 * kWaves) void wo_kernel(const uint16_t* X, const int8_t* Bw, int m, int n, int k,
+                                                         int rows, const float* __restrict__ sb,
+                                                         const void* __restrict__ bias, int bias_kind,
+                                                         void* __restrict__ Y) {
+    __shared__ f32x4 red[kWaves][TM * G][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 16 * NG;
     const int r16 = lane & 15, grp = lane >> 4;
-    int8_t* my = smem + wave * D * STAGE;
+    const int row0 = blockIdx.x * rows;
+    const int rend = min(row0 + rows, n);
 
-    // ---- DMA sources. Weight load q (0..3) of group g: rows 4q .. 4q+3,
-    // lane i -> row 4q + i/16, slot i%16; token load q (0..7) of group t:
-    // rows 2q, 2q+1, lane i -> row 2q + i/32, slot i%32.
-    const int8_t* wsrc[NG][4];
+    // row pointers: a row past the workgroup's rows reads the last row, a
+    // token past m the last token (addresses another lane of the
+    // instruction reads); their sums land in outputs that are not stored
+    const int8_t* wrow[G];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < G; ++g) wrow[g] = Bw + (int64_t)min(row0 + g * 16 + r16, rend - 1) * k;
+    const uint16_t* xrow[TM];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = 4 * q + grp;
-            wsrc[g][q] = Bw + (int64_t)min(n0 + g * 16 + r, n - 1) * k + slot(r, r16) * 16;
-        }
-    const int8_t* xsrc[TM][8];
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int r = 2 * q + (lane >> 5);
-            xsrc[t][q] = (const int8_t*)(X + (int64_t)min(t * 16 + r, m - 1) * k) + slot(r, lane & 31) * 16;
-        }
-    auto issue = [&](int seg, int buf) {
-        int8_t* st = my + buf * STAGE;
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_global_load_lds((const void*)(wsrc[g][q] + seg * kSegK),
-                                                 (lds_ptr_t)(st + g * kWTile + q * 1024), 16, 0, 0);
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                __builtin_amdgcn_global_load_lds((const void*)(xsrc[t][q] + seg * kSegK * 2),
-                                                 (lds_ptr_t)(st + NG * kWTile + t * kXTile + q * 1024), 16, 0, 0);
+    for (int t = 0; t < TM; ++t) xrow[t] = X + (int64_t)min(t * 16 + r16, m - 1) * k;
+
+    // chunks of this wavefront: wave, wave + 8, ...; every wavefront runs
+    // the same number of batches; pieces past K read the last 16 elements
+    // of the row and their activations are zeroed where they are used
+    const int nchunks = (k + kChunk - 1) / kChunk;
+    const int per_wave = (nchunks + kWaves - 1) / kWaves;
+    // batches, padded to a multiple of NB (the loop handles NB at a time; a
+    // padding batch holds only pieces past K)
+    const int nb = ((per_wave + CB - 1) / CB + NB - 1) / NB * NB;
+    auto koff = [&](int b, int j, bool& ok) {
+        const int off = (wave + kWaves * (b * CB + j)) * kChunk + grp * 16;
+        ok = off < k;  // k is a multiple of 16: a piece is whole or absent
+        return ok ? off : k - 16;
     };
 
-    f32x4 acc[TM][NG];
+    // NB register buffers, each with a batch of weights and the matching
+    // activations
+    struct Batch {
+        u32x4 w[G][CB];
+        u32x4 x[TM][CB][2];
+    };
+    Batch bufs[NB];
+    f32x4 acc[TM][G];
 #pragma unroll
     for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[t][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int g = 0; g < G; ++g) acc[t][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int KS = k / kSegK;
-    const int nseg = KS > wave ? (KS - wave + W - 1) / W : 0;
+    // activations first: the memory counter is in order, and a batch's
+    // activations (cache hits) must not wait behind its weights
+    auto load = [&](Batch& buf, int b) {
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < nseg) issue(wave + W * d, d);
-    for (int i = 0; i < nseg; ++i) {
-        const int buf = i % D;
-        if (D >= 2 && i + 1 < nseg) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        const int8_t* st = my + buf * STAGE;
+        for (int j = 0; j < CB; ++j) {
+            bool ok;
+            const int off = koff(b, j, ok);
 #pragma unroll
-        for (int b = 0; b < kSegK / 32; ++b) {
-            bf16x8 wf[NG], xf[TM];
+            for (int t = 0; t < TM; ++t) {
+                buf.x[t][j][0] = *(const u32x4*)(xrow[t] + off);
+                buf.x[t][j][1] = *(const u32x4*)(xrow[t] + off + 8);
+            }
+        }
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int c = 2 * b + (grp >> 1);
-                wf[g] = widen(*(const u32x2*)(st + g * kWTile + r16 * kSegK + slot(r16, c) * 16 + (grp & 1) * 8));
+        for (int j = 0; j < CB; ++j) {
+            bool ok;
+            const int off = koff(b, j, ok);
+#pragma unroll
+            for (int g = 0; g < G; ++g) buf.w[g][j] = *(const u32x4*)(wrow[g] + off);
+        }
+    };
+    auto compute = [&](const Batch& buf, int b) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            bool ok;
+            koff(b, j, ok);
+            bf16x8 xa[TM], xb[TM];
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                xa[t] = __builtin_bit_cast(bf16x8, ok ? buf.x[t][j][0] : u32x4{0u, 0u, 0u, 0u});
+                xb[t] = __builtin_bit_cast(bf16x8, ok ? buf.x[t][j][1] : u32x4{0u, 0u, 0u, 0u});
             }
 #pragma unroll
-            for (int t = 0; t < TM; ++t)
-                xf[t] = *(const bf16x8*)(st + NG * kWTile + t * kXTile + r16 * 512 + slot(r16, 4 * b + grp) * 16);
+            for (int g = 0; g < G; ++g) {
+                const bf16x8 wlo = widen(buf.w[g][j][0], buf.w[g][j][1]);
+                const bf16x8 whi = widen(buf.w[g][j][2], buf.w[g][j][3]);
 #pragma unroll
-            for (int t = 0; t < TM; ++t)
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[t], wf[g], acc[t][g], 0, 0, 0);
+                for (int t = 0; t < TM; ++t) {
+                    acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], wlo, acc[t][g], 0, 0, 0);
+                    acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[t], whi, acc[t][g], 0, 0, 0);
+                }
+            }
         }
-        if (i + D < nseg) {
-            __builtin_amdgcn_s_waitcnt(kLgkm0);
-            issue(wave + W * (i + D), buf);
+    };
+
+    // Every path issues the same loads in the same order and the loop has a
+    // single exit, its last pair peeled: a load issued on one path only (or
+    // a second exit, which the control-flow structurizer turns into a path
+    // that skips the loads) leaves the compiler's wait counts at their most
+    // pessimistic. An empty asm with a memory clobber closes every group of
+    // loads (X and Bw are not restrict-qualified, so the clobber holds for
+    // them; it keeps the prologue's and the loop's loads in their blocks),
+    // and a scheduling barrier keeps the compute that follows, register work
+    // included, behind them: the scheduler would otherwise place each load
+    // just before its use.
+    auto fence = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load(bufs[i], i);
+    fence();
+    int b = 0;
+    for (; b + NB < nb; b += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            compute(bufs[i], b + i);
+            load(bufs[i], b + i + NB);
+            fence();
         }
     }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) compute(bufs[i], b + i);
 
-    // ---- K past the segments: 32-element blocks through registers, then a
-    // ---- last partial block (k is a multiple of 16), zero-filled
-    const bf16x8 zero8 = {};
-    for (int kb = KS * (kSegK / 32) + wave; kb * 32 < k; kb += W) {
-        const int k0 = kb * 32 + grp * 8;
-        const bool in = k0 < k;  // whole block, or the 16-element tail
-        bf16x8 wf[NG], xf[TM];
+    // ---- the wavefronts' partial sums meet in LDS; fragment f = t * G + g
+    // ---- is summed in wavefront order by wavefront f % 8
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int8_t* p = Bw + (int64_t)min(n0 + g * 16 + r16, n - 1) * k + k0;
-            wf[g] = in ? widen(*(const u32x2*)p) : zero8;
-        }
+    for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const uint16_t* p = X + (int64_t)min(t * 16 + r16, m - 1) * k + k0;
-            xf[t] = in ? *(const bf16x8*)p : zero8;
-        }
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-                acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[t], wf[g], acc[t][g], 0, 0, 0);
-    }
-
-    // ---- the wavefronts' partial sums meet in LDS (the staging area, free
-    // ---- once every wavefront is past its loop), in a fixed order
+        for (int g = 0; g < G; ++g) red[wave][t * G + g][lane] = acc[t][g];
     __syncthreads();
-    f32x4 (*red)[TM][NG][64] = (f32x4 (*)[TM][NG][64])smem;
-    if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
+    for (int f = 0; f < TM * G; ++f) {
+        if (f % kWaves != wave) continue;
+        const int t = f / G, g = f % G;
+        f32x4 s = red[0][f][lane];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) red[wave - 1][t][g][lane] = acc[t][g];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < W - 1; ++w)
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int g = 0; g < NG; ++g) acc[t][g] += red[w][t][g][lane];
-
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int o = n0 + g * 16 + r16;
-        if (o >= n) continue;
+        for (int w = 1; w < kWaves; ++w) s += red[w][f][lane];
+        const int o = row0 + g * 16 + r16;
+        if (g * 16 + r16 >= rows || o >= n) continue;
         const float swo = sb[o];
         float bo = 0.0f;
         if (bias_kind == 1) bo = ((const float*)bias)[o];
         else if (bias_kind == 2) bo = __uint_as_float((uint32_t)((const uint16_t*)bias)[o] << 16);
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = t * 16 + grp * 4 + r;
-                if (row >= m) continue;
-                float y = acc[t][g][r] * swo;
-                if (bias_kind) y = y + bo;
-                const int64_t off = (int64_t)row * n + o;
-                if constexpr (OUT == 0) ((float*)Y)[off] = y;
-                else ((__bf16*)Y)[off] = (__bf16)y;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int tok = t * 16 + grp * 4 + r;
+            if (tok >= m) continue;
+            float y = s[r] * swo;
+            if (bias_kind) y = y + bo;
+            const int64_t off = (int64_t)tok * n + o;
+            if constexpr (OUT == 0) ((float*)Y)[off] = y;
+            else ((__bf16*)Y)[off] = (__bf16)y;
         }
     }
 }
 
-template <int TM, int D>
-hipError_t launch_wo(const uint16_t* x, int m, const int8_t* wq, const float* sw, int n, int k, const void* bias,
-                     int bias_kind, void* y, int out_kind, hipStream_t st) {
-    constexpr int NG = 2, W = 2;
-    const dim3 grid((n + 16 * NG - 1) / (16 * NG)), block(64 * W);
+template <int TM, int G, int CB, int NB>
+hipError_t launch_wo(const uint16_t* x, int m, const int8_t* wq, const float* sw, int n, int k, int rows,
+                     const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+    const dim3 grid((n + rows - 1) / rows), block(64 * kWaves);
     if (out_kind == 0)
-        hipLaunchKernelGGL((wo_kernel<TM, NG, D, W, 0>), grid, block, 0, st, x, wq, m, n, k, sw, bias, bias_kind, y);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 0>), grid, block, 0, st, x, wq, m, n, k, rows, sw, bias,
+                           bias_kind, y);
     else
-        hipLaunchKernelGGL((wo_kernel<TM, NG, D, W, 1>), grid, block, 0, st, x, wq, m, n, k, sw, bias, bias_kind, y);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 1>), grid, block, 0, st, x, wq, m, n, k, rows, sw, bias,
+                           bias_kind, y);
     return hipGetLastError();
+}
+
+// One chunk per batch, two register buffers: measured on the decode shapes,
+// larger batches leave more compute after the last bytes arrive and more
+// buffers only lengthen the queues (both slower).
+template <int TM>
+hipError_t launch_wo_t(int groups, const uint16_t* x, int m, const int8_t* wq, const float* sw, int n, int k,
+                       int rows, const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+    switch (groups) {
+        case 1: return launch_wo<TM, 1, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
+        case 2: return launch_wo<TM, 2, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
+        default: return launch_wo<TM, 3, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
+    }
+}
+
+// compute units of the current device, asked once per device
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
 }
 
 }  // namespace
 
 // Tokens are processed in chunks of up to 64 (each chunk streams the
-// weights once): the kernel is built for the decode shape.
+// weights once): the kernel is built for the decode shape. Rows per
+// workgroup: the rows spread evenly over the compute units in as few rounds
+// as keep a workgroup at 48 rows or fewer, and at least 16.
 hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw, int64_t n,
                                const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+    const int64_t cus = compute_units();
+    const int64_t rounds = (n + cus * kMaxRows - 1) / (cus * kMaxRows);
+    int rows = (int)((n + cus * rounds - 1) / (cus * rounds));
+    if (rows < 16) rows = 16;
+    const int groups = (rows + 15) / 16;
     const int ob = out_kind == 0 ? 4 : 2;
+    const int ni = (int)n, ki = (int)k;
     for (int64_t r0 = 0; r0 < m; r0 += 64) {
         const int mc = (int)((m - r0 < 64) ? m - r0 : 64);
         const uint16_t* xc = (const uint16_t*)x + r0 * k;
         void* yc = (int8_t*)y + r0 * n * ob;
         hipError_t e;
         switch ((mc + 15) / 16) {
-            case 1: e = launch_wo<1, 2>(xc, mc, wq, sw, (int)n, (int)k, bias, bias_kind, yc, out_kind, st); break;
-            case 2: e = launch_wo<2, 1>(xc, mc, wq, sw, (int)n, (int)k, bias, bias_kind, yc, out_kind, st); break;
-            case 3: e = launch_wo<3, 1>(xc, mc, wq, sw, (int)n, (int)k, bias, bias_kind, yc, out_kind, st); break;
-            default: e = launch_wo<4, 1>(xc, mc, wq, sw, (int)n, (int)k, bias, bias_kind, yc, out_kind, st); break;
+            case 1: e = launch_wo_t<1>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
+            case 2: e = launch_wo_t<2>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
+            case 3: e = launch_wo_t<3>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
+            default: e = launch_wo_t<4>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
         }
         if (e != hipSuccess) return e;
     }
