@@ -59,6 +59,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "sqo_dequant": ([_P, _P, _P, _P, _I64, _I64, _P], None),
         "sqo_simulated_forward": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], None),
         "sqo_f64_to_bf16": ([_P, _I64, _P], None),
+        "sqo_reference_linear": ([_P, _P, _P, _I64, _I64, _I64, _P], None),
+        "sqo_relative_error": ([_P, _P, _I64, _P], ctypes.c_double),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -71,7 +73,8 @@ class Oracle:
     """numpy front end of one build of sq_oracle.c."""
 
     def __init__(self, lib_path: str = _LIB_PATH):
-        if not os.path.exists(lib_path):
+        if not os.path.exists(lib_path) or (
+                lib_path == _LIB_PATH and os.path.getmtime(_SRC) > os.path.getmtime(lib_path)):
             build(lib_path)
         self.lib = _bind(ctypes.CDLL(lib_path))
         self.mutant = self.lib.sqo_mutant()
@@ -179,6 +182,29 @@ class Oracle:
         self.lib.sqo_wo_linear(self._ptr(x), self._ptr(wq), self._ptr(sw), self._ptr(b), m, n, k, self._ptr(y))
         return y
 
+    def reference_linear(self, x, w, bias=None) -> np.ndarray:
+        """quantization_error's Y_fp: the unquantised linear x @ w^T + bias
+        in binary64 (x [m, k], w [n, k] float32)."""
+        x = self._f32(x)
+        w = self._f32(w)
+        m, k = x.shape
+        n = w.shape[0]
+        assert w.shape[1] == k
+        b = None if bias is None else self._f32(bias)
+        y = np.empty((m, n), np.float64)
+        self.lib.sqo_reference_linear(self._ptr(x), self._ptr(w), self._ptr(b), m, n, k, self._ptr(y))
+        return y
+
+    def relative_error(self, y_fp, y_q):
+        """quantization_error's measure ||y_fp - y_q||_F / max(||y_fp||_F,
+        1e-12) in binary64; returns (ratio, ||y_fp - y_q||_F, ||y_fp||_F)."""
+        a = np.ascontiguousarray(y_fp, np.float64)
+        b = np.ascontiguousarray(y_q, np.float64)
+        assert a.shape == b.shape
+        norms = np.empty(2, np.float64)
+        r = self.lib.sqo_relative_error(self._ptr(a), self._ptr(b), a.size, self._ptr(norms))
+        return float(r), float(norms[0]), float(norms[1])
+
     def int_gemm(self, xq, wq) -> np.ndarray:
         """INT8 x INT8 -> INT32: acc[t, o] = sum_j xq[t, j] wq[o, j]."""
         xq = np.ascontiguousarray(xq, np.int8)
@@ -244,6 +270,15 @@ class Oracle:
         acc = self.int_gemm(xq, wq)
         y = self.dequant(acc, sx, sw, bias)
         return xq, sx, acc, y
+
+
+    def quantization_error(self, x, w, bias, mx, alpha: float) -> float:
+        """SmoothQuantW8A8.quantization_error after a freeze with running max
+        ``mx`` (None = never calibrated) and ``alpha``: the unquantised
+        linear against the quantized forward (integer route), both binary64."""
+        s, wq, sw = self.prepare_weight(w, mx, alpha)
+        y_q = self.linear(x, s, wq, sw, bias)[3]
+        return self.relative_error(self.reference_linear(x, w, bias), y_q)[0]
 
 
 _default: Oracle | None = None

@@ -308,6 +308,62 @@ void sqo_wo_linear(const float* x, const int8_t* wq, const float* scale_w,
 }
 
 /* ---------------------------------------------------------------------
+ * The full-precision side of quantization_error (page
+ * "w8a8_smoothquant.py", SmoothQuantW8A8.quantization_error): Y_fp is the
+ * plain linear layer on the unquantised input and weights, plus the bias,
+ *   y_fp[t][o] = sum_j x[t][j] * w[o][j] + bias[o]
+ * in binary64 (fp32 or bf16 values widened by the caller: every product is
+ * exact, the sum nearly so).
+ * ------------------------------------------------------------------ */
+void sqo_reference_linear(const float* x, const float* w, const float* bias,
+                          int64_t m, int64_t n, int64_t k, double* y)
+{
+#if SQO_MUTANT == 18
+    /* MUTANT 18: the last term of every k sum is dropped. */
+    const int64_t kk = k - 1;
+#else
+    const int64_t kk = k;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t o = 0; o < n; ++o) {
+            double sum = 0.0;
+            for (int64_t j = 0; j < kk; ++j)
+                sum += (double)x[t * k + j] * (double)w[o * k + j];
+            if (bias) sum += (double)bias[o];
+            y[t * n + o] = sum;
+        }
+}
+
+/* ---------------------------------------------------------------------
+ * quantization_error's measure (same page and method): the Frobenius norm
+ * of the difference of the two outputs over the norm of the full-precision
+ * one, the latter floored at 1e-12:
+ *   ratio = ||y_fp - y_q||_F / max(||y_fp||_F, 1e-12)
+ * in binary64, summing in index order. norms[0] and norms[1] receive the
+ * two norms; returns the ratio.
+ * ------------------------------------------------------------------ */
+double sqo_relative_error(const double* y_fp, const double* y_q, int64_t count,
+                          double* norms)
+{
+    double d2 = 0.0, f2 = 0.0;
+    for (int64_t i = 0; i < count; ++i) {
+        const double d = y_fp[i] - y_q[i];
+        d2 += d * d;
+#if SQO_MUTANT == 19
+        /* MUTANT 19: the denominator measures y_q instead of y_fp. */
+        f2 += y_q[i] * y_q[i];
+#else
+        f2 += y_fp[i] * y_fp[i];
+#endif
+    }
+    const double num = sqrt(d2), den = sqrt(f2);
+    norms[0] = num;
+    norms[1] = den;
+    return num / (den > 1e-12 ? den : 1e-12);
+}
+
+/* ---------------------------------------------------------------------
  * The INT8 x INT8 -> INT32 product the page's forward stands in for:
  *   acc[t, o] = sum_j xq[t, j] * wq[o, j]
  * accumulated in int64. Returns the number of entries that do not fit in

@@ -536,4 +536,76 @@ def _bf16_round(v):
     return (r.astype(np.uint32) << 16).view(np.float32)
 
 
+# ---------------------------------------------------------------------------
+# quantization_error (page "w8a8_smoothquant.py",
+# SmoothQuantW8A8.quantization_error): the unquantised linear Y_fp and the
+# measure ||Y_fp - Y_q||_F / max(||Y_fp||_F, 1e-12).
+# ---------------------------------------------------------------------------
+def pin_reference_linear_exact(o):
+    """Dyadic inputs with few significant bits make every partial sum exact in
+    binary64: the oracle must equal the exact rational x w^T + b. Random fp32
+    inputs: within the binary64 summation bound of the exact value."""
+    rng = _rng(131)
+    m, n, k = 3, 5, 7
+    x = (rng.integers(-15, 16, (m, k)) * 2.0 ** -3).astype(np.float32)
+    w = (rng.integers(-31, 32, (n, k)) * 2.0 ** -6).astype(np.float32)
+    b = (rng.integers(-9, 10, n) * 2.0 ** -4).astype(np.float32)
+    for bias in (b, None):
+        y = o.reference_linear(x, w, bias)
+        for t in range(m):
+            for c in range(n):
+                exact = sum(Fraction(float(x[t, j])) * Fraction(float(w[c, j])) for j in range(k))
+                if bias is not None:
+                    exact += Fraction(float(bias[c]))
+                assert Fraction(float(y[t, c])) == exact, (t, c)
+    x = rng.standard_normal((4, 33), dtype=np.float32)
+    w = rng.standard_normal((6, 33), dtype=np.float32)
+    y = o.reference_linear(x, w, None)
+    for t in range(4):
+        for c in range(6):
+            terms = [Fraction(float(x[t, j])) * Fraction(float(w[c, j])) for j in range(33)]
+            exact = sum(terms)
+            bound = 33 * 2.0 ** -53 * float(sum(abs(v) for v in terms))
+            assert abs(float(Fraction(float(y[t, c])) - exact)) <= bound, (t, c)
+
+
+def pin_relative_error_closed_forms(o):
+    """Equal outputs give 0; y_q = y_fp (1 - 2^-e) with fp32-valued y_fp gives
+    exactly 2^-e (every step scales exactly by a power of two); disjoint
+    supports add in quadrature (3, 4 -> 5/3); a zero reference divides by the
+    floor 1e-12."""
+    rng = _rng(137)
+    a = rng.standard_normal(257, dtype=np.float32).astype(np.float64)
+    r, num, den = o.relative_error(a, a)
+    assert r == 0.0 and num == 0.0 and den > 0
+    for e in (1, 7, 20):
+        d = 2.0 ** -e
+        r, num, den = o.relative_error(a, a * (1.0 - d))
+        assert r == d and num == d * den, (e, r)
+    r, num, den = o.relative_error(np.array([3.0, 0.0]), np.array([0.0, 4.0]))
+    assert (num, den) == (5.0, 3.0) and abs(r - 5.0 / 3.0) <= 2.0 ** -52
+    r, num, den = o.relative_error(np.zeros(2), np.array([3.0, 4.0]))
+    assert (num, den) == (5.0, 0.0) and abs(r / 5e12 - 1.0) <= 2.0 ** -52
+
+
+def pin_quantization_error(o):
+    """On the outlier-channel layer of the error-bound pin: the oracle's
+    quantization_error times ||Y_fp||_F equals the error measured there
+    independently (numpy's binary64 product), smoothing with alpha = 0.5
+    beats the never-calibrated s = 1 (the method's purpose on outlier
+    channels), and alpha = 0.5 stays below the provable bound."""
+    rng = _rng(91)
+    x = _outlier_acts(rng, 16, 256, chans=(3, 77, 200), mult=40.0)
+    w = rng.standard_normal((128, 256), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal(128, dtype=np.float32) * np.float32(0.01)
+    mx = o.calibrate(x)
+    yfp = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    q_half = o.quantization_error(x, w, b, mx, 0.5)
+    err, _, provable = error_bound_terms(o, x, w, b, 0.5)
+    assert abs(q_half * np.linalg.norm(yfp) - err) <= 1e-9 * err
+    assert q_half * np.linalg.norm(yfp) <= provable * (1 + 1e-9)
+    q_plain = o.quantization_error(x, w, b, None, 0.5)
+    assert q_half < q_plain, (q_half, q_plain)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -21,6 +21,8 @@ MUTANTS = {
     15: "per-tensor max divided by 128",
     16: "weight-only linear scaled by the token index",
     17: "weight-only linear drops the bias",
+    18: "reference linear drops the last k term",
+    19: "relative error measured against y_q",
 }
 
 
