@@ -240,6 +240,70 @@ sq_status sq_selfcheck_reciprocal(unsigned long long* mismatches, void* stream);
 sq_status sq_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long long* mismatches,
                                 void* stream);
 
+/*
+ * sq_weight_col_max -- the weight side's per-input-channel maximum, stored
+ * so that a new alpha needs no second pass over W: max_w of
+ * calibrate_smoothquant (page "w8a8_smoothquant.py"),
+ *   w_max_abs[j] = max(max_o |w[o][j]|, 1e-8)
+ *   w          [n][k] in wt (F32 or BF16), 16-byte aligned, n >= 1
+ *   w_max_abs  [k] fp32 out, 16-byte aligned
+ */
+sq_status sq_weight_col_max(const void* w, sq_dtype wt, int64_t n, int64_t k, float* w_max_abs,
+                            void* stream);
+
+/*
+ * sq_recompute_smooth_scale -- SmoothQuantW8A8.recompute_smooth_scale (page
+ * "w8a8_smoothquant.py"): s and the int8 weights for a new alpha from the
+ * stored activation and weight maxima, with one pass over W (the column
+ * max is not recomputed). The results are bit-identical to
+ * sq_prepare_weight(w, ..., x_max_abs, alpha, ...) when w_max_abs comes from
+ * sq_weight_col_max of the same w.
+ *   x_max_abs  [k] fp32 from sq_calibrate, or NULL: never calibrated, s = 1
+ *              and the call returns SQ_WARN_UNCALIBRATED
+ *   w_max_abs  [k] fp32 from sq_weight_col_max (required with x_max_abs;
+ *              every entry a finite binary32 >= 0), 16-byte aligned
+ *   the other arguments and outputs as sq_prepare_weight
+ */
+sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64_t k,
+                                    const float* x_max_abs, const float* w_max_abs, float alpha,
+                                    float* smooth, int8_t* w_q, float* w_scale, void* stream);
+
+/*
+ * sq_reference_linear -- the full-precision output quantization_error
+ * compares against (page "w8a8_smoothquant.py",
+ * SmoothQuantW8A8.quantization_error: the plain linear layer on the
+ * unquantised input and weights):
+ *   y[t][o] = f32(sum_j x[t][j] * w[o][j]) + bias[o]   -> yt
+ * every product exact in fp32 (bf16 operands) or rounded once (fp32
+ * operands), the sum accumulated in fp32 by the matrix units (order
+ * unspecified).
+ *   x     [m][k] in xt (F32 or BF16), 16-byte aligned
+ *   w     [n][k] in xt (the same type as x), 16-byte aligned
+ *   bias  [n] in bias_t (F32 or BF16), or NULL
+ *   y     [m][n] in yt (SQ_F32 or SQ_BF16), 16-byte aligned
+ * m = 0 is a no-op.
+ */
+sq_status sq_reference_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const void* w,
+                              int64_t n, const void* bias, sq_dtype bias_t, void* y, sq_dtype yt,
+                              void* stream);
+
+/*
+ * sq_relative_error -- quantization_error's measure (page
+ * "w8a8_smoothquant.py", SmoothQuantW8A8.quantization_error):
+ *   result[0] = ||y_fp - y_q||_F,  result[1] = ||y_fp||_F,
+ *   result[2] = result[0] / max(result[1], 1e-12)
+ * with the sums of squares in binary64, in a fixed order (the same count
+ * gives the same bits).
+ *   y_fp, y_q  [count] fp32 each (e.g. sq_reference_linear and
+ *              sq_w8a8_gemm outputs), 16-byte aligned, count >= 1
+ *   workspace  device memory of sq_relative_error_workspace_bytes(count)
+ *              bytes, 8-byte aligned (partial sums; overwritten)
+ *   result     [3] binary64 out, device memory, 8-byte aligned
+ */
+sq_status sq_relative_error(const float* y_fp, const float* y_q, int64_t count, void* workspace,
+                            size_t workspace_bytes, double* result, void* stream);
+size_t sq_relative_error_workspace_bytes(int64_t count);
+
 /* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);
 

@@ -188,3 +188,64 @@ def test_wo_linear_errors(L):
     assert call(sw=None) == B.SQ_ERR_ARG
     assert call(x=BAD) == B.SQ_ERR_ALIGN
     assert call(m=0, x=None) == B.SQ_OK
+
+
+def test_weight_col_max_errors(L):
+    f = L.sq_weight_col_max
+    assert f(OK_PTR, B.SQ_I32, 4, 64, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, 0, 64, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 40, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(None, B.SQ_BF16, 4, 64, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, None, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, BAD, None) == B.SQ_ERR_ALIGN
+
+
+def test_recompute_smooth_scale_errors(L):
+    f = L.sq_recompute_smooth_scale
+
+    def call(w=OK_PTR, wt=B.SQ_BF16, n=4, k=64, mx=OK_PTR, mw=OK_PTR, alpha=0.5, s=OK_PTR, wq=OK_PTR, sw=OK_PTR):
+        return f(w, wt, n, k, mx, mw, alpha, s, wq, sw, None)
+
+    assert call(wt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=8) == B.SQ_ERR_ALIGN
+    assert call(alpha=1.5) == B.SQ_ERR_ARG
+    assert call(alpha=float("nan")) == B.SQ_ERR_ARG
+    assert call(mw=None) == B.SQ_ERR_ARG          # calibrated needs the stored weight max
+    assert call(s=None) == B.SQ_ERR_ARG
+    assert call(mw=BAD) == B.SQ_ERR_ALIGN
+    assert call(wq=BAD) == B.SQ_ERR_ALIGN
+
+
+def test_reference_linear_errors(L):
+    f = L.sq_reference_linear
+
+    def call(x=OK_PTR, xt=B.SQ_BF16, m=4, k=64, w=OK_PTR, n=8, bias=None, bt=B.SQ_F32, y=OK_PTR, yt=B.SQ_F32):
+        return f(x, xt, m, k, w, n, bias, bt, y, yt, None)
+
+    assert call(xt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(yt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(bias=OK_PTR, bt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=B.SQ_MAX_K + 16) == B.SQ_ERR_SHAPE
+    assert call(k=20) == B.SQ_ERR_ALIGN
+    assert call(w=None) == B.SQ_ERR_ARG
+    assert call(y=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0, x=None, w=None, y=None) == B.SQ_OK
+
+
+def test_relative_error_errors(L):
+    f = L.sq_relative_error
+    need = L.sq_relative_error_workspace_bytes(1000)
+    assert need >= 16 and need % 16 == 0
+    assert L.sq_relative_error_workspace_bytes(0) == 0
+    # more elements never need fewer partial sums, and the block count is capped
+    assert L.sq_relative_error_workspace_bytes(10 ** 9) >= need
+    assert L.sq_relative_error_workspace_bytes(10 ** 12) == L.sq_relative_error_workspace_bytes(10 ** 11)
+    assert f(OK_PTR, OK_PTR, 0, OK_PTR, need, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(None, OK_PTR, 1000, OK_PTR, need, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, OK_PTR, 1000, OK_PTR, need, None, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, OK_PTR, 1000, None, need, OK_PTR, None) == B.SQ_ERR_WORKSPACE
+    assert f(OK_PTR, OK_PTR, 1000, OK_PTR, need - 1, OK_PTR, None) == B.SQ_ERR_WORKSPACE
+    assert f(BAD, OK_PTR, 1000, OK_PTR, need, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(OK_PTR, OK_PTR, 1000, OK_PTR, need, OK_PTR + 4, None) == B.SQ_ERR_ALIGN

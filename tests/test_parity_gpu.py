@@ -447,3 +447,153 @@ def test_wo_linear(orc, shape, out, bias):
     yref = orc.wo_linear(c.x.f32, wq, sw, bias_f)
     mag = (np.abs(c.x.f32.astype(np.float64)) @ np.abs(wq.astype(np.float64)).T) * sw[None, :].astype(np.float64)
     _assert_wo_close(down(y), yref, mag, k, out)
+
+
+# ---------------------------------------------------------------------------
+# Re-smoothing from stored maxima and quantization_error (page
+# "w8a8_smoothquant.py": recompute_smooth_scale, quantization_error).
+# ---------------------------------------------------------------------------
+def _with_zero_column(t, dtype):
+    """The weights of a case with input channel 0 all zero (floored max)."""
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(t.bits).copy()
+        bits[:, 0] = 0
+        f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return up(bits), f32
+    f32 = t.f32.copy()
+    f32[:, 0] = 0.0
+    return up(f32), f32
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_weight_col_max(orc, shape, dtype):
+    c = _case(shape, dtype)
+    w, w_np = _with_zero_column(c.w, dtype)
+    mw = torch.full((c.k,), -1.0, dtype=torch.float32, device=DEV)
+    assert B.sq_weight_col_max(w, mw) == B.SQ_OK
+    torch.cuda.synchronize()
+    want = orc.weight_col_max(w_np)
+    assert want[0] == np.float32(1e-8)
+    assert_equal(down(mw), want, "weight column max")
+
+
+@pytest.mark.parametrize("alpha", ALPHAS, ids=lambda a: f"a{a}")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(7, 17, 48), (130, 260, 528), (64, 512, 4096), (5, 40, 11008)], ids=_id)
+def test_recompute_smooth_scale(orc, shape, dtype, alpha):
+    c = _case(shape, dtype)
+    w = up(c.w)
+    mx = orc.calibrate(c.x.f32)
+    mw = _zeros(c.k, torch.float32)
+    B.sq_weight_col_max(w, mw)
+    s, wq, sw = _zeros(c.k, torch.float32), _zeros((c.n, c.k), torch.int8), _zeros(c.n, torch.float32)
+    # a stale result of another alpha first: every output must be rewritten
+    B.sq_recompute_smooth_scale(w, up(mx), mw, 0.9, s, wq, sw)
+    st = B.sq_recompute_smooth_scale(w, None if alpha is None else up(mx), mw, 0.5 if alpha is None else alpha,
+                                     s, wq, sw)
+    torch.cuda.synchronize()
+    assert st == (B.SQ_WARN_UNCALIBRATED if alpha is None else B.SQ_OK)
+    s_ref, wq_ref, sw_ref = orc.prepare_weight(c.w.f32, None if alpha is None else mx,
+                                               0.5 if alpha is None else alpha)
+    assert_equal(down(s), s_ref, "smooth")
+    assert_equal(down(sw), sw_ref, "w_scale")
+    assert_equal(down(wq), wq_ref, "w_q")
+
+
+def _assert_sum_close(got, yref, mag, terms, out):
+    """An fp32 sum of `terms` rounded terms (any order) is within
+    terms 2^-24 sum|term| of the exact sum; the bias add rounds once more,
+    a bf16 output adds half a bf16 ulp."""
+    if out == "f32":
+        g = got.astype(np.float64)
+        half_ulp = 0.0
+    else:
+        g = (got.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        e = np.floor(np.log2(np.maximum(np.abs(yref), 2.0 ** -126)))
+        half_ulp = 2.0 ** (e - 8)
+    bound = terms * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(yref) + half_ulp + 1e-30
+    err = np.abs(g - yref)
+    bad = err > bound
+    assert not bad.any(), (int(bad.sum()), float((err / bound).max()))
+
+
+REF = [(1, 1, 16), (3, 17, 48), (33, 7, 272), (130, 260, 528), (257, 300, 1040), (300, 129, 2064)]
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", REF, ids=_id)
+def test_reference_linear(orc, shape, dtype, out, bias):
+    m, n, k = shape
+    c = _case(shape, dtype, seed=31, bias=True)
+    bias_t = bias_f = None
+    if bias == "f32":
+        bias_f = c.bias.f32.astype(np.float32)
+        bias_t = up(bias_f)
+    elif bias == "bf16":
+        bt = torch.from_numpy(c.bias.f32.astype(np.float32)).to(torch.bfloat16)
+        bias_f = bt.float().numpy()
+        bias_t = bt.to(DEV)
+    y = _zeros((m, n), torch.float32 if out == "f32" else torch.bfloat16)
+    assert B.sq_reference_linear(up(c.x), up(c.w), bias_t, y) == B.SQ_OK
+    torch.cuda.synchronize()
+    yref = orc.reference_linear(c.x.f32, c.w.f32, bias_f)
+    mag = np.abs(c.x.f32.astype(np.float64)) @ np.abs(c.w.f32.astype(np.float64)).T
+    _assert_sum_close(down(y), yref, mag, k + 1 if dtype == "f32" else k, out)
+
+
+@pytest.mark.parametrize("count", [1, 3, 4, 1000, 4099, (1 << 20) + 5, 3 * (1 << 22) + 1])
+def test_relative_error(orc, count):
+    rng = np.random.default_rng(count)
+    a = rng.standard_normal(count, dtype=np.float32)
+    b = (a + rng.standard_normal(count, dtype=np.float32) * np.float32(0.01)).astype(np.float32)
+    ws = torch.empty(max(B.sq_relative_error_workspace_bytes(count), 8), dtype=torch.uint8, device=DEV)
+    res = torch.empty(3, dtype=torch.float64, device=DEV)
+    a_d, b_d = up(a), up(b)
+    assert B.sq_relative_error(a_d, b_d, ws, res) == B.SQ_OK
+    got = down(res).copy()
+    ratio, num, den = orc.relative_error(a.astype(np.float64), b.astype(np.float64))
+    # a sum of `count` non-negative binary64 terms is within (count - 1) 2^-53
+    # of the exact sum relative to it, in any order (the oracle's sequential
+    # sum and the kernel's blocked one each); a square root halves a relative
+    # error, the ratio adds two
+    tol = (count + 64) * 2.0 ** -53
+    for g, w, t in zip(got, (num, den, ratio), (tol, tol, 2 * tol)):
+        assert abs(g - w) <= t * abs(w), (g, w)
+    # the same count gives the same bits
+    B.sq_relative_error(a_d, b_d, ws, res)
+    assert np.array_equal(down(res).view(np.uint64), got.view(np.uint64))
+    # a zero reference: the denominator floor
+    zero = _zeros(count, torch.float32)
+    B.sq_relative_error(zero, b_d, ws, res)
+    got = down(res)
+    ratio, num, den = orc.relative_error(np.zeros(count), b.astype(np.float64))
+    assert got[1] == 0.0 and den == 0.0
+    assert abs(got[0] - num) <= tol * num and abs(got[2] - ratio) <= 2 * tol * ratio
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_quantization_error(orc, dtype):
+    """The layer's quantization_error (reference linear, quantized forward in
+    fp32, relative error) against the oracle's, within the bound the two
+    outputs' own tolerances give: y_q within 1e-6 (|acc sx sw| + |bias|),
+    y_fp within (k + 1) 2^-24 sum|x w| + 2^-24 |y_fp|."""
+    c = inputs.tiny() if dtype == "f32" else inputs.small(48, 96, 272, seed=5, dtype="bf16")
+    layer = B.SmoothQuantLinear(up(c.w), up(c.bias), alpha=0.5)
+    layer.calibrate(up(c.x))
+    layer.freeze()
+    mx = orc.calibrate(c.x.f32)
+    x64, w64 = c.x.f32.astype(np.float64), c.w.f32.astype(np.float64)
+    for alpha in (0.5, 0.25, 1.0, 0.0):
+        layer.recompute(alpha)
+        got = layer.quantization_error(up(c.x))
+        want = orc.quantization_error(c.x.f32, c.w.f32, c.bias.f32, mx, alpha)
+        s, wq, sw = orc.prepare_weight(c.w.f32, mx, alpha)
+        xq, sx, acc, y = orc.linear(c.x.f32, s, wq, sw, c.bias.f32)
+        yfp = orc.reference_linear(c.x.f32, c.w.f32, c.bias.f32)
+        bq = 1e-6 * (np.abs(acc * sx[:, None].astype(np.float64) * sw[None, :]) + np.abs(c.bias.f32)[None, :])
+        bfp = (c.k + 1) * 2.0 ** -24 * (np.abs(x64) @ np.abs(w64).T) + 2.0 ** -24 * np.abs(yfp)
+        tol = (np.linalg.norm(bq) + np.linalg.norm(bfp)) / np.linalg.norm(yfp)
+        assert abs(got - want) <= tol + 1e-12, (alpha, got, want, tol)

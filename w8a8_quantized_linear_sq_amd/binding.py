@@ -46,6 +46,11 @@ _SIGNATURES = {
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
     "sq_w8a8_gemm_per_tensor": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_wo_linear": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_weight_col_max": ([_P, _E, _I64, _I64, _P, _P], _E),
+    "sq_recompute_smooth_scale": ([_P, _E, _I64, _I64, _P, _P, _F, _P, _P, _P, _P], _E),
+    "sq_reference_linear": ([_P, _E, _I64, _I64, _P, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_relative_error": ([_P, _P, _I64, _P, _SZ, _P, _P], _E),
+    "sq_relative_error_workspace_bytes": ([_I64], _SZ),
     "sq_selfcheck_reciprocal": ([_P, _P], _E),
     "sq_selfcheck_division": ([ctypes.c_uint, ctypes.c_uint, _P, _P], _E),
 }
@@ -232,6 +237,60 @@ def sq_wo_linear(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, bias
                    _ptr(y), _dtype_code(y), _stream(stream, x))
 
 
+def sq_weight_col_max(w: torch.Tensor, w_max_abs: torch.Tensor, stream=None) -> int:
+    """w_max_abs[j] = max(max_o |w[o, j]|, 1e-8)."""
+    n, k = w.shape
+    _need_dtype(w_max_abs, torch.float32, "w_max_abs")
+    return _invoke("sq_weight_col_max", _ptr(w), _dtype_code(w), n, k, _ptr(w_max_abs), _stream(stream, w))
+
+
+def sq_recompute_smooth_scale(w: torch.Tensor, x_max_abs: torch.Tensor | None, w_max_abs: torch.Tensor | None,
+                              alpha: float, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                              stream=None) -> int:
+    """s, int8 weights and scales for a new alpha from the stored maxima (one
+    pass over w); SQ_WARN_UNCALIBRATED when x_max_abs is None."""
+    n, k = w.shape
+    _need_dtype(smooth, torch.float32, "smooth")
+    _need_dtype(w_q, torch.int8, "w_q")
+    _need_dtype(w_scale, torch.float32, "w_scale")
+    for t, nm in ((x_max_abs, "x_max_abs"), (w_max_abs, "w_max_abs")):
+        if t is not None:
+            _need_dtype(t, torch.float32, nm)
+    return _invoke("sq_recompute_smooth_scale", _ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), _ptr(w_max_abs),
+                   float(alpha), _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w))
+
+
+def sq_reference_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, y: torch.Tensor,
+                        stream=None) -> int:
+    """The unquantised linear y = x w^T + bias (x and w both fp32 or both
+    bf16; fp32 sums)."""
+    m, k = x.shape
+    n = w.shape[0]
+    if w.dtype != x.dtype or w.shape[1] != k:
+        raise TypeError("w must have x's dtype and k columns")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_reference_linear", _ptr(x), _dtype_code(x), m, k, _ptr(w), n, _ptr(bias), bt, _ptr(y),
+                   _dtype_code(y), _stream(stream, x))
+
+
+def sq_relative_error_workspace_bytes(count: int) -> int:
+    return int(lib().sq_relative_error_workspace_bytes(count))
+
+
+def sq_relative_error(y_fp: torch.Tensor, y_q: torch.Tensor, workspace: torch.Tensor, result: torch.Tensor,
+                      stream=None) -> int:
+    """result (3 float64, device) = ||y_fp - y_q||_F, ||y_fp||_F and their
+    ratio (denominator floored at 1e-12); y_fp and y_q fp32 of one size."""
+    _need_dtype(y_fp, torch.float32, "y_fp")
+    _need_dtype(y_q, torch.float32, "y_q")
+    _need_dtype(result, torch.float64, "result")
+    if y_fp.numel() != y_q.numel() or result.numel() < 3:
+        raise ValueError("y_fp and y_q must have one size, result at least 3 elements")
+    nbytes = workspace.numel() * workspace.element_size()
+    return _invoke("sq_relative_error", _ptr(y_fp), _ptr(y_q), y_fp.numel(), _ptr(workspace), nbytes,
+                   _ptr(result), _stream(stream, y_fp))
+
+
 def sq_selfcheck_reciprocal(mismatches: torch.Tensor, stream=None) -> int:
     """Adds to mismatches[0] (int64, device) the count of s in [2^-100, 2^100)
     whose kernel reciprocal differs from the IEEE 1/s."""
@@ -290,6 +349,7 @@ class SmoothQuantLinear:
         self.smooth = torch.ones(k, dtype=torch.float32, device=dev)
         self.weight_int8 = torch.zeros((n, k), dtype=torch.int8, device=dev)
         self.weight_scale = torch.ones(n, dtype=torch.float32, device=dev)
+        self.weight_max_abs = torch.empty(k, dtype=torch.float32, device=dev)
         self.is_quantized = False
 
     def calibrate(self, x: torch.Tensor) -> None:
@@ -300,19 +360,40 @@ class SmoothQuantLinear:
         self.calib_count += x2.shape[0]
 
     def freeze(self) -> int:
-        """Returns SQ_OK, or SQ_WARN_UNCALIBRATED when no batch was seen."""
+        """Returns SQ_OK, or SQ_WARN_UNCALIBRATED when no batch was seen. The
+        weight column max is kept for recompute."""
         mx = self.calib_max_abs if self.calib_count else None
-        st = sq_prepare_weight(self.weight, mx, self.alpha, self.smooth, self.weight_int8, self.weight_scale)
+        sq_weight_col_max(self.weight, self.weight_max_abs)
+        st = sq_recompute_smooth_scale(self.weight, mx, self.weight_max_abs, self.alpha, self.smooth,
+                                       self.weight_int8, self.weight_scale)
         self.is_quantized = True
         return st
 
     def recompute(self, alpha: float) -> int:
-        """Re-smooth and re-quantise the weights for a new alpha."""
+        """recompute_smooth_scale: re-smooth and re-quantise the weights for a
+        new alpha from the stored maxima (one pass over the weights)."""
         if not self.is_quantized:
             raise RuntimeError("recompute before freeze")
         self.alpha = float(alpha)
         mx = self.calib_max_abs if self.calib_count else None
-        return sq_prepare_weight(self.weight, mx, self.alpha, self.smooth, self.weight_int8, self.weight_scale)
+        return sq_recompute_smooth_scale(self.weight, mx, self.weight_max_abs, self.alpha, self.smooth,
+                                         self.weight_int8, self.weight_scale)
+
+    def quantization_error(self, x: torch.Tensor) -> float:
+        """||Y_fp - Y_q||_F / max(||Y_fp||_F, 1e-12): the unquantised linear
+        against the quantized forward, both fp32 outputs."""
+        if not self.is_quantized:
+            raise RuntimeError("quantization_error before freeze")
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        w = self.weight if self.weight.dtype == x2.dtype else self.weight.to(x2.dtype)
+        y_fp = torch.empty((x2.shape[0], w.shape[0]), dtype=torch.float32, device=x2.device)
+        sq_reference_linear(x2, w, self.bias, y_fp)
+        y_q = self.forward(x2, out_dtype=torch.float32)
+        ws = torch.empty(max(sq_relative_error_workspace_bytes(y_fp.numel()), 8), dtype=torch.uint8,
+                         device=x2.device)
+        result = torch.empty(3, dtype=torch.float64, device=x2.device)
+        sq_relative_error(y_fp, y_q, ws, result)
+        return float(result[2].item())
 
     def forward(self, x: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
         if not self.is_quantized:

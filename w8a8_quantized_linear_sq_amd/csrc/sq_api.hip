@@ -161,6 +161,77 @@ sq_status sq_wo_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const i
                                         yt == SQ_F32 ? 0 : 1, as_stream(stream)));
 }
 
+sq_status sq_weight_col_max(const void* w, sq_dtype wt, int64_t n, int64_t k, float* w_max_abs, void* stream) {
+    if (!fp_in(wt)) return SQ_ERR_DTYPE;
+    if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!w || !w_max_abs) return SQ_ERR_ARG;
+    if (!aligned16(w) || !aligned16(w_max_abs)) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    // the running max starts at the floor, so the result is the floored max
+    hipError_t e = sq_launch_fill(w_max_abs, sq::kFloor, k, s);
+    if (e == hipSuccess) e = sq_launch_colmax(w, wt == SQ_BF16, n, k, w_max_abs, s);
+    return launched(e);
+}
+
+sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* x_max_abs,
+                                    const float* w_max_abs, float alpha, float* smooth, int8_t* w_q,
+                                    float* w_scale, void* stream) {
+    if (!fp_in(wt)) return SQ_ERR_DTYPE;
+    if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (!w || !smooth || !w_q || !w_scale) return SQ_ERR_ARG;
+    if (x_max_abs && !w_max_abs) return SQ_ERR_ARG;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    if (x_max_abs && (!aligned16(x_max_abs) || !aligned16(w_max_abs))) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    hipError_t e;
+    if (!x_max_abs) {
+        e = sq_launch_fill(smooth, 1.0f, k, s);
+    } else {
+        // the stored column max stands for the single row group of the
+        // smoothing-factor kernel (non-negative binary32: its bit pattern
+        // orders as the value)
+        e = sq_launch_smooth_factor(x_max_abs, (const unsigned*)w_max_abs, 1, (double)alpha, 1.0 - (double)alpha,
+                                    k, smooth, s);
+    }
+    if (e == hipSuccess) e = sq_launch_quantize_weight(w, wt == SQ_BF16, smooth, n, k, w_q, w_scale, s);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
+}
+
+sq_status sq_reference_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const void* w, int64_t n,
+                              const void* bias, sq_dtype bias_t, void* y, sq_dtype yt, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (!(yt == SQ_F32 || yt == SQ_BF16)) return SQ_ERR_DTYPE;
+    if (bias && !fp_in(bias_t)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (m == 0) return SQ_OK;
+    if (!x || !w || !y) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_reference_gemm(x, w, xt == SQ_BF16, m, n, k, bias, bias_kind(bias, bias_t), y,
+                                             out_kind(yt), as_stream(stream)));
+}
+
+size_t sq_relative_error_workspace_bytes(int64_t count) {
+    return count <= 0 ? 0 : (size_t)16 * (size_t)sq_relative_error_blocks(count);
+}
+
+sq_status sq_relative_error(const float* y_fp, const float* y_q, int64_t count, void* workspace,
+                            size_t workspace_bytes, double* result, void* stream) {
+    if (count <= 0) return SQ_ERR_SHAPE;
+    if (!y_fp || !y_q || !result) return SQ_ERR_ARG;
+    if (!workspace || workspace_bytes < sq_relative_error_workspace_bytes(count)) return SQ_ERR_WORKSPACE;
+    if (!aligned16(y_fp) || !aligned16(y_q) || ((uintptr_t)workspace & 7u) != 0 || ((uintptr_t)result & 7u) != 0)
+        return SQ_ERR_ALIGN;
+    return launched(sq_launch_relative_error(y_fp, y_q, count, (double*)workspace, result, as_stream(stream)));
+}
+
 sq_status sq_selfcheck_reciprocal(unsigned long long* mismatches, void* stream) {
     if (!mismatches) return SQ_ERR_ARG;
     if (((uintptr_t)mismatches & 7u) != 0) return SQ_ERR_ALIGN;

@@ -64,6 +64,17 @@ hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsign
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                           void* y, int out_kind, int scalar_scales, hipStream_t st);
+// the reference linear of quantization_error: x [m][k] times w [n][k]
+// (both bf16, or both fp32), fp32 sums, plus bias; out_kind 0 fp32, 1 bf16
+hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int64_t m, int64_t n, int64_t k,
+                                    const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st);
+// relative Frobenius error of y_q against y_fp ([count] fp32 each, 16-byte
+// aligned): sq_relative_error_blocks(count) pairs of binary64 partial sums
+// in partial, then out[0] = ||y_fp - y_q||, out[1] = ||y_fp||, out[2] the
+// ratio (denominator floored at 1e-12)
+int sq_relative_error_blocks(int64_t count);
+hipError_t sq_launch_relative_error(const float* y_fp, const float* y_q, int64_t count, double* partial,
+                                    double* out, hipStream_t st);
 // the same product for m <= 64 tokens (weight-streaming kernel)
 constexpr int64_t kSkinnyMaxM = 64;
 hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,

@@ -36,7 +36,17 @@
 //     hardware deals workgroups round-robin over the 8 XCDs) form a compact
 //     block sharing A rows and B columns in that XCD's L2;
 //   * the epilogue stages each 32-row slab through LDS and writes whole
-//     16-byte row chunks.
+//     16-byte row chunks;
+//   * the same kernel, with the operands' element type as a parameter (K
+//     counted in bytes, so the LDS layout and the DMA are unchanged), is the
+//     full-precision reference of quantization_error (page
+//     "w8a8_smoothquant.py", SmoothQuantW8A8.quantization_error: the plain
+//     linear layer on the unquantised operands): bf16 operands on
+//     v_mfma_f32_32x32x16_bf16, whose 16-byte fragment is 8 bf16 at k offset
+//     8 (l / 32), the int8 fragment's bytes; fp32 operands on four
+//     v_mfma_f32_32x32x2_f32 per fragment, the e-th taking element e of
+//     every lane's four (the same k permutation in both operands); fp32
+//     sums, the bias added in the epilogue, no scales.
 //
 // Measured at M = N = K = 4096 (bf16 out): the clock under this load is
 // power-limited to about 1.7 GHz (int8 MFMA at 32 busy cycles per
@@ -51,7 +61,8 @@ using namespace sq;
 namespace {
 
 constexpr int kBK = 64;            // bytes of K per step
-constexpr int kStages = 4;         // LDS ring depth
+constexpr int kStagesPingPong = 4;  // LDS ring depth, 8-wavefront tiles
+constexpr int kStagesInterleaved = 4;  // LDS ring depth, 4-wavefront tile
 constexpr int kRowLanes = kBK / 16;        // lanes of one DMA load per row
 constexpr int kBlockRows = 64 / kRowLanes; // rows per 1 KiB DMA load
 constexpr int kXcds = 8;
@@ -90,18 +101,27 @@ __device__ __forceinline__ void sched_slice() {
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// operand element types: int8 codes, or the reference's bf16 / fp32
+constexpr int kI8 = 0, kBf16 = 1, kF32 = 2;
 
 // MFMA 32x32x32 i8 operand: lane l holds 16 k-consecutive bytes of row
 // (l % 32) at k offset 16 * (l / 32) of a 32-wide k slice; A and B use the
 // same mapping, so the hardware's pairing of bytes is the same for both.
 // Result: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 
-template <int BM, int BN, int WGM, int WGN, int OUT>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
+// ET: operand element type (kI8: the int8 product with the dequantisation;
+// kBf16 / kF32: the reference linear). k is the row length in bytes.
+template <int ET, int BM, int BN, int WGM, int WGN, int OUT>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
     int bias_kind, void* __restrict__ Y, int grid_m, int grid_n, int scalar_scales) {
     constexpr int NW = WGM * WGN;                 // wavefronts (WGM x WGN grid)
+    constexpr int kStages = NW == 8 ? kStagesPingPong : kStagesInterleaved;
+    static_assert(kStages >= 3 && kStages <= 5, "the prologue's wait covers up to three later stages");
     constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wavefront block
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int STAGE = (BM + BN) * kBK;          // bytes of one LDS stage (A rows, then B rows)
@@ -165,11 +185,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
         }
     };
 
-    i32x16 acc[TM][TN];
+    static_assert(ET == kI8 || OUT != 2, "int32 output is the int8 product's");
+    using Acc = std::conditional_t<ET == kI8, i32x16, f32x16>;
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = i32x16{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
 
     // fragment offsets inside a stage: row (.. + fr), k chunk 2 s + lane / 32
     const int fr = lane & 31;
@@ -192,8 +214,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (ET == kI8) {
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+                } else if constexpr (ET == kBf16) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i]),
+                                                                        __builtin_bit_cast(bf16x8, xb[j]),
+                                                                        acc[i][j], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(xa[i][e]),
+                                                                         __int_as_float(xb[j][e]), acc[i][j], 0, 0, 0);
+                }
+            }
     };
     auto barrier = [] {
         __builtin_amdgcn_sched_barrier(0);
@@ -212,9 +246,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     for (int st = 0; st < kStages - 1; ++st)
         if (st < KF) issue_stage(st, st);
     if (KF > 0) {
-        // stage 0 landed (later ones may be in flight), visible to all
-        if (KF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
-        else if (KF > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        // stage 0 landed (the later ones issued may be in flight), visible
+        // to all
+        const int later = min(KF, kStages - 1) - 1;
+        if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LOADS));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         barrier();
     }
@@ -325,13 +362,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
         swc[j] = 0.0f;
         bc[j] = 0.0f;
         if constexpr (OUT != 2) {
-            swc[j] = sb[scalar_scales ? 0 : col];
+            if constexpr (ET == kI8) swc[j] = sb[scalar_scales ? 0 : col];
             if (bias_kind == 1) bc[j] = ((const float*)bias)[col];
             else if (bias_kind == 2) bc[j] = __uint_as_float((uint32_t)((const uint16_t*)bias)[col] << 16);
         }
     }
     auto value = [&](int i, int j, int r, float sar) -> float {
-        float y = (float)acc[i][j][r] * sar * swc[j];
+        float y;
+        if constexpr (ET == kI8) y = (float)acc[i][j][r] * sar * swc[j];
+        else y = acc[i][j][r];
         if (bias_kind) y = y + bc[j];
         return y;
     };
@@ -348,8 +387,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int rbase = m0 + wm * WM + i * 32;
-            float sar[4][4];
-            if constexpr (OUT != 2) {
+            float sar[4][4] = {};
+            if constexpr (OUT != 2 && ET == kI8) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float4 v = scalar_scales ? make_float4(sa[0], sa[0], sa[0], sa[0])
@@ -413,7 +452,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
                 if constexpr (OUT == 2) {
                     ((int*)Y)[off] = acc[i][j][r];
                 } else {
-                    const float y = value(i, j, r, sa[scalar_scales ? 0 : row]);
+                    float sar = 0.0f;
+                    if constexpr (ET == kI8) sar = sa[scalar_scales ? 0 : row];
+                    const float y = value(i, j, r, sar);
                     if constexpr (OUT == 0) ((float*)Y)[off] = y;
                     else ((__bf16*)Y)[off] = (__bf16)y;
                 }
@@ -422,43 +463,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int ET, int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
-                       int n, int k, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
+                       int n, int kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
                        hipStream_t st) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
     dim3 grid(gm * gn), block(64 * WGM * WGN);
-    switch (out_kind) {
-        case 0:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 0>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn, scalar_scales);
-            break;
-        case 1:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 1>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn, scalar_scales);
-            break;
-        default:
-            hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WGM, WGN, 2>), grid, block, 0, st, xq, wq, m, n, k, sx, sw,
-                               bias, bias_kind, y, gm, gn, scalar_scales);
-            break;
-    }
+    if (out_kind == 0)
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
+                           bias, bias_kind, y, gm, gn, scalar_scales);
+    else if (out_kind == 1)
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
+                           bias, bias_kind, y, gm, gn, scalar_scales);
+    else if constexpr (ET == kI8)
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 2>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
+                           bias, bias_kind, y, gm, gn, scalar_scales);
     return hipGetLastError();
 }
-
-}  // namespace
 
 // Tile choice: the configuration with the least estimated time, whole waves
 // of 256 workgroups (one per CU) times the time of one tile, which is its
 // area over the configuration's measured speed per unit area on MI355X
-// (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs).
-hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
-                          const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
-                          void* y, int out_kind, int scalar_scales, hipStream_t st) {
-    if (m <= 0 || n <= 0) return hipSuccess;
-    // few tokens: the product streams the weights; the tiled kernel would
-    // leave most CUs idle
-    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales,
-                                                          st);
+// (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs of
+// the int8 product).
+template <int ET>
+hipError_t launch_tiled(const int8_t* a, const float* sx, int64_t m, const int8_t* b, const float* sw, int64_t n,
+                        int64_t kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
+                        hipStream_t st) {
     struct Cfg { int bm, bn; double speed; };
     const Cfg cfgs[] = {{256, 256, 1.0}, {128, 256, 0.80}, {128, 128, 0.73}};
     int best = 0;
@@ -472,10 +503,32 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
             best = i;
         }
     }
-    const int mi = (int)m, ni = (int)n, ki = (int)k;
+    const int mi = (int)m, ni = (int)n, ki = (int)kbytes;
     switch (best) {
-        case 0: return launch_tile<256, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        case 1: return launch_tile<128, 256, 2, 4>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        default: return launch_tile<128, 128, 2, 2>(xq, sx, mi, wq, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 0: return launch_tile<ET, 256, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 1: return launch_tile<ET, 128, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        default: return launch_tile<ET, 128, 128, 2, 2>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
     }
+}
+
+}  // namespace
+
+hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
+                          const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
+                          void* y, int out_kind, int scalar_scales, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    // few tokens: the product streams the weights; the tiled kernel would
+    // leave most CUs idle
+    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales,
+                                                          st);
+    return launch_tiled<kI8>(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales, st);
+}
+
+hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int64_t m, int64_t n, int64_t k,
+                                    const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    const int8_t* a = (const int8_t*)x;
+    const int8_t* b = (const int8_t*)w;
+    if (bf16) return launch_tiled<kBf16>(a, nullptr, m, b, nullptr, n, 2 * k, bias, bias_kind, y, out_kind, 0, st);
+    return launch_tiled<kF32>(a, nullptr, m, b, nullptr, n, 4 * k, bias, bias_kind, y, out_kind, 0, st);
 }
