@@ -199,3 +199,67 @@ def test_weight_only_decode_16x4096x11008(orc):
 
 def test_weight_only_prefill_2048x4096x4096(orc):
     _wo_case(orc, inputs.prefill(), 64)
+
+
+def test_mlp_up_alpha_sweep_quantization_error(orc):
+    """quantization_error across the MLP up-projection's alpha sweep (page
+    "w8a8_smoothquant.py": recompute_smooth_scale from the stored maxima, then
+    quantization_error): the stored weight column max and every alpha's s,
+    codes and scales bit for bit; the reference linear and the quantized
+    output (fp32) on sampled rows; the error reduction against the oracle's
+    on the full outputs, within the binary64 summation bound."""
+    case = inputs.mlp_up()
+    m, n, k = case.m, case.n, case.k
+    print(f"alpha sweep {case.name}", flush=True)
+    x_dev, w_dev, b_dev = up(case.x), up(case.w), up(case.bias)
+    run = _calibrate(case)
+    mw = _empty(k, torch.float32)
+    B.sq_weight_col_max(w_dev, mw)
+    y_fp = _empty((m, n), torch.float32)
+    B.sq_reference_linear(x_dev, w_dev, b_dev, y_fp)
+    torch.cuda.synchronize()
+    run_ref = np.zeros(k, np.float32)
+    for cb in case.calib:
+        orc.calibrate(cb.f32, run_ref)
+    assert_equal(down(mw), orc.weight_col_max(case.w.f32), "weight column max")
+
+    rows = _rows(m, 12, seed=99)
+    x_rows = np.ascontiguousarray(case.x.f32[rows])
+    yfp_ref = orc.reference_linear(x_rows, case.w.f32, case.bias.f32)
+    mag = np.abs(x_rows.astype(np.float64)) @ np.abs(case.w.f32.astype(np.float64)).T
+    got = down(y_fp[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    bound = k * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(yfp_ref)
+    assert (np.abs(got - yfp_ref) <= bound).all()
+    y_fp_host = down(y_fp).astype(np.float64)
+
+    s, wq, sw = _empty(k, torch.float32), _empty((n, k), torch.int8), _empty(n, torch.float32)
+    xq, xs = _empty((m, k), torch.int8), _empty(m, torch.float32)
+    y_q = _empty((m, n), torch.float32)
+    ws = _empty(B.sq_relative_error_workspace_bytes(m * n), torch.uint8)
+    res = _empty(3, torch.float64)
+    errors = {}
+    for alpha in (*case.alphas, None):
+        st = B.sq_recompute_smooth_scale(w_dev, None if alpha is None else run, mw, 0.5 if alpha is None else alpha,
+                                         s, wq, sw)
+        assert st == (B.SQ_WARN_UNCALIBRATED if alpha is None else B.SQ_OK)
+        B.sq_quantize_act(x_dev, s, xq, xs)
+        B.sq_w8a8_gemm(xq, xs, wq, sw, b_dev, y_q)
+        B.sq_relative_error(y_fp, y_q, ws, res)
+        torch.cuda.synchronize()
+        s_ref, wq_ref, sw_ref = orc.prepare_weight(case.w.f32, None if alpha is None else run_ref,
+                                                   0.5 if alpha is None else alpha)
+        assert_equal(down(s), s_ref, f"smooth (alpha {alpha})")
+        assert_equal(down(sw), sw_ref, f"w_scale (alpha {alpha})")
+        assert_equal(down(wq), wq_ref, f"w_q (alpha {alpha})")
+        xq_ref, xs_ref = orc.quantize_act(case.x.f32, s_ref)
+        assert_equal(down(xs), xs_ref, f"x_scale (alpha {alpha})")
+        _check_y(orc, y_q, xq_ref, xs_ref, wq_ref, sw_ref, case.bias.f32, rows)
+        got = down(res)
+        ratio, num, den = orc.relative_error(y_fp_host, down(y_q))
+        tol = (m * n + 64) * 2.0 ** -53
+        assert abs(got[0] - num) <= tol * num and abs(got[1] - den) <= tol * den
+        assert abs(got[2] - ratio) <= 2 * tol * ratio
+        errors[alpha] = float(got[2])
+        print(f"alpha {alpha}: quantization_error {got[2]:.6g}", flush=True)
+    # smoothing helps on outlier channels (x100 on 0.5% of them)
+    assert errors[0.5] < errors[None], errors
