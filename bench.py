@@ -211,6 +211,50 @@ def cpu_baseline(case, mode: str, budget_s: float):
     }
 
 
+def alpha_sweep(torch, B, case, s, stream):
+    """The workload's alpha sweep after the timed region (page
+    "w8a8_smoothquant.py": recompute_smooth_scale, then quantization_error):
+    the weight column max once, the reference linear once (bf16 MFMA, fp32
+    out), then per alpha (and for s = 1) the one-pass re-smoothing, the
+    quantized forward with fp32 output and the error reduction, all on the
+    GPU; the re-smoothing and the reference linear are timed with events."""
+    m, n, k = case.m, case.n, case.k
+    dev = s["w"].device
+    mw = torch.empty(k, dtype=torch.float32, device=dev)
+    y_fp = torch.empty((m, n), dtype=torch.float32, device=dev)
+    y_q = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.sq_relative_error_workspace_bytes(m * n), dtype=torch.uint8, device=dev)
+    res = torch.empty(3, dtype=torch.float64, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    B.sq_weight_col_max(s["w"], mw, stream)
+    B.sq_reference_linear(s["x"], s["w"], s["bias"], y_fp, stream)  # warm
+    ev[0].record(stream)
+    B.sq_reference_linear(s["x"], s["w"], s["bias"], y_fp, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ref_ms = ev[0].elapsed_time(ev[1])
+    out = {"reference_linear_us": round(ref_ms * 1e3, 1),
+           "reference_linear_tflops_bf16": round(2.0 * m * n * k / (ref_ms * 1e-3) / 1e12, 1),
+           "note": "after the timed region; recompute = sq_recompute_smooth_scale (one pass over W)"}
+    for alpha in (*case.alphas, None):
+        mx = None if alpha is None else s["run"]
+        a = 0.5 if alpha is None else alpha
+        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], s["wq"], s["ws"], stream)  # warm
+        ev[0].record(stream)
+        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], s["wq"], s["ws"], stream)
+        ev[1].record(stream)
+        B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
+        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], y_q, stream)
+        B.sq_relative_error(y_fp, y_q, ws, res, stream)
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1])
+        gbs = (2 * n * k + n * k + 4 * n + 12 * k) / (t * 1e-3) / 1e9
+        out["s=1" if alpha is None else f"alpha={alpha}"] = {
+            "quantization_error": float(res[2].item()), "recompute_us": round(t * 1e3, 1),
+            "recompute_hbm_frac": round(gbs / PEAK_HBM_GBS, 3)}
+    return out
+
+
 def counter_pass(torch, B, s, stream):
     """A copy of known size (reads and writes 256 MiB: torch.neg over 2^26
     fp32) gives the factor between the HBM counters and real bytes; then the
@@ -488,6 +532,8 @@ def main():
         "gemm_tops": round(gemm_tops, 2),
         "wall_s_timed": round(t_wall, 4),
     }
+    if mode == "full" and len(case.alphas) > 1:
+        line["alpha_sweep"] = alpha_sweep(torch, B, case, sets[0], stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, mode, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
