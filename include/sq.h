@@ -269,6 +269,35 @@ sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64
                                     float* smooth, int8_t* w_q, float* w_scale, void* stream);
 
 /*
+ * sq_smoothing_factor -- step a3 alone (calibrate_smoothquant, page
+ * "w8a8_smoothquant.py"): s from the stored maxima, exactly as
+ * sq_prepare_weight computes it,
+ *   s_j = max(f32(P(max(x_max_abs[j], 1e-8), alpha)) /
+ *             f32(P(max(w_max_abs[j], 1e-8), 1 - alpha)), 1e-8)
+ *   x_max_abs  [k] fp32 from sq_calibrate, or NULL: never calibrated, s = 1
+ *              and the call returns SQ_WARN_UNCALIBRATED
+ *   w_max_abs  [k] fp32 from sq_weight_col_max (every entry a finite
+ *              binary32 >= 0), 16-byte aligned
+ *   alpha      in [0, 1];  smooth [k] fp32 out, 16-byte aligned
+ * With sq_weight_col_max and sq_quantize_weight it splits sq_prepare_weight
+ * into separate calls (the column max does not need the activations'
+ * maxima; s can be recomputed for a new alpha without touching W).
+ */
+sq_status sq_smoothing_factor(const float* x_max_abs, const float* w_max_abs, float alpha, int64_t k,
+                              float* smooth, void* stream);
+
+/*
+ * sq_quantize_weight -- steps a4-a5 alone (freeze_quantization, page
+ * "w8a8_smoothquant.py"): w~ = f32(w * s), one scale per output row,
+ * int8 codes, exactly as sq_prepare_weight writes them.
+ *   w       [n][k] in wt (F32 or BF16), 16-byte aligned, n >= 1
+ *   smooth  [k] fp32 (every s_j > 0), 16-byte aligned
+ *   w_q     [n][k] int8 out, 16-byte aligned;  w_scale [n] fp32 out
+ */
+sq_status sq_quantize_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* smooth,
+                             int8_t* w_q, float* w_scale, void* stream);
+
+/*
  * sq_reference_linear -- the full-precision output quantization_error
  * compares against (page "w8a8_smoothquant.py",
  * SmoothQuantW8A8.quantization_error: the plain linear layer on the

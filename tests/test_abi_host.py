@@ -249,3 +249,22 @@ def test_relative_error_errors(L):
     assert f(OK_PTR, OK_PTR, 1000, OK_PTR, need - 1, OK_PTR, None) == B.SQ_ERR_WORKSPACE
     assert f(BAD, OK_PTR, 1000, OK_PTR, need, OK_PTR, None) == B.SQ_ERR_ALIGN
     assert f(OK_PTR, OK_PTR, 1000, OK_PTR, need, OK_PTR + 4, None) == B.SQ_ERR_ALIGN
+
+
+def test_smoothing_factor_errors(L):
+    f = L.sq_smoothing_factor
+    assert f(OK_PTR, OK_PTR, 0.5, 0, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, OK_PTR, 0.5, 40, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(OK_PTR, OK_PTR, -0.1, 64, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, None, 0.5, 64, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, OK_PTR, 0.5, 64, None, None) == B.SQ_ERR_ARG
+    assert f(BAD, OK_PTR, 0.5, 64, OK_PTR, None) == B.SQ_ERR_ALIGN
+
+
+def test_quantize_weight_errors(L):
+    f = L.sq_quantize_weight
+    assert f(OK_PTR, B.SQ_I32, 4, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, 0, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 72, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN

@@ -597,3 +597,30 @@ def test_layer_quantization_error(orc, dtype):
         bfp = (c.k + 1) * 2.0 ** -24 * (np.abs(x64) @ np.abs(w64).T) + 2.0 ** -24 * np.abs(yfp)
         tol = (np.linalg.norm(bq) + np.linalg.norm(bfp)) / np.linalg.norm(yfp)
         assert abs(got - want) <= tol + 1e-12, (alpha, got, want, tol)
+
+
+@pytest.mark.parametrize("alpha", ALPHAS, ids=lambda a: f"a{a}")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(7, 17, 48), (130, 260, 528), (64, 512, 4096), (5, 40, 11008)], ids=_id)
+def test_split_prepare(orc, shape, dtype, alpha):
+    """sq_weight_col_max -> sq_smoothing_factor -> sq_quantize_weight (the
+    weight preparation as separate calls, the column max on a second stream)
+    equals the oracle's preparation bit for bit."""
+    c = _case(shape, dtype)
+    w = up(c.w)
+    mx = orc.calibrate(c.x.f32)
+    side = torch.cuda.Stream()
+    mw = _zeros(c.k, torch.float32)
+    with torch.cuda.stream(side):
+        B.sq_weight_col_max(w, mw)
+    torch.cuda.current_stream().wait_stream(side)
+    s, wq, sw = _zeros(c.k, torch.float32), _zeros((c.n, c.k), torch.int8), _zeros(c.n, torch.float32)
+    st = B.sq_smoothing_factor(None if alpha is None else up(mx), mw, 0.5 if alpha is None else alpha, s)
+    assert st == (B.SQ_WARN_UNCALIBRATED if alpha is None else B.SQ_OK)
+    assert B.sq_quantize_weight(w, s, wq, sw) == B.SQ_OK
+    torch.cuda.synchronize()
+    s_ref, wq_ref, sw_ref = orc.prepare_weight(c.w.f32, None if alpha is None else mx,
+                                               0.5 if alpha is None else alpha)
+    assert_equal(down(s), s_ref, "smooth")
+    assert_equal(down(sw), sw_ref, "w_scale")
+    assert_equal(down(wq), wq_ref, "w_q")

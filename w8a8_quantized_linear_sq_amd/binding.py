@@ -48,6 +48,8 @@ _SIGNATURES = {
     "sq_wo_linear": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_weight_col_max": ([_P, _E, _I64, _I64, _P, _P], _E),
     "sq_recompute_smooth_scale": ([_P, _E, _I64, _I64, _P, _P, _F, _P, _P, _P, _P], _E),
+    "sq_smoothing_factor": ([_P, _P, _F, _I64, _P, _P], _E),
+    "sq_quantize_weight": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
     "sq_reference_linear": ([_P, _E, _I64, _I64, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_relative_error": ([_P, _P, _I64, _P, _SZ, _P, _P], _E),
     "sq_relative_error_workspace_bytes": ([_I64], _SZ),
@@ -258,6 +260,30 @@ def sq_recompute_smooth_scale(w: torch.Tensor, x_max_abs: torch.Tensor | None, w
             _need_dtype(t, torch.float32, nm)
     return _invoke("sq_recompute_smooth_scale", _ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), _ptr(w_max_abs),
                    float(alpha), _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w))
+
+
+def sq_smoothing_factor(x_max_abs: torch.Tensor | None, w_max_abs: torch.Tensor, alpha: float, smooth: torch.Tensor,
+                        stream=None) -> int:
+    """s from the stored maxima (SQ_WARN_UNCALIBRATED when x_max_abs is None)."""
+    k = smooth.numel()
+    for t, nm in ((x_max_abs, "x_max_abs"), (w_max_abs, "w_max_abs"), (smooth, "smooth")):
+        if t is not None:
+            _need_dtype(t, torch.float32, nm)
+            if t.numel() != k:
+                raise ValueError(f"{nm} must have {k} elements")
+    return _invoke("sq_smoothing_factor", _ptr(x_max_abs), _ptr(w_max_abs), float(alpha), k, _ptr(smooth),
+                   _stream(stream, smooth))
+
+
+def sq_quantize_weight(w: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                       stream=None) -> int:
+    """Int8 codes and per-output-channel scales of w * smooth."""
+    n, k = w.shape
+    _need_dtype(smooth, torch.float32, "smooth")
+    _need_dtype(w_q, torch.int8, "w_q")
+    _need_dtype(w_scale, torch.float32, "w_scale")
+    return _invoke("sq_quantize_weight", _ptr(w), _dtype_code(w), n, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale),
+                   _stream(stream, w))
 
 
 def sq_reference_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, y: torch.Tensor,

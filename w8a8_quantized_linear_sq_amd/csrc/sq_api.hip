@@ -203,6 +203,30 @@ sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64
     return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
 }
 
+sq_status sq_smoothing_factor(const float* x_max_abs, const float* w_max_abs, float alpha, int64_t k,
+                              float* smooth, void* stream) {
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (!w_max_abs || !smooth) return SQ_ERR_ARG;
+    if (!aligned16(w_max_abs) || !aligned16(smooth) || (x_max_abs && !aligned16(x_max_abs))) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    if (!x_max_abs) return launched(sq_launch_fill(smooth, 1.0f, k, s)) == SQ_OK ? SQ_WARN_UNCALIBRATED : SQ_ERR_HIP;
+    return launched(sq_launch_smooth_factor(x_max_abs, (const unsigned*)w_max_abs, 1, (double)alpha,
+                                            1.0 - (double)alpha, k, smooth, s));
+}
+
+sq_status sq_quantize_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* smooth, int8_t* w_q,
+                             float* w_scale, void* stream) {
+    if (!fp_in(wt)) return SQ_ERR_DTYPE;
+    if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!w || !smooth || !w_q || !w_scale) return SQ_ERR_ARG;
+    if (!aligned16(w) || !aligned16(smooth) || !aligned16(w_q)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_quantize_weight(w, wt == SQ_BF16, smooth, n, k, w_q, w_scale, as_stream(stream)));
+}
+
 sq_status sq_reference_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const void* w, int64_t n,
                               const void* bias, sq_dtype bias_t, void* y, sq_dtype yt, void* stream) {
     if (!fp_in(xt)) return SQ_ERR_DTYPE;
