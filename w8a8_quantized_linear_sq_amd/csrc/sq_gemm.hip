@@ -273,6 +273,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
         //        stage kt+1, which the next M phase (by either group) reads.
         // C(kt): the MFMAs of both slices.
         const bool second = wave >= NW / 2;
+        // the wavefront in its MFMA phase runs at raised priority, so that the
+        // SIMD's arbiter serves it first whenever both wavefronts are ready
+        // (measured 1-3% faster)
+        auto mfma_phase = [&] {
+            __builtin_amdgcn_s_setprio(1);
+            mfmas(fa, fb);
+            mfmas(ga, gb);
+            __builtin_amdgcn_s_setprio(0);
+        };
         if (second) barrier();
         int kt = 0;
         for (; kt + kStages - 1 < KF; ++kt) {
@@ -282,8 +291,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
             issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
             __builtin_amdgcn_s_waitcnt(vm_lgkm_imm((kStages - 2) * LOADS));
             barrier();
-            mfmas(fa, fb);
-            mfmas(ga, gb);
+            mfma_phase();
             barrier();
         }
         for (; kt < KF; ++kt) {
@@ -292,8 +300,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
             read_frags(buf, 1, ga, gb);
             __builtin_amdgcn_s_waitcnt(vm_lgkm_imm(0));
             barrier();
-            mfmas(fa, fb);
-            mfmas(ga, gb);
+            mfma_phase();
             barrier();
         }
         if (!second) barrier();
