@@ -7,8 +7,10 @@ Default workload (the headline): the transformer block's O projection
 (M = N = K = 4096, bf16 in and out, alpha = 0.5, calibrated on 512 separate
 tokens fed as 4 batches of 128). One step is one pass of the whole path
 over one batch of synthetic input:
-  reset the running max -> 4 x sq_calibrate -> sq_prepare_weight ->
-  sq_quantize_act -> sq_w8a8_gemm (int8 GEMM + fused dequant).
+  reset the running max -> 4 x sq_calibrate -> sq_prepare_weight_tiled ->
+  sq_quantize_act_tiled -> sq_w8a8_gemm_tiled (int8 GEMM + fused dequant),
+the int8 codes kept in 16 x 64 tiles (--layout row: the row-major calls
+sq_prepare_weight, sq_quantize_act and sq_w8a8_gemm instead).
 Other workloads (--workload) are the remaining shapes of the method's
 workloads: prefill, the block's qkv / up / down linears and the MLP
 up-projection run the same full step; decode times the per-call path
@@ -86,22 +88,25 @@ def _args():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="o_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--layout", choices=("tiled", "row"), default="tiled",
+                   help="int8 code layout of the full step: 16 x 64 tiles (default) or row-major")
     p.add_argument("--counter-pass", action="store_true",
                    help="run only a 256 MiB fp32 copy (known bytes) and the GEMM, 3 times each, for "
                         "rocprofv3 --pmc passes; prints no JSON line")
     return p.parse_args()
 
 
-def _gemm_traffic():
+def _gemm_traffic(layout: str):
     """HBM bytes per GEMM launch of the O projection from the committed
     rocprofv3 counter summary, or None when the GEMM source changed since
-    the counters were taken."""
+    the counters were taken or they were taken on the other layout."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_sha and m_b):
+    m_l = re.search(r"layout:\s*(\w+)", text)
+    if not (m_sha and m_b and m_l) or m_l.group(1) != layout:
         return None
     sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     if sha != m_sha.group(1):
@@ -220,6 +225,8 @@ def alpha_sweep(torch, B, case, s, stream):
     GPU; the re-smoothing and the reference linear are timed with events."""
     m, n, k = case.m, case.n, case.k
     dev = s["w"].device
+    wq = torch.empty((n, k), dtype=torch.int8, device=dev)
+    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
     mw = torch.empty(k, dtype=torch.float32, device=dev)
     y_fp = torch.empty((m, n), dtype=torch.float32, device=dev)
     y_q = torch.empty((m, n), dtype=torch.float32, device=dev)
@@ -239,12 +246,12 @@ def alpha_sweep(torch, B, case, s, stream):
     for alpha in (*case.alphas, None):
         mx = None if alpha is None else s["run"]
         a = 0.5 if alpha is None else alpha
-        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], s["wq"], s["ws"], stream)  # warm
+        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], wq, s["ws"], stream)  # warm
         ev[0].record(stream)
-        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], s["wq"], s["ws"], stream)
+        B.sq_recompute_smooth_scale(s["w"], mx, mw, a, s["smooth"], wq, s["ws"], stream)
         ev[1].record(stream)
-        B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
-        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], y_q, stream)
+        B.sq_quantize_act(s["x"], s["smooth"], xq, s["xs"], stream)
+        B.sq_w8a8_gemm(xq, s["xs"], wq, s["ws"], s["bias"], y_q, stream)
         B.sq_relative_error(y_fp, y_q, ws, res, stream)
         torch.cuda.synchronize()
         t = ev[0].elapsed_time(ev[1])
@@ -255,21 +262,30 @@ def alpha_sweep(torch, B, case, s, stream):
     return out
 
 
-def counter_pass(torch, B, s, stream):
+def counter_pass(torch, B, s, stream, tiled):
     """A copy of known size (reads and writes 256 MiB: torch.neg over 2^26
     fp32) gives the factor between the HBM counters and real bytes; then the
     product of the benchmark step on prepared operands."""
     src = torch.ones(1 << 26, dtype=torch.float32, device=s["x"].device)
     dst = torch.empty_like(src)
     B.sq_calibrate(s["calib"][0], s["run"], stream)
-    B.sq_prepare_weight(s["w"], s["run"], 0.5, s["smooth"], s["wq"], s["ws"], stream)
-    B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
+    m, k = s["x"].shape
+    n = s["w"].shape[0]
+    if tiled:
+        B.sq_prepare_weight_tiled(s["w"], s["run"], 0.5, s["smooth"], s["wq"], s["ws"], stream)
+        B.sq_quantize_act_tiled(s["x"], s["smooth"], s["xq"], s["xs"], stream)
+    else:
+        B.sq_prepare_weight(s["w"], s["run"], 0.5, s["smooth"], s["wq"], s["ws"], stream)
+        B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
     torch.cuda.synchronize()
     for _ in range(3):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     for _ in range(3):
-        B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], s["y"], stream)
+        if tiled:
+            B.sq_w8a8_gemm_tiled(s["xq"], s["xs"], m, s["wq"], s["ws"], n, k, s["bias"], s["y"], stream)
+        else:
+            B.sq_w8a8_gemm(s["xq"], s["xs"], s["wq"], s["ws"], s["bias"], s["y"], stream)
     torch.cuda.synchronize()
     print("counter pass done", flush=True)
 
@@ -300,6 +316,8 @@ def main():
     case = _make_case(inputs, spec)
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
+    # the full step keeps the int8 codes in 16 x 64 tiles unless asked not to
+    tiled = mode == "full" and args.layout == "tiled"
 
     def bf16(t):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -325,9 +343,9 @@ def main():
             bias=None if b0 is None else b0.clone(),
             run=torch.zeros(k, dtype=torch.float32, device=dev),
             smooth=torch.empty(k, dtype=torch.float32, device=dev),
-            wq=torch.empty((n, k), dtype=torch.int8, device=dev),
+            wq=B.tiled_empty(n, k, dev) if tiled else torch.empty((n, k), dtype=torch.int8, device=dev),
             ws=torch.empty(n, dtype=torch.float32, device=dev),
-            xq=torch.empty((m, k), dtype=torch.int8, device=dev),
+            xq=B.tiled_empty(m, k, dev) if tiled else torch.empty((m, k), dtype=torch.int8, device=dev),
             xs=torch.empty(m, dtype=torch.float32, device=dev),
             y=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
             tsx=torch.empty(1, dtype=torch.float32, device=dev),
@@ -338,7 +356,7 @@ def main():
     stream = torch.cuda.Stream(dev)
     torch.cuda.set_stream(stream)
     if args.counter_pass:
-        counter_pass(torch, B, sets[0], stream)
+        counter_pass(torch, B, sets[0], stream, tiled)
         return
     if mode in ("per_call", "weight_only"):
         # weights prepared once per copy, outside the timed region; the bf16
@@ -375,6 +393,14 @@ def main():
             continue
         if mode == "full":
             s["calls_calib"] = [B.prepared(B.sq_calibrate, cb, s["run"], stream) for cb in s["calib"]]
+        if tiled:
+            s["call_prep"] = B.prepared(B.sq_prepare_weight_tiled, s["w"], s["run"], alpha, s["smooth"], s["wq"],
+                                        s["ws"], stream)
+            s["call_act"] = B.prepared(B.sq_quantize_act_tiled, s["x"], s["smooth"], s["xq"], s["xs"], stream)
+            s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_tiled, s["xq"], s["xs"], m, s["wq"], s["ws"], n, k,
+                                        s["bias"], s["y"], stream)
+            continue
+        if mode == "full":
             s["call_prep"] = B.prepared(B.sq_prepare_weight, s["w"], s["run"], alpha, s["smooth"], s["wq"],
                                         s["ws"], stream)
         s["call_act"] = B.prepared(B.sq_quantize_act, s["x"], s["smooth"], s["xq"], s["xs"], stream)
@@ -480,6 +506,7 @@ def main():
         stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_ms["prepare_weight"])
         stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_ms["reset+calibrate"])
     kernel_name = ("int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)" if mode == "per_tensor"
+                   else "int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_tiled)" if tiled
                    else "int8 GEMM + fused dequant (sq_w8a8_gemm)")
     if mode == "weight_only":
         # the weight-only product on the decode shape: bound by reading the
@@ -495,7 +522,7 @@ def main():
                 "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        traffic = _gemm_traffic() if args.workload == "o_proj" else None
+        traffic = _gemm_traffic(args.layout) if args.workload == "o_proj" else None
         roof = {"bound": "mfma", "kernel": kernel_name,
                 "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
@@ -505,6 +532,7 @@ def main():
               "out_dtype": "bf16", "bias": case.bias is not None, "rotated_buffer_sets": rotate}
     if mode == "full":
         config["calib_tokens"] = calib_rows
+        config["int8_layout"] = "16x64 tiles" if tiled else "row-major"
     stages = {nm: round(v * 1e3, 2) for nm, v in stage_ms.items()}
     stages["note"] = "second pass of the same K steps with an event between stages"
     line = {

@@ -268,3 +268,56 @@ def test_quantize_weight_errors(L):
     assert f(OK_PTR, B.SQ_BF16, 4, 72, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
     assert f(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
     assert f(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN
+
+
+def test_tiled_bytes(L):
+    # rows padded to 16, k to a multiple of 64
+    assert L.sq_tiled_bytes(0, 64) == 0
+    assert L.sq_tiled_bytes(4, 0) == 0
+    assert L.sq_tiled_bytes(1, 16) == 16 * 64
+    assert L.sq_tiled_bytes(17, 80) == 32 * 128
+    assert L.sq_tiled_bytes(4096, 4096) == 4096 * 4096
+    assert L.sq_tiled_bytes(4096, 11008) == 4096 * 11008  # 11008 = 172 * 64
+    assert L.sq_tiled_bytes(333, 4000) == 336 * 4032
+
+
+def test_untile_matches_the_layout_formula():
+    import torch
+    rows, k = 19, 80
+    r16, k64 = 32, 128
+    flat = torch.arange(r16 * k64, dtype=torch.int64)
+    a = B.untile(flat, rows, k)
+    for i in (0, 1, 15, 16, 18):
+        for j in (0, 5, 63, 64, 79):
+            assert a[i, j] == ((i // 16) * (k64 // 64) + j // 64) * 1024 + (i % 16) * 64 + j % 64
+
+
+def test_tiled_entry_errors(L):
+    f = L.sq_quantize_act_tiled
+    assert f(OK_PTR, 5, 4, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert f(OK_PTR, B.SQ_BF16, -3, 64, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert f(OK_PTR, B.SQ_BF16, 4, 56, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert f(None, B.SQ_BF16, 0, 64, None, None, None, None) == B.SQ_OK
+
+    g = L.sq_prepare_weight_tiled
+    assert g(OK_PTR, B.SQ_I32, 8, 64, OK_PTR, 0.5, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert g(OK_PTR, B.SQ_BF16, 0, 64, OK_PTR, 0.5, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert g(OK_PTR, B.SQ_BF16, 8, 40, OK_PTR, 0.5, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert g(OK_PTR, B.SQ_BF16, 8, 64, OK_PTR, 1.5, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ARG
+    assert g(OK_PTR, B.SQ_BF16, 8, 64, OK_PTR, 0.5, OK_PTR, None, OK_PTR, None) == B.SQ_ERR_ARG
+    assert g(OK_PTR, B.SQ_BF16, 8, 64, BAD, 0.5, OK_PTR, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+
+    h = L.sq_w8a8_gemm_tiled
+
+    def call(xq=OK_PTR, sx=OK_PTR, m=4, wq=OK_PTR, sw=OK_PTR, n=8, k=64, bias=None, bt=B.SQ_F32, y=OK_PTR,
+             yt=B.SQ_BF16):
+        return h(xq, sx, m, wq, sw, n, k, bias, bt, y, yt, None)
+
+    assert call(yt=9) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=8) == B.SQ_ERR_ALIGN
+    assert call(wq=None) == B.SQ_ERR_ARG
+    assert call(y=BAD) == B.SQ_ERR_ALIGN
+    assert call(m=0, xq=None, y=None) == B.SQ_OK

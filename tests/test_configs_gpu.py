@@ -72,9 +72,9 @@ def _check_y(orc, y_dev, xq_ref, xs_ref, wq_ref, sw_ref, bias_f, rows):
         assert_bf16_within_one_ulp(got, orc.to_bf16(yref), yref, scale)
 
 
-def _run_and_check(orc, case, alphas, sample_rows, out_dtype, fused=False):
+def _run_and_check(orc, case, alphas, sample_rows, out_dtype, fused=False, tiled=False):
     m, n, k = case.m, case.n, case.k
-    print(f"config {case.name}: m={m} n={n} k={k} alphas={alphas} fused={fused}", flush=True)
+    print(f"config {case.name}: m={m} n={n} k={k} alphas={alphas} fused={fused} tiled={tiled}", flush=True)
     x_dev, w_dev = up(case.x), up(case.w)
     bias_dev = None if case.bias is None else up(case.bias)
     bias_f = None if case.bias is None else case.bias.f32
@@ -88,9 +88,17 @@ def _run_and_check(orc, case, alphas, sample_rows, out_dtype, fused=False):
 
     rows = _rows(m, sample_rows, seed=m + n + k)
     for alpha in alphas:
-        s, wq, sw = _prepare(w_dev, run, alpha, n, k)
+        if tiled:
+            s, wq, sw = _empty(k, torch.float32), B.tiled_empty(n, k, DEV), _empty(n, torch.float32)
+            B.sq_prepare_weight_tiled(w_dev, run, alpha, s, wq, sw)
+        else:
+            s, wq, sw = _prepare(w_dev, run, alpha, n, k)
         y = _empty((m, n), out_dtype)
-        if fused:
+        if tiled:
+            xq, xs = B.tiled_empty(m, k, DEV), _empty(m, torch.float32)
+            B.sq_quantize_act_tiled(x_dev, s, xq, xs)
+            B.sq_w8a8_gemm_tiled(xq, xs, m, wq, sw, n, k, bias_dev, y)
+        elif fused:
             ws = _empty(B.sq_w8a8_linear_workspace_bytes(m, k), torch.uint8)
             B.sq_w8a8_linear(x_dev, s, wq, sw, bias_dev, y, ws)
             xq, xs = B.workspace_views(ws, m, k)
@@ -99,6 +107,8 @@ def _run_and_check(orc, case, alphas, sample_rows, out_dtype, fused=False):
             B.sq_quantize_act(x_dev, s, xq, xs)
             B.sq_w8a8_gemm(xq, xs, wq, sw, bias_dev, y)
         torch.cuda.synchronize()
+        if tiled:
+            wq, xq = B.untile(wq, n, k), B.untile(xq, m, k)
 
         s_ref, wq_ref, sw_ref = orc.prepare_weight(case.w.f32, run_ref, alpha)
         assert_equal(down(s), s_ref, f"smooth (alpha {alpha})")
@@ -128,6 +138,17 @@ def test_decode_16x4096x11008(orc):
                          ids=[f"{nm}_{n}x{k}" for nm, n, k in inputs.BLOCK_LINEARS])
 def test_block_linear(orc, layer):
     _run_and_check(orc, inputs.block_linear(layer), (0.5,), 96, torch.bfloat16)
+
+
+@pytest.mark.parametrize("layer", range(len(inputs.BLOCK_LINEARS)),
+                         ids=[f"{nm}_{n}x{k}" for nm, n, k in inputs.BLOCK_LINEARS])
+def test_block_linear_tiled(orc, layer):
+    """The same layers with the int8 codes in 16 x 64 tiles."""
+    _run_and_check(orc, inputs.block_linear(layer), (0.5,), 96, torch.bfloat16, tiled=True)
+
+
+def test_prefill_2048x4096x4096_tiled(orc):
+    _run_and_check(orc, inputs.prefill(), (0.5,), None, torch.bfloat16, tiled=True)
 
 
 def test_mlp_up_8192x8192x28672_alpha_sweep(orc):

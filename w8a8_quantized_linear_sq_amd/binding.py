@@ -49,6 +49,10 @@ _SIGNATURES = {
     "sq_weight_col_max": ([_P, _E, _I64, _I64, _P, _P], _E),
     "sq_recompute_smooth_scale": ([_P, _E, _I64, _I64, _P, _P, _F, _P, _P, _P, _P], _E),
     "sq_smoothing_factor": ([_P, _P, _F, _I64, _P, _P], _E),
+    "sq_tiled_bytes": ([_I64, _I64], _SZ),
+    "sq_prepare_weight_tiled": ([_P, _E, _I64, _I64, _P, _F, _P, _P, _P, _P], _E),
+    "sq_quantize_act_tiled": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
+    "sq_w8a8_gemm_tiled": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_quantize_weight": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
     "sq_reference_linear": ([_P, _E, _I64, _I64, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_relative_error": ([_P, _P, _I64, _P, _SZ, _P, _P], _E),
@@ -260,6 +264,65 @@ def sq_recompute_smooth_scale(w: torch.Tensor, x_max_abs: torch.Tensor | None, w
             _need_dtype(t, torch.float32, nm)
     return _invoke("sq_recompute_smooth_scale", _ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), _ptr(w_max_abs),
                    float(alpha), _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w))
+
+
+def sq_tiled_bytes(rows: int, k: int) -> int:
+    """Bytes of a [rows][k] int8 matrix in 16 x 64 tiles."""
+    return int(lib().sq_tiled_bytes(rows, k))
+
+
+def tiled_empty(rows: int, k: int, device) -> torch.Tensor:
+    """A flat int8 device buffer for a [rows][k] matrix in 16 x 64 tiles."""
+    return torch.empty(max(sq_tiled_bytes(rows, k), 16), dtype=torch.int8, device=device)
+
+
+def _need_tiled(t: torch.Tensor, rows: int, k: int, what: str):
+    _need_dtype(t, torch.int8, what)
+    if t.numel() < sq_tiled_bytes(rows, k):
+        raise ValueError(f"{what} needs {sq_tiled_bytes(rows, k)} bytes for {rows} x {k} in tiles")
+
+
+def sq_prepare_weight_tiled(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: float, smooth: torch.Tensor,
+                            w_q: torch.Tensor, w_scale: torch.Tensor, stream=None) -> int:
+    """sq_prepare_weight with w_q (flat int8) in 16 x 64 tiles."""
+    n, k = w.shape
+    _need_dtype(smooth, torch.float32, "smooth")
+    _need_tiled(w_q, n, k, "w_q")
+    _need_dtype(w_scale, torch.float32, "w_scale")
+    if x_max_abs is not None:
+        _need_dtype(x_max_abs, torch.float32, "x_max_abs")
+    return _invoke("sq_prepare_weight_tiled", _ptr(w), _dtype_code(w), n, k, _ptr(x_max_abs), float(alpha),
+                   _ptr(smooth), _ptr(w_q), _ptr(w_scale), _stream(stream, w))
+
+
+def sq_quantize_act_tiled(x: torch.Tensor, smooth: torch.Tensor, x_q: torch.Tensor, x_scale: torch.Tensor,
+                          stream=None) -> int:
+    """sq_quantize_act with x_q (flat int8) in 16 x 64 tiles."""
+    m, k = x.shape
+    _need_tiled(x_q, m, k, "x_q")
+    _need_dtype(x_scale, torch.float32, "x_scale")
+    return _invoke("sq_quantize_act_tiled", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(x_q), _ptr(x_scale),
+                   _stream(stream, x))
+
+
+def sq_w8a8_gemm_tiled(x_q: torch.Tensor, x_scale: torch.Tensor | None, m: int, w_q: torch.Tensor,
+                       w_scale: torch.Tensor | None, n: int, k: int, bias: torch.Tensor | None, y: torch.Tensor,
+                       stream=None) -> int:
+    """sq_w8a8_gemm on operands in 16 x 64 tiles (flat int8 buffers; the
+    shape is given)."""
+    _need_tiled(x_q, m, k, "x_q")
+    _need_tiled(w_q, n, k, "w_q")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_w8a8_gemm_tiled", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k, _ptr(bias), bt,
+                   _ptr(y), _dtype_code(y), _stream(stream, y))
+
+
+def untile(t: torch.Tensor, rows: int, k: int) -> torch.Tensor:
+    """The [rows][k] matrix held by a 16 x 64 tiled buffer (host-side view
+    helper for tests and inspection; a copy)."""
+    r16, k64 = (rows + 15) // 16 * 16, (k + 63) // 64 * 64
+    a = t[: r16 * k64].reshape(r16 // 16, k64 // 64, 16, 64).permute(0, 2, 1, 3).reshape(r16, k64)
+    return a[:rows, :k].contiguous()
 
 
 def sq_smoothing_factor(x_max_abs: torch.Tensor | None, w_max_abs: torch.Tensor, alpha: float, smooth: torch.Tensor,

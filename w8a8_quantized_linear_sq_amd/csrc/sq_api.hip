@@ -203,6 +203,61 @@ sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64
     return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
 }
 
+size_t sq_tiled_bytes(int64_t rows, int64_t k) {
+    if (rows <= 0 || k <= 0) return 0;
+    return (size_t)((rows + 15) / 16 * 16) * (size_t)((k + 63) / 64 * 64);
+}
+
+sq_status sq_prepare_weight_tiled(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* x_max_abs,
+                                  float alpha, float* smooth, int8_t* w_q, float* w_scale, void* stream) {
+    if (!fp_in(wt)) return SQ_ERR_DTYPE;
+    if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (!w || !smooth || !w_q || !w_scale) return SQ_ERR_ARG;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    if (x_max_abs && !aligned16(x_max_abs)) return SQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    const int bf16 = wt == SQ_BF16;
+    hipError_t e;
+    if (!x_max_abs) {
+        e = sq_launch_fill(smooth, 1.0f, k, s);
+    } else {
+        // the row-group column maxima live in w_q (at least n * k bytes)
+        // until the codes overwrite them, or in smooth for a single group
+        const int64_t groups = sq_colmax_partial_groups(n, k, bf16, n * k);
+        unsigned* partial = groups == 1 ? (unsigned*)smooth : (unsigned*)w_q;
+        e = sq_launch_colmax_partial(w, bf16, n, k, groups, partial, s);
+        if (e == hipSuccess)
+            e = sq_launch_smooth_factor(x_max_abs, partial, groups, (double)alpha, 1.0 - (double)alpha, k, smooth, s);
+    }
+    if (e == hipSuccess) e = sq_launch_quantize_weight_tiled(w, bf16, smooth, n, k, w_q, w_scale, s);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
+}
+
+sq_status sq_quantize_act_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                                int8_t* x_q, float* x_scale, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (m == 0) return SQ_OK;
+    if (!x || !smooth || !x_q || !x_scale) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(smooth) || !aligned16(x_q)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_quantize_act_tiled(x, xt == SQ_BF16, smooth, m, k, x_q, x_scale, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_tiled(const int8_t* x_q, const float* x_scale, int64_t m, const int8_t* w_q,
+                             const float* w_scale, int64_t n, int64_t k, const void* bias, sq_dtype bias_t, void* y,
+                             sq_dtype yt, void* stream) {
+    sq_status st = check_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    return launched(sq_launch_gemm_tiled(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
+                                         out_kind(yt), 0, as_stream(stream)));
+}
+
 sq_status sq_smoothing_factor(const float* x_max_abs, const float* w_max_abs, float alpha, int64_t k,
                               float* smooth, void* stream) {
     sq_status st = check_k(k);

@@ -64,6 +64,17 @@ hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsign
 hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                           const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                           void* y, int out_kind, int scalar_scales, hipStream_t st);
+// 16 x 64 tiled int8 (rows in groups of 16, K in 64-byte chunks, tile (g, c)
+// at (g * K64 / 64 + c) * 1 KiB, each tile row-major, K64 = k rounded up to
+// 64, padding columns zero): the quantisers writing codes in that layout,
+// and the product reading both operands in it
+hipError_t sq_launch_quantize_act_tiled(const void* x, int bf16, const float* s, int64_t m, int64_t k, int8_t* xq,
+                                        float* x_scale, hipStream_t st);
+hipError_t sq_launch_quantize_weight_tiled(const void* w, int bf16, const float* s, int64_t n, int64_t k, int8_t* wq,
+                                           float* w_scale, hipStream_t st);
+hipError_t sq_launch_gemm_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq, const float* sw,
+                                int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
+                                int scalar_scales, hipStream_t st);
 // the reference linear of quantization_error: x [m][k] times w [n][k]
 // (both bf16, or both fp32), fp32 sums, plus bias; out_kind 0 fp32, 1 bf16
 hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int64_t m, int64_t n, int64_t k,

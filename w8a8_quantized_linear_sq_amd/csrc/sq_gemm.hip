@@ -114,7 +114,11 @@ constexpr int kI8 = 0, kBf16 = 1, kF32 = 2;
 
 // ET: operand element type (kI8: the int8 product with the dequantisation;
 // kBf16 / kF32: the reference linear). k is the row length in bytes.
-template <int ET, int BM, int BN, int WGM, int WGN, int OUT>
+// TILED: both operands in 16 x 64 tiles (rows in groups of 16, K in 64-byte
+// chunks, tile (g, c) at (g * k / 64 + c) * 1 KiB, each tile row-major; k is
+// then the padded row length, a multiple of 64, and the padding is zero):
+// every DMA load reads one whole tile, 1 KiB contiguous.
+template <int ET, int BM, int BN, int WGM, int WGN, int OUT, bool TILED>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
@@ -158,14 +162,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
         const int row = blk * kBlockRows + lane / kRowLanes;  // row in the A|B stage space
         const int pos = lane % kRowLanes;
         const int chunk = pos ^ swz(row);
-        const int8_t* g;
-        if (row < BM) g = A + (int64_t)min(m0 + row, m - 1) * k;
-        else g = B + (int64_t)min(n0 + row - BM, n - 1) * k;
-        src[q] = g + chunk * 16;
+        if constexpr (TILED) {
+            // the block's 16 rows are one row group; groups past the last
+            // (tiles past m or n) read the last one, never stored
+            const int8_t* g;
+            if (row < BM) g = A + (int64_t)min((m0 >> 4) + blk, (m - 1) >> 4) * k * 16;
+            else g = B + (int64_t)min((n0 >> 4) + blk - BM / kBlockRows, (n - 1) >> 4) * k * 16;
+            src[q] = g + (lane / kRowLanes) * kBK + chunk * 16;
+        } else {
+            const int8_t* g;
+            if (row < BM) g = A + (int64_t)min(m0 + row, m - 1) * k;
+            else g = B + (int64_t)min(n0 + row - BM, n - 1) * k;
+            src[q] = g + chunk * 16;
+        }
         dst[q] = blk * 1024;
     }
     auto issue_stage = [&](int kt, int buf) {
-        const int kb = kt * kBK;
+        const int64_t kb = TILED ? (int64_t)kt * 1024 : (int64_t)kt * kBK;
 #pragma unroll
         for (int q = 0; q < LOADS; ++q)
             __builtin_amdgcn_global_load_lds((const void*)(src[q] + kb), (lds_ptr_t)(smem + buf * STAGE + dst[q]),
@@ -344,7 +357,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
             mfmas(ga, gb);
         }
     }
-    if (k % kBK) {
+    if (!TILED && k % kBK) {
         // a last partial step through registers: its buffer was last read
         // kStages steps ago
         __syncthreads();
@@ -470,21 +483,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     }
 }
 
-template <int ET, int BM, int BN, int WGM, int WGN>
+template <int ET, bool TILED, int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
                        int n, int kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
                        hipStream_t st) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
     dim3 grid(gm * gn), block(64 * WGM * WGN);
     if (out_kind == 0)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
-                           bias, bias_kind, y, gm, gn, scalar_scales);
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
+                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
     else if (out_kind == 1)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
-                           bias, bias_kind, y, gm, gn, scalar_scales);
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
+                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
     else if constexpr (ET == kI8)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 2>), grid, block, 0, st, xq, wq, m, n, kbytes, sx, sw,
-                           bias, bias_kind, y, gm, gn, scalar_scales);
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 2, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
+                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
     return hipGetLastError();
 }
 
@@ -493,7 +506,7 @@ hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* w
 // area over the configuration's measured speed per unit area on MI355X
 // (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs of
 // the int8 product).
-template <int ET>
+template <int ET, bool TILED = false>
 hipError_t launch_tiled(const int8_t* a, const float* sx, int64_t m, const int8_t* b, const float* sw, int64_t n,
                         int64_t kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
                         hipStream_t st) {
@@ -512,9 +525,9 @@ hipError_t launch_tiled(const int8_t* a, const float* sx, int64_t m, const int8_
     }
     const int mi = (int)m, ni = (int)n, ki = (int)kbytes;
     switch (best) {
-        case 0: return launch_tile<ET, 256, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        case 1: return launch_tile<ET, 128, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        default: return launch_tile<ET, 128, 128, 2, 2>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 0: return launch_tile<ET, TILED, 256, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 1: return launch_tile<ET, TILED, 128, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        default: return launch_tile<ET, TILED, 128, 128, 2, 2>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
     }
 }
 
@@ -529,6 +542,15 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
     if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales,
                                                           st);
     return launch_tiled<kI8>(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales, st);
+}
+
+// both operands in 16 x 64 tiles (k the unpadded row length)
+hipError_t sq_launch_gemm_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq, const float* sw,
+                                int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
+                                int scalar_scales, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    const int64_t k64 = (k + 63) / 64 * 64;
+    return launch_tiled<kI8, true>(xq, sx, m, wq, sw, n, k64, bias, bias_kind, y, out_kind, scalar_scales, st);
 }
 
 hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int64_t m, int64_t n, int64_t k,

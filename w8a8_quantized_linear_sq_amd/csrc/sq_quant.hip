@@ -341,7 +341,11 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint3
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // [a, b, c, d]
 }
 
-template <bool BF16, bool DIV, int T, int C>
+// TILED: the codes go to 16 x 64 tiles (rows in groups of 16, K in 64-byte
+// chunks, tile (g, c) at (g * K64 / 64 + c) * 1 KiB, each tile row-major;
+// K64 = k rounded up to 64), the padding columns of every row written as
+// zero codes.
+template <bool BF16, bool DIV, int T, int C, bool TILED>
 __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict__ x, const float* __restrict__ s,
                                                           int64_t m, int64_t k, int8_t* __restrict__ q,
                                                           float* __restrict__ scale_out) {
@@ -462,15 +466,21 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
             uint32_t b[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(div_rn(xs[c][i], scale, rs) + kMagic);
-            if (j8 < k8)
-                *(u32x2*)(q + row * k + j8 * 8) =
-                    u32x2{pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7])};
+            const u32x2 codes = u32x2{pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7])};
+            if constexpr (TILED) {
+                const int64_t k64 = (k + 63) & ~(int64_t)63;
+                if (j8 < (k64 >> 3))
+                    *(u32x2*)(q + ((row >> 4) * (k64 >> 6) + (j8 >> 3)) * 1024 + (row & 15) * 64 + (j8 & 7) * 8) =
+                        j8 < k8 ? codes : u32x2{0u, 0u};
+            } else {
+                if (j8 < k8) *(u32x2*)(q + row * k + j8 * 8) = codes;
+            }
         }
         if (tid == 0) scale_out[row] = scale;
     }
 }
 
-template <bool BF16, bool DIV>
+template <bool BF16, bool DIV, bool TILED = false>
 static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t k, int8_t* q, float* scale,
                               hipStream_t st) {
     // threads per row T and 8-channel chunks per thread C, with T * C * 8 >= k
@@ -495,7 +505,7 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
     dim3 grid((unsigned)blocks), block(T);
 #define SQ_ROWS_CASE(TT, CC)                                                                                  \
     if (T == TT && C == CC) {                                                                                 \
-        hipLaunchKernelGGL((quantize_rows_kernel<BF16, DIV, TT, CC>), grid, block, 0, st, x, s, m, k, q, scale); \
+        hipLaunchKernelGGL((quantize_rows_kernel<BF16, DIV, TT, CC, TILED>), grid, block, 0, st, x, s, m, k, q, scale); \
         return hipGetLastError();                                                                             \
     }
     SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(704, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
@@ -515,6 +525,21 @@ hipError_t sq_launch_quantize_weight(const void* w, int bf16, const float* s, in
     if (n <= 0) return hipSuccess;
     return bf16 ? launch_rows<true, false>(w, s, n, k, wq, w_scale, st)
                 : launch_rows<false, false>(w, s, n, k, wq, w_scale, st);
+}
+
+// the same codes in 16 x 64 tiles (the buffers hold the padded size)
+hipError_t sq_launch_quantize_act_tiled(const void* x, int bf16, const float* s, int64_t m, int64_t k, int8_t* xq,
+                                        float* x_scale, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    return bf16 ? launch_rows<true, true, true>(x, s, m, k, xq, x_scale, st)
+                : launch_rows<false, true, true>(x, s, m, k, xq, x_scale, st);
+}
+
+hipError_t sq_launch_quantize_weight_tiled(const void* w, int bf16, const float* s, int64_t n, int64_t k, int8_t* wq,
+                                           float* w_scale, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    return bf16 ? launch_rows<true, false, true>(w, s, n, k, wq, w_scale, st)
+                : launch_rows<false, false, true>(w, s, n, k, wq, w_scale, st);
 }
 
 // ---------------------------------------------------------------------------
