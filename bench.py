@@ -14,11 +14,12 @@ sq_prepare_weight, sq_quantize_act and sq_w8a8_gemm instead).
 Other workloads (--workload) are the remaining shapes of the method's
 workloads: prefill, the block's qkv / up / down linears and the MLP
 up-projection run the same full step; decode times the per-call path
-(sq_quantize_act + sq_w8a8_gemm) on weights prepared once, as a decode
-step uses them; o_proj_per_tensor times the per-tensor variant as its
-layer runs it (sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor);
-decode_weight_only times the weight-only int8 linear (sq_wo_linear) on the
-decode shape.
+(sq_quantize_act_tiled + sq_w8a8_gemm_tiled, which streams the weights for
+m <= 64) on weights prepared once, as a decode step uses them;
+o_proj_per_tensor times the per-tensor variant as its layer runs it
+(sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor; row-major);
+decode_weight_only times the weight-only int8 linear (sq_wo_linear_tiled)
+on the decode shape. --layout row gives the row-major calls throughout.
 
 Inputs are resident in HBM before the timed region; enough copies of every
 buffer a step reads are rotated (at least 512 MiB per cycle, 2 to 12
@@ -316,8 +317,9 @@ def main():
     case = _make_case(inputs, spec)
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
-    # the full step keeps the int8 codes in 16 x 64 tiles unless asked not to
-    tiled = mode == "full" and args.layout == "tiled"
+    # the int8 codes in 16 x 64 tiles unless asked not to (the per-tensor
+    # variant has row-major calls only)
+    tiled = mode != "per_tensor" and args.layout == "tiled"
 
     def bf16(t):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -361,13 +363,14 @@ def main():
     if mode in ("per_call", "weight_only"):
         # weights prepared once per copy, outside the timed region; the bf16
         # weights are then released (weight-only: never calibrated, s = 1)
+        prep = B.sq_prepare_weight_tiled if tiled else B.sq_prepare_weight
         for s in sets:
             if mode == "weight_only":
-                B.sq_prepare_weight(s["w"], None, alpha, s["smooth"], s["wq"], s["ws"], stream)
+                prep(s["w"], None, alpha, s["smooth"], s["wq"], s["ws"], stream)
                 continue
             for cb in s["calib"]:
                 B.sq_calibrate(cb, s["run"], stream)
-            B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
+            prep(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
         torch.cuda.synchronize()
         for s in sets:
             s["w"] = None
@@ -389,13 +392,18 @@ def main():
             continue
         if mode == "weight_only":
             s["call_act"] = None
-            s["call_gemm"] = B.prepared(B.sq_wo_linear, s["x"], s["wq"], s["ws"], s["bias"], s["y"], stream)
+            if tiled:
+                s["call_gemm"] = B.prepared(B.sq_wo_linear_tiled, s["x"], s["wq"], s["ws"], n, s["bias"], s["y"],
+                                            stream)
+            else:
+                s["call_gemm"] = B.prepared(B.sq_wo_linear, s["x"], s["wq"], s["ws"], s["bias"], s["y"], stream)
             continue
         if mode == "full":
             s["calls_calib"] = [B.prepared(B.sq_calibrate, cb, s["run"], stream) for cb in s["calib"]]
         if tiled:
-            s["call_prep"] = B.prepared(B.sq_prepare_weight_tiled, s["w"], s["run"], alpha, s["smooth"], s["wq"],
-                                        s["ws"], stream)
+            if mode == "full":
+                s["call_prep"] = B.prepared(B.sq_prepare_weight_tiled, s["w"], s["run"], alpha, s["smooth"],
+                                            s["wq"], s["ws"], stream)
             s["call_act"] = B.prepared(B.sq_quantize_act_tiled, s["x"], s["smooth"], s["xq"], s["xs"], stream)
             s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_tiled, s["xq"], s["xs"], m, s["wq"], s["ws"], n, k,
                                         s["bias"], s["y"], stream)
@@ -512,13 +520,17 @@ def main():
         # the weight-only product on the decode shape: bound by reading the
         # int8 weights once
         gbs = wo_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "weight-only int8 linear, bf16 MFMA (sq_wo_linear)",
+        roof = {"bound": "hbm", "kernel": ("weight-only int8 linear on 16 x 64 weight tiles, bf16 MFMA "
+                                           "(sq_wo_linear_tiled)" if tiled else
+                                           "weight-only int8 linear, bf16 MFMA (sq_wo_linear)"),
                 "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     elif m <= 64:
         # the weight-streaming product: bound by reading the int8 weights
         gbs = (n * k + m * k + 2 * m * n + 4 * (m + n)) / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "weight-streaming int8 product + fused dequant (sq_w8a8_gemm, m <= 64)",
+        roof = {"bound": "hbm", "kernel": ("weight-streaming int8 product + fused dequant on 16 x 64 tiles "
+                                           "(sq_w8a8_gemm_tiled, m <= 64)" if tiled else
+                                           "weight-streaming int8 product + fused dequant (sq_w8a8_gemm, m <= 64)"),
                 "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
@@ -532,7 +544,7 @@ def main():
               "out_dtype": "bf16", "bias": case.bias is not None, "rotated_buffer_sets": rotate}
     if mode == "full":
         config["calib_tokens"] = calib_rows
-        config["int8_layout"] = "16x64 tiles" if tiled else "row-major"
+    config["int8_layout"] = "16x64 tiles" if tiled else "row-major"
     stages = {nm: round(v * 1e3, 2) for nm, v in stage_ms.items()}
     stages["note"] = "second pass of the same K steps with an event between stages"
     line = {

@@ -215,6 +215,17 @@ sq_status sq_wo_linear(const void* x, sq_dtype xt, int64_t m, int64_t k,
                        void* stream);
 
 /*
+ * sq_wo_linear_tiled -- sq_wo_linear with w_q in the 16 x 64 tiled layout
+ * (from sq_prepare_weight_tiled; sq_tiled_bytes(n, k) bytes, 16-byte
+ * aligned). Each weight load then reads one 1 KiB tile contiguously. The
+ * other arguments, the arithmetic and the output as sq_wo_linear.
+ */
+sq_status sq_wo_linear_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                             const int8_t* w_q, const float* w_scale, int64_t n,
+                             const void* bias, sq_dtype bias_t, void* y, sq_dtype yt,
+                             void* stream);
+
+/*
  * sq_selfcheck_reciprocal -- device self-check behind the activation path.
  * For bf16 activations, sq_quantize_act / sq_w8a8_linear form x / s as
  * fma(fma(-q0, s, x), y, q0) with q0 = x * y and y the correctly rounded

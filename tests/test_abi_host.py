@@ -321,3 +321,12 @@ def test_tiled_entry_errors(L):
     assert call(wq=None) == B.SQ_ERR_ARG
     assert call(y=BAD) == B.SQ_ERR_ALIGN
     assert call(m=0, xq=None, y=None) == B.SQ_OK
+
+    w = L.sq_wo_linear_tiled
+    assert w(OK_PTR, B.SQ_F32, 4, 64, OK_PTR, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_DTYPE
+    assert w(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_I32, None) == B.SQ_ERR_DTYPE
+    assert w(OK_PTR, B.SQ_BF16, 4, 64, OK_PTR, OK_PTR, 0, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+    assert w(OK_PTR, B.SQ_BF16, 4, 40, OK_PTR, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ALIGN
+    assert w(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ARG
+    assert w(OK_PTR, B.SQ_BF16, 4, 64, BAD, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ALIGN
+    assert w(None, B.SQ_BF16, 0, 64, None, None, 8, None, B.SQ_F32, None, B.SQ_BF16, None) == B.SQ_OK

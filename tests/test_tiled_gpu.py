@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 # several 256-row tiles, the largest K
 SMALL = [(1, 1, 16), (3, 5, 32), (7, 17, 48), (17, 33, 272), (33, 7, 16), (130, 260, 528),
          (257, 300, 1040), (64, 512, 4096), (5, 40, 11008), (300, 129, 2064), (70, 33, 16384)]
-GEMM_SHAPES = SMALL + [(256, 256, 64), (384, 640, 1024), (1000, 1000, 336), (513, 769, 4160)]
+GEMM_SHAPES = SMALL + [(256, 256, 64), (384, 640, 1024), (1000, 1000, 336), (513, 769, 4160), (48, 777, 208),
+                       (16, 11008, 4096)]
 
 
 def _id(s):
@@ -132,11 +133,13 @@ def test_gemm_tiled_int32(orc, shape):
 
 @pytest.mark.parametrize("bias", [None, "f32", "bf16"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(3, 5, 32), (130, 260, 528), (257, 300, 1040), (1000, 1000, 336)], ids=_id)
+@pytest.mark.parametrize("shape", [(3, 5, 32), (16, 4099, 80), (64, 300, 1040), (130, 260, 528), (257, 300, 1040),
+                                   (1000, 1000, 336)], ids=_id)
 def test_gemm_tiled_dequant(orc, shape, out, bias):
     """Against the oracle, and bit for bit against the row-major product on
-    the same codes (the same kernel arithmetic) where that runs the tiled
-    kernel too (more than 64 rows)."""
+    the same codes: both compute the exact int32 sums and the same epilogue
+    expression (f32(acc) * sx * sw, then + bias), whether the product runs
+    on MFMA tiles (more than 64 rows) or streams the weights (64 or fewer)."""
     m, n, k = shape
     rng = np.random.default_rng(m + n + k + 1)
     a, b = _codes(rng, m, k), _codes(rng, n, k)
@@ -165,13 +168,13 @@ def test_gemm_tiled_dequant(orc, shape, out, bias):
         assert_f32_rel(down(y), yref, scale)
     else:
         assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
-    if m > 64:  # the row-major call takes another kernel up to 64 rows
-        assert_equal(down(y), down(y_rm), "tiled vs row-major")
+    assert_equal(down(y), down(y_rm), "tiled vs row-major")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(3, 5, 32), (17, 33, 272), (130, 260, 528), (257, 300, 1040),
-                                   (70, 33, 16384)], ids=_id)
+                                   (70, 33, 16384), (16, 11008, 4096), (64, 1000, 4160), (1, 4096, 11008)],
+                         ids=_id)
 def test_linear_tiled(orc, shape, dtype):
     """The three tiled calls in a row, as a layer runs them."""
     m, n, k = shape
@@ -203,3 +206,77 @@ def test_linear_tiled(orc, shape, dtype):
         assert_f32_rel(down(y), yref, scale)
     else:
         assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
+
+
+# ---------------------------------------------------------------------------
+# Weight-only int8 linear on tiled weights (torchao page
+# "quantization/subclass.py", Int8WeightOnlyQuantizedLinearWeight). The bar
+# is the row-major call's, derived from the arithmetic (exact products, an
+# fp32 sum of K terms in any order within K 2^-24 sum |x w|, one rounding
+# each for the scale and the bias, half a bf16 ulp for bf16 output), and the
+# result equals the row-major call's bit for bit (same sums in the same
+# order; the padding columns add zeros).
+# ---------------------------------------------------------------------------
+WO_SHAPES = [(1, 1, 16), (3, 17, 48), (16, 100, 272), (16, 200, 4096), (33, 64, 528), (64, 129, 1040),
+             (80, 70, 256), (130, 40, 4112), (16, 11008, 4096), (5, 4099, 80)]
+
+
+def _assert_wo_close(got, yref, mag, k, out):
+    if out == "f32":
+        g = got.astype(np.float64)
+        half_ulp = 0.0
+    else:
+        g = (got.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        e = np.floor(np.log2(np.maximum(np.abs(yref), 2.0 ** -126)))
+        half_ulp = 2.0 ** (e - 8)
+    bound = k * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(yref) + half_ulp + 1e-30
+    bad = np.abs(g - yref) > bound
+    assert not bad.any(), int(bad.sum())
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WO_SHAPES, ids=_id)
+def test_wo_linear_tiled(orc, shape, out, bias):
+    m, n, k = shape
+    print(f"tiled weight-only {m}x{n}x{k} out={out} bias={bias}", flush=True)
+    rng = np.random.default_rng(m * 3 + n * 5 + k + 1)
+    c = inputs.small(m, n, k, seed=23 + m + n + k, dtype="bf16", bias=bias is not None)
+    wq = _codes(rng, n, k)
+    sw = (rng.random(n, dtype=np.float32) * np.float32(0.002) + np.float32(1e-4)).astype(np.float32)
+    bias_f = bias_t = None
+    if bias == "f32":
+        bias_f, bias_t = c.bias.f32, up(c.bias.f32)
+    elif bias == "bf16":
+        bias_f, bias_t = c.bias.f32, up(c.bias)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    y = torch.zeros((m, n), dtype=odt, device=DEV)
+    x_dev = up(c.x)
+    B.sq_wo_linear_tiled(x_dev, up(_tile_host(wq, rng)), up(sw), n, bias_t, y)
+    y_rm = torch.zeros((m, n), dtype=odt, device=DEV)
+    B.sq_wo_linear(x_dev, up(wq), up(sw), bias_t, y_rm)
+    torch.cuda.synchronize()
+    yref = orc.wo_linear(c.x.f32, wq, sw, bias_f)
+    mag = (np.abs(c.x.f32.astype(np.float64)) @ np.abs(wq.astype(np.float64)).T) * sw[None, :].astype(np.float64)
+    _assert_wo_close(down(y), yref, mag, k, out)
+    assert_equal(down(y), down(y_rm), "tiled vs row-major")
+
+
+def test_wo_linear_tiled_from_prepared_weights(orc):
+    """The layer's route: weights prepared uncalibrated into tiles (s = 1),
+    then the tiled weight-only product on the decode shape."""
+    m, n, k = 16, 11008, 4096
+    c = inputs.small(m, n, k, seed=5, dtype="bf16", bias=False)
+    s = torch.empty(k, dtype=torch.float32, device=DEV)
+    wq = B.tiled_empty(n, k, DEV)
+    sw = torch.empty(n, dtype=torch.float32, device=DEV)
+    assert B.sq_prepare_weight_tiled(up(c.w), None, 0.5, s, wq, sw) == B.SQ_WARN_UNCALIBRATED
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    B.sq_wo_linear_tiled(up(c.x), wq, sw, n, None, y)
+    torch.cuda.synchronize()
+    wq_ref, sw_ref = orc.quantize_rows(c.w.f32.copy())
+    assert_equal(down(sw), sw_ref, "w_scale")
+    assert_equal(down(B.untile(wq, n, k)), wq_ref, "w_q")
+    yref = orc.wo_linear(c.x.f32, wq_ref, sw_ref, None)
+    mag = (np.abs(c.x.f32.astype(np.float64)) @ np.abs(wq_ref.astype(np.float64)).T) * sw_ref[None, :]
+    _assert_wo_close(down(y), yref, mag, k, "bf16")

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
     "sq_w8a8_gemm_per_tensor": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_wo_linear": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_wo_linear_tiled": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_weight_col_max": ([_P, _E, _I64, _I64, _P, _P], _E),
     "sq_recompute_smooth_scale": ([_P, _E, _I64, _I64, _P, _P, _F, _P, _P, _P, _P], _E),
     "sq_smoothing_factor": ([_P, _P, _F, _I64, _P, _P], _E),
@@ -241,6 +242,16 @@ def sq_wo_linear(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, bias
     bt = _dtype_code(bias) if bias is not None else SQ_F32
     return _invoke("sq_wo_linear", _ptr(x), _dtype_code(x), m, k, _ptr(w_q), _ptr(w_scale), n, _ptr(bias), bt,
                    _ptr(y), _dtype_code(y), _stream(stream, x))
+
+
+def sq_wo_linear_tiled(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, n: int,
+                       bias: torch.Tensor | None, y: torch.Tensor, stream=None) -> int:
+    """sq_wo_linear with w_q (flat int8) in 16 x 64 tiles."""
+    m, k = x.shape
+    _need_tiled(w_q, n, k, "w_q")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_wo_linear_tiled", _ptr(x), _dtype_code(x), m, k, _ptr(w_q), _ptr(w_scale), n, _ptr(bias),
+                   bt, _ptr(y), _dtype_code(y), _stream(stream, x))
 
 
 def sq_weight_col_max(w: torch.Tensor, w_max_abs: torch.Tensor, stream=None) -> int:

@@ -161,6 +161,22 @@ sq_status sq_wo_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const i
                                         yt == SQ_F32 ? 0 : 1, as_stream(stream)));
 }
 
+sq_status sq_wo_linear_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k, const int8_t* w_q,
+                             const float* w_scale, int64_t n, const void* bias, sq_dtype bias_t, void* y, sq_dtype yt,
+                             void* stream) {
+    if (xt != SQ_BF16) return SQ_ERR_DTYPE;
+    if (!(yt == SQ_F32 || yt == SQ_BF16)) return SQ_ERR_DTYPE;
+    if (bias && !fp_in(bias_t)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (m == 0) return SQ_OK;
+    if (!x || !w_q || !w_scale || !y) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(w_q) || ((uintptr_t)y & 3u) != 0) return SQ_ERR_ALIGN;
+    return launched(sq_launch_wo_linear_tiled(x, m, k, w_q, w_scale, n, bias, bias_kind(bias, bias_t), y,
+                                              yt == SQ_F32 ? 0 : 1, as_stream(stream)));
+}
+
 sq_status sq_weight_col_max(const void* w, sq_dtype wt, int64_t n, int64_t k, float* w_max_abs, void* stream) {
     if (!fp_in(wt)) return SQ_ERR_DTYPE;
     if (n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;

@@ -95,3 +95,12 @@ hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, c
 // scales sw [n]; out_kind 0 fp32, 1 bf16; bias_kind as above
 hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw, int64_t n,
                                const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st);
+// the same with w_q in 16 x 64 tiles
+hipError_t sq_launch_wo_linear_tiled(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw,
+                                     int64_t n, const void* bias, int bias_kind, void* y, int out_kind,
+                                     hipStream_t st);
+// the W8A8 product for m <= kSkinnyMaxM on operands in 16 x 64 tiles (the
+// weight stream of the weight-only kernel, int8 activation codes)
+hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
+                                       const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
+                                       void* y, int out_kind, int scalar_scales, hipStream_t st);

@@ -1,5 +1,6 @@
 // sq_wo.hip -- weight-only int8 linear: bf16 activations times int8 weights
-// with one scale per output channel, for few tokens (the decode shape).
+// with one scale per output channel, for few tokens (the decode shape); and
+// the same weight stream for the W8A8 product on tiled int8 codes.
 //
 // Follows the torchao page "quantization/subclass.py",
 // Int8WeightOnlyQuantizedLinearWeight._quantized_op: the int8 weights are
@@ -38,8 +39,23 @@
 //     times a finite int8 adds nothing);
 //   * the 8 partial sums of a 16 x 16 output fragment meet in LDS and are
 //     added in wavefront order by one wavefront, which applies the scale and
-//     the bias.
+//     the bias;
+//   * TILED: the weights in 16 x 64 tiles (16-row groups, K in 64-byte
+//     chunks, tile (g, c) at (g * K64 / 64 + c) * 1 KiB, row-major inside,
+//     zero padding columns). A chunk's 16 rows x 64 bytes are then one
+//     tile, so each weight load instruction reads 1 KiB contiguously
+//     instead of 16 separate 64-byte pieces. A workgroup owns whole groups
+//     (the groups spread evenly over the workgroups, G or G - 1 each);
+//   * I8: the W8A8 product for few tokens (page "w8a8_smoothquant.py",
+//     SmoothQuantW8A8.forward, integer route) on int8 activation codes and
+//     weights both in tiles: per chunk a lane loads 16 code bytes of each
+//     token group (one 1 KiB tile per instruction, like the weights) and
+//     one v_mfma_i32_16x16x64_i8 takes the chunk (lane l: row l % 16, bytes
+//     16 (l / 16) .. +16, the tile's own order). The int32 sums are exact;
+//     the epilogue is the GEMM's, f32(acc) * sx[t] * sw[o] (+ bias[o]), or
+//     the raw int32 sums (OUT = 2).
 #include <atomic>
+#include <type_traits>
 
 #include "sq_device.h"
 
@@ -69,32 +85,56 @@ __device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi) {
 // v_mfma_f32_16x16x32_bf16 operands: lane l holds 8 k-consecutive bf16 of
 // row (l % 16) at k offset 8 * (l / 16); result lane l, register r -> row
 // 4 * (l / 16) + r (token), column l % 16 (weight row).
-template <int TM, int G, int CB, int NB, int OUT>
-__global__ __launch_bounds__(64 * kWaves) void wo_kernel(const uint16_t* X, const int8_t* Bw, int m, int n, int k,
-                                                         int rows, const float* __restrict__ sb,
-                                                         const void* __restrict__ bias, int bias_kind,
-                                                         void* __restrict__ Y) {
-    __shared__ f32x4 red[kWaves][TM * G][64];
+template <int TM, int G, int CB, int NB, int OUT, bool TILED, bool I8>
+__global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const int8_t* Bw, int m, int n, int k,
+                                                         int rows, const float* __restrict__ sa,
+                                                         const float* __restrict__ sb, const void* __restrict__ bias,
+                                                         int bias_kind, void* __restrict__ Y, int scalar_scales) {
+    static_assert(TILED || !I8, "int8 activations come in tiles");
+    static_assert(I8 || OUT != 2, "raw int32 sums only for the int8 product");
+    typedef typename std::conditional<I8, i32x4, f32x4>::type acc_t;
+    constexpr int XV = I8 ? 1 : 2;  // 16-byte activation loads per token group and chunk
+    __shared__ acc_t red[kWaves][TM * G][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
-    const int row0 = blockIdx.x * rows;
-    const int rend = min(row0 + rows, n);
-
-    // row pointers: a row past the workgroup's rows reads the last row, a
-    // token past m the last token (addresses another lane of the
-    // instruction reads); their sums land in outputs that are not stored
+    const int nchunks = (k + kChunk - 1) / kChunk;
+    int row0;
     const int8_t* wrow[G];
+    if constexpr (TILED) {
+        // groups [g0, g1) of the ceil(n / 16); a group past g1 reads group
+        // g1 - 1 (another lane's addresses), never stored
+        const int ng = (n + 15) / 16;
+        const int g0 = (int)((int64_t)blockIdx.x * ng / gridDim.x);
+        const int g1 = (int)((int64_t)(blockIdx.x + 1) * ng / gridDim.x);
+        row0 = g0 * 16;
+        rows = (g1 - g0) * 16;
 #pragma unroll
-    for (int g = 0; g < G; ++g) wrow[g] = Bw + (int64_t)min(row0 + g * 16 + r16, rend - 1) * k;
-    const uint16_t* xrow[TM];
+        for (int g = 0; g < G; ++g)
+            wrow[g] = Bw + (int64_t)min(g0 + g, g1 - 1) * nchunks * 1024 + r16 * 64 + grp * 16;
+    } else {
+        // row pointers: a row past the workgroup's rows reads the last row,
+        // a token past m the last token (addresses another lane of the
+        // instruction reads); their sums land in outputs that are not stored
+        row0 = blockIdx.x * rows;
+        const int rend = min(row0 + rows, n);
 #pragma unroll
-    for (int t = 0; t < TM; ++t) xrow[t] = X + (int64_t)min(t * 16 + r16, m - 1) * k;
+        for (int g = 0; g < G; ++g) wrow[g] = Bw + (int64_t)min(row0 + g * 16 + r16, rend - 1) * k;
+    }
+    // activation rows: bf16, a token past m reads the last token; int8
+    // tiles, the lane's position in token group t's first tile (tokens past
+    // m are the group's padding rows, never stored)
+    const int8_t* xrow[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        if constexpr (I8) xrow[t] = (const int8_t*)X + (int64_t)t * nchunks * 1024 + r16 * 64 + grp * 16;
+        else xrow[t] = (const int8_t*)((const uint16_t*)X + (int64_t)min(t * 16 + r16, m - 1) * k);
+    }
 
     // chunks of this wavefront: wave, wave + 8, ...; every wavefront runs
     // the same number of batches; pieces past K read the last 16 elements
-    // of the row and their activations are zeroed where they are used
-    const int nchunks = (k + kChunk - 1) / kChunk;
+    // of the row (tiled weights: the last chunk's tile) and their
+    // activations are zeroed where they are used
     const int per_wave = (nchunks + kWaves - 1) / kWaves;
     // batches, padded to a multiple of NB (the loop handles NB at a time; a
     // padding batch holds only pieces past K)
@@ -104,37 +144,52 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const uint16_t* X, cons
         ok = off < k;  // k is a multiple of 16: a piece is whole or absent
         return ok ? off : k - 16;
     };
+    // byte offset of a batch piece in a weight row (tiled: of the chunk's
+    // tile from the lane's position in the group's first tile)
+    auto woff = [&](int b, int j) {
+        if constexpr (TILED) {
+            return min(wave + kWaves * (b * CB + j), nchunks - 1) * 1024;
+        } else {
+            bool ok;
+            return koff(b, j, ok);
+        }
+    };
 
     // NB register buffers, each with a batch of weights and the matching
     // activations
     struct Batch {
         u32x4 w[G][CB];
-        u32x4 x[TM][CB][2];
+        u32x4 x[TM][CB][XV];
     };
     Batch bufs[NB];
-    f32x4 acc[TM][G];
+    acc_t acc[TM][G];
 #pragma unroll
     for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[t][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int g = 0; g < G; ++g) acc[t][g] = acc_t{0, 0, 0, 0};
 
     // activations first: the memory counter is in order, and a batch's
     // activations (cache hits) must not wait behind its weights
     auto load = [&](Batch& buf, int b) {
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
-            bool ok;
-            const int off = koff(b, j, ok);
+            if constexpr (I8) {
+                const int off = woff(b, j);
 #pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                buf.x[t][j][0] = *(const u32x4*)(xrow[t] + off);
-                buf.x[t][j][1] = *(const u32x4*)(xrow[t] + off + 8);
+                for (int t = 0; t < TM; ++t) buf.x[t][j][0] = *(const u32x4*)(xrow[t] + off);
+            } else {
+                bool ok;
+                const int off = koff(b, j, ok);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    buf.x[t][j][0] = *(const u32x4*)((const uint16_t*)xrow[t] + off);
+                    buf.x[t][j][1] = *(const u32x4*)((const uint16_t*)xrow[t] + off + 8);
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
-            bool ok;
-            const int off = koff(b, j, ok);
+            const int off = woff(b, j);
 #pragma unroll
             for (int g = 0; g < G; ++g) buf.w[g][j] = *(const u32x4*)(wrow[g] + off);
         }
@@ -144,20 +199,36 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const uint16_t* X, cons
         for (int j = 0; j < CB; ++j) {
             bool ok;
             koff(b, j, ok);
+            if constexpr (I8) {
+                i32x4 xa[TM];
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    xa[t] = __builtin_bit_cast(i32x4, ok ? buf.x[t][j][0] : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const i32x4 wv = __builtin_bit_cast(i32x4, buf.w[g][j]);
+#pragma unroll
+                    for (int t = 0; t < TM; ++t)
+                        acc[t][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[t], wv, acc[t][g], 0, 0, 0);
+                }
+                continue;
+            }
             bf16x8 xa[TM], xb[TM];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 xa[t] = __builtin_bit_cast(bf16x8, ok ? buf.x[t][j][0] : u32x4{0u, 0u, 0u, 0u});
                 xb[t] = __builtin_bit_cast(bf16x8, ok ? buf.x[t][j][1] : u32x4{0u, 0u, 0u, 0u});
             }
+            if constexpr (!I8) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const bf16x8 wlo = widen(buf.w[g][j][0], buf.w[g][j][1]);
-                const bf16x8 whi = widen(buf.w[g][j][2], buf.w[g][j][3]);
+                for (int g = 0; g < G; ++g) {
+                    const bf16x8 wlo = widen(buf.w[g][j][0], buf.w[g][j][1]);
+                    const bf16x8 whi = widen(buf.w[g][j][2], buf.w[g][j][3]);
 #pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], wlo, acc[t][g], 0, 0, 0);
-                    acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[t], whi, acc[t][g], 0, 0, 0);
+                    for (int t = 0; t < TM; ++t) {
+                        acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], wlo, acc[t][g], 0, 0, 0);
+                        acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[t], whi, acc[t][g], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -203,53 +274,96 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const uint16_t* X, cons
     for (int f = 0; f < TM * G; ++f) {
         if (f % kWaves != wave) continue;
         const int t = f / G, g = f % G;
-        f32x4 s = red[0][f][lane];
+        acc_t s = red[0][f][lane];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) s += red[w][f][lane];
         const int o = row0 + g * 16 + r16;
         if (g * 16 + r16 >= rows || o >= n) continue;
-        const float swo = sb[o];
-        float bo = 0.0f;
-        if (bias_kind == 1) bo = ((const float*)bias)[o];
-        else if (bias_kind == 2) bo = __uint_as_float((uint32_t)((const uint16_t*)bias)[o] << 16);
+        float swo = 0.0f, bo = 0.0f;
+        if constexpr (OUT != 2) {
+            swo = sb[I8 && scalar_scales ? 0 : o];
+            if (bias_kind == 1) bo = ((const float*)bias)[o];
+            else if (bias_kind == 2) bo = __uint_as_float((uint32_t)((const uint16_t*)bias)[o] << 16);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = t * 16 + grp * 4 + r;
             if (tok >= m) continue;
-            float y = s[r] * swo;
-            if (bias_kind) y = y + bo;
             const int64_t off = (int64_t)tok * n + o;
-            if constexpr (OUT == 0) ((float*)Y)[off] = y;
-            else ((__bf16*)Y)[off] = (__bf16)y;
+            if constexpr (OUT == 2) {
+                ((int*)Y)[off] = s[r];
+            } else {
+                float y;
+                if constexpr (I8) y = (float)s[r] * sa[scalar_scales ? 0 : tok] * swo;
+                else y = s[r] * swo;
+                if (bias_kind) y = y + bo;
+                if constexpr (OUT == 0) ((float*)Y)[off] = y;
+                else ((__bf16*)Y)[off] = (__bf16)y;
+            }
         }
     }
 }
 
-template <int TM, int G, int CB, int NB>
-hipError_t launch_wo(const uint16_t* x, int m, const int8_t* wq, const float* sw, int n, int k, int rows,
-                     const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
-    const dim3 grid((n + rows - 1) / rows), block(64 * kWaves);
+// grid: row-major weights, ceil(n / rows) workgroups of `rows` rows; tiled
+// weights, `rows` is the workgroup count (the groups spread over them)
+template <int TM, int G, int CB, int NB, bool TILED, bool I8>
+hipError_t launch_wo(const void* x, const float* sx, int m, const int8_t* wq, const float* sw, int n, int k,
+                     int rows, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
+                     hipStream_t st) {
+    const dim3 grid(TILED ? rows : (n + rows - 1) / rows), block(64 * kWaves);
     if (out_kind == 0)
-        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 0>), grid, block, 0, st, x, wq, m, n, k, rows, sw, bias,
-                           bias_kind, y);
-    else
-        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 1>), grid, block, 0, st, x, wq, m, n, k, rows, sw, bias,
-                           bias_kind, y);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 0, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
+                           sw, bias, bias_kind, y, scalar_scales);
+    else if (out_kind == 1)
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 1, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
+                           sw, bias, bias_kind, y, scalar_scales);
+    else if constexpr (I8)
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 2, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
+                           sw, bias, bias_kind, y, scalar_scales);
     return hipGetLastError();
 }
 
 // One chunk per batch, two register buffers: measured on the decode shapes,
 // larger batches leave more compute after the last bytes arrive and more
 // buffers only lengthen the queues (both slower).
-template <int TM>
-hipError_t launch_wo_t(int groups, const uint16_t* x, int m, const int8_t* wq, const float* sw, int n, int k,
-                       int rows, const void* bias, int bias_kind, void* y, int out_kind, hipStream_t st) {
+template <int TM, bool TILED, bool I8>
+hipError_t launch_wo_t(int groups, const void* x, const float* sx, int m, const int8_t* wq, const float* sw, int n,
+                       int k, int rows, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
+                       hipStream_t st) {
     switch (groups) {
-        case 1: return launch_wo<TM, 1, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
-        case 2: return launch_wo<TM, 2, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
-        default: return launch_wo<TM, 3, 1, 2>(x, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, st);
+        case 1: return launch_wo<TM, 1, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 2: return launch_wo<TM, 2, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
+        default: return launch_wo<TM, 3, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
     }
 }
+
+// Tokens in chunks of up to 64, each chunk streaming the weights once: the
+// kernel is built for the decode shape. bf16 activations are [m][k]; int8
+// codes are 16 x 64 tiles (a 64-token chunk is 4 whole groups).
+template <bool TILED, bool I8>
+hipError_t wo_chunks(const void* x, const float* sx, int64_t m, int64_t k, const int8_t* wq, const float* sw,
+                     int64_t n, int rows, int groups, const void* bias, int bias_kind, void* y, int out_kind,
+                     int scalar_scales, hipStream_t st) {
+    const int ob = out_kind == 1 ? 2 : 4;
+    const int ni = (int)n, ki = (int)k;
+    const int64_t k64 = (k + 63) / 64 * 64;
+    for (int64_t r0 = 0; r0 < m; r0 += 64) {
+        const int mc = (int)((m - r0 < 64) ? m - r0 : 64);
+        const void* xc = I8 ? (const void*)((const int8_t*)x + r0 * k64) : (const void*)((const uint16_t*)x + r0 * k);
+        const float* sxc = (I8 && !scalar_scales) ? sx + r0 : sx;
+        void* yc = (int8_t*)y + r0 * n * ob;
+        hipError_t e;
+        switch ((mc + 15) / 16) {
+            case 1: e = launch_wo_t<1, TILED, I8>(groups, xc, sxc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, scalar_scales, st); break;
+            case 2: e = launch_wo_t<2, TILED, I8>(groups, xc, sxc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, scalar_scales, st); break;
+            case 3: e = launch_wo_t<3, TILED, I8>(groups, xc, sxc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, scalar_scales, st); break;
+            default: e = launch_wo_t<4, TILED, I8>(groups, xc, sxc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, scalar_scales, st); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 
 // compute units of the current device, asked once per device
 int compute_units() {
@@ -264,6 +378,17 @@ int compute_units() {
     return c;
 }
 
+// tiled weights: the ceil(n / 16) row groups spread evenly over the
+// workgroups, at most 3 groups each, as few rounds as that allows
+void tiled_grid(int64_t n, int& wgs, int& groups) {
+    const int64_t cus = compute_units();
+    const int64_t ng = (n + 15) / 16;
+    const int64_t rounds = (ng + cus * 3 - 1) / (cus * 3);
+    const int64_t w = ng < cus * rounds ? ng : cus * rounds;
+    wgs = (int)w;
+    groups = (int)((ng + w - 1) / w);
+}
+
 }  // namespace
 
 // Tokens are processed in chunks of up to 64 (each chunk streams the
@@ -276,21 +401,25 @@ hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t
     const int64_t rounds = (n + cus * kMaxRows - 1) / (cus * kMaxRows);
     int rows = (int)((n + cus * rounds - 1) / (cus * rounds));
     if (rows < 16) rows = 16;
-    const int groups = (rows + 15) / 16;
-    const int ob = out_kind == 0 ? 4 : 2;
-    const int ni = (int)n, ki = (int)k;
-    for (int64_t r0 = 0; r0 < m; r0 += 64) {
-        const int mc = (int)((m - r0 < 64) ? m - r0 : 64);
-        const uint16_t* xc = (const uint16_t*)x + r0 * k;
-        void* yc = (int8_t*)y + r0 * n * ob;
-        hipError_t e;
-        switch ((mc + 15) / 16) {
-            case 1: e = launch_wo_t<1>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
-            case 2: e = launch_wo_t<2>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
-            case 3: e = launch_wo_t<3>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
-            default: e = launch_wo_t<4>(groups, xc, mc, wq, sw, ni, ki, rows, bias, bias_kind, yc, out_kind, st); break;
-        }
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return wo_chunks<false, false>(x, nullptr, m, k, wq, sw, n, rows, (rows + 15) / 16, bias, bias_kind, y,
+                                   out_kind, 0, st);
+}
+
+hipError_t sq_launch_wo_linear_tiled(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw,
+                                     int64_t n, const void* bias, int bias_kind, void* y, int out_kind,
+                                     hipStream_t st) {
+    int wgs, groups;
+    tiled_grid(n, wgs, groups);
+    return wo_chunks<true, false>(x, nullptr, m, k, wq, sw, n, wgs, groups, bias, bias_kind, y, out_kind, 0, st);
+}
+
+// the W8A8 product for m <= 64 on tiled codes (both operands in 16 x 64 tiles)
+hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
+                                       const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
+                                       void* y, int out_kind, int scalar_scales, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    int wgs, groups;
+    tiled_grid(n, wgs, groups);
+    return wo_chunks<true, true>(xq, sx, m, k, wq, sw, n, wgs, groups, bias, bias_kind, y, out_kind, scalar_scales,
+                                 st);
 }
