@@ -121,6 +121,61 @@ def test_quantize_act(orc, shape, dtype):
     assert_equal(down(xq), xq_ref, "x_q")
 
 
+def _extreme_case(dtype, k=528, seed=3):
+    """Activations and smoothing factors that reach every branch of the
+    quotient x / s: quotients below 2^-50 (tiny x, or x over a huge s),
+    subnormal x, quotients above 2^120 (huge x over a small s), factors at
+    and above 2^40 (whose reciprocal is out of the fast path's range), zero
+    rows, mixed rows. Every quotient and every row max stays finite."""
+    rng = np.random.default_rng(seed)
+    m = 12
+    s = np.exp(rng.uniform(np.log(1e-8), np.log(1e4), size=k)).astype(np.float32)
+    s[:8] = np.float32(2.0 ** 40)
+    s[8:16] = np.float32(3.5e12)
+    s[16:24] = np.float32(1e-8)
+    x = (rng.standard_normal((m, k)) * 2.0).astype(np.float32)
+    x[0] = (rng.standard_normal(k) * 1e-30).astype(np.float32)   # all quotients tiny
+    x[1, ::3] = np.float32(1e-30)                                # tiny among normal
+    x[2] = 0.0                                                   # zero row
+    x[3, :] = 0.0
+    x[3, 5] = np.float32(1e-41 if dtype == "f32" else 1e-39)     # subnormal, alone
+    x[4, 24:40] = np.float32(2.5e36)                             # quotients above 2^120 where s >= 1
+    x[5, :24] = np.float32(3e30)                                 # huge over huge or tiny s
+    x[6, 16:24] = np.float32(1e30)                               # 1e30 / 1e-8 = 1e38: finite, above 2^120
+    x[7, 8:16] = np.float32(-7.0)                                # normal over s >= 2^40
+    x[8] = -x[8]
+    # keep every quotient finite: rows with huge numerators only over s >= 1
+    big = np.abs(x) > 1e29
+    x[big & (s[None, :] < 1.0) & ~((np.arange(m)[:, None] == 6) & (np.arange(k)[None, :] < 24))] = 1.0
+    if dtype == "bf16":
+        bits = inputs.bf16_bits(x)
+        return inputs.Tensor(inputs.bf16_to_f32(bits), bits), s
+    return inputs.Tensor(x, None), s
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_act_extreme_ranges(orc, dtype, tiled):
+    xt, s = _extreme_case(dtype)
+    m, k = xt.f32.shape
+    with np.errstate(over="raise", invalid="raise"):
+        q = xt.f32.astype(np.float64) / s.astype(np.float64)[None, :]
+    assert np.isfinite(q).all() and np.abs(q).max() < 2.0 ** 127
+    assert (np.abs(q[q != 0]) < 2.0 ** -50).any() and (np.abs(q) > 2.0 ** 120).any()
+    xs = _zeros(m, torch.float32)
+    if tiled:
+        xq = B.tiled_empty(m, k, DEV)
+        B.sq_quantize_act_tiled(up(xt), up(s), xq, xs)
+        xq = B.untile(xq, m, k)
+    else:
+        xq = _zeros((m, k), torch.int8)
+        B.sq_quantize_act(up(xt), up(s), xq, xs)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = orc.quantize_act(xt.f32, s)
+    assert_equal(down(xs), xs_ref, "x_scale")
+    assert_equal(down(xq), xq_ref, "x_q")
+
+
 # ---------------------------------------------------------------------------
 # a8-a9: int8 GEMM, raw int32 and dequantised
 # ---------------------------------------------------------------------------

@@ -260,9 +260,18 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 // holds for all operands as long as no step under- or overflows.
 //   * x / s_j: y_j = RN(1/s_j) comes from recip_rn (also checked against
 //     IEEE 1/s on the device, sq_selfcheck_reciprocal) for s_j in
-//     [2^-40, 2^40), else NaN. The quotient is taken when 2^-50 <= |q0| <=
-//     2^120 or q0 = 0 (then |x| >= 2^-90: no step leaves the normal range);
-//     otherwise, once per row and only if needed, the IEEE division.
+//     [2^-40, 2^40), else NaN. For 2^-50 <= |q0| <= 2^120 (then
+//     |x| >= 2^-90) or q0 = 0 no step leaves the normal range, so q1 is the
+//     IEEE quotient. Where |q0| < 2^-50 a step may underflow and q1 may
+//     differ from it, but both are below 2^-49 in magnitude, and such a
+//     value changes no output: its code is 0 (the row scale is at least
+//     floor / 127, about 2^-33.6), and it sets the row max only if every
+//     quotient of the row is that small, when both maxima are below the
+//     floor and the scale is floor / 127 either way. So the only guard is
+//     on the other side, checked once per row and thread on the largest
+//     |q0| (an infinite x gives q0 = inf): above 2^120, or where a y is
+//     NaN, the thread's out-of-range quotients are recomputed with the IEEE
+//     division. A NaN x gives NaN on both routes.
 //   * v / scale: scale is in [2^-34, 2^122] (floor / 127 up to max / 127)
 //     and |v / scale| <= 127.00002, so no step overflows; a step can only
 //     underflow when |v| < 2^-90, where the quotient is below 2^-50 and its
@@ -357,6 +366,7 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
     const int64_t k8 = k >> 3;
 
     float sv[C][8], yv[DIV ? C : 1][8];
+    bool y_bad = false;  // a factor outside the fast reciprocal's range
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int64_t j8 = (int64_t)c * T + tid;
@@ -374,7 +384,10 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
         }
         if constexpr (DIV) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) yv[c][i] = recip_rn(sv[c][i]);
+            for (int i = 0; i < 8; ++i) {
+                yv[c][i] = recip_rn(sv[c][i]);
+                y_bad |= __builtin_isnan(yv[c][i]);
+            }
         }
     }
 
@@ -406,8 +419,7 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
             }
         }
     };
-    // the fast quotient's proven range; q0 = 0 (x = 0) is exact as well but is
-    // left to the rare path, which skips it element by element
+    // the fast quotient's proven range (q0 = 0 is exact as well)
     auto in_range = [](float q0) {
         const float a0 = __builtin_fabsf(q0);
         return a0 >= 0x1p-50f && a0 <= 0x1p120f;
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
     load_row(row);
     for (int parity = 0; row < m; row += gridDim.x, parity ^= 1) {
         float xs[C][8];
-        bool exact_needed = false;  // one branch per row, never taken for sane inputs
+        float qmax = 0.0f;  // largest |q0| of the thread's quotients (NaN ignored)
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             float v[8];
@@ -426,14 +438,15 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
             for (int i = 0; i < 8; ++i) {
                 if constexpr (DIV) {
                     xs[c][i] = div_rn(v[i], sv[c][i], yv[c][i]);
-                    exact_needed |= !in_range(v[i] * yv[c][i]);
+                    qmax = fmaxf(qmax, __builtin_fabsf(v[i] * yv[c][i]));
                 } else {
                     xs[c][i] = v[i] * sv[c][i];
                 }
             }
         }
         if constexpr (DIV) {
-            if (exact_needed) {
+            // one branch per row, never taken for sane inputs
+            if (y_bad || !(qmax <= 0x1p120f)) {
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     float v[8];
