@@ -151,6 +151,11 @@ def test_prefill_2048x4096x4096_tiled(orc):
     _run_and_check(orc, inputs.prefill(), (0.5,), None, torch.bfloat16, tiled=True)
 
 
+def test_mlp_up_8192x8192x28672_tiled(orc):
+    """The MLP up-projection (with its bias) on tiled codes, alpha 0.5."""
+    _run_and_check(orc, inputs.mlp_up(), (0.5,), 40, torch.bfloat16, tiled=True)
+
+
 def test_mlp_up_8192x8192x28672_alpha_sweep(orc):
     case = inputs.mlp_up()
     _run_and_check(orc, case, case.alphas, 40, torch.bfloat16)
