@@ -288,9 +288,11 @@ sq_status sq_recompute_smooth_scale(const void* w, sq_dtype wt, int64_t n, int64
  *   ((i / 16) * (K64 / 64) + j / 64) * 1024 + (i % 16) * 64 + j % 64.
  * The codes are the same as in the row-major layout; the padding columns
  * of every row hold zeros, the padding rows are never read into a stored
- * output. The product reads each tile as one contiguous 1 KiB load (a
- * row-major 16-row x 64-byte block is 16 separate 64-byte pieces), which
- * measures about 14% faster at M = N = K = 4096.
+ * output. The products read each tile as one contiguous 1 KiB load (a
+ * row-major 16-row x 64-byte block is 16 separate 64-byte pieces): at
+ * M = N = K = 4096 the int8 product measures 65 us against 72 us
+ * row-major (paired runs), and on the decode shape (16 x 4096 -> 11008)
+ * 10.7 us against 13.1 us.
  * sq_tiled_bytes(rows, k) is the size of such an array (0 for rows <= 0).
  */
 size_t sq_tiled_bytes(int64_t rows, int64_t k);
@@ -316,7 +318,9 @@ sq_status sq_quantize_act_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k
  * sq_w8a8_gemm_tiled -- sq_w8a8_gemm with both x_q and w_q in the tiled
  * layout (from sq_quantize_act_tiled and sq_prepare_weight_tiled); the other
  * arguments, the arithmetic and the output as sq_w8a8_gemm (yt SQ_I32 gives
- * the raw int32 products).
+ * the raw int32 products), bit-identical to it. Up to 64 tokens the product
+ * streams the weights (one pass over w_q per 64 tokens), beyond that it
+ * runs on MFMA tiles.
  */
 sq_status sq_w8a8_gemm_tiled(const int8_t* x_q, const float* x_scale, int64_t m,
                              const int8_t* w_q, const float* w_scale, int64_t n, int64_t k,
