@@ -352,16 +352,17 @@ def test_division_scheme_is_correctly_rounded():
 # ---------------------------------------------------------------------------
 # a8-a9 for few tokens (m <= 64: the weight-streaming kernel): token counts
 # around every 16-row group, weight rows around every 16-row block, K tails
-# of 16/32/48 bytes and K long enough for several rounds of every wavefront;
-# m = 65 and 80 cross over to the tiled kernel.
+# of 16/32/48 bytes and K long enough for several rounds of every wavefront,
+# weight rows over several workgroups of up to 48; m = 65 and 80 cross over
+# to the tiled kernel.
 # ---------------------------------------------------------------------------
-SKINNY = [(1, 1, 16), (2, 17, 48), (15, 16, 64), (16, 100, 208), (17, 31, 4096), (31, 15, 1040),
+STREAM = [(1, 1, 16), (2, 17, 48), (15, 16, 64), (16, 100, 208), (17, 31, 4096), (31, 15, 1040),
           (32, 33, 11008), (33, 64, 80), (48, 47, 336), (49, 200, 2048), (63, 65, 4112),
-          (64, 129, 4096), (65, 70, 272), (80, 33, 4096)]
+          (64, 129, 4096), (16, 12289, 272), (64, 4099, 1040), (65, 70, 272), (80, 33, 4096)]
 
 
-@pytest.mark.parametrize("shape", SKINNY, ids=_id)
-def test_skinny_int32(orc, shape):
+@pytest.mark.parametrize("shape", STREAM, ids=_id)
+def test_stream_int32(orc, shape):
     m, n, k = shape
     rng = np.random.default_rng(m * 31 + n * 17 + k)
     a, b = _codes(rng, m, k), _codes(rng, n, k)
@@ -374,7 +375,7 @@ def test_skinny_int32(orc, shape):
 @pytest.mark.parametrize("bias", [None, "f32", "bf16"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 33, 64), (16, 200, 4096), (37, 129, 1040), (64, 100, 528)], ids=_id)
-def test_skinny_dequant(orc, shape, out, bias):
+def test_stream_dequant(orc, shape, out, bias):
     test_gemm_dequant(orc, shape, out, bias)
 
 

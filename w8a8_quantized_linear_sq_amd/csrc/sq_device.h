@@ -86,11 +86,9 @@ hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int6
 int sq_relative_error_blocks(int64_t count);
 hipError_t sq_launch_relative_error(const float* y_fp, const float* y_q, int64_t count, double* partial,
                                     double* out, hipStream_t st);
-// the same product for m <= 64 tokens (weight-streaming kernel)
-constexpr int64_t kSkinnyMaxM = 64;
-hipError_t sq_launch_gemm_skinny(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
-                                 const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
-                                 void* y, int out_kind, int scalar_scales, hipStream_t st);
+// tokens up to which the product streams the weights instead of running on
+// MFMA tiles
+constexpr int64_t kStreamMaxM = 64;
 // weight-only int8 linear: bf16 x [m][k] times int8 wq [n][k] with fp32
 // scales sw [n]; out_kind 0 fp32, 1 bf16; bias_kind as above
 hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw, int64_t n,
@@ -99,7 +97,12 @@ hipError_t sq_launch_wo_linear(const void* x, int64_t m, int64_t k, const int8_t
 hipError_t sq_launch_wo_linear_tiled(const void* x, int64_t m, int64_t k, const int8_t* wq, const float* sw,
                                      int64_t n, const void* bias, int bias_kind, void* y, int out_kind,
                                      hipStream_t st);
-// the W8A8 product for m <= kSkinnyMaxM on operands in 16 x 64 tiles (the
+// the W8A8 product for m <= kStreamMaxM on row-major operands through the
+// weight-only kernel's stream
+hipError_t sq_launch_gemm_stream(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq, const float* sw,
+                                 int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
+                                 int scalar_scales, hipStream_t st);
+// the W8A8 product for m <= kStreamMaxM on operands in 16 x 64 tiles (the
 // weight stream of the weight-only kernel, int8 activation codes)
 hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                                        const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,

@@ -539,8 +539,8 @@ hipError_t sq_launch_gemm(const int8_t* xq, const float* sx, int64_t m, const in
     if (m <= 0 || n <= 0) return hipSuccess;
     // few tokens: the product streams the weights; the tiled kernel would
     // leave most CUs idle
-    if (m <= kSkinnyMaxM) return sq_launch_gemm_skinny(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales,
-                                                          st);
+    if (m <= kStreamMaxM)
+        return sq_launch_gemm_stream(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales, st);
     return launch_tiled<kI8>(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales, st);
 }
 
@@ -550,7 +550,7 @@ hipError_t sq_launch_gemm_tiled(const int8_t* xq, const float* sx, int64_t m, co
                                 int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
                                 int scalar_scales, hipStream_t st) {
     if (m <= 0 || n <= 0) return hipSuccess;
-    if (m <= kSkinnyMaxM)
+    if (m <= kStreamMaxM)
         return sq_launch_gemm_stream_tiled(xq, sx, m, wq, sw, n, k, bias, bias_kind, y, out_kind, scalar_scales, st);
     const int64_t k64 = (k + 63) / 64 * 64;
     return launch_tiled<kI8, true>(xq, sx, m, wq, sw, n, k64, bias, bias_kind, y, out_kind, scalar_scales, st);

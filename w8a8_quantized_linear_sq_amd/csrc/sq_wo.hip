@@ -47,13 +47,13 @@
 //     instead of 16 separate 64-byte pieces. A workgroup owns whole groups
 //     (the groups spread evenly over the workgroups, G or G - 1 each);
 //   * I8: the W8A8 product for few tokens (page "w8a8_smoothquant.py",
-//     SmoothQuantW8A8.forward, integer route) on int8 activation codes and
-//     weights both in tiles: per chunk a lane loads 16 code bytes of each
-//     token group (one 1 KiB tile per instruction, like the weights) and
-//     one v_mfma_i32_16x16x64_i8 takes the chunk (lane l: row l % 16, bytes
-//     16 (l / 16) .. +16, the tile's own order). The int32 sums are exact;
-//     the epilogue is the GEMM's, f32(acc) * sx[t] * sw[o] (+ bias[o]), or
-//     the raw int32 sums (OUT = 2).
+//     SmoothQuantW8A8.forward, integer route) on int8 activation codes:
+//     per chunk a lane loads 16 code bytes of each token group (tiled: one
+//     1 KiB tile per instruction, like the weights; row-major: 16 rows x 64
+//     bytes) and one v_mfma_i32_16x16x64_i8 takes the chunk (lane l: row
+//     l % 16, bytes 16 (l / 16) .. +16, the tile's own order). The int32
+//     sums are exact; the epilogue is the GEMM's, f32(acc) * sx[t] * sw[o]
+//     (+ bias[o]), or the raw int32 sums (OUT = 2).
 #include <atomic>
 #include <type_traits>
 
@@ -90,7 +90,6 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const in
                                                          int rows, const float* __restrict__ sa,
                                                          const float* __restrict__ sb, const void* __restrict__ bias,
                                                          int bias_kind, void* __restrict__ Y, int scalar_scales) {
-    static_assert(TILED || !I8, "int8 activations come in tiles");
     static_assert(I8 || OUT != 2, "raw int32 sums only for the int8 product");
     typedef typename std::conditional<I8, i32x4, f32x4>::type acc_t;
     constexpr int XV = I8 ? 1 : 2;  // 16-byte activation loads per token group and chunk
@@ -127,7 +126,8 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const in
     const int8_t* xrow[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-        if constexpr (I8) xrow[t] = (const int8_t*)X + (int64_t)t * nchunks * 1024 + r16 * 64 + grp * 16;
+        if constexpr (I8 && TILED) xrow[t] = (const int8_t*)X + (int64_t)t * nchunks * 1024 + r16 * 64 + grp * 16;
+        else if constexpr (I8) xrow[t] = (const int8_t*)X + (int64_t)min(t * 16 + r16, m - 1) * k;
         else xrow[t] = (const int8_t*)((const uint16_t*)X + (int64_t)min(t * 16 + r16, m - 1) * k);
     }
 
@@ -349,7 +349,8 @@ hipError_t wo_chunks(const void* x, const float* sx, int64_t m, int64_t k, const
     const int64_t k64 = (k + 63) / 64 * 64;
     for (int64_t r0 = 0; r0 < m; r0 += 64) {
         const int mc = (int)((m - r0 < 64) ? m - r0 : 64);
-        const void* xc = I8 ? (const void*)((const int8_t*)x + r0 * k64) : (const void*)((const uint16_t*)x + r0 * k);
+        const void* xc = I8 ? (const void*)((const int8_t*)x + r0 * (TILED ? k64 : k))
+                            : (const void*)((const uint16_t*)x + r0 * k);
         const float* sxc = (I8 && !scalar_scales) ? sx + r0 : sx;
         void* yc = (int8_t*)y + r0 * n * ob;
         hipError_t e;
@@ -411,6 +412,19 @@ hipError_t sq_launch_wo_linear_tiled(const void* x, int64_t m, int64_t k, const 
     int wgs, groups;
     tiled_grid(n, wgs, groups);
     return wo_chunks<true, false>(x, nullptr, m, k, wq, sw, n, wgs, groups, bias, bias_kind, y, out_kind, 0, st);
+}
+
+// the W8A8 product for m <= 64 on row-major codes
+hipError_t sq_launch_gemm_stream(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq, const float* sw,
+                                 int64_t n, int64_t k, const void* bias, int bias_kind, void* y, int out_kind,
+                                 int scalar_scales, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    const int64_t cus = compute_units();
+    const int64_t rounds = (n + cus * kMaxRows - 1) / (cus * kMaxRows);
+    int rows = (int)((n + cus * rounds - 1) / (cus * rounds));
+    if (rows < 16) rows = 16;
+    return wo_chunks<false, true>(xq, sx, m, k, wq, sw, n, rows, (rows + 15) / 16, bias, bias_kind, y, out_kind,
+                                  scalar_scales, st);
 }
 
 // the W8A8 product for m <= 64 on tiled codes (both operands in 16 x 64 tiles)
