@@ -317,9 +317,10 @@ def main():
     case = _make_case(inputs, spec)
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
-    # the int8 codes in 16 x 64 tiles unless asked not to (the per-tensor
-    # variant has row-major calls only)
-    tiled = mode != "per_tensor" and args.layout == "tiled"
+    # the int8 codes in 16 x 64 tiles unless asked not to; the per-tensor
+    # variant quantises W on every call, and its tiled codes kernel costs
+    # what the tiled product saves, so it stays row-major
+    tiled = args.layout == "tiled" and mode != "per_tensor"
 
     def bf16(t):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)

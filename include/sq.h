@@ -190,6 +190,28 @@ sq_status sq_w8a8_gemm_per_tensor(const int8_t* x_q, const float* x_scale, int64
                                   sq_dtype yt, void* stream);
 
 /*
+ * sq_quantize_tensor_tiled -- sq_quantize_tensor of a [rows][k] matrix with
+ * the codes in the 16 x 64 tiled layout (see sq_tiled_bytes): the same one
+ * scale and the same codes, the padding columns of every row zero.
+ *   x      [rows][k] in xt (F32 or BF16), 16-byte aligned; k a multiple of 16
+ *   q      sq_tiled_bytes(rows, k) bytes, 16-byte aligned (also scratch
+ *          during the call, as in sq_quantize_tensor)
+ *   scale  [1] fp32 out, device memory
+ */
+sq_status sq_quantize_tensor_tiled(const void* x, sq_dtype xt, int64_t rows, int64_t k,
+                                   int8_t* q, float* scale, void* stream);
+
+/*
+ * sq_w8a8_gemm_per_tensor_tiled -- sq_w8a8_gemm_per_tensor with both codes
+ * in the tiled layout (from sq_quantize_tensor_tiled); the arithmetic and
+ * the output as sq_w8a8_gemm_per_tensor, bit-identical to it.
+ */
+sq_status sq_w8a8_gemm_per_tensor_tiled(const int8_t* x_q, const float* x_scale, int64_t m,
+                                        const int8_t* w_q, const float* w_scale, int64_t n,
+                                        int64_t k, const void* bias, sq_dtype bias_t, void* y,
+                                        sq_dtype yt, void* stream);
+
+/*
  * sq_wo_linear -- weight-only int8 linear: bf16 activations, int8 weights.
  * Follows Int8WeightOnlyQuantizedLinearWeight._quantized_op of the torchao
  * page "quantization/subclass.py": the int8 weights are converted to the

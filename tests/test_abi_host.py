@@ -330,3 +330,14 @@ def test_tiled_entry_errors(L):
     assert w(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ARG
     assert w(OK_PTR, B.SQ_BF16, 4, 64, BAD, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ALIGN
     assert w(None, B.SQ_BF16, 0, 64, None, None, 8, None, B.SQ_F32, None, B.SQ_BF16, None) == B.SQ_OK
+
+    t = L.sq_quantize_tensor_tiled
+    assert t(OK_PTR, B.SQ_I32, 4, 64, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE
+    assert t(OK_PTR, B.SQ_BF16, 0, 64, OK_PTR, OK_PTR, None) == B.SQ_ERR_SHAPE
+    assert t(OK_PTR, B.SQ_BF16, 4, 40, OK_PTR, OK_PTR, None) == B.SQ_ERR_ALIGN
+    assert t(OK_PTR, B.SQ_BF16, 4, 64, None, OK_PTR, None) == B.SQ_ERR_ARG
+    assert t(OK_PTR, B.SQ_BF16, 4, 64, BAD, OK_PTR, None) == B.SQ_ERR_ALIGN
+    p = L.sq_w8a8_gemm_per_tensor_tiled
+    assert p(OK_PTR, OK_PTR, 4, OK_PTR, OK_PTR, 8, 64, None, B.SQ_F32, OK_PTR, 9, None) == B.SQ_ERR_DTYPE
+    assert p(OK_PTR, OK_PTR, 4, OK_PTR, OK_PTR, 0, 64, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+    assert p(None, OK_PTR, 4, OK_PTR, OK_PTR, 8, 64, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ARG

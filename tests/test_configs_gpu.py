@@ -161,20 +161,29 @@ def test_mlp_up_8192x8192x28672_alpha_sweep(orc):
     _run_and_check(orc, case, case.alphas, 40, torch.bfloat16)
 
 
-def test_per_tensor_o_proj_4096(orc):
+@pytest.mark.parametrize("tiled", [False, True], ids=["row", "tiled"])
+def test_per_tensor_o_proj_4096(orc, tiled):
     """The per-tensor variant (page "quantized_linear.py") at the O
     projection's size: codes and scales of X and W in full, the output on
-    sampled rows."""
+    sampled rows; row-major codes, or tiled as the benchmark runs it."""
     case = inputs.o_proj()
     m, n, k = case.m, case.n, case.k
-    print(f"per-tensor {case.name}", flush=True)
-    xq, sx = _empty((m, k), torch.int8), _empty(1, torch.float32)
-    wq, sw = _empty((n, k), torch.int8), _empty(1, torch.float32)
-    B.sq_quantize_tensor(up(case.x), xq, sx)
-    B.sq_quantize_tensor(up(case.w), wq, sw)
+    print(f"per-tensor {case.name} tiled={tiled}", flush=True)
+    sx, sw = _empty(1, torch.float32), _empty(1, torch.float32)
     y = _empty((m, n), torch.bfloat16)
-    B.sq_w8a8_gemm_per_tensor(xq, sx, wq, sw, None, y)
-    torch.cuda.synchronize()
+    if tiled:
+        xq, wq = B.tiled_empty(m, k, DEV), B.tiled_empty(n, k, DEV)
+        B.sq_quantize_tensor_tiled(up(case.x), xq, sx)
+        B.sq_quantize_tensor_tiled(up(case.w), wq, sw)
+        B.sq_w8a8_gemm_per_tensor_tiled(xq, sx, m, wq, sw, n, k, None, y)
+        torch.cuda.synchronize()
+        xq, wq = B.untile(xq, m, k), B.untile(wq, n, k)
+    else:
+        xq, wq = _empty((m, k), torch.int8), _empty((n, k), torch.int8)
+        B.sq_quantize_tensor(up(case.x), xq, sx)
+        B.sq_quantize_tensor(up(case.w), wq, sw)
+        B.sq_w8a8_gemm_per_tensor(xq, sx, wq, sw, None, y)
+        torch.cuda.synchronize()
     xq_ref, sx_ref = orc.quantize_tensor(case.x.f32)
     wq_ref, sw_ref = orc.quantize_tensor(case.w.f32)
     assert_equal(down(sx)[0], sx_ref, "x scale")

@@ -280,3 +280,64 @@ def test_wo_linear_tiled_from_prepared_weights(orc):
     yref = orc.wo_linear(c.x.f32, wq_ref, sw_ref, None)
     mag = (np.abs(c.x.f32.astype(np.float64)) @ np.abs(wq_ref.astype(np.float64)).T) * sw_ref[None, :]
     _assert_wo_close(down(y), yref, mag, k, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Per-tensor variant on tiled codes (page "quantized_linear.py",
+# quantize_tensor and QuantizedLinear.forward): the one scale and the codes
+# equal the oracle's and the row-major call's; the product equals the
+# row-major per-tensor product bit for bit and the oracle to the usual bar.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (17, 80), (130, 528), (257, 1040), (1000, 4096)], ids=_id)
+def test_quantize_tensor_tiled(orc, shape, dtype):
+    m, k = shape
+    c = inputs.small(m, 8, k, seed=13 + m + k, dtype=dtype, bias=False)
+    q = _garbage(m, k)
+    sc = torch.zeros(1, dtype=torch.float32, device=DEV)
+    B.sq_quantize_tensor_tiled(up(c.x), q, sc)
+    torch.cuda.synchronize()
+    q_ref, sc_ref = orc.quantize_tensor(c.x.f32)
+    assert_equal(down(sc)[0], sc_ref, "scale")
+    assert_equal(down(B.untile(q, m, k)), q_ref, "codes")
+    assert not _padding_columns(q, m, k).any(), "padding columns not zero"
+
+
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 5, 32), (16, 200, 4096), (64, 129, 528), (130, 260, 528),
+                                   (257, 300, 1040)], ids=_id)
+def test_gemm_per_tensor_tiled(orc, shape, out, bias):
+    m, n, k = shape
+    c = inputs.small(m, n, k, seed=5 + m + n + k, dtype="bf16", bias=bias is not None)
+    x_dev, w_dev = up(c.x), up(c.w)
+    xq, sx = B.tiled_empty(m, k, DEV), torch.zeros(1, dtype=torch.float32, device=DEV)
+    wq, sw = B.tiled_empty(n, k, DEV), torch.zeros(1, dtype=torch.float32, device=DEV)
+    B.sq_quantize_tensor_tiled(x_dev, xq, sx)
+    B.sq_quantize_tensor_tiled(w_dev, wq, sw)
+    bias_f = bias_t = None
+    if bias == "f32":
+        bias_f, bias_t = c.bias.f32, up(c.bias.f32)
+    elif bias == "bf16":
+        bias_f, bias_t = c.bias.f32, up(c.bias)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    y = torch.zeros((m, n), dtype=odt, device=DEV)
+    B.sq_w8a8_gemm_per_tensor_tiled(xq, sx, m, wq, sw, n, k, bias_t, y)
+    xq_r, sx_r = torch.zeros((m, k), dtype=torch.int8, device=DEV), torch.zeros(1, dtype=torch.float32, device=DEV)
+    wq_r, sw_r = torch.zeros((n, k), dtype=torch.int8, device=DEV), torch.zeros(1, dtype=torch.float32, device=DEV)
+    B.sq_quantize_tensor(x_dev, xq_r, sx_r)
+    B.sq_quantize_tensor(w_dev, wq_r, sw_r)
+    y_rm = torch.zeros((m, n), dtype=odt, device=DEV)
+    B.sq_w8a8_gemm_per_tensor(xq_r, sx_r, wq_r, sw_r, bias_t, y_rm)
+    torch.cuda.synchronize()
+    xq_ref, sx_ref, wq_ref, sw_ref, acc, yref = orc.linear_per_tensor(c.x.f32, c.w.f32, bias_f)
+    assert_equal(down(B.untile(xq, m, k)), xq_ref, "x codes")
+    assert_equal(down(B.untile(wq, n, k)), wq_ref, "w codes")
+    scale = np.abs(acc.astype(np.float64) * float(sx_ref) * float(sw_ref))
+    if bias_f is not None:
+        scale = scale + np.abs(bias_f)[None, :]
+    if out == "f32":
+        assert_f32_rel(down(y), yref, scale)
+    else:
+        assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
+    assert_equal(down(y), down(y_rm), "tiled vs row-major")

@@ -45,6 +45,8 @@ _SIGNATURES = {
     "sq_abi_version": ([], _E),
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
     "sq_w8a8_gemm_per_tensor": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
+    "sq_quantize_tensor_tiled": ([_P, _E, _I64, _I64, _P, _P, _P], _E),
+    "sq_w8a8_gemm_per_tensor_tiled": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_wo_linear": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_wo_linear_tiled": ([_P, _E, _I64, _I64, _P, _P, _I64, _P, _E, _P, _E, _P], _E),
     "sq_weight_col_max": ([_P, _E, _I64, _I64, _P, _P], _E),
@@ -232,6 +234,27 @@ def sq_w8a8_gemm_per_tensor(x_q: torch.Tensor, x_scale: torch.Tensor, w_q: torch
     bt = _dtype_code(bias) if bias is not None else SQ_F32
     return _invoke("sq_w8a8_gemm_per_tensor", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k,
                    _ptr(bias), bt, _ptr(y), _dtype_code(y), _stream(stream, x_q))
+
+
+def sq_quantize_tensor_tiled(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None) -> int:
+    """Per-tensor int8 codes of a [rows][k] x into 16 x 64 tiles (flat int8 q)
+    and its one scale."""
+    rows, k = x.shape
+    _need_tiled(q, rows, k, "q")
+    _need_dtype(scale, torch.float32, "scale")
+    return _invoke("sq_quantize_tensor_tiled", _ptr(x), _dtype_code(x), rows, k, _ptr(q), _ptr(scale),
+                   _stream(stream, x))
+
+
+def sq_w8a8_gemm_per_tensor_tiled(x_q: torch.Tensor, x_scale: torch.Tensor, m: int, w_q: torch.Tensor,
+                                  w_scale: torch.Tensor, n: int, k: int, bias: torch.Tensor | None, y: torch.Tensor,
+                                  stream=None) -> int:
+    """sq_w8a8_gemm_per_tensor on operands in 16 x 64 tiles (flat int8)."""
+    _need_tiled(x_q, m, k, "x_q")
+    _need_tiled(w_q, n, k, "w_q")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    return _invoke("sq_w8a8_gemm_per_tensor_tiled", _ptr(x_q), _ptr(x_scale), m, _ptr(w_q), _ptr(w_scale), n, k,
+                   _ptr(bias), bt, _ptr(y), _dtype_code(y), _stream(stream, y))
 
 
 def sq_wo_linear(x: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None,

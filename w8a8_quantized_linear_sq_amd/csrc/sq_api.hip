@@ -146,6 +146,26 @@ sq_status sq_w8a8_gemm_per_tensor(const int8_t* x_q, const float* x_scale, int64
                                    out_kind(yt), 1, as_stream(stream)));
 }
 
+sq_status sq_quantize_tensor_tiled(const void* x, sq_dtype xt, int64_t rows, int64_t k, int8_t* q, float* scale,
+                                   void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (rows <= 0 || rows > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!x || !q || !scale) return SQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scale & 3u) != 0) return SQ_ERR_ALIGN;
+    return launched(sq_launch_quantize_tensor_tiled(x, xt == SQ_BF16, rows, k, q, scale, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_per_tensor_tiled(const int8_t* x_q, const float* x_scale, int64_t m, const int8_t* w_q,
+                                        const float* w_scale, int64_t n, int64_t k, const void* bias,
+                                        sq_dtype bias_t, void* y, sq_dtype yt, void* stream) {
+    sq_status st = check_gemm(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    return launched(sq_launch_gemm_tiled(x_q, x_scale, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y,
+                                         out_kind(yt), 1, as_stream(stream)));
+}
+
 sq_status sq_wo_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const int8_t* w_q, const float* w_scale,
                        int64_t n, const void* bias, sq_dtype bias_t, void* y, sq_dtype yt, void* stream) {
     if (xt != SQ_BF16) return SQ_ERR_DTYPE;

@@ -53,6 +53,9 @@ hipError_t sq_launch_quantize_act(const void* x, int bf16, const float* s, int64
 // aligned, also holds the block maxima until the codes overwrite them)
 hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int8_t* q, float* scale,
                                      hipStream_t st);
+// the same codes into 16 x 64 tiles of a [rows][k] matrix
+hipError_t sq_launch_quantize_tensor_tiled(const void* x, int bf16, int64_t rows, int64_t k, int8_t* q,
+                                           float* scale, hipStream_t st);
 // counts s in [2^-100, 2^100) whose kernel reciprocal differs from IEEE 1/s
 hipError_t sq_launch_selfcheck_reciprocal(unsigned long long* mismatches, hipStream_t st);
 // counts significand pairs (divisors [b_begin, b_end)) where the kernels'

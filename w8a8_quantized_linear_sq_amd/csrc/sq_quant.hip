@@ -650,6 +650,50 @@ __global__ __launch_bounds__(256) void tensor_codes_kernel(const u32x4* __restri
     }
 }
 
+// The codes into 16 x 64 tiles, the padding columns of every row written as
+// zero codes: the row-major walk of the flat kernel above over rows x K64 / 8
+// groups of 8 elements (reads contiguous; each thread's 8 bytes go to their
+// tile). Staging 16-row slabs through LDS to store whole tiles, or walking
+// in the tiles' order, measured slower.
+template <bool BF16>
+__global__ __launch_bounds__(256) void tensor_codes_tiled_kernel(const u32x4* __restrict__ x, int64_t rows,
+                                                                 int64_t k, const float* __restrict__ scale,
+                                                                 int8_t* __restrict__ q) {
+    constexpr int kV = BF16 ? 1 : 2;  // 16-byte loads per 8 elements
+    const float sc = *scale;
+    const float rs = 1.0f / sc;
+    const int64_t k8 = k >> 3, k64 = (k + 63) & ~(int64_t)63, p8 = k64 >> 3;
+    const int64_t groups = rows * p8;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += (int64_t)gridDim.x * 256) {
+        const int64_t row = g / p8, j8 = g - row * p8;
+        u32x2 codes = {0u, 0u};
+        if (j8 < k8) {
+            const int64_t src = row * k8 + j8;
+            float v[8];
+            if constexpr (BF16) {
+                const u32x4 a = x[src];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_lo(a[i]);
+                    v[2 * i + 1] = bf16_hi(a[i]);
+                }
+            } else {
+                const u32x4 a = x[src * kV], b = x[src * kV + 1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = __uint_as_float(a[i]);
+                    v[4 + i] = __uint_as_float(b[i]);
+                }
+            }
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = __float_as_uint(div_rn(v[i], sc, rs) + kMagic);
+            codes = u32x2{pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7])};
+        }
+        *(u32x2*)(q + ((row >> 4) * (k64 >> 6) + (j8 >> 3)) * 1024 + (row & 15) * 64 + (j8 & 7) * 8) = codes;
+    }
+}
+
 int64_t sq_tensor_max_blocks(int64_t count) {
     int64_t b = count / 8192;  // about 8 KiB of input per block
     if (b < 1) b = 1;
@@ -657,8 +701,9 @@ int64_t sq_tensor_max_blocks(int64_t count) {
     return b;  // the partials (4 bytes each) fit in the count-byte code buffer
 }
 
-hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int8_t* q, float* scale,
-                                     hipStream_t st) {
+// rows > 0: the codes into 16 x 64 tiles of a [rows][count / rows] matrix
+static hipError_t quantize_tensor(const void* x, int bf16, int64_t count, int64_t rows, int8_t* q, float* scale,
+                                  hipStream_t st) {
     const int64_t nvec = bf16 ? count / 8 : count / 4;
     const int64_t blocks = sq_tensor_max_blocks(count);
     unsigned* partial = (unsigned*)q;
@@ -673,6 +718,20 @@ hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, st, (const unsigned*)partial, (int)blocks, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (rows > 0) {
+        const int64_t k = count / rows;
+        const int64_t groups = rows * ((k + 63) / 64 * 8);
+        int64_t cb = (groups + 255) / 256;
+        if (cb > 4096) cb = 4096;
+        const dim3 grid((unsigned)cb);
+        if (bf16)
+            hipLaunchKernelGGL(tensor_codes_tiled_kernel<true>, grid, dim3(256), 0, st, (const u32x4*)x, rows, k,
+                               (const float*)scale, q);
+        else
+            hipLaunchKernelGGL(tensor_codes_tiled_kernel<false>, grid, dim3(256), 0, st, (const u32x4*)x, rows, k,
+                               (const float*)scale, q);
+        return hipGetLastError();
+    }
     const int64_t groups = count / 8;
     int64_t cb = (groups + 255) / 256;
     if (cb > 4096) cb = 4096;
@@ -683,4 +742,14 @@ hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int
         hipLaunchKernelGGL(tensor_codes_kernel<false>, dim3((unsigned)cb), dim3(256), 0, st, (const u32x4*)x, groups,
                            (const float*)scale, q);
     return hipGetLastError();
+}
+
+hipError_t sq_launch_quantize_tensor(const void* x, int bf16, int64_t count, int8_t* q, float* scale,
+                                     hipStream_t st) {
+    return quantize_tensor(x, bf16, count, 0, q, scale, st);
+}
+
+hipError_t sq_launch_quantize_tensor_tiled(const void* x, int bf16, int64_t rows, int64_t k, int8_t* q,
+                                           float* scale, hipStream_t st) {
+    return quantize_tensor(x, bf16, rows * k, rows, q, scale, st);
 }
