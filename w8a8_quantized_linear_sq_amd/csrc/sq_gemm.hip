@@ -36,7 +36,7 @@
 //     hardware deals workgroups round-robin over the 8 XCDs) form a compact
 //     block sharing A rows and B columns in that XCD's L2;
 //   * the epilogue stages each 32-row slab through LDS and writes whole
-//     16-byte row chunks;
+//     16-byte row chunks with streaming (non-temporal) stores;
 //   * the same kernel, with the operands' element type as a parameter (K
 //     counted in bytes, so the LDS layout and the DMA are unchanged), is the
 //     full-precision reference of quantization_error (page
@@ -447,13 +447,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
                     }
                 }
             }
-            // the same wavefront reads back what it wrote: LDS keeps its order
+            // the same wavefront reads back what it wrote: LDS keeps its order.
+            // The output is written once and not read here: streaming
+            // (non-temporal) stores, measured 1-3% faster over the launch
+            // (the tiles all end together, so the output burst is exposed)
 #pragma unroll
             for (int c = lane; c < SLAB_CHUNKS; c += 64) {
                 const int lr = c / ROW_CHUNKS, cc = c % ROW_CHUNKS;
                 const i32x4 v = *(const i32x4*)(stage + lr * PITCH + cc * 16);
                 int8_t* out = (int8_t*)Y + ((int64_t)(rbase + lr) * n + n0 + wn * WN) * OB + cc * 16;
-                *(i32x4*)out = v;
+                __builtin_nontemporal_store(v, (i32x4*)out);
             }
         }
         return;
