@@ -53,6 +53,7 @@ PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20     # bytes read per rotation cycle, at least
 GEMM_LAUNCHES = 64           # product launches in the graph that times the product kernel
+STAGE_LAUNCHES = 16          # repetitions of a stage in the graph that times it alone
 GEMM_SOURCE = os.path.join(ROOT, "w8a8_quantized_linear_sq_amd", "csrc", "sq_gemm.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_o_proj_4096_traffic.md")
 
@@ -504,10 +505,41 @@ def main():
     stage_ms = {nm: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
                 for j, nm in enumerate(stage_names)}
 
+    # each stage on its own: a graph of STAGE_LAUNCHES repetitions over the
+    # rotated buffer sets, replayed untimed and then between events (the
+    # per-launch floor between dependent kernels included, no event gaps);
+    # these figures give the stages' rooflines
+    def stage_calls(s, nm):
+        if nm == "reset+calibrate":
+            return [s["run"].zero_] + s["calls_calib"]
+        if nm in ("prepare_weight", "quantize_weight"):
+            return [s["call_prep"]]
+        if nm == "quantize_act":
+            return [s["call_act"]]
+        return [s["call_gemm"]]
+
+    stage_graph_ms = {}
+    for nm in stage_names:
+        if nm == "gemm":
+            stage_graph_ms[nm] = gemm_ms
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(STAGE_LAUNCHES):
+                for call in stage_calls(sets[i % rotate], nm):
+                    call()
+        g.replay()
+        torch.cuda.synchronize()
+        gev[0].record(stream)
+        g.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize()
+        stage_graph_ms[nm] = gev[0].elapsed_time(gev[1]) / STAGE_LAUNCHES
+
     ops = 2.0 * m * n * k
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    act_ms = stage_ms.get("quantize_act", 0.0)
+    act_ms = stage_graph_ms.get("quantize_act", 0.0)
     linear_tops = ops / ((act_ms + gemm_ms) * 1e-3) / 1e12
 
     def hbm(bytes_, ms):
@@ -519,15 +551,15 @@ def main():
     # whole pass over the tensor before its first code: two reads)
     wo_bytes = n * k + m * k * 2 + 2 * m * n + 4 * n
     if mode == "weight_only":
-        stage_roof = {"wo_linear": hbm(wo_bytes, stage_ms["wo_linear"])}
+        stage_roof = {"wo_linear": hbm(wo_bytes, stage_graph_ms["wo_linear"])}
     elif mode == "per_tensor":
         stage_roof = {"quantize_act": hbm(2 * m * k * 2 + m * k, act_ms),
-                      "quantize_weight": hbm(2 * n * k * 2 + n * k, stage_ms["quantize_weight"])}
+                      "quantize_weight": hbm(2 * n * k * 2 + n * k, stage_graph_ms["quantize_weight"])}
     else:
         stage_roof = {"quantize_act": hbm(m * k * 2 + m * k + 4 * m + 4 * k, act_ms)}
     if mode == "full":
-        stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_ms["prepare_weight"])
-        stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_ms["reset+calibrate"])
+        stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_graph_ms["prepare_weight"])
+        stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_graph_ms["reset+calibrate"])
     kernel_name = ("int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)" if mode == "per_tensor"
                    else "int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_tiled)" if tiled
                    else "int8 GEMM + fused dequant (sq_w8a8_gemm)")
@@ -562,6 +594,9 @@ def main():
     config["int8_layout"] = "16x64 tiles" if tiled else "row-major"
     stages = {nm: round(v * 1e3, 2) for nm, v in stage_ms.items()}
     stages["note"] = "second pass of the same K steps with an event between stages"
+    stages_graph = {nm: round(v * 1e3, 2) for nm, v in stage_graph_ms.items()}
+    stages_graph["note"] = (f"each stage alone: a graph of {STAGE_LAUNCHES} repetitions over the rotated sets "
+                            "(the product: its own graph); the stage rooflines use these")
     line = {
         "metric": (METRIC if args.workload == "o_proj" else
                    f"weight-only int8 linear TOPS at M={m} N={n} K={k}" if mode == "weight_only" else
@@ -583,6 +618,7 @@ def main():
         "gemm_launches_timed": GEMM_LAUNCHES,
         "gemm_us_warm": round(gemm_warm_ms * 1e3, 2),
         "stages_us": stages,
+        "stages_us_graph": stages_graph,
         "stage_rooflines": stage_roof,
         "linear_tops": round(linear_tops, 2),
         "gemm_tops": round(gemm_tops, 2),
