@@ -1,6 +1,7 @@
 // sq_wo.hip -- weight-only int8 linear: bf16 activations times int8 weights
 // with one scale per output channel, for few tokens (the decode shape); and
-// the same weight stream for the W8A8 product on tiled int8 codes.
+// the same weight stream for the W8A8 product of up to 64 tokens on int8
+// codes (row-major or tiled).
 //
 // Follows the torchao page "quantization/subclass.py",
 // Int8WeightOnlyQuantizedLinearWeight._quantized_op: the int8 weights are
