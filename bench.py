@@ -91,7 +91,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--layout", choices=("tiled", "row"), default="tiled",
-                   help="int8 code layout of the full step: 16 x 64 tiles (default) or row-major")
+                   help="int8 code layout: 16 x 64 tiles (default) or row-major (the per-tensor workload "
+                        "is always row-major)")
     p.add_argument("--counter-pass", action="store_true",
                    help="run only a 256 MiB fp32 copy (known bytes) and the GEMM, 3 times each, for "
                         "rocprofv3 --pmc passes; prints no JSON line")
