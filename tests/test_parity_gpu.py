@@ -154,6 +154,36 @@ def _extreme_case(dtype, k=528, seed=3):
 
 
 @pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("shape", [(1024, 8208), (1030, 11008), (2051, 11264), (1000, 10000)], ids=_id)
+def test_quantize_long_rows(orc, shape, tiled):
+    """Rows of 8200-11264 channels: with 1024 rows or more the quantiser
+    runs 384 threads x 4 chunks per row, below 1024 rows 704 x 2; both
+    quantisers (activations and weights), both layouts, bit for bit."""
+    r, k = shape
+    c = inputs.small(r, r, k, seed=31 + r + k, dtype="bf16", bias=False)
+    mx = orc.calibrate(c.x.f32)
+    s, wq_ref, sw_ref = orc.prepare_weight(c.w.f32, mx, 0.5)
+    xq_ref, xs_ref = orc.quantize_act(c.x.f32, s)
+    xs, sw = _zeros(r, torch.float32), _zeros(r, torch.float32)
+    s_dev = _zeros(k, torch.float32)
+    if tiled:
+        xq, wq = B.tiled_empty(r, k, DEV), B.tiled_empty(r, k, DEV)
+        B.sq_quantize_act_tiled(up(c.x), up(s), xq, xs)
+        B.sq_prepare_weight_tiled(up(c.w), up(mx), 0.5, s_dev, wq, sw)
+        xq, wq = B.untile(xq, r, k), B.untile(wq, r, k)
+    else:
+        xq, wq = _zeros((r, k), torch.int8), _zeros((r, k), torch.int8)
+        B.sq_quantize_act(up(c.x), up(s), xq, xs)
+        B.sq_prepare_weight(up(c.w), up(mx), 0.5, s_dev, wq, sw)
+    torch.cuda.synchronize()
+    assert_equal(down(s_dev), s, "s")
+    assert_equal(down(xs), xs_ref, "x_scale")
+    assert_equal(down(xq), xq_ref, "x_q")
+    assert_equal(down(sw), sw_ref, "w_scale")
+    assert_equal(down(wq), wq_ref, "w_q")
+
+
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_act_extreme_ranges(orc, dtype, tiled):
     xt, s = _extreme_case(dtype)

@@ -358,6 +358,7 @@ template <bool BF16, bool DIV, int T, int C, bool TILED>
 __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict__ x, const float* __restrict__ s,
                                                           int64_t m, int64_t k, int8_t* __restrict__ q,
                                                           float* __restrict__ scale_out) {
+    static_assert(T % 64 == 0, "whole wavefronts: the block max goes through one LDS slot per wavefront");
     constexpr int NW = T / 64;
     constexpr int kV = BF16 ? 1 : 2;  // 16-byte loads per 8 channels
     __shared__ float red[2][NW];
@@ -504,7 +505,13 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
     int T, C;
     if (k8 <= 512) { T = 256; C = k8 <= 256 ? 1 : 2; }
     else if (k8 <= 1024) { T = 512; C = 2; }
-    else if (k8 <= 1408) { T = 704; C = 2; }
+    else if (k8 <= 1408) {
+        // many rows: 6 wavefronts with 4 chunks each beat 11 with 2 (paired
+        // runs, 4096 x 11008 bf16: 34.1 -> 29.9 us); few rows: the wider
+        // block's shorter chain per row wins (256 rows: 5.3 against 5.8 us)
+        if (m >= 1024) { T = 384; C = 4; }
+        else { T = 704; C = 2; }
+    }
     else if (k8 <= 1536) { T = 512; C = 3; }
     else if (k8 <= 2048) { T = 1024; C = 2; }
     else return hipErrorInvalidValue;
@@ -524,7 +531,7 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
         hipLaunchKernelGGL((quantize_rows_kernel<BF16, DIV, TT, CC, TILED>), grid, block, 0, st, x, s, m, k, q, scale); \
         return hipGetLastError();                                                                             \
     }
-    SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(704, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
+    SQ_ROWS_CASE(256, 1) SQ_ROWS_CASE(256, 2) SQ_ROWS_CASE(512, 2) SQ_ROWS_CASE(384, 4) SQ_ROWS_CASE(704, 2) SQ_ROWS_CASE(512, 3) SQ_ROWS_CASE(1024, 2)
 #undef SQ_ROWS_CASE
     return hipErrorInvalidValue;
 }
