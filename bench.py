@@ -22,9 +22,10 @@ decode_weight_only times the weight-only int8 linear (sq_wo_linear_tiled)
 on the decode shape. --layout row gives the row-major calls throughout.
 
 Inputs are resident in HBM before the timed region; enough copies of every
-buffer a step reads are rotated (at least 512 MiB per cycle, 2 to 12
-copies) that a step does not find its inputs in the 256 MB Infinity Cache
-left there by the previous step. The K timed steps are captured into one
+buffer a step reads are rotated (at least 512 MiB per cycle, counting the
+step's bytes and also the product's alone; 2 to 12 copies) that neither a
+step nor a product launch finds its inputs in the 256 MB Infinity Cache
+left there by the previous one. The K timed steps are captured into one
 HIP graph on the launch stream and replayed once between two HIP events
 (no host launch cost between kernels); a second graph of 64 product
 launches over the same buffer sets, replayed between events, gives the
@@ -340,7 +341,10 @@ def main():
         set_bytes = m * k * 2 + n * k * 2 + n * k + m * k + m * n * 2
     else:
         set_bytes = m * k * 2 + n * k * 2 + calib_rows * k * 2 + n * k + m * k + m * n * 2
-    rotate = max(2, min(12, math.ceil(ROTATE_BYTES / set_bytes)))
+    # ... and the bytes of one product launch alone (its graph rotates over
+    # the same sets): enough sets that neither cycle fits the cache
+    gemm_bytes = (m * k + n * k) + m * n * 2 if mode != "weight_only" else n * k + m * k * 2 + m * n * 2
+    rotate = max(2, min(12, math.ceil(ROTATE_BYTES / min(set_bytes, gemm_bytes))))
     sets = []
     for _ in range(rotate):
         sets.append(dict(
