@@ -298,3 +298,31 @@ def test_mlp_up_alpha_sweep_quantization_error(orc):
         print(f"alpha {alpha}: quantization_error {got[2]:.6g}", flush=True)
     # smoothing helps on outlier channels (x100 on 0.5% of them)
     assert errors[0.5] < errors[None], errors
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["row", "tiled"])
+def test_int32_product_matches_vendor_library_4096(tiled):
+    """The exact int32 product at M = N = K = 4096 on the O projection's
+    codes, every element, against the vendor library's int8 GEMM
+    (torch._int_mm): two exact integer products must agree bit for bit. The
+    oracle checks these codes and sampled rows of the product; this covers
+    all 16.8M outputs."""
+    case = inputs.o_proj()
+    m, n, k = case.m, case.n, case.k
+    run = _calibrate(case)
+    s, sx, sw = _empty(k, torch.float32), _empty(m, torch.float32), _empty(n, torch.float32)
+    y = _empty((m, n), torch.int32)
+    if tiled:
+        xq, wq = B.tiled_empty(m, k, DEV), B.tiled_empty(n, k, DEV)
+        B.sq_prepare_weight_tiled(up(case.w), run, 0.5, s, wq, sw)
+        B.sq_quantize_act_tiled(up(case.x), s, xq, sx)
+        B.sq_w8a8_gemm_tiled(xq, None, m, wq, None, n, k, None, y)
+        xr, wr = B.untile(xq, m, k), B.untile(wq, n, k)
+    else:
+        xr, wr = _empty((m, k), torch.int8), _empty((n, k), torch.int8)
+        B.sq_prepare_weight(up(case.w), run, 0.5, s, wr, sw)
+        B.sq_quantize_act(up(case.x), s, xr, sx)
+        B.sq_w8a8_gemm(xr, None, wr, None, None, y)
+    ref = torch._int_mm(xr, wr.t())  # (k x n): the transposed view of W_q
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref), int((y != ref).sum())
