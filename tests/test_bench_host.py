@@ -39,6 +39,9 @@ def test_cpu_baseline_object(mode):
     assert cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
     assert cb["seconds_measured"] >= 0
+    if mode == "full":
+        # the tiny layer fits the budget: whole steps repeated until it is spent
+        assert "whole steps" in cb["sample"] and cb["seconds_measured"] >= 0.2 or "50 whole steps" in cb["sample"]
 
 
 def test_every_workload_names_a_case_and_mode():
