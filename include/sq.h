@@ -19,7 +19,8 @@
  *     is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *     the call returns at once. Outputs are valid when the stream reaches
  *     that point. Calls on different streams that write the same buffer race.
- *   - Row-major, dense: X is [m][k], W and wq are [n][k], Y is [m][n].
+ *   - Row-major, dense: X is [m][k], W and wq are [n][k], Y is [m][n]
+ *     (wq and xq may instead be tiled, below).
  *   - k must be a positive multiple of 16. Every pointer to a [.][k] array
  *     must be 16-byte aligned. m and n may be any size >= 1 (a call with
  *     m == 0 is a no-op that touches nothing).
@@ -30,6 +31,11 @@
  *     round-half-to-even of that quotient, clamped to [-128, 127].
  *   - The floor 1e-8 (the binary32 value 0x322BCC77) is applied to every
  *     maximum that is divided by, and to s.
+ *   - Inputs (activations, weights, bias) must be finite, and every
+ *     quotient x / s finite; the method is not defined on infinities or
+ *     NaNs (their maxima and codes are left unspecified here).
+ *   - Layout: the [.][k] int8 code arrays are row-major, or in 16 x 64
+ *     tiles for the entry points named *_tiled (see sq_tiled_bytes).
  *   - Errors: arguments are checked before anything is enqueued; a negative
  *     status means nothing was enqueued. SQ_ERR_HIP means a launch failed
  *     (earlier launches of the same call may have run). No exception or
