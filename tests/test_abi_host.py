@@ -341,3 +341,27 @@ def test_tiled_entry_errors(L):
     assert p(OK_PTR, OK_PTR, 4, OK_PTR, OK_PTR, 8, 64, None, B.SQ_F32, OK_PTR, 9, None) == B.SQ_ERR_DTYPE
     assert p(OK_PTR, OK_PTR, 4, OK_PTR, OK_PTR, 0, 64, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
     assert p(None, OK_PTR, 4, OK_PTR, OK_PTR, 8, 64, None, B.SQ_F32, OK_PTR, B.SQ_BF16, None) == B.SQ_ERR_ARG
+
+
+def test_tiled_layout_roundtrip_random_shapes(L):
+    """For random shapes: placing every element at the layout formula's
+    address and reading it back with binding.untile is the identity, the
+    placements never collide, and they fill exactly sq_tiled_bytes minus the
+    padding (host only)."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        rows = int(rng.integers(1, 70))
+        k = int(rng.integers(1, 40)) * 16
+        size = L.sq_tiled_bytes(rows, k)
+        r16, k64 = (rows + 15) // 16 * 16, (k + 63) // 64 * 64
+        assert size == r16 * k64
+        a = rng.integers(-128, 128, size=(rows, k)).astype(np.int8)
+        i, j = np.meshgrid(np.arange(rows), np.arange(k), indexing="ij")
+        addr = ((i // 16) * (k64 // 64) + j // 64) * 1024 + (i % 16) * 64 + j % 64
+        assert len(np.unique(addr)) == rows * k and addr.max() < size
+        flat = np.zeros(size, np.int8)
+        flat[addr] = a
+        back = B.untile(torch.from_numpy(flat), rows, k).numpy()
+        assert np.array_equal(back, a)
