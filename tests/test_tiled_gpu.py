@@ -208,6 +208,42 @@ def test_linear_tiled(orc, shape, dtype):
         assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(5, 40, 272), (70, 33, 1040), (300, 129, 528), (16, 1000, 4096)], ids=_id)
+def test_layer_tiled_matches_row(orc, shape, dtype):
+    """SmoothQuantLinear with tiled weights: the same smoothing factor,
+    scales, codes (untiled) and outputs as the row-major layer, bit for bit,
+    through calibrate -> freeze -> forward, a recompute for a new alpha, an
+    empty batch and quantization_error; and the codes equal the oracle's."""
+    m, n, k = shape
+    c = inputs.small(m, n, k, seed=23 + m + n + k, dtype=dtype)
+    bias_dev = None if c.bias is None else up(c.bias)
+    layers = {lay: B.SmoothQuantLinear(up(c.w), bias_dev, alpha=0.5, layout=lay) for lay in ("row", "tiled")}
+    x = up(c.x)
+    for layer in layers.values():
+        layer.calibrate(x[: (m + 1) // 2])
+        layer.calibrate(x[(m + 1) // 2:])
+        assert layer.freeze() == B.SQ_OK
+    row, tiled = layers["row"], layers["tiled"]
+    mx = orc.calibrate(c.x.f32)
+    for alpha in (0.5, 0.25):
+        if alpha != 0.5:
+            for layer in layers.values():
+                assert layer.recompute(alpha) == B.SQ_OK
+        y_row, y_tiled = row.forward(x), tiled.forward(x)
+        torch.cuda.synchronize()
+        s_ref, wq_ref, sw_ref = orc.prepare_weight(c.w.f32, mx, alpha)
+        assert_equal(down(tiled.smooth), s_ref, "smooth")
+        assert_equal(down(tiled.weight_scale), sw_ref, "weight_scale")
+        assert_equal(down(B.untile(tiled.weight_int8, n, k)), wq_ref, "weight codes")
+        assert_equal(down(row.weight_int8), wq_ref, "row-major weight codes")
+        assert_equal(down(y_tiled), down(y_row), f"output, alpha {alpha}")
+    assert tiled.forward(x[:0]).shape == (0, n)
+    assert tiled.quantization_error(x) == row.quantization_error(x)
+    with pytest.raises(ValueError):
+        B.SmoothQuantLinear(up(c.w), layout="columns")
+
+
 # ---------------------------------------------------------------------------
 # Weight-only int8 linear on tiled weights (torchao page
 # "quantization/subclass.py", Int8WeightOnlyQuantizedLinearWeight). The bar

@@ -457,11 +457,22 @@ def sq_w8a8_linear(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_s
 # (SmoothQuantW8A8 in "w8a8_smoothquant.py"). Buffers only; no arithmetic.
 # ---------------------------------------------------------------------------
 class SmoothQuantLinear:
-    """Holds a layer's buffers and drives the ABI in the page's order."""
+    """Holds a layer's buffers and drives the ABI in the page's order.
 
-    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, alpha: float = 0.5):
+    layout "row" keeps the int8 weights as [n][k] row-major and runs the
+    forward as one sq_w8a8_linear call; "tiled" keeps them in 16 x 64 tiles
+    (flat, sq_tiled_bytes(n, k)) and runs the forward as
+    sq_quantize_act_tiled + sq_w8a8_gemm_tiled. Both give the same smoothing
+    factor, scales, codes and outputs, bit for bit; the tiled products are
+    the faster ones."""
+
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, alpha: float = 0.5,
+                 layout: str = "row"):
         if not weight.is_cuda:
             raise ValueError("weight must be a device tensor")
+        if layout not in ("row", "tiled"):
+            raise ValueError(f"layout must be 'row' or 'tiled', not {layout!r}")
+        self.layout = layout
         self.weight = weight.contiguous()
         self.bias = None if bias is None else bias.contiguous()
         self.alpha = float(alpha)
@@ -470,7 +481,10 @@ class SmoothQuantLinear:
         self.calib_max_abs = torch.zeros(k, dtype=torch.float32, device=dev)
         self.calib_count = 0
         self.smooth = torch.ones(k, dtype=torch.float32, device=dev)
-        self.weight_int8 = torch.zeros((n, k), dtype=torch.int8, device=dev)
+        if layout == "tiled":
+            self.weight_int8 = tiled_empty(n, k, dev).zero_()
+        else:
+            self.weight_int8 = torch.zeros((n, k), dtype=torch.int8, device=dev)
         self.weight_scale = torch.ones(n, dtype=torch.float32, device=dev)
         self.weight_max_abs = torch.empty(k, dtype=torch.float32, device=dev)
         self.is_quantized = False
@@ -485,12 +499,20 @@ class SmoothQuantLinear:
     def freeze(self) -> int:
         """Returns SQ_OK, or SQ_WARN_UNCALIBRATED when no batch was seen. The
         weight column max is kept for recompute."""
-        mx = self.calib_max_abs if self.calib_count else None
         sq_weight_col_max(self.weight, self.weight_max_abs)
-        st = sq_recompute_smooth_scale(self.weight, mx, self.weight_max_abs, self.alpha, self.smooth,
-                                       self.weight_int8, self.weight_scale)
+        st = self._quantize_weight()
         self.is_quantized = True
         return st
+
+    def _quantize_weight(self) -> int:
+        mx = self.calib_max_abs if self.calib_count else None
+        if self.layout == "tiled":
+            # the tiled weight preparation takes the weight column max itself
+            # (one more pass over W than the route from the stored maxima)
+            return sq_prepare_weight_tiled(self.weight, mx, self.alpha, self.smooth, self.weight_int8,
+                                           self.weight_scale)
+        return sq_recompute_smooth_scale(self.weight, mx, self.weight_max_abs, self.alpha, self.smooth,
+                                         self.weight_int8, self.weight_scale)
 
     def recompute(self, alpha: float) -> int:
         """recompute_smooth_scale: re-smooth and re-quantise the weights for a
@@ -498,9 +520,7 @@ class SmoothQuantLinear:
         if not self.is_quantized:
             raise RuntimeError("recompute before freeze")
         self.alpha = float(alpha)
-        mx = self.calib_max_abs if self.calib_count else None
-        return sq_recompute_smooth_scale(self.weight, mx, self.weight_max_abs, self.alpha, self.smooth,
-                                         self.weight_int8, self.weight_scale)
+        return self._quantize_weight()
 
     def quantization_error(self, x: torch.Tensor) -> float:
         """||Y_fp - Y_q||_F / max(||Y_fp||_F, 1e-12): the unquantised linear
@@ -524,8 +544,15 @@ class SmoothQuantLinear:
         shape = x.shape
         x2 = x.reshape(-1, shape[-1]).contiguous()
         m, k = x2.shape
-        n = self.weight_int8.shape[0]
+        n = self.weight_scale.shape[0]
         y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
-        ws = torch.empty(max(sq_w8a8_linear_workspace_bytes(m, k), 1), dtype=torch.uint8, device=x.device)
-        sq_w8a8_linear(x2, self.smooth, self.weight_int8, self.weight_scale, self.bias, y, ws)
+        if self.layout == "tiled":
+            if m:
+                x_q = tiled_empty(m, k, x.device)
+                x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+                sq_quantize_act_tiled(x2, self.smooth, x_q, x_scale)
+                sq_w8a8_gemm_tiled(x_q, x_scale, m, self.weight_int8, self.weight_scale, n, k, self.bias, y)
+        else:
+            ws = torch.empty(max(sq_w8a8_linear_workspace_bytes(m, k), 1), dtype=torch.uint8, device=x.device)
+            sq_w8a8_linear(x2, self.smooth, self.weight_int8, self.weight_scale, self.bias, y, ws)
         return y.reshape(*shape[:-1], n)
