@@ -100,8 +100,8 @@ sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k,
  *   w_q[o][j]  = clamp(round_half_even(w~[o][j] / w_scale[o]), -128, 127)
  *   w         [n][k] in wt (F32 or BF16), 16-byte aligned
  *   x_max_abs [k] fp32 from sq_calibrate, or NULL: never calibrated, s = 1
- *             and the call returns SQ_WARN_UNCALIBRATED (the page warns
- *             "using s = 1" in that case)
+ *             and the call returns SQ_WARN_UNCALIBRATED (the page's warning
+ *             for that case announces a fallback to s = 1)
  *   alpha     in [0, 1]
  *   smooth    [k] fp32 out (also used as scratch during the call)
  *   w_q       [n][k] int8 out, 16-byte aligned (also used as scratch for
