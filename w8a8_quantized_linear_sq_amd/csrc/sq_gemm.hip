@@ -13,8 +13,13 @@
 //     32 x 32 tiles of v_mfma_i32_32x32x32_i8 (the 16x16x64 int8 form
 //     measures at half the rate on this chip);
 //   * K advances in BK = 64-byte steps through a ring of 4 LDS stages filled
-//     by direct global -> LDS loads (global_load_lds_dwordx4: no VGPR
-//     staging, no LDS store instructions), issued three steps ahead;
+//     by direct-to-LDS loads (buffer_load_dwordx4 ... lds: no VGPR staging,
+//     no LDS store instructions), issued three steps ahead. On gfx950 a
+//     SIMD that issues vector-memory loads loses MFMA cycles to them; the
+//     buffer form (a descriptor in scalar registers, one 32-bit offset per
+//     lane) costs the MFMA stream fewer of them than the global form (a
+//     64-bit address per lane): 58.6 against 62.2 us at 4096^3, the same
+//     bits;
 //   * a DMA load writes 64 lanes x 16 bytes contiguously, so the LDS rows
 //     (64 bytes) cannot be padded; instead chunk c of row r is stored at
 //     position c ^ swz(r), swz(r) = (r >> 2) & 3, under which the 16-byte
@@ -50,8 +55,8 @@
 //
 // Measured at M = N = K = 4096 (bf16 out): the clock under this load is
 // power-limited to about 1.7 GHz (int8 MFMA at 32 busy cycles per
-// instruction per SIMD), and the main loop keeps the MFMA units about 70%
-// busy; HBM traffic is the per-XCD minimum of the tile order.
+// instruction per SIMD); HBM traffic is the per-XCD minimum of the tile
+// order.
 #include "sq_device.h"
 
 #include <type_traits>
@@ -100,7 +105,23 @@ __device__ __forceinline__ void sched_slice() {
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
+// Word 3 of a raw buffer descriptor (gfx9 layout): a non-zero data format
+// (32-bit), stride 0, so offsets are plain bytes checked against the record
+// count.
+constexpr int kBufferFlags = 0x00020000;
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One direct-to-LDS load of 16 bytes per lane: lane i reads byte voff (its
+// own) of the `bytes`-long record at base (uniform) and writes LDS at dst +
+// 16 i. The descriptor lives in scalar registers. (Kept out of the kernel
+// templates: built inside them, the descriptor type makes the host pass
+// drop the kernels' launch stubs.)
+__device__ __forceinline__ void dma_load16(const int8_t* base, int bytes, int voff, lds_ptr_t dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferFlags),
+                                             dst, 16, voff, 0, 0, 0);
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -154,35 +175,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     // ---- DMA mapping: wave w fills blocks w, w + 4, ...; lane i of a block
     // ---- writes LDS granule i = (row i / 4, position i % 4) and reads the
     // ---- global chunk that position holds.
-    const int8_t* src[LOADS];
+    // ---- The loads are buffer loads (a descriptor in scalar registers over
+    // ---- the block's 16 rows, one 32-bit offset per lane): on gfx950 they
+    // ---- cost the MFMA stream of their SIMD far fewer cycles than global
+    // ---- loads with a 64-bit address per lane.
+    const int8_t* src[LOADS];   // per-lane address (the partial-step tail)
+    const int8_t* gbase[LOADS]; // the block's first byte (uniform)
+    int voff[LOADS];
     int dst[LOADS];
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
         const int blk = wave + NW * q;
+        const bool in_a = blk * kBlockRows < BM;              // the block's 16 rows are all A or all B
         const int row = blk * kBlockRows + lane / kRowLanes;  // row in the A|B stage space
         const int pos = lane % kRowLanes;
         const int chunk = pos ^ swz(row);
+        const int8_t* g;  // first byte of the block's 16 rows (uniform)
         if constexpr (TILED) {
             // the block's 16 rows are one row group; groups past the last
             // (tiles past m or n) read the last one, never stored
-            const int8_t* g;
-            if (row < BM) g = A + (int64_t)min((m0 >> 4) + blk, (m - 1) >> 4) * k * 16;
+            if (in_a) g = A + (int64_t)min((m0 >> 4) + blk, (m - 1) >> 4) * k * 16;
             else g = B + (int64_t)min((n0 >> 4) + blk - BM / kBlockRows, (n - 1) >> 4) * k * 16;
-            src[q] = g + (lane / kRowLanes) * kBK + chunk * 16;
+            voff[q] = (lane / kRowLanes) * kBK + chunk * 16;
         } else {
-            const int8_t* g;
-            if (row < BM) g = A + (int64_t)min(m0 + row, m - 1) * k;
-            else g = B + (int64_t)min(n0 + row - BM, n - 1) * k;
-            src[q] = g + chunk * 16;
+            // rows past m or n are clamped to the last one (never stored);
+            // every lane's row is at or after the block's clamped first row
+            const int r0 = in_a ? min(m0 + blk * kBlockRows, m - 1) : min(n0 + blk * kBlockRows - BM, n - 1);
+            const int r = in_a ? min(m0 + row, m - 1) : min(n0 + row - BM, n - 1);
+            g = (in_a ? A : B) + (int64_t)r0 * k;
+            voff[q] = (r - r0) * k + chunk * 16;
         }
+        src[q] = g + voff[q];
+        gbase[q] = g;
         dst[q] = blk * 1024;
     }
     auto issue_stage = [&](int kt, int buf) {
-        const int64_t kb = TILED ? (int64_t)kt * 1024 : (int64_t)kt * kBK;
+        const int kb = TILED ? kt * 1024 : kt * kBK;
 #pragma unroll
         for (int q = 0; q < LOADS; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)(src[q] + kb), (lds_ptr_t)(smem + buf * STAGE + dst[q]),
-                                             16, 0, 0);
+            // 16 rows of k bytes from the block's first byte: every offset
+            // a stage adds stays below that record count
+            dma_load16(gbase[q], 16 * k, voff[q] + kb, (lds_ptr_t)(smem + buf * STAGE + dst[q]));
     };
     // a last partial step: the same layout through registers, chunks past k
     // zero-filled
