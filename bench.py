@@ -17,7 +17,7 @@ up-projection run the same full step; decode times the per-call path
 (sq_quantize_act_tiled + sq_w8a8_gemm_tiled, which streams the weights for
 m <= 64) on weights prepared once, as a decode step uses them;
 o_proj_per_tensor times the per-tensor variant as its layer runs it
-(sq_quantize_tensor of W and of X, sq_w8a8_gemm_per_tensor; row-major);
+(sq_quantize_tensor_tiled of W and of X, sq_w8a8_gemm_per_tensor_tiled);
 decode_weight_only times the weight-only int8 linear (sq_wo_linear_tiled)
 on the decode shape. --layout row gives the row-major calls throughout.
 
@@ -340,10 +340,8 @@ def main():
     case = _make_case(inputs, spec)
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
-    # the int8 codes in 16 x 64 tiles unless asked not to; the per-tensor
-    # variant quantises W on every call, and its tiled codes kernel costs
-    # what the tiled product saves, so it stays row-major
-    tiled = args.layout == "tiled" and mode != "per_tensor"
+    # the int8 codes in 16 x 64 tiles unless asked not to
+    tiled = args.layout == "tiled"
 
     def bf16(t):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -412,10 +410,15 @@ def main():
     # the timed loop then only repeats the C calls
     for s in sets:
         if mode == "per_tensor":
-            s["call_prep"] = B.prepared(B.sq_quantize_tensor, s["w"], s["wq"], s["tsw"], stream)
-            s["call_act"] = B.prepared(B.sq_quantize_tensor, s["x"], s["xq"], s["tsx"], stream)
-            s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_per_tensor, s["xq"], s["tsx"], s["wq"], s["tsw"], s["bias"],
-                                        s["y"], stream)
+            quant = B.sq_quantize_tensor_tiled if tiled else B.sq_quantize_tensor
+            s["call_prep"] = B.prepared(quant, s["w"], s["wq"], s["tsw"], stream)
+            s["call_act"] = B.prepared(quant, s["x"], s["xq"], s["tsx"], stream)
+            if tiled:
+                s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_per_tensor_tiled, s["xq"], s["tsx"], m, s["wq"], s["tsw"],
+                                            n, k, s["bias"], s["y"], stream)
+            else:
+                s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_per_tensor, s["xq"], s["tsx"], s["wq"], s["tsw"],
+                                            s["bias"], s["y"], stream)
             continue
         if mode == "weight_only":
             s["call_act"] = None
@@ -585,7 +588,8 @@ def main():
     if mode == "full":
         stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_graph_ms["prepare_weight"])
         stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_graph_ms["reset+calibrate"])
-    kernel_name = ("int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)" if mode == "per_tensor"
+    kernel_name = (("int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_per_tensor_tiled)" if tiled
+                    else "int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)") if mode == "per_tensor"
                    else "int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_tiled)" if tiled
                    else "int8 GEMM + fused dequant (sq_w8a8_gemm)")
     if mode == "weight_only":
