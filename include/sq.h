@@ -22,8 +22,11 @@
  *   - Row-major, dense: X is [m][k], W and wq are [n][k], Y is [m][n]
  *     (wq and xq may instead be tiled, below).
  *   - k must be a positive multiple of 16. Every pointer to a [.][k] array
- *     must be 16-byte aligned. m and n may be any size >= 1 (a call with
- *     m == 0 is a no-op that touches nothing).
+ *     must be 16-byte aligned. m and n may be any size from 1 to
+ *     SQ_MAX_ROWS (a call with m == 0 is a no-op that touches nothing); the
+ *     products (sq_w8a8_gemm*, sq_w8a8_linear, sq_reference_linear) also
+ *     return SQ_ERR_SHAPE when ceil(m / 128) * ceil(n / 128) exceeds
+ *     SQ_MAX_TILES (an output of more than about 1.4e11 elements).
  *   - Floating-point input types: SQ_F32 or SQ_BF16 (widened exactly to
  *     fp32). All scale and code arithmetic is IEEE binary32 with
  *     round-to-nearest-even, every quotient one correctly rounded division
@@ -70,6 +73,11 @@ typedef enum {
 
 /* Largest k the kernels accept (one token row of X~ is held on chip). */
 #define SQ_MAX_K 16384
+/* Largest row count (m, n, rows) any entry point accepts: the kernels count
+ * rows, tiles and row groups in 32-bit integers. */
+#define SQ_MAX_ROWS (1LL << 30)
+/* Largest number of 128 x 128 output tiles of one product. */
+#define SQ_MAX_TILES ((1LL << 23) - 1)
 
 /*
  * sq_calibrate -- running per-input-channel max of |X| over calibration rows.

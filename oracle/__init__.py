@@ -32,10 +32,18 @@ CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
           "-shared", "-fopenmp", "-Wall", "-Wextra"]
 
 
-def build(out_path: str = _LIB_PATH, mutant: int = 0) -> str:
+# AddressSanitizer and UndefinedBehaviorSanitizer for a checked CPU build
+# (the sanitizer runtimes must then be preloaded into the host process).
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out_path: str = _LIB_PATH, mutant: int = 0, sanitize: bool = False) -> str:
     """Compile the oracle with gcc. ``mutant`` > 0 plants one deliberate
-    mistake (the MUTANT sites in sq_oracle.c) for the pin-sensitivity tests."""
-    cmd = ["gcc", *CFLAGS, f"-DSQO_MUTANT={int(mutant)}", _SRC, "-o", out_path, "-lm"]
+    mistake (the MUTANT sites in sq_oracle.c) for the pin-sensitivity tests;
+    ``sanitize`` builds it with AddressSanitizer and UBSan."""
+    flags = [f for f in CFLAGS if not (sanitize and f == "-fopenmp")]
+    cmd = ["gcc", *flags, *(SANITIZE if sanitize else []), f"-DSQO_MUTANT={int(mutant)}", _SRC, "-o",
+           out_path, "-lm"]
     subprocess.run(cmd, check=True)
     return out_path
 

@@ -124,7 +124,15 @@ static double sqo_pow(double x, double a)
     if (a == 0.5) return sqrt(x);
     if (a == 0.25) return sqrt(sqrt(x));
     if (a == 0.75) return sqrt(x) * sqrt(sqrt(x));
+#if SQO_MUTANT == 20
+    /* MUTANT 20: base and exponent passed the wrong way round. */
+    return pow(a, x);
+#elif SQO_MUTANT == 21
+    /* MUTANT 21: the complementary exponent 1 - a. */
+    return pow(x, 1.0 - a);
+#else
     return pow(x, a);
+#endif
 }
 
 /* ---------------------------------------------------------------------
@@ -468,34 +476,4 @@ void sqo_f64_to_bf16(const double* v, int64_t count, uint16_t* out)
         memcpy(&bits, &f, 4);
         out[i] = (uint16_t)(sign | ((bits >> 16) & 0x7FFFu));
     }
-}
-
-/* ---------------------------------------------------------------------
- * One-call composition of the whole frozen path for convenience of the
- * tests and the CPU baseline. All arrays are caller-owned.
- *   x      [m*k]  activations (fp32 values; bf16 inputs widened)
- *   w      [n*k]  weights
- *   bias   [n]    or NULL
- *   calib  [rc*k] calibration rows, or NULL (R6)
- * Outputs: mx[k], s[k], wq[n*k], sw[n], xq[m*k], sx[m], acc[m*n], y[m*n].
- * Scratch: ws[max(m,n)*k] fp32.
- * Returns the int32 overflow count from sqo_int_gemm.
- * ------------------------------------------------------------------ */
-int64_t sqo_linear(const float* x, const float* w, const float* bias,
-                   const float* calib, int64_t rc, int64_t m, int64_t n,
-                   int64_t k, float alpha, float* mx, float* mw, float* s,
-                   int8_t* wq, float* sw, int8_t* xq, float* sx, int32_t* acc,
-                   double* y, float* ws)
-{
-    for (int64_t j = 0; j < k; ++j) mx[j] = 0.0f;
-    if (calib) sqo_calibrate(calib, rc, k, mx);
-    sqo_weight_col_max(w, n, k, mw);
-    sqo_smoothing_factor(calib ? mx : NULL, mw, alpha, k, s);
-    sqo_smooth_weight(w, s, n, k, ws);
-    sqo_quantize_rows(ws, n, k, wq, sw);
-    sqo_smooth_act(x, s, m, k, ws);
-    sqo_quantize_rows(ws, m, k, xq, sx);
-    int64_t ov = sqo_int_gemm(xq, wq, m, n, k, acc);
-    sqo_dequant(acc, sx, sw, bias, m, n, y);
-    return ov;
 }

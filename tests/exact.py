@@ -102,3 +102,30 @@ def rn_f32_root(x: Fraction, num: int, den: int, extra_bits: int = 96) -> Fracti
 
 
 FLOOR = rn_f32(Fraction(1, 10 ** 8))  # the floor 1e-8 as a binary32 number
+
+
+def pow_enclosure(x: Fraction, a: Fraction, digits: int = 60) -> tuple[Fraction, Fraction]:
+    """An interval [lo, hi] holding x^a (x > 0, a rational), from
+    exp(a ln x) evaluated with the standard library's decimal module at
+    ``digits`` significant digits. decimal's ln and exp are correctly
+    rounded at the working precision, so a relative margin of 10^(10 -
+    digits) is far wider than the evaluation's error."""
+    import decimal
+    ctx = decimal.Context(prec=digits)
+    xd = ctx.divide(decimal.Decimal(x.numerator), decimal.Decimal(x.denominator))
+    ad = ctx.divide(decimal.Decimal(a.numerator), decimal.Decimal(a.denominator))
+    v = Fraction(ctx.exp(ctx.multiply(ad, ctx.ln(xd))))
+    margin = Fraction(1, 10 ** (digits - 10))
+    return v * (1 - margin), v * (1 + margin)
+
+
+def rn_f32_pow(x: Fraction, a: Fraction, guard_bits: int = 44) -> Fraction | None:
+    """The correctly rounded binary32 value of x^a, or None when x^a lies
+    within 2^-guard_bits relative of a rounding boundary between two
+    binary32 numbers. The guard covers a binary64 evaluation that is
+    faithful (within one binary64 ulp, 2^-52) and then rounded to binary32:
+    outside the guard band both routes give the same binary32 number."""
+    lo, hi = pow_enclosure(x, a)
+    g = Fraction(1, 2 ** guard_bits)
+    r_lo, r_hi = rn_f32(lo * (1 - g)), rn_f32(hi * (1 + g))
+    return r_lo if r_lo == r_hi else None

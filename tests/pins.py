@@ -20,8 +20,8 @@ from fractions import Fraction
 
 import numpy as np
 
-from exact import (FLOOR, bf16_bits_of, rn_bf16, rn_f32, rn_f32_root,
-                   round_half_even)
+from exact import (FLOOR, bf16_bits_of, rn_bf16, rn_f32, rn_f32_pow,
+                   rn_f32_root, round_half_even)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -183,6 +183,62 @@ def pin_alpha_quarters(o):
             den = rn_f32_root(Fraction(float(mw[j])), 4 - a_num, 4)
             want = max(rn_f32(num / den), FLOOR)
             assert Fraction(float(s[j])) == want, (alpha, j)
+
+
+def pin_alpha_general(o):
+    """alpha outside {0, 1/4, 1/2, 3/4, 1} (the page's alpha is any value in
+    [0, 1], trained through a sigmoid): each power is the correctly rounded
+    binary32 value of mx^alpha and mw^(1 - alpha), computed independently as
+    exp(a ln x) with the standard library's decimal arithmetic at 60 digits
+    (1 - alpha is exact: alpha is a binary32 number), then one binary32
+    division and the floor. Values whose power lies within 2^-44 relative of
+    a binary32 rounding boundary are skipped (there a binary64 pow, faithful
+    to one binary64 ulp, may round either way); they are counted and must be
+    rare."""
+    x, w = _layer(25)
+    x[:, 5] = 0.0                                   # a floored channel too
+    mx = o.calibrate(x)
+    mw = o.weight_col_max(w)
+    checked = skipped = 0
+    for alpha in (0.1, 0.3, 0.6, 0.7, 0.9, 0.05, 0.999):
+        a = Fraction(float(np.float32(alpha)))
+        s = o.smoothing_factor(mx, mw, float(np.float32(alpha)))
+        for j in range(len(mx)):
+            bx = max(Fraction(float(mx[j])), FLOOR)
+            bw = Fraction(float(mw[j]))
+            num = rn_f32_pow(bx, a)
+            den = rn_f32_pow(bw, 1 - a)
+            if num is None or den is None:
+                skipped += 1
+                continue
+            want = max(rn_f32(num / den), FLOOR)
+            assert Fraction(float(s[j])) == want, (alpha, j, float(s[j]), float(want))
+            checked += 1
+    assert skipped <= checked // 100, (skipped, checked)
+
+
+def pin_alpha_monotone(o):
+    """s_j = mx^alpha / mw^(1 - alpha) = exp(alpha (ln mx + ln mw)) / mw is
+    monotone in alpha: non-decreasing where mx mw > 1, non-increasing where
+    mx mw < 1. Across a sweep that mixes the closed-form exponents and the
+    general ones, each step may move against that direction by at most the
+    three binary32 roundings (2^-22 relative), and s passes through the
+    closed-form values at alpha = 0 (1 / mw) and 1 (mx)."""
+    x, w = _layer(26, k=64)
+    x[:, 9] *= np.float32(1e4)                      # mx mw well above 1
+    mx = o.calibrate(x)
+    mw = o.weight_col_max(w)
+    alphas = [0.0, 0.05, 0.1, 0.25, 0.3, 0.4, 0.5, 0.6, 0.7, 0.75, 0.8, 0.9, 1.0]
+    ss = np.stack([o.smoothing_factor(mx, mw, a).astype(np.float64) for a in alphas])
+    assert np.array_equal(ss[0], (np.float32(1.0) / mw).astype(np.float64))
+    assert np.array_equal(ss[-1], mx.astype(np.float64))
+    prod = mx.astype(np.float64) * mw.astype(np.float64)
+    slack = 2.0 ** -22
+    up = prod > 1.0
+    assert up.any() and (~up).any()
+    d = np.diff(ss, axis=0)
+    assert np.all(d[:, up] >= -slack * ss[1:, up])
+    assert np.all(d[:, ~up] <= slack * ss[1:, ~up])
 
 
 # ---------------------------------------------------------------------------

@@ -365,3 +365,38 @@ def test_tiled_layout_roundtrip_random_shapes(L):
         flat[addr] = a
         back = B.untile(torch.from_numpy(flat), rows, k).numpy()
         assert np.array_equal(back, a)
+
+
+def test_size_limits(L):
+    """Row counts above SQ_MAX_ROWS, and products with more than
+    SQ_MAX_TILES output tiles of 128 x 128, return SQ_ERR_SHAPE before
+    anything is launched (the kernels count rows and tiles in int32)."""
+    big, over = B.SQ_MAX_ROWS, B.SQ_MAX_ROWS + 1
+    P = OK_PTR
+    assert L.sq_calibrate(P, B.SQ_BF16, over, 64, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_calibrate(P, B.SQ_BF16, 1 << 31, 64, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_prepare_weight(P, B.SQ_BF16, over, 64, P, 0.5, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_prepare_weight_tiled(P, B.SQ_BF16, 1 << 31, 64, P, 0.5, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_quantize_act(P, B.SQ_BF16, over, 64, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_quantize_act_tiled(P, B.SQ_BF16, 1 << 31, 64, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_weight_col_max(P, B.SQ_BF16, over, 64, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_quantize_weight(P, B.SQ_BF16, over, 64, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_recompute_smooth_scale(P, B.SQ_BF16, over, 64, P, P, 0.5, P, P, P, None) == B.SQ_ERR_SHAPE
+    assert L.sq_quantize_tensor_tiled(P, B.SQ_BF16, over, 64, P, P, None) == B.SQ_ERR_SHAPE
+    for fn in (L.sq_w8a8_gemm, L.sq_w8a8_gemm_tiled, L.sq_w8a8_gemm_per_tensor, L.sq_w8a8_gemm_per_tensor_tiled):
+        # 2^31 tokens or channels (the value that wrapped negative in int32)
+        assert fn(P, P, 1 << 31, P, P, 8, 64, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+        assert fn(P, P, 8, P, P, 1 << 31, 64, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+        assert fn(P, P, 4, P, P, over, 64, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+        # each size allowed, the output too large for the tile grid
+        assert fn(P, P, big, P, P, big, 64, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+        side = 128 * 2897                     # 2897^2 = 8392609 > 2^23 - 1 tiles
+        assert fn(P, P, side, P, P, side, 64, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+    for fn in (L.sq_wo_linear, L.sq_wo_linear_tiled):
+        assert fn(P, B.SQ_BF16, 4, 64, P, P, 1 << 31, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+        assert fn(P, B.SQ_BF16, over, 64, P, P, 8, None, B.SQ_F32, P, B.SQ_BF16, None) == B.SQ_ERR_SHAPE
+    assert L.sq_reference_linear(P, B.SQ_BF16, big, 64, P, big, None, B.SQ_F32, P, B.SQ_F32,
+                                 None) == B.SQ_ERR_SHAPE
+    ws = L.sq_w8a8_linear_workspace_bytes(4, 64)
+    assert L.sq_w8a8_linear(P, B.SQ_BF16, 4, 64, P, P, P, 1 << 31, None, P, B.SQ_BF16, P, ws,
+                            None) == B.SQ_ERR_SHAPE

@@ -23,6 +23,8 @@ MUTANTS = {
     17: "weight-only linear drops the bias",
     18: "reference linear drops the last k term",
     19: "relative error measured against y_q",
+    20: "general-alpha power with base and exponent swapped",
+    21: "general-alpha power with the complementary exponent",
 }
 
 

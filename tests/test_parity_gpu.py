@@ -257,8 +257,78 @@ def test_gemm_dequant(orc, shape, out, bias):
         scale = scale + np.abs(bias_f)[None, :]
     if out == "f32":
         assert_f32_rel(down(y), yref, scale)
+    elif bias_f is None:
+        # without a bias nothing cancels: the strict 1-ulp bar applies
+        assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref))
     else:
         assert_bf16_within_one_ulp(down(y), orc.to_bf16(yref), yref, scale)
+
+
+# ---------------------------------------------------------------------------
+# Degenerate weights: an all-zero output row (its scale is the floor over
+# 127, 0x2EAD26C5, and its codes are zero: quantize_per_channel_symmetric's
+# clamp(min=1e-8)) and an all-zero input column (its maximum is the floor),
+# through every entry point that prepares weights
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("alpha", [0.5, 0.3, None], ids=lambda a: f"a{a}")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(24, 40, 272), (70, 300, 1040)], ids=_id)
+def test_zero_weight_rows_and_columns(orc, shape, dtype, alpha):
+    m, n, k = shape
+    c = _case(shape, dtype)
+    wf = c.w.f32.copy()
+    wf[3] = 0.0                      # all-zero output rows
+    wf[n - 1] = 0.0
+    wf[:, 5] = 0.0                   # all-zero input columns
+    wf[:, k - 16:k - 13] = 0.0
+    wt = inputs.Tensor(wf, None if c.w.bits is None else inputs.bf16_bits(wf))
+    xf = c.x.f32.copy()
+    xf[:, k - 16] = 0.0              # one of them never seen in calibration either
+    mx = orc.calibrate(xf)
+    a = 0.5 if alpha is None else alpha
+    mxa = None if alpha is None else mx
+    mw_ref = orc.weight_col_max(wf)
+    s_ref = orc.smoothing_factor(mxa, mw_ref, a)
+    zero_scale = np.array([0x2EAD26C5], np.uint32).view(np.float32)[0]
+
+    def check(s_dev, wq_np, ws_dev, what):
+        s_gpu = down(s_dev)
+        if alpha == 0.3:
+            ulps = np.abs(s_gpu.view(np.int32).astype(np.int64) - s_ref.view(np.int32))
+            assert ulps.max() <= 1, what
+        else:
+            assert_equal(s_gpu, s_ref, f"s ({what})")
+        wq_ref, ws_ref = orc.quantize_rows(orc.smooth_weight(wf, s_gpu))
+        assert ws_ref[3] == zero_scale and ws_ref[n - 1] == zero_scale
+        assert not wq_ref[3].any() and not wq_ref[n - 1].any()
+        assert not wq_ref[:, 5].any() and not wq_ref[:, k - 16:k - 13].any()
+        assert_equal(down(ws_dev), ws_ref, f"w_scale ({what})")
+        assert_equal(wq_np, wq_ref, f"w_q ({what})")
+
+    w_dev = up(wt)
+    mx_dev = None if mxa is None else up(mx)
+    # sq_prepare_weight and its tiled twin
+    s1, wq1, ws1 = _zeros(k, torch.float32), _zeros((n, k), torch.int8), _zeros(n, torch.float32)
+    B.sq_prepare_weight(w_dev, mx_dev, a, s1, wq1, ws1)
+    s2, wq2, ws2 = _zeros(k, torch.float32), B.tiled_empty(n, k, DEV), _zeros(n, torch.float32)
+    B.sq_prepare_weight_tiled(w_dev, mx_dev, a, s2, wq2, ws2)
+    # the split calls: column max, smoothing factor, weight codes
+    mw = _zeros(k, torch.float32)
+    B.sq_weight_col_max(w_dev, mw)
+    s3 = _zeros(k, torch.float32)
+    B.sq_smoothing_factor(mx_dev, mw, a, s3)
+    wq3, ws3 = _zeros((n, k), torch.int8), _zeros(n, torch.float32)
+    B.sq_quantize_weight(w_dev, s3, wq3, ws3)
+    # re-smoothing from the stored maxima
+    s4, wq4, ws4 = _zeros(k, torch.float32), _zeros((n, k), torch.int8), _zeros(n, torch.float32)
+    B.sq_recompute_smooth_scale(w_dev, mx_dev, mw, a, s4, wq4, ws4)
+    torch.cuda.synchronize()
+    assert_equal(down(mw), mw_ref, "weight column max")
+    assert mw_ref[5] == np.float32(1e-8)
+    check(s1, down(wq1), ws1, "prepare")
+    check(s2, down(B.untile(wq2, n, k)), ws2, "prepare tiled")
+    check(s3, down(wq3), ws3, "split calls")
+    check(s4, down(wq4), ws4, "recompute")
 
 
 # ---------------------------------------------------------------------------
@@ -355,6 +425,38 @@ def test_layer_lifecycle():
     fresh = B.SmoothQuantLinear(up(c.w), None)
     assert fresh.freeze() == B.SQ_WARN_UNCALIBRATED
     assert torch.all(fresh.smooth == 1.0)
+
+
+@pytest.mark.parametrize("layout", ["row", "tiled"])
+def test_layer_fp32_weights_bf16_activations(orc, layout):
+    """fp32 weights and bias with bf16 activations: the forward takes the
+    bias in its own type on both layouts (the same bits), and
+    quantization_error widens the bf16 activations (exactly) rather than
+    narrowing the weights."""
+    c32 = inputs.small(40, 24, 272, seed=91, dtype="f32", bias=True)
+    cb = inputs.small(40, 24, 272, seed=91, dtype="bf16", bias=False)
+    x_bits = cb.x.bits
+    x_f = cb.x.f32                                  # bf16 values, exactly
+    layer = B.SmoothQuantLinear(up(c32.w), up(c32.bias), alpha=0.5, layout=layout)
+    layer.calibrate(up(x_bits))
+    assert layer.freeze() == B.SQ_OK
+    y = layer.forward(up(x_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    mx = orc.calibrate(x_f)
+    s, wq, sw = orc.prepare_weight(c32.w.f32, mx, 0.5)
+    xq, sx, acc, yref = orc.linear(x_f, s, wq, sw, c32.bias.f32)
+    scale = np.abs(acc.astype(np.float64) * sx[:, None] * sw[None, :]) + np.abs(c32.bias.f32)[None, :]
+    assert_f32_rel(down(y), yref, scale)
+    # the bound the two outputs' own tolerances give (as for the layer's
+    # quantization_error below): y_q within 1e-6 (|acc sx sw| + |bias|),
+    # y_fp (fp32 operands) within (k + 1) 2^-24 sum|x w| + 2^-24 |y_fp|
+    got = layer.quantization_error(up(x_bits))
+    yfp = orc.reference_linear(x_f, c32.w.f32, c32.bias.f32)
+    want = orc.relative_error(yfp, yref)[0]
+    bfp = (c32.k + 1) * 2.0 ** -24 * (np.abs(x_f.astype(np.float64)) @ np.abs(c32.w.f32.astype(np.float64)).T)
+    bfp = bfp + 2.0 ** -24 * np.abs(yfp)
+    tol = (np.linalg.norm(1e-6 * scale) + np.linalg.norm(bfp)) / np.linalg.norm(yfp)
+    assert abs(got - want) <= tol + 1e-12, (got, want, tol)
 
 
 def test_hardware_reciprocal_is_correctly_rounded():

@@ -24,6 +24,8 @@ SQ_OK, SQ_WARN_UNCALIBRATED = 0, 1
 SQ_ERR_ARG, SQ_ERR_SHAPE, SQ_ERR_DTYPE, SQ_ERR_ALIGN, SQ_ERR_WORKSPACE, SQ_ERR_HIP = -1, -2, -3, -4, -5, -6
 SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
 SQ_MAX_K = 16384
+SQ_MAX_ROWS = 1 << 30
+SQ_MAX_TILES = (1 << 23) - 1
 
 
 class SQError(RuntimeError):
@@ -460,7 +462,8 @@ class SmoothQuantLinear:
     """Holds a layer's buffers and drives the ABI in the page's order.
 
     layout "row" keeps the int8 weights as [n][k] row-major and runs the
-    forward as one sq_w8a8_linear call; "tiled" keeps them in 16 x 64 tiles
+    forward as one sq_w8a8_linear call (sq_quantize_act + sq_w8a8_gemm when
+    the bias type differs from x's); "tiled" keeps them in 16 x 64 tiles
     (flat, sq_tiled_bytes(n, k)) and runs the forward as
     sq_quantize_act_tiled + sq_w8a8_gemm_tiled. Both give the same smoothing
     factor, scales, codes and outputs, bit for bit; the tiled products are
@@ -528,9 +531,14 @@ class SmoothQuantLinear:
         if not self.is_quantized:
             raise RuntimeError("quantization_error before freeze")
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
-        w = self.weight if self.weight.dtype == x2.dtype else self.weight.to(x2.dtype)
+        w = self.weight
+        xr = x2
+        if w.dtype != x2.dtype:
+            # the reference takes one operand type: widen the bf16 side to
+            # fp32 (exact), never narrow the other
+            xr, w = x2.float(), w.float()
         y_fp = torch.empty((x2.shape[0], w.shape[0]), dtype=torch.float32, device=x2.device)
-        sq_reference_linear(x2, w, self.bias, y_fp)
+        sq_reference_linear(xr, w, self.bias, y_fp)
         y_q = self.forward(x2, out_dtype=torch.float32)
         ws = torch.empty(max(sq_relative_error_workspace_bytes(y_fp.numel()), 8), dtype=torch.uint8,
                          device=x2.device)
@@ -552,6 +560,14 @@ class SmoothQuantLinear:
                 x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
                 sq_quantize_act_tiled(x2, self.smooth, x_q, x_scale)
                 sq_w8a8_gemm_tiled(x_q, x_scale, m, self.weight_int8, self.weight_scale, n, k, self.bias, y)
+        elif self.bias is not None and self.bias.dtype != x2.dtype:
+            # sq_w8a8_linear takes the bias in x's type; another bias type
+            # goes through the two calls it is made of, which take its type
+            if m:
+                x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+                x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+                sq_quantize_act(x2, self.smooth, x_q, x_scale)
+                sq_w8a8_gemm(x_q, x_scale, self.weight_int8, self.weight_scale, self.bias, y)
         else:
             ws = torch.empty(max(sq_w8a8_linear_workspace_bytes(m, k), 1), dtype=torch.uint8, device=x.device)
             sq_w8a8_linear(x2, self.smooth, self.weight_int8, self.weight_scale, self.bias, y, ws)

@@ -12,7 +12,18 @@ bool fp_in(sq_dtype t) { return t == SQ_F32 || t == SQ_BF16; }
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-constexpr int64_t kMaxRows = (int64_t)1 << 31;  // m, n, rows: int32 tile indexing
+// m, n, rows: the kernels index rows, tiles and row groups in int32, adding
+// at most a tile (256) or a row group to a row count, so every count stays
+// at or below 2^30
+constexpr int64_t kMaxRows = SQ_MAX_ROWS;
+// output tiles of the MFMA-tile product (counted at its smallest tile,
+// 128 x 128): one workgroup of up to 512 threads each, and a launch's grid
+// times its block size must stay below 2^32
+constexpr int64_t kMaxTiles = SQ_MAX_TILES;
+
+bool tiles_fit(int64_t m, int64_t n) {
+    return ((m + 127) / 128) * ((n + 127) / 128) <= kMaxTiles;
+}
 
 sq_status launched(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
 
@@ -106,7 +117,7 @@ static sq_status check_gemm(const int8_t* x_q, const float* x_scale, int64_t m, 
                             sq_dtype bias_t, const void* y, sq_dtype yt) {
     if (!(yt == SQ_F32 || yt == SQ_BF16 || yt == SQ_I32)) return SQ_ERR_DTYPE;
     if (bias && !fp_in(bias_t)) return SQ_ERR_DTYPE;
-    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows || !tiles_fit(m, n)) return SQ_ERR_SHAPE;
     sq_status st = check_k(k);
     if (st != SQ_OK) return st;
     if (m == 0) return SQ_OK;
@@ -323,7 +334,7 @@ sq_status sq_reference_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, 
     if (!fp_in(xt)) return SQ_ERR_DTYPE;
     if (!(yt == SQ_F32 || yt == SQ_BF16)) return SQ_ERR_DTYPE;
     if (bias && !fp_in(bias_t)) return SQ_ERR_DTYPE;
-    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows) return SQ_ERR_SHAPE;
+    if (m < 0 || m > kMaxRows || n <= 0 || n > kMaxRows || !tiles_fit(m, n)) return SQ_ERR_SHAPE;
     sq_status st = check_k(k);
     if (st != SQ_OK) return st;
     if (m == 0) return SQ_OK;

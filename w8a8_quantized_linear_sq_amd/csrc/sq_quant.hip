@@ -253,7 +253,12 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 //   q[j]  = round_half_even(v[j] / scale)
 //
 // Division. For a binary32 quotient a / b the kernels use y = RN(1/b),
-// q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0). On gfx950 q1 equals the
+// q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0): Markstein's correction
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", IBM J. Res. Dev. 34(1), 1990). With y the
+// correctly rounded reciprocal and q0 within an ulp of a / b, the residual
+// a - q0 b is exact in one fma and q0 + residual * y rounds to the correctly
+// rounded quotient. Here that is not taken on trust: on gfx950 q1 equals the
 // IEEE quotient RN(a/b) for every pair of binary32 significands (2^46
 // pairs, checked on the device by sq_selfcheck_division); as every step is
 // one correctly rounded operation, powers of two scale it exactly, so it
@@ -290,7 +295,8 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
 // RN(1/s) for s in [2^-40, 2^40): the hardware reciprocal refined by one
-// Newton step; on gfx950 it equals the IEEE quotient 1/s for every binary32
+// Newton-Raphson step for 1/s in its fma form, r + r (1 - s r); on gfx950 it
+// equals the IEEE quotient 1/s for every binary32
 // s in [2^-100, 2^100) (sq_selfcheck_reciprocal). Elsewhere NaN, which fails
 // every guard below.
 __device__ __forceinline__ float recip_rn(float s) {
