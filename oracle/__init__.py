@@ -69,6 +69,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "sqo_f64_to_bf16": ([_P, _I64, _P], None),
         "sqo_reference_linear": ([_P, _P, _P, _I64, _I64, _I64, _P], None),
         "sqo_relative_error": ([_P, _P, _I64, _P], ctypes.c_double),
+        "sqo_alpha_from_eta": ([ctypes.c_float], ctypes.c_float),
+        "sqo_eta_from_alpha": ([ctypes.c_double], ctypes.c_float),
+        "sqo_ste_backward": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I64,
+                              _P, _P, _P, _P, _P], None),
+        "sqo_aux_loss_grad": ([_P, _P, _I64, _P], ctypes.c_double),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -258,6 +263,58 @@ class Oracle:
         out = np.empty(y.shape, np.uint16)
         self.lib.sqo_f64_to_bf16(self._ptr(y), y.size, self._ptr(out))
         return out
+
+    # -- the learnable alpha and the straight-through backward ---------------
+    def alpha_from_eta(self, eta: float) -> np.float32:
+        """SmoothQuantW8A8.alpha: sigmoid(eta) in binary64, rounded to binary32."""
+        return np.float32(self.lib.sqo_alpha_from_eta(float(np.float32(eta))))
+
+    def eta_from_alpha(self, alpha: float) -> np.float32:
+        """SmoothQuantW8A8.__init__: log(a / max(1e-6, 1 - a)) stored as binary32."""
+        return np.float32(self.lib.sqo_eta_from_alpha(float(alpha)))
+
+    def ste_backward(self, dy, x, w, s, xq, sx, wq, sw, mx, mw, alpha):
+        """The straight-through backward of the quantized forward (binary64):
+        returns dict(dx, dw, db, ds, dalpha, deta)."""
+        dy, x, w, s = self._f32(dy), self._f32(x), self._f32(w), self._f32(s)
+        xq = np.ascontiguousarray(xq, np.int8)
+        wq = np.ascontiguousarray(wq, np.int8)
+        sx, sw, mx, mw = self._f32(sx), self._f32(sw), self._f32(mx), self._f32(mw)
+        m, k = x.shape
+        n = w.shape[0]
+        assert dy.shape == (m, n) and w.shape == (n, k) and xq.shape == (m, k) and wq.shape == (n, k)
+        dx = np.empty((m, k), np.float64)
+        dw = np.empty((n, k), np.float64)
+        db = np.empty(n, np.float64)
+        ds = np.empty(k, np.float64)
+        da = np.empty(2, np.float64)
+        self.lib.sqo_ste_backward(self._ptr(dy), self._ptr(x), self._ptr(w), self._ptr(s), self._ptr(xq),
+                                  self._ptr(sx), self._ptr(wq), self._ptr(sw), self._ptr(mx), self._ptr(mw),
+                                  float(np.float32(alpha)), m, n, k, self._ptr(dx), self._ptr(dw), self._ptr(db),
+                                  self._ptr(ds), self._ptr(da))
+        return dict(dx=dx, dw=dw, db=db, ds=ds, dalpha=float(da[0]), deta=float(da[1]))
+
+    def aux_loss_grad(self, y_fp, y_q):
+        """The docstring's auxiliary loss ||y_fp - y_q||^2 / ||y_fp||^2 and its
+        gradient at y_q (binary64): returns (loss, dL/dy_q)."""
+        a = np.ascontiguousarray(y_fp, np.float64)
+        b = np.ascontiguousarray(y_q, np.float64)
+        assert a.shape == b.shape
+        g = np.empty(a.shape, np.float64)
+        loss = self.lib.sqo_aux_loss_grad(self._ptr(a), self._ptr(b), a.size, self._ptr(g))
+        return float(loss), g
+
+    def training_step(self, x, w, bias, mx, eta, dy):
+        """The quantized forward at alpha = sigmoid(eta) and its
+        straight-through backward for the upstream gradient dy: returns the
+        forward's quantities and the gradients (all from the oracle)."""
+        alpha = self.alpha_from_eta(eta)
+        mw = self.weight_col_max(w)
+        s = self.smoothing_factor(mx, mw, alpha)
+        wq, sw = self.quantize_rows(self.smooth_weight(w, s))
+        xq, sx, acc, y = self.linear(x, s, wq, sw, bias)
+        g = self.ste_backward(dy, x, w, s, xq, sx, wq, sw, mx, mw, alpha)
+        return dict(alpha=alpha, mw=mw, s=s, wq=wq, sw=sw, xq=xq, sx=sx, y=y, **g)
 
     # -- compositions ---------------------------------------------------------
     def prepare_weight(self, w, mx, alpha: float):

@@ -477,3 +477,172 @@ void sqo_f64_to_bf16(const double* v, int64_t count, uint16_t* out)
         out[i] = (uint16_t)(sign | ((bits >> 16) & 0x7FFFu));
     }
 }
+
+/* =====================================================================
+ * The learnable alpha and the straight-through backward (page
+ * "w8a8_smoothquant.py": the module docstring's V5 notes, STEQuantize,
+ * ste_quantize, SmoothQuantW8A8.alpha / __init__ / forward).
+ *
+ * alpha = sigmoid(eta) with eta a trained parameter. In the quantized
+ * forward s(alpha) is recomputed from the stored maxima, X~ = X / s and
+ * W~ = W * s are quantised with round / clamp, and the straight-through
+ * estimator passes the gradient of the dequantised operands to X~ and W~
+ * unchanged (no gradient reaches the scales: STEQuantize returns none for
+ * them). With Y = Xd Wd^T + b, Xd[t][j] = xq[t][j] sx[t] and
+ * Wd[o][j] = wq[o][j] sw[o]:
+ *   gX[t][j] = sum_o dy[t][o] Wd[o][j]          (the gradient at X~)
+ *   gW[o][j] = sum_t dy[t][o] Xd[t][j]          (the gradient at W~)
+ *   dx[t][j] = gX[t][j] / s_j                   (X~ = X / s)
+ *   dw[o][j] = gW[o][j] * s_j                   (W~ = W * s)
+ *   db[o]    = sum_t dy[t][o]
+ *   ds_j     = sum_o gW[o][j] w[o][j] - sum_t gX[t][j] x[t][j] / s_j^2
+ * s = max(s_raw, 1e-8): the gradient passes the floor only where
+ * s_raw >= 1e-8 (a clamp passes its gradient inside its range). With
+ * s_raw = mx^alpha / mw^(1 - alpha) (both maxima floored, neither
+ * differentiated: the activation maximum is a stored buffer and the weight
+ * maximum is taken on detached weights),
+ *   d s_raw / d alpha = s_raw (ln mx + ln mw)
+ *   dalpha = sum_j [s_raw_j >= 1e-8] ds_j s_raw_j (ln mx_j + ln mw_j)
+ *   deta   = dalpha alpha (1 - alpha)           (sigmoid' = a (1 - a))
+ * Everything here is binary64 on binary32 inputs; s_raw is the binary32
+ * quotient of sqo_smoothing_factor before its floor.
+ * ===================================================================== */
+
+/* SmoothQuantW8A8.alpha: sigmoid(eta), taken in binary64 and rounded once
+ * to binary32 (the page holds eta and alpha as fp32 tensors). */
+float sqo_alpha_from_eta(float eta)
+{
+    const double e = (double)eta;
+#if SQO_MUTANT == 22
+    /* MUTANT 22: the logistic function of -eta. */
+    return (float)(1.0 / (1.0 + exp(e)));
+#else
+    return (float)(1.0 / (1.0 + exp(-e)));
+#endif
+}
+
+/* SmoothQuantW8A8.__init__: eta = log(a / max(1e-6, 1 - a)) for an initial
+ * alpha a, in binary64 (Python floats), stored as binary32. */
+float sqo_eta_from_alpha(double a)
+{
+    const double d = 1.0 - a;
+    return (float)log(a / (d > 1e-6 ? d : 1e-6));
+}
+
+/* The binary32 quotient s_raw_j = f32(P(mx_j, alpha)) / f32(P(mw_j,
+ * 1 - alpha)) of sqo_smoothing_factor, before its floor (mx floored at
+ * 1e-8 first; mw is already floored). */
+static float sqo_smooth_raw(float mxj, float mwj, float alpha)
+{
+    const float mx = fmax_f(mxj, SQO_FLOOR);
+    const float num = (float)sqo_pow((double)mx, (double)alpha);
+    const float den = (float)sqo_pow((double)mwj, 1.0 - (double)alpha);
+    return num / den;
+}
+
+/* ---------------------------------------------------------------------
+ * The straight-through backward of the quantized forward.
+ *   dy   [m][n]  gradient of the loss at Y (fp32 values)
+ *   x    [m][k]  the forward's activations X; w [n][k] its weights W
+ *   s    [k]     the forward's smoothing factor (floored)
+ *   xq, sx       per-token codes and scales of X / s (the forward's)
+ *   wq, sw       per-output-channel codes and scales of W * s
+ *   mx   [k]     stored activation maxima; mw [k] floored weight maxima
+ *   alpha        the forward's alpha (binary32)
+ * Outputs (binary64): dx [m][k], dw [n][k], db [n], ds [k], and
+ * dalpha_deta[0] = dalpha, dalpha_deta[1] = deta.
+ * ------------------------------------------------------------------ */
+void sqo_ste_backward(const float* dy, const float* x, const float* w, const float* s,
+                      const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                      const float* mx, const float* mw, float alpha, int64_t m, int64_t n,
+                      int64_t k, double* dx, double* dw, double* db, double* ds,
+                      double* dalpha_deta)
+{
+    /* gX and gW (in dx and dw first) */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            double acc = 0.0;
+            for (int64_t o = 0; o < n; ++o)
+                acc += (double)dy[t * n + o] * ((double)wq[o * k + j] * (double)sw[o]);
+            dx[t * k + j] = acc;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < n; ++o)
+        for (int64_t j = 0; j < k; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < m; ++t)
+#if SQO_MUTANT == 23
+                /* MUTANT 23: the activation scale of the wrong token. */
+                acc += (double)dy[t * n + o] * ((double)xq[t * k + j] * (double)sx[(t + 1) % m]);
+#else
+                acc += (double)dy[t * n + o] * ((double)xq[t * k + j] * (double)sx[t]);
+#endif
+            dw[o * k + j] = acc;
+        }
+    for (int64_t o = 0; o < n; ++o) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < m; ++t) acc += (double)dy[t * n + o];
+        db[o] = acc;
+    }
+    /* ds from the two smoothing maps, then dx, dw through them */
+    for (int64_t j = 0; j < k; ++j) {
+        double from_w = 0.0, from_x = 0.0;
+        for (int64_t o = 0; o < n; ++o) from_w += dw[o * k + j] * (double)w[o * k + j];
+        for (int64_t t = 0; t < m; ++t) from_x += dx[t * k + j] * (double)x[t * k + j];
+#if SQO_MUTANT == 24
+        /* MUTANT 24: X / s differentiated as if it were X * s. */
+        ds[j] = from_w + from_x;
+#else
+        ds[j] = from_w - from_x / ((double)s[j] * (double)s[j]);
+#endif
+    }
+    for (int64_t t = 0; t < m; ++t)
+        for (int64_t j = 0; j < k; ++j) dx[t * k + j] /= (double)s[j];
+    for (int64_t o = 0; o < n; ++o)
+        for (int64_t j = 0; j < k; ++j) dw[o * k + j] *= (double)s[j];
+    /* through the floor of s, s_raw(alpha) and sigmoid(eta) */
+    double da = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+        const float raw = sqo_smooth_raw(mx[j], mw[j], alpha);
+#if SQO_MUTANT != 25
+        /* MUTANT 25 (when defined): the floor's mask is dropped. */
+        if (!(raw >= SQO_FLOOR)) continue;
+#endif
+        const double lnsum = log((double)fmax_f(mx[j], SQO_FLOOR)) + log((double)mw[j]);
+        da += ds[j] * (double)raw * lnsum;
+    }
+    dalpha_deta[0] = da;
+#if SQO_MUTANT == 26
+    /* MUTANT 26: the sigmoid's derivative left out. */
+    dalpha_deta[1] = da;
+#else
+    dalpha_deta[1] = da * (double)alpha * (1.0 - (double)alpha);
+#endif
+}
+
+/* ---------------------------------------------------------------------
+ * The auxiliary loss of the module docstring: the relative squared error
+ *   L = ||y_fp - y_q||_F^2 / ||y_fp||_F^2       (denominator floored at 1e-24)
+ * and its gradient at y_q, dL/dy_q = 2 (y_q - y_fp) / ||y_fp||_F^2, the
+ * part of it that reaches eta (y_fp, the unquantised linear, does not
+ * depend on alpha). binary64. Returns L.
+ * ------------------------------------------------------------------ */
+double sqo_aux_loss_grad(const double* y_fp, const double* y_q, int64_t count, double* dy_q)
+{
+    double d2 = 0.0, f2 = 0.0;
+    for (int64_t i = 0; i < count; ++i) {
+        const double d = y_q[i] - y_fp[i];
+        d2 += d * d;
+        f2 += y_fp[i] * y_fp[i];
+    }
+    const double den = f2 > 1e-24 ? f2 : 1e-24;
+    for (int64_t i = 0; i < count; ++i)
+#if SQO_MUTANT == 27
+        /* MUTANT 27: the factor 2 of the square left out. */
+        dy_q[i] = (y_q[i] - y_fp[i]) / den;
+#else
+        dy_q[i] = 2.0 * (y_q[i] - y_fp[i]) / den;
+#endif
+    return d2 / den;
+}

@@ -664,4 +664,198 @@ def pin_quantization_error(o):
     assert q_half < q_plain, (q_half, q_plain)
 
 
+
+
+# ---------------------------------------------------------------------------
+# The learnable alpha and the straight-through backward (page
+# "w8a8_smoothquant.py": the docstring's V5 notes, STEQuantize /
+# ste_quantize, SmoothQuantW8A8.alpha and forward).
+# ---------------------------------------------------------------------------
+def _ste_layer(seed, m=5, n=6, k=32, masked=False):
+    """A small outlier layer, its frozen forward at alpha = sigmoid(eta) and
+    an upstream gradient. With ``masked`` one channel's s_raw falls below
+    the floor (never activated, huge weights), so the floor passes no
+    gradient there."""
+    rng = _rng(seed)
+    x = _outlier_acts(rng, m, k, chans=(2, 11), mult=30.0)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.05)
+    if masked:
+        x[:, 7] = (rng.standard_normal(m) * 1e-6).astype(np.float32)
+        w[:, 7] = (rng.standard_normal(n) * 1e12).astype(np.float32)
+    b = rng.standard_normal(n, dtype=np.float32) * np.float32(0.1)
+    dy = rng.standard_normal((m, n), dtype=np.float32)
+    return x, w, b, dy
+
+
+def _surrogate_loss(x, w, b, dy, mx, mw, eta, dx_off, dw_off):
+    """sum(dy * G) for the straight-through surrogate of the quantized
+    forward: G = (X / s(eta) + Dx)(W * s(eta) + Dw)^T + b, where the
+    quantisation offsets Dx, Dw are held at their values at the base point
+    (the estimator passes gradients through round and clamp unchanged) and
+    s(eta) = max(exp(a ln mx - (1 - a) ln mw), 1e-8), a = 1/(1 + e^-eta),
+    all in binary64."""
+    a = 1.0 / (1.0 + np.exp(-eta))
+    lmx = np.log(np.maximum(mx.astype(np.float64), float(FLOOR)))
+    lmw = np.log(mw.astype(np.float64))
+    s = np.maximum(np.exp(a * lmx - (1.0 - a) * lmw), float(FLOOR))
+    xs = x / s[None, :] + dx_off
+    ws = w * s[None, :] + dw_off
+    return float(np.sum(dy * (xs @ ws.T + b[None, :])))
+
+
+def pin_ste_finite_differences(o):
+    """Central finite differences of the straight-through surrogate (codes
+    held fixed, binary64) agree with the oracle's analytic gradients at X,
+    W, the bias and eta, including a channel where the floor of s is
+    active. The oracle works from binary32 alpha and s, the surrogate from
+    binary64 ones, so they agree to about 1e-7; the bar is 1e-5 of each
+    gradient's scale."""
+    for masked, eta in ((False, 0.4), (True, -0.3), (False, 0.0)):
+        x, w, b, dy = _ste_layer(140 + int(masked), masked=masked)
+        mx = o.calibrate(x)
+        r = o.training_step(x, w, b, mx, eta, dy)
+        x64, w64, b64, dy64 = (v.astype(np.float64) for v in (x, w, b, dy))
+        s64 = r["s"].astype(np.float64)
+        dx_off = r["xq"].astype(np.float64) * r["sx"].astype(np.float64)[:, None] - x64 / s64[None, :]
+        dw_off = r["wq"].astype(np.float64) * r["sw"].astype(np.float64)[:, None] - w64 * s64[None, :]
+        mw = r["mw"]
+
+        def L(xx=x64, ww=w64, bb=b64, ee=float(np.float32(eta))):
+            return _surrogate_loss(xx, ww, bb, dy64, mx, mw, ee, dx_off, dw_off)
+
+        # the magnitude of the surrogate's terms bounds the rounding error of
+        # one evaluation (a few hundred binary64 roundings at most)
+        xs = x64 / s64[None, :] + dx_off
+        ws = w64 * s64[None, :] + dw_off
+        mag = float(np.sum(np.abs(dy64) * (np.abs(xs) @ np.abs(ws).T + np.abs(b64)[None, :])))
+
+        def fd(f, v, h):
+            return (f(v + h) - f(v - h)) / (2 * h)
+
+        def fd_tol(h):
+            return 1e-13 * mag / h
+
+        rng = _rng(150)
+        for _ in range(12):
+            t, j = rng.integers(x.shape[0]), rng.integers(x.shape[1])
+            h = 1e-4 * max(1.0, abs(x64[t, j]))
+
+            def fx(v, t=t, j=j):
+                xx = x64.copy()
+                xx[t, j] = v
+                return L(xx=xx)
+            g = fd(fx, x64[t, j], h)
+            assert abs(g - r["dx"][t, j]) <= 1e-5 * np.abs(r["dx"]).max() + fd_tol(h), ("dx", t, j, g, r["dx"][t, j])
+            o_, j = rng.integers(w.shape[0]), rng.integers(w.shape[1])
+            h = 1e-4 * max(1e-3, abs(w64[o_, j]))
+
+            def fw(v, o_=o_, j=j):
+                ww = w64.copy()
+                ww[o_, j] = v
+                return L(ww=ww)
+            g = fd(fw, w64[o_, j], h)
+            assert abs(g - r["dw"][o_, j]) <= 1e-5 * np.abs(r["dw"]).max() + fd_tol(h), ("dw", o_, j, g, r["dw"][o_, j])
+        for o_ in range(w.shape[0]):
+            def fb(v, o_=o_):
+                bb = b64.copy()
+                bb[o_] = v
+                return L(bb=bb)
+            assert abs(fd(fb, b64[o_], 1e-3) - r["db"][o_]) <= 1e-9 * abs(r["db"][o_]) + fd_tol(1e-3)
+        e0 = float(np.float32(eta))
+        g = fd(lambda v: L(ee=v), e0, 1e-4)
+        assert abs(g - r["deta"]) <= 1e-5 * abs(r["deta"]) + fd_tol(1e-4), (masked, g, r["deta"], fd_tol(1e-4))
+        a = float(r["alpha"])
+        assert abs(r["deta"] - r["dalpha"] * a * (1 - a)) <= 1e-15 * abs(r["dalpha"])
+        if masked:
+            # the floored channel: s is the floor there and ds is far from
+            # zero, yet it passes nothing to alpha (the finite difference
+            # above agrees)
+            assert r["s"][7] == np.float32(float(FLOOR)) and abs(r["ds"][7]) > 1.0
+
+
+def pin_ste_exact_quantisers_give_no_alpha_gradient(o):
+    """The smoothing transform is an identity (module docstring: X~ W~^T =
+    X W^T), so when both quantisers are exact (X / s and W * s already on
+    their code grids) the straight-through gradient reaching s, alpha and
+    eta is exactly zero, while the gradients at X and W are the plain
+    linear's (dy W and dy^T X). Dyadic values make every binary64 sum
+    exact."""
+    rng = _rng(160)
+    m, n, k = 4, 5, 16
+    xq = rng.integers(-126, 127, size=(m, k)).astype(np.int8)
+    wq = rng.integers(-126, 127, size=(n, k)).astype(np.int8)
+    xq[np.arange(m), rng.integers(k, size=m)] = 127
+    wq[np.arange(n), rng.integers(k, size=n)] = -127
+    sx = (2.0 ** rng.integers(-9, -3, size=m)).astype(np.float32)
+    sw = (2.0 ** rng.integers(-12, -6, size=n)).astype(np.float32)
+    s = (2.0 ** rng.integers(-3, 4, size=k)).astype(np.float32)
+    x = (xq.astype(np.float64) * sx[:, None] * s[None, :]).astype(np.float32)
+    w = (wq.astype(np.float64) * sw[:, None] / s[None, :]).astype(np.float32)
+    # the quantisers reproduce the codes exactly at this s
+    q1, c1 = o.quantize_act(x, s)
+    q2, c2 = o.quantize_rows(o.smooth_weight(w, s))
+    assert np.array_equal(q1, xq) and np.array_equal(c1, sx) and np.array_equal(q2, wq) and np.array_equal(c2, sw)
+    dy = rng.integers(-8, 9, size=(m, n)).astype(np.float32)
+    mx = np.abs(x).max(axis=0)
+    mw = o.weight_col_max(w)
+    r = o.ste_backward(dy, x, w, s, xq, sx, wq, sw, mx, mw, np.float32(0.5))
+    assert np.all(r["ds"] == 0.0) and r["dalpha"] == 0.0 and r["deta"] == 0.0
+    assert np.array_equal(r["dx"], dy.astype(np.float64) @ w.astype(np.float64))
+    assert np.array_equal(r["dw"], dy.astype(np.float64).T @ x.astype(np.float64))
+    assert np.array_equal(r["db"], dy.astype(np.float64).sum(axis=0))
+
+
+def pin_sigmoid_parametrisation(o):
+    """alpha = sigmoid(eta) rounded once to binary32 (checked against a
+    60-digit decimal evaluation), eta = 0 gives exactly 1/2, the page's
+    initial eta round-trips alpha to within one binary32 ulp, and
+    sigmoid(-eta) = 1 - sigmoid(eta) to within an ulp."""
+    import decimal
+    ctx = decimal.Context(prec=60)
+    assert o.alpha_from_eta(0.0) == np.float32(0.5)
+    assert o.eta_from_alpha(0.5) == np.float32(0.0)
+    for eta in (-6.0, -2.5, -0.75, -0.1, 0.3, 1.0, 4.0, 9.0):
+        e = Fraction(float(np.float32(eta)))
+        ed = ctx.divide(decimal.Decimal(e.numerator), decimal.Decimal(e.denominator))
+        exact = Fraction(ctx.divide(decimal.Decimal(1), ctx.add(decimal.Decimal(1), ctx.exp(-ed))))
+        lo, hi = rn_f32(exact * (1 - Fraction(1, 2 ** 44))), rn_f32(exact * (1 + Fraction(1, 2 ** 44)))
+        got = Fraction(float(o.alpha_from_eta(eta)))
+        if lo == hi:
+            assert got == lo, (eta, float(got), float(lo))
+        a, a_neg = float(o.alpha_from_eta(eta)), float(o.alpha_from_eta(-eta))
+        assert abs(a + a_neg - 1.0) <= 2.0 ** -23
+    for alpha in (0.05, 0.25, 0.5, 0.75, 0.9):
+        back = float(o.alpha_from_eta(o.eta_from_alpha(alpha)))
+        assert abs(back - alpha) <= 2.0 ** -23 * max(alpha, 0.5), (alpha, back)
+    # the page's guard: an initial alpha of 1 gives log(1 / 1e-6)
+    assert o.eta_from_alpha(1.0) == np.float32(np.log(1e6))
+
+
+def pin_aux_loss(o):
+    """The docstring's auxiliary loss ||y_fp - y_q||^2 / ||y_fp||^2: zero with
+    a zero gradient at y_q = y_fp; exactly 2^-2e with gradient
+    -2^(1-e) y_fp / ||y_fp||^2 at y_q = y_fp (1 - 2^-e) (every step exact for
+    binary32-valued y_fp in binary64, up to the final division); and its
+    gradient matches central finite differences."""
+    rng = _rng(170)
+    y = rng.standard_normal(37, dtype=np.float32).astype(np.float64)
+    loss, g = o.aux_loss_grad(y, y)
+    assert loss == 0.0 and np.all(g == 0.0)
+    f2 = float(np.sum(y * y))
+    for e in (3, 11):
+        d = 2.0 ** -e
+        loss, g = o.aux_loss_grad(y, y * (1 - d))
+        assert abs(loss - d * d) <= 2.0 ** -50 * d * d
+        assert np.allclose(g, -2 * d * y / f2, rtol=1e-14, atol=0)
+    yq = y + rng.standard_normal(37) * 0.1
+    loss, g = o.aux_loss_grad(y, yq)
+    for i in range(0, 37, 5):
+        h = 1e-6
+        p, mm = yq.copy(), yq.copy()
+        p[i] += h
+        mm[i] -= h
+        fd = (o.aux_loss_grad(y, p)[0] - o.aux_loss_grad(y, mm)[0]) / (2 * h)
+        assert abs(fd - g[i]) <= 1e-7 * np.abs(g).max()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

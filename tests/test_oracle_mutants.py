@@ -25,6 +25,12 @@ MUTANTS = {
     19: "relative error measured against y_q",
     20: "general-alpha power with base and exponent swapped",
     21: "general-alpha power with the complementary exponent",
+    22: "alpha = sigmoid(-eta)",
+    23: "straight-through weight gradient with the wrong token's scale",
+    24: "X / s differentiated as X * s",
+    25: "the floor of s passes the gradient everywhere",
+    26: "the sigmoid's derivative left out of deta",
+    27: "auxiliary loss gradient without the factor 2",
 }
 
 
