@@ -431,6 +431,33 @@ size_t sq_relative_error_workspace_bytes(int64_t count);
 /* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);
 
+/*
+ * sq_w8a8_linear_noalloc -- sq_w8a8_linear for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same launches, arithmetic and
+ * outputs (bit for bit), with the activation codes and scales kept in a
+ * fixed device array of the library instead of a caller workspace. The
+ * call allocates and frees nothing.
+ *   - Limits: m <= SQ_NOALLOC_MAX_TOKENS and m * k <= SQ_NOALLOC_MAX_CODES
+ *     (16 MiB of codes: e.g. 4096 tokens of 4096 channels); larger calls
+ *     return SQ_ERR_WORKSPACE before launching anything.
+ *   - The array: one copy per GPU, held from the library's load until the
+ *     process ends (SQ_NOALLOC_MAX_CODES + 4 * SQ_NOALLOC_MAX_TOKENS bytes);
+ *     its address is looked up on the first call on each device, which must
+ *     be the current device (and the stream's).
+ *   - Every call on one GPU shares that array: calls that overlap on one
+ *     GPU (different streams, or different host threads) race and may read
+ *     each other's codes. The codes and scales are not readable through the
+ *     ABI.
+ * The other arguments, checks and statuses are sq_w8a8_linear's.
+ */
+#define SQ_NOALLOC_MAX_CODES (1LL << 24)
+#define SQ_NOALLOC_MAX_TOKENS (1LL << 14)
+sq_status sq_w8a8_linear_noalloc(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                                 const float* smooth, const int8_t* w_q,
+                                 const float* w_scale, int64_t n, const void* bias,
+                                 void* y, sq_dtype yt, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* sq_status_string(sq_status status);
 

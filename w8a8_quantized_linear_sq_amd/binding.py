@@ -26,6 +26,8 @@ SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
 SQ_MAX_K = 16384
 SQ_MAX_ROWS = 1 << 30
 SQ_MAX_TILES = (1 << 23) - 1
+SQ_NOALLOC_MAX_CODES = 1 << 24
+SQ_NOALLOC_MAX_TOKENS = 1 << 14
 
 
 class SQError(RuntimeError):
@@ -43,6 +45,7 @@ _SIGNATURES = {
     "sq_w8a8_gemm": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
     "sq_w8a8_linear": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P, _SZ, _P], _E),
     "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
+    "sq_w8a8_linear_noalloc": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P], _E),
     "sq_status_string": ([_E], ctypes.c_char_p),
     "sq_abi_version": ([], _E),
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
@@ -452,6 +455,19 @@ def sq_w8a8_linear(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_s
     nbytes = workspace.numel() * workspace.element_size()
     return _invoke("sq_w8a8_linear", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale), n,
                    _ptr(bias), _ptr(y), _dtype_code(y), _ptr(workspace), nbytes, _stream(stream, x))
+
+
+def sq_w8a8_linear_noalloc(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                           bias: torch.Tensor | None, y: torch.Tensor, stream=None) -> int:
+    """sq_w8a8_linear with the activation codes in the library's own fixed
+    device array (no workspace, nothing allocated; calls overlapping on one
+    GPU race)."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    if bias is not None:
+        _need_dtype(bias, x.dtype, "bias")
+    return _invoke("sq_w8a8_linear_noalloc", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q),
+                   _ptr(w_scale), n, _ptr(bias), _ptr(y), _dtype_code(y), _stream(stream, x))
 
 
 # ---------------------------------------------------------------------------

@@ -4,6 +4,8 @@
 #include "../../include/sq.h"
 #include "sq_device.h"
 
+#include <mutex>
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -399,3 +401,61 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// sq_w8a8_linear_noalloc: sq_w8a8_linear with its workspace (the activation
+// codes and scales) in a fixed device array of this library instead of
+// caller memory. Every GPU the library runs on holds its own copy of the
+// array from the library's load until the process ends; every call on one
+// GPU shares it (the codes and scales of the last call stay there), so calls
+// that overlap on one GPU race. Nothing in it needs clearing: each call
+// writes every code and scale it reads.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchCodes = SQ_NOALLOC_MAX_CODES;        // x_q bytes
+constexpr size_t kScratchScales = 4 * SQ_NOALLOC_MAX_TOKENS;  // x_scale bytes
+
+static __device__ __align__(256) unsigned char scratch[kScratchCodes + kScratchScales];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// The device address of this GPU's copy of `scratch` (the array's name in
+// host code is only a host-side stand-in), looked up once per device with
+// that device current. nullptr on failure.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" sq_status sq_w8a8_linear_noalloc(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                                            const int8_t* w_q, const float* w_scale, int64_t n, const void* bias,
+                                            void* y, sq_dtype yt, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    sq_status st = check_gemm(w_q, w_scale, m, w_q, w_scale, n, k, bias, xt, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    if (!x || !smooth) return SQ_ERR_ARG;
+    if (m > SQ_NOALLOC_MAX_TOKENS || (uint64_t)m * (uint64_t)k > (uint64_t)SQ_NOALLOC_MAX_CODES)
+        return SQ_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    char* base = (char*)scratch_on_current_device();
+    if (!base) return SQ_ERR_HIP;
+    int8_t* xq = (int8_t*)base;
+    float* xs = (float*)(base + kScratchCodes);
+    hipStream_t s = as_stream(stream);
+    hipError_t e = sq_launch_quantize_act(x, xt == SQ_BF16, smooth, m, k, xq, xs, s);
+    if (e == hipSuccess)
+        e = sq_launch_gemm(xq, xs, m, w_q, w_scale, n, k, bias, bias_kind(bias, xt), y, out_kind(yt), 0, s);
+    return launched(e);
+}
