@@ -428,6 +428,82 @@ sq_status sq_relative_error(const float* y_fp, const float* y_q, int64_t count, 
                             size_t workspace_bytes, double* result, void* stream);
 size_t sq_relative_error_workspace_bytes(int64_t count);
 
+/*
+ * The learnable alpha (page "w8a8_smoothquant.py", the module docstring's
+ * notes on it and SmoothQuantW8A8.__init__ / alpha): alpha = sigmoid(eta)
+ * with eta the trained parameter, initialised to log(a / max(1e-6, 1 - a))
+ * for an initial alpha a. Both computed in binary64 and rounded once to
+ * binary32. Host functions (no device work).
+ */
+float sq_alpha_from_eta(float eta);
+float sq_eta_from_alpha(double alpha);
+
+/*
+ * sq_ste_backward -- the straight-through backward of the quantized forward
+ * and the gradient of the learnable alpha. Follows STEQuantize / ste_quantize
+ * and SmoothQuantW8A8.forward (page "w8a8_smoothquant.py"): the forward
+ * recomputes s from alpha, quantises X~ = X / s per token and W~ = W * s per
+ * output channel, and multiplies the dequantised operands; the estimator
+ * passes the gradient of each dequantised operand to X~ and W~ unchanged
+ * (no gradient reaches the quantisers' scales). For the upstream gradient
+ * dy of Y = Xd Wd^T + bias, Xd = x_q * x_scale, Wd = w_q * w_scale:
+ *   gX[t][j] = sum_o dy[t][o] w_q[o][j] w_scale[o]
+ *   gW[o][j] = sum_t dy[t][o] x_q[t][j] x_scale[t]
+ *   dx[t][j] = gX[t][j] / s_j          dw[o][j] = gW[o][j] * s_j
+ *   dbias[o] = sum_t dy[t][o]
+ *   dsmooth_j = sum_o gW[o][j] w[o][j] - sum_t gX[t][j] x[t][j] / s_j^2
+ *   dalpha = sum_j [s_raw_j >= 1e-8] dsmooth_j s_raw_j (ln mx_j + ln mw_j)
+ *   deta = dalpha alpha (1 - alpha)
+ * where s_raw_j is the smoothing factor before its floor (the floor is a
+ * clamp, which passes no gradient below it), mx_j = max(x_max_abs[j],
+ * 1e-8) and mw_j = w_max_abs[j]; neither maximum is differentiated (the
+ * page keeps the activation maximum as a buffer and takes the weight
+ * maximum of detached weights).
+ * Arithmetic: the gradient products run on bf16 MFMA with every product
+ * exact (the fp32 factor RN32(dy * scale) split into three bf16 planes, the
+ * int8 codes exact in bf16) and fp32 sums; dx divides with IEEE binary32
+ * division; the sums behind dsmooth, dalpha and dbias are binary64 in a
+ * fixed order (the same inputs give the same bits).
+ *   dy        [m][n] in dyt (F32 or BF16), aligned to its element
+ *   x         [m][k] in xt, w [n][k] in wt (the forward's inputs), 16-byte aligned
+ *   smooth    [k] the forward's s;  x_q [m][k], x_scale [m], w_q [n][k],
+ *             w_scale [n] the forward's codes and scales (row-major,
+ *             16-byte aligned)
+ *   x_max_abs [k] the stored activation maxima, or NULL: never calibrated,
+ *             s = 1 does not depend on alpha, dalpha = deta = 0 and the call
+ *             returns SQ_WARN_UNCALIBRATED
+ *   w_max_abs [k] from sq_weight_col_max (required with x_max_abs)
+ *   alpha     the forward's alpha, in [0, 1]
+ *   dx [m][k], dw [n][k] fp32 out, 16-byte aligned; dbias [n] fp32 out or
+ *   NULL; dsmooth [k] fp32 out or NULL; dalpha_deta [2] binary64 out
+ *   workspace sq_ste_backward_workspace_bytes(m, n, k) bytes, 256-byte
+ *             aligned (overwritten)
+ * m and n from 1 to SQ_STE_MAX_ROWS.
+ */
+#define SQ_STE_MAX_ROWS (1LL << 24)
+size_t sq_ste_backward_workspace_bytes(int64_t m, int64_t n, int64_t k);
+sq_status sq_ste_backward(const void* dy, sq_dtype dyt, int64_t m, int64_t n, int64_t k,
+                          const void* x, sq_dtype xt, const void* w, sq_dtype wt,
+                          const float* smooth, const int8_t* x_q, const float* x_scale,
+                          const int8_t* w_q, const float* w_scale, const float* x_max_abs,
+                          const float* w_max_abs, float alpha, float* dx, float* dw,
+                          float* dbias, float* dsmooth, double* dalpha_deta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sq_aux_loss_grad -- the auxiliary loss of the module docstring (page
+ * "w8a8_smoothquant.py"), the relative squared error of the quantized
+ * output, and its gradient at y_q (the part that reaches eta):
+ *   loss = ||y_fp - y_q||_F^2 / max(||y_fp||_F^2, 1e-24)        (binary64)
+ *   dy_q = 2 (y_q - y_fp) / max(||y_fp||_F^2, 1e-24)            (fp32)
+ *   y_fp, y_q [count] fp32, 16-byte aligned;  dy_q [count] fp32 out
+ *   loss      [1] binary64 out, device memory
+ *   workspace sq_aux_loss_grad_workspace_bytes(count) bytes, 256-byte aligned
+ */
+size_t sq_aux_loss_grad_workspace_bytes(int64_t count);
+sq_status sq_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, float* dy_q,
+                           double* loss, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);
 

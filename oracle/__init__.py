@@ -72,7 +72,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "sqo_alpha_from_eta": ([ctypes.c_float], ctypes.c_float),
         "sqo_eta_from_alpha": ([ctypes.c_double], ctypes.c_float),
         "sqo_ste_backward": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I64,
-                              _P, _P, _P, _P, _P], None),
+                              _P, _P, _P, _P, _P, _P, _P], None),
+        "sqo_ste_chain": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I64, _P, _P, _P, _P], None),
         "sqo_aux_loss_grad": ([_P, _P, _I64, _P], ctypes.c_double),
     }
     for name, (args, res) in sig.items():
@@ -275,14 +276,18 @@ class Oracle:
 
     def ste_backward(self, dy, x, w, s, xq, sx, wq, sw, mx, mw, alpha):
         """The straight-through backward of the quantized forward (binary64):
-        returns dict(dx, dw, db, ds, dalpha, deta)."""
+        returns dict(gx, gw, dx, dw, db, ds, dalpha, deta); ``mx`` None =
+        never calibrated (no alpha gradient)."""
         dy, x, w, s = self._f32(dy), self._f32(x), self._f32(w), self._f32(s)
         xq = np.ascontiguousarray(xq, np.int8)
         wq = np.ascontiguousarray(wq, np.int8)
-        sx, sw, mx, mw = self._f32(sx), self._f32(sw), self._f32(mx), self._f32(mw)
+        sx, sw, mw = self._f32(sx), self._f32(sw), self._f32(mw)
+        mx = None if mx is None else self._f32(mx)
         m, k = x.shape
         n = w.shape[0]
         assert dy.shape == (m, n) and w.shape == (n, k) and xq.shape == (m, k) and wq.shape == (n, k)
+        gx = np.empty((m, k), np.float64)
+        gw = np.empty((n, k), np.float64)
         dx = np.empty((m, k), np.float64)
         dw = np.empty((n, k), np.float64)
         db = np.empty(n, np.float64)
@@ -290,9 +295,28 @@ class Oracle:
         da = np.empty(2, np.float64)
         self.lib.sqo_ste_backward(self._ptr(dy), self._ptr(x), self._ptr(w), self._ptr(s), self._ptr(xq),
                                   self._ptr(sx), self._ptr(wq), self._ptr(sw), self._ptr(mx), self._ptr(mw),
-                                  float(np.float32(alpha)), m, n, k, self._ptr(dx), self._ptr(dw), self._ptr(db),
-                                  self._ptr(ds), self._ptr(da))
-        return dict(dx=dx, dw=dw, db=db, ds=ds, dalpha=float(da[0]), deta=float(da[1]))
+                                  float(np.float32(alpha)), m, n, k, self._ptr(gx), self._ptr(gw), self._ptr(dx),
+                                  self._ptr(dw), self._ptr(db), self._ptr(ds), self._ptr(da))
+        return dict(gx=gx, gw=gw, dx=dx, dw=dw, db=db, ds=ds, dalpha=float(da[0]), deta=float(da[1]))
+
+    def ste_chain(self, gx, gw, x, w, s, mx, mw, alpha):
+        """The chain rule from the gradients at X~ and W~ (binary64 arrays)
+        to X, W, s, alpha and eta: returns dict(dx, dw, ds, dalpha, deta)."""
+        gx = np.ascontiguousarray(gx, np.float64)
+        gw = np.ascontiguousarray(gw, np.float64)
+        x, w, s, mw = self._f32(x), self._f32(w), self._f32(s), self._f32(mw)
+        mx = None if mx is None else self._f32(mx)
+        m, k = x.shape
+        n = w.shape[0]
+        assert gx.shape == (m, k) and gw.shape == (n, k)
+        dx = np.empty((m, k), np.float64)
+        dw = np.empty((n, k), np.float64)
+        ds = np.empty(k, np.float64)
+        da = np.empty(2, np.float64)
+        self.lib.sqo_ste_chain(self._ptr(gx), self._ptr(gw), self._ptr(x), self._ptr(w), self._ptr(s),
+                               self._ptr(mx), self._ptr(mw), float(np.float32(alpha)), m, n, k, self._ptr(dx),
+                               self._ptr(dw), self._ptr(ds), self._ptr(da))
+        return dict(dx=dx, dw=dw, ds=ds, dalpha=float(da[0]), deta=float(da[1]))
 
     def aux_loss_grad(self, y_fp, y_q):
         """The docstring's auxiliary loss ||y_fp - y_q||^2 / ||y_fp||^2 and its

@@ -541,55 +541,22 @@ static float sqo_smooth_raw(float mxj, float mwj, float alpha)
 }
 
 /* ---------------------------------------------------------------------
- * The straight-through backward of the quantized forward.
- *   dy   [m][n]  gradient of the loss at Y (fp32 values)
- *   x    [m][k]  the forward's activations X; w [n][k] its weights W
- *   s    [k]     the forward's smoothing factor (floored)
- *   xq, sx       per-token codes and scales of X / s (the forward's)
- *   wq, sw       per-output-channel codes and scales of W * s
- *   mx   [k]     stored activation maxima; mw [k] floored weight maxima
- *   alpha        the forward's alpha (binary32)
- * Outputs (binary64): dx [m][k], dw [n][k], db [n], ds [k], and
- * dalpha_deta[0] = dalpha, dalpha_deta[1] = deta.
+ * The chain rule from the gradients at X~ and W~ to X, W, s, alpha, eta:
+ *   gx [m][k], gw [n][k]  the gradients at X~ = X / s and W~ = W * s
+ *   x, w, s, mx, mw, alpha as in sqo_ste_backward below
+ * Outputs (binary64): dx [m][k], dw [n][k], ds [k], dalpha_deta [2].
  * ------------------------------------------------------------------ */
-void sqo_ste_backward(const float* dy, const float* x, const float* w, const float* s,
-                      const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                      const float* mx, const float* mw, float alpha, int64_t m, int64_t n,
-                      int64_t k, double* dx, double* dw, double* db, double* ds,
-                      double* dalpha_deta)
+void sqo_ste_chain(const double* gx, const double* gw, const float* x, const float* w,
+                   const float* s, const float* mx, const float* mw, float alpha, int64_t m,
+                   int64_t n, int64_t k, double* dx, double* dw, double* ds,
+                   double* dalpha_deta)
 {
-    /* gX and gW (in dx and dw first) */
-#pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < m; ++t)
-        for (int64_t j = 0; j < k; ++j) {
-            double acc = 0.0;
-            for (int64_t o = 0; o < n; ++o)
-                acc += (double)dy[t * n + o] * ((double)wq[o * k + j] * (double)sw[o]);
-            dx[t * k + j] = acc;
-        }
-#pragma omp parallel for schedule(static)
-    for (int64_t o = 0; o < n; ++o)
-        for (int64_t j = 0; j < k; ++j) {
-            double acc = 0.0;
-            for (int64_t t = 0; t < m; ++t)
-#if SQO_MUTANT == 23
-                /* MUTANT 23: the activation scale of the wrong token. */
-                acc += (double)dy[t * n + o] * ((double)xq[t * k + j] * (double)sx[(t + 1) % m]);
-#else
-                acc += (double)dy[t * n + o] * ((double)xq[t * k + j] * (double)sx[t]);
-#endif
-            dw[o * k + j] = acc;
-        }
-    for (int64_t o = 0; o < n; ++o) {
-        double acc = 0.0;
-        for (int64_t t = 0; t < m; ++t) acc += (double)dy[t * n + o];
-        db[o] = acc;
-    }
     /* ds from the two smoothing maps, then dx, dw through them */
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < k; ++j) {
         double from_w = 0.0, from_x = 0.0;
-        for (int64_t o = 0; o < n; ++o) from_w += dw[o * k + j] * (double)w[o * k + j];
-        for (int64_t t = 0; t < m; ++t) from_x += dx[t * k + j] * (double)x[t * k + j];
+        for (int64_t o = 0; o < n; ++o) from_w += gw[o * k + j] * (double)w[o * k + j];
+        for (int64_t t = 0; t < m; ++t) from_x += gx[t * k + j] * (double)x[t * k + j];
 #if SQO_MUTANT == 24
         /* MUTANT 24: X / s differentiated as if it were X * s. */
         ds[j] = from_w + from_x;
@@ -598,12 +565,13 @@ void sqo_ste_backward(const float* dy, const float* x, const float* w, const flo
 #endif
     }
     for (int64_t t = 0; t < m; ++t)
-        for (int64_t j = 0; j < k; ++j) dx[t * k + j] /= (double)s[j];
+        for (int64_t j = 0; j < k; ++j) dx[t * k + j] = gx[t * k + j] / (double)s[j];
     for (int64_t o = 0; o < n; ++o)
-        for (int64_t j = 0; j < k; ++j) dw[o * k + j] *= (double)s[j];
-    /* through the floor of s, s_raw(alpha) and sigmoid(eta) */
+        for (int64_t j = 0; j < k; ++j) dw[o * k + j] = gw[o * k + j] * (double)s[j];
+    /* through the floor of s, s_raw(alpha) and sigmoid(eta); no alpha
+     * gradient when never calibrated (s = 1 does not depend on alpha) */
     double da = 0.0;
-    for (int64_t j = 0; j < k; ++j) {
+    for (int64_t j = 0; mx && j < k; ++j) {
         const float raw = sqo_smooth_raw(mx[j], mw[j], alpha);
 #if SQO_MUTANT != 25
         /* MUTANT 25 (when defined): the floor's mask is dropped. */
@@ -619,6 +587,65 @@ void sqo_ste_backward(const float* dy, const float* x, const float* w, const flo
 #else
     dalpha_deta[1] = da * (double)alpha * (1.0 - (double)alpha);
 #endif
+}
+
+/* ---------------------------------------------------------------------
+ * The straight-through backward of the quantized forward.
+ *   dy   [m][n]  gradient of the loss at Y (fp32 values)
+ *   x    [m][k]  the forward's activations X; w [n][k] its weights W
+ *   s    [k]     the forward's smoothing factor (floored)
+ *   xq, sx       per-token codes and scales of X / s (the forward's)
+ *   wq, sw       per-output-channel codes and scales of W * s
+ *   mx   [k]     stored activation maxima (NULL: never calibrated, no
+ *                alpha gradient); mw [k] floored weight maxima
+ *   alpha        the forward's alpha (binary32)
+ * Outputs (binary64): dx [m][k], dw [n][k], db [n], ds [k], and
+ * dalpha_deta[0] = dalpha, dalpha_deta[1] = deta. gx, gw [m][k], [n][k]
+ * receive the gradients at X~ and W~.
+ * ------------------------------------------------------------------ */
+void sqo_ste_backward(const float* dy, const float* x, const float* w, const float* s,
+                      const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                      const float* mx, const float* mw, float alpha, int64_t m, int64_t n,
+                      int64_t k, double* gx, double* gw, double* dx, double* dw, double* db,
+                      double* ds, double* dalpha_deta)
+{
+    /* the gradients at X~ and W~: the estimator passes the gradient of the
+     * dequantised operand straight through round and clamp. Each sum runs
+     * over its index in increasing order; the loops are nested so that the
+     * innermost one walks a row (j) of the output. */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < m; ++t) {
+        double* acc = gx + t * k;
+        for (int64_t j = 0; j < k; ++j) acc[j] = 0.0;
+        for (int64_t o = 0; o < n; ++o) {
+            const double d = (double)dy[t * n + o];
+            const double so = (double)sw[o];
+            const int8_t* q = wq + o * k;
+            for (int64_t j = 0; j < k; ++j) acc[j] += d * ((double)q[j] * so);
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < n; ++o) {
+        double* acc = gw + o * k;
+        for (int64_t j = 0; j < k; ++j) acc[j] = 0.0;
+        for (int64_t t = 0; t < m; ++t) {
+            const double d = (double)dy[t * n + o];
+#if SQO_MUTANT == 23
+            /* MUTANT 23: the activation scale of the wrong token. */
+            const double st = (double)sx[(t + 1) % m];
+#else
+            const double st = (double)sx[t];
+#endif
+            const int8_t* q = xq + t * k;
+            for (int64_t j = 0; j < k; ++j) acc[j] += d * ((double)q[j] * st);
+        }
+    }
+    for (int64_t o = 0; o < n; ++o) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < m; ++t) acc += (double)dy[t * n + o];
+        db[o] = acc;
+    }
+    sqo_ste_chain(gx, gw, x, w, s, mx, mw, alpha, m, n, k, dx, dw, ds, dalpha_deta);
 }
 
 /* ---------------------------------------------------------------------

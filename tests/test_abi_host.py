@@ -400,3 +400,49 @@ def test_size_limits(L):
     ws = L.sq_w8a8_linear_workspace_bytes(4, 64)
     assert L.sq_w8a8_linear(P, B.SQ_BF16, 4, 64, P, P, P, 1 << 31, None, P, B.SQ_BF16, P, ws,
                             None) == B.SQ_ERR_SHAPE
+
+
+def test_alpha_from_eta_matches_oracle(L, orc):
+    """The library's host sigmoid and initial eta equal the oracle's bit for
+    bit (both binary64 rounded once to binary32)."""
+    import numpy as np
+    for eta in np.linspace(-12.0, 12.0, 241, dtype=np.float32):
+        assert np.float32(L.sq_alpha_from_eta(float(eta))) == orc.alpha_from_eta(float(eta)), eta
+    for a in (1e-7, 0.05, 0.25, 0.5, 0.75, 0.9, 1.0):
+        assert np.float32(L.sq_eta_from_alpha(a)) == orc.eta_from_alpha(a), a
+    assert L.sq_alpha_from_eta(0.0) == 0.5
+
+
+def test_ste_backward_errors(L):
+    f = L.sq_ste_backward
+    need = L.sq_ste_backward_workspace_bytes(8, 6, 64)
+    assert need > 0 and L.sq_ste_backward_workspace_bytes(0, 6, 64) == 0
+
+    def call(dy=OK_PTR, dyt=B.SQ_F32, m=8, n=6, k=64, x=OK_PTR, xt=B.SQ_BF16, w=OK_PTR, wt=B.SQ_BF16, s=OK_PTR,
+             xq=OK_PTR, sx=OK_PTR, wq=OK_PTR, sw=OK_PTR, mx=OK_PTR, mw=OK_PTR, alpha=0.5, dx=OK_PTR, dw=OK_PTR,
+             db=None, ds=None, da=OK_PTR, ws=OK_PTR, wsb=need):
+        return f(dy, dyt, m, n, k, x, xt, w, wt, s, xq, sx, wq, sw, mx, mw, alpha, dx, dw, db, ds, da, ws, wsb, None)
+
+    assert call(dyt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(xt=7) == B.SQ_ERR_DTYPE
+    assert call(m=0) == B.SQ_ERR_SHAPE
+    assert call(n=B.SQ_STE_MAX_ROWS + 1) == B.SQ_ERR_SHAPE
+    assert call(k=40) == B.SQ_ERR_ALIGN
+    assert call(alpha=1.5) == B.SQ_ERR_ARG
+    for key in ("dy", "x", "w", "s", "xq", "sx", "wq", "sw", "dx", "dw", "da"):
+        assert call(**{key: None}) == B.SQ_ERR_ARG, key
+    assert call(mw=None) == B.SQ_ERR_ARG
+    assert call(ws=None) == B.SQ_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.SQ_ERR_WORKSPACE
+    for key in ("x", "w", "xq", "wq", "dx", "dw"):
+        assert call(**{key: BAD}) == B.SQ_ERR_ALIGN, key
+    assert call(ws=OK_PTR + 16) == B.SQ_ERR_ALIGN
+
+
+def test_aux_loss_grad_errors(L):
+    f = L.sq_aux_loss_grad
+    need = L.sq_aux_loss_grad_workspace_bytes(100)
+    assert f(OK_PTR, OK_PTR, 0, OK_PTR, OK_PTR, OK_PTR, need, None) == B.SQ_ERR_SHAPE
+    assert f(None, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need, None) == B.SQ_ERR_ARG
+    assert f(OK_PTR, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need - 1, None) == B.SQ_ERR_WORKSPACE
+    assert f(BAD, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need, None) == B.SQ_ERR_ALIGN

@@ -1,0 +1,312 @@
+"""GPU parity of the learnable alpha and the straight-through backward (page
+"w8a8_smoothquant.py": the docstring's notes on the learnable alpha,
+STEQuantize / ste_quantize, SmoothQuantW8A8.alpha and forward) against the
+oracle, through the C ABI.
+
+The forward (alpha from eta, s, codes, scales) is bit-exact. The gradients
+are fp32 sums on the GPU and binary64 in the oracle; the bars follow from
+the arithmetic: every product of the two straight-through products is
+exact (three bf16 planes of RN32(dy * scale) against exact bf16 codes), so
+a gradient differs from the exact sum by at most the fp32 rounding of the
+factor (2^-24) and of an accumulation of 3 n (or 3 m) terms (3 n 2^-24 of
+the sum of the terms' magnitudes), then one fp32 rounding of the folded
+output. ds, dalpha and deta take those bounds through their sums."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, assert_equal, down, require_gpu, up
+from w8a8_quantized_linear_sq_amd import binding as B
+from w8a8_quantized_linear_sq_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    B.lib()
+
+
+def _zeros(shape, dtype):
+    return torch.zeros(shape, dtype=dtype, device=DEV)
+
+
+def _dy(m, n, seed, dtype):
+    rng = np.random.default_rng(seed)
+    d = rng.standard_normal((m, n), dtype=np.float32)
+    if dtype == "bf16":
+        bits = inputs.bf16_bits(d)
+        return inputs.Tensor(inputs.bf16_to_f32(bits), bits)
+    return inputs.Tensor(d, None)
+
+
+def _forward(c, eta, orc):
+    """The quantized forward on the GPU at alpha = sigmoid(eta): returns the
+    device tensors and their host copies (checked against the oracle)."""
+    m, n, k = c.m, c.n, c.k
+    alpha = B.sq_alpha_from_eta(eta)
+    assert np.float32(alpha) == orc.alpha_from_eta(eta)
+    x, w = up(c.x), up(c.w)
+    mx = _zeros(k, torch.float32)
+    B.sq_calibrate(x, mx)
+    mw = _zeros(k, torch.float32)
+    B.sq_weight_col_max(w, mw)
+    s = _zeros(k, torch.float32)
+    B.sq_smoothing_factor(mx, mw, alpha, s)
+    wq, sw = _zeros((n, k), torch.int8), _zeros(n, torch.float32)
+    B.sq_quantize_weight(w, s, wq, sw)
+    xq, sx = _zeros((m, k), torch.int8), _zeros(m, torch.float32)
+    B.sq_quantize_act(x, s, xq, sx)
+    torch.cuda.synchronize()
+    mx_h, mw_h, s_h = down(mx), down(mw), down(s)
+    assert_equal(mx_h, orc.calibrate(c.x.f32), "mx")
+    assert_equal(mw_h, orc.weight_col_max(c.w.f32), "mw")
+    s_ref = orc.smoothing_factor(mx_h, mw_h, alpha)
+    if alpha in (0.0, 0.25, 0.5, 0.75, 1.0):
+        assert_equal(s_h, s_ref, "s")
+    else:
+        # binary64 pow of two math libraries: one ulp of s at most
+        assert np.abs(s_h.view(np.int32).astype(np.int64) - s_ref.view(np.int32)).max() <= 1
+    wq_ref, sw_ref = orc.quantize_rows(orc.smooth_weight(c.w.f32, s_h))
+    assert_equal(down(wq), wq_ref, "w_q")
+    assert_equal(down(sw), sw_ref, "w_scale")
+    xq_ref, sx_ref = orc.quantize_act(c.x.f32, s_h)
+    assert_equal(down(xq), xq_ref, "x_q")
+    assert_equal(down(sx), sx_ref, "x_scale")
+    dev = dict(x=x, w=w, mx=mx, mw=mw, s=s, wq=wq, sw=sw, xq=xq, sx=sx)
+    host = dict(mx=mx_h, mw=mw_h, s=s_h, wq=wq_ref, sw=sw_ref, xq=xq_ref, sx=sx_ref)
+    return alpha, dev, host
+
+
+def _backward(c, dy, alpha, dev, bias=True, with_mx=True):
+    m, n, k = c.m, c.n, c.k
+    dx, dw = _zeros((m, k), torch.float32), _zeros((n, k), torch.float32)
+    db = _zeros(n, torch.float32) if bias else None
+    ds = _zeros(k, torch.float32)
+    da = _zeros(2, torch.float64)
+    ws = torch.empty(B.sq_ste_backward_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    st = B.sq_ste_backward(up(dy), dev["x"], dev["w"], dev["s"], dev["xq"], dev["sx"], dev["wq"], dev["sw"],
+                           dev["mx"] if with_mx else None, dev["mw"], alpha, dx, dw, db, ds, da, ws)
+    torch.cuda.synchronize()
+    assert st == (B.SQ_OK if with_mx else B.SQ_WARN_UNCALIBRATED)
+    return dict(dx=down(dx), dw=down(dw), db=None if db is None else down(db), ds=down(ds), da=down(da))
+
+
+def _check_grads(c, dyt, alpha, host, got, orc, with_mx=True):
+    m, n, k = c.m, c.n, c.k
+    x64, w64 = c.x.f32.astype(np.float64), c.w.f32.astype(np.float64)
+    dy64 = dyt.f32.astype(np.float64)
+    s64 = host["s"].astype(np.float64)
+    mx_or_none = host["mx"] if with_mx else None
+    ref = orc.ste_backward(dyt.f32, c.x.f32, c.w.f32, host["s"], host["xq"], host["sx"], host["wq"], host["sw"],
+                           mx_or_none, host["mw"], alpha)
+    wd = np.abs(host["wq"].astype(np.float64) * host["sw"].astype(np.float64)[:, None])
+    xd = np.abs(host["xq"].astype(np.float64) * host["sx"].astype(np.float64)[:, None])
+    mag_x = np.abs(dy64) @ wd                # sum_o |dy Wd|   [m][k]
+    mag_w = np.abs(dy64).T @ xd              # sum_t |dy Xd|   [n][k]
+    eg_x = (3.05 * n + 2) * U * mag_x        # bound on gX's error
+    eg_w = (3.05 * m + 2) * U * mag_w        # bound on gW's error
+    tol_dx = eg_x / s64[None, :] + U * np.abs(ref["dx"])
+    tol_dw = eg_w * s64[None, :] + U * np.abs(ref["dw"])
+    def ratio(err, tol):
+        return float(np.max(np.divide(err, tol, out=np.zeros_like(err), where=tol > 0)))
+
+    print(f"{m}x{k}->{n}: max |err| / bound: dx {ratio(np.abs(got['dx'] - ref['dx']), tol_dx):.3g}, "
+          f"dw {ratio(np.abs(got['dw'] - ref['dw']), tol_dw):.3g}", flush=True)
+    bad = np.argwhere(np.abs(got["dx"] - ref["dx"]) > tol_dx)
+    assert bad.size == 0, f"dx: {len(bad)} beyond the bound, first {bad[:3].tolist()}"
+    bad = np.argwhere(np.abs(got["dw"] - ref["dw"]) > tol_dw)
+    assert bad.size == 0, f"dw: {len(bad)} beyond the bound, first {bad[:3].tolist()}"
+    if got["db"] is not None:
+        tol_db = U * np.abs(ref["db"]) + (m + 1) * 2.0 ** -53 * np.abs(dy64).sum(axis=0)
+        assert np.all(np.abs(got["db"] - ref["db"]) <= tol_db), "db"
+    # ds: the gX / gW errors through its two sums, binary64 rounding of
+    # those sums, then one fp32 rounding
+    sum_w = np.sum(np.abs(ref["dw"] / s64[None, :]) * np.abs(w64), axis=0)
+    sum_x = np.sum(np.abs(ref["dx"] * s64[None, :]) * np.abs(x64), axis=0) / (s64 * s64)
+    tol_ds = (np.sum(eg_w * np.abs(w64), axis=0) + np.sum(eg_x * np.abs(x64), axis=0) / (s64 * s64)
+              + (m + n + 4) * 2.0 ** -52 * (sum_w + sum_x))
+    assert np.all(np.abs(got["ds"] - ref["ds"]) <= tol_ds + U * np.abs(ref["ds"])), "ds"
+    # dalpha: per channel |d ds| |s_raw (ln mx + ln mw)|, plus a few ulps of
+    # s_raw and the logarithms from two math libraries
+    if with_mx:
+        mxf = np.maximum(host["mx"].astype(np.float64), 1e-8)
+        mwf = host["mw"].astype(np.float64)
+        raw = mxf ** float(alpha) / mwf ** (1.0 - float(alpha))
+        lam = np.abs(raw * (np.log(mxf) + np.log(mwf)))
+        tol_da = float(np.sum(tol_ds * lam) + np.sum(np.abs(ref["ds"]) * lam) * 2.0 ** -20 + 1e-300)
+        print(f"   ds {ratio(np.abs(got['ds'] - ref['ds']), tol_ds + U * np.abs(ref['ds'])):.3g}, dalpha "
+              f"{abs(got['da'][0] - ref['dalpha']) / tol_da:.3g} (dalpha {ref['dalpha']:.6g}, bound {tol_da:.3g})",
+              flush=True)
+        assert abs(got["da"][0] - ref["dalpha"]) <= tol_da, (got["da"][0], ref["dalpha"], tol_da)
+        a = float(alpha)
+        assert abs(got["da"][1] - ref["deta"]) <= tol_da * a * (1 - a) + 2.0 ** -50 * abs(ref["deta"])
+    else:
+        assert got["da"][0] == 0.0 and got["da"][1] == 0.0
+    # The worst-case bars above grow with m n for ds and dalpha (errors of
+    # single products summed with one sign); the reduction stage is also
+    # checked sharply on its own: the oracle's chain rule applied to the
+    # GPU's own gX = dx s and gW = dw / s (each within 2^-24 of the GPU's
+    # fp32 sums) must give the GPU's ds, dalpha and deta within the
+    # binary64 summation error and those 2^-24.
+    s32 = host["s"].astype(np.float64)
+    gx_gpu = got["dx"].astype(np.float64) * s32[None, :]
+    gw_gpu = got["dw"].astype(np.float64) / s32[None, :]
+    ch = orc.ste_chain(gx_gpu, gw_gpu, c.x.f32, c.w.f32, host["s"], mx_or_none, host["mw"], alpha)
+    mag = np.sum(np.abs(gw_gpu * w64), axis=0) + np.sum(np.abs(gx_gpu * x64), axis=0) / (s32 * s32)
+    tol_ch = (2 * U + (m + n + 4) * 2.0 ** -52) * mag + U * np.abs(ch["ds"])
+    assert np.all(np.abs(got["ds"] - ch["ds"]) <= tol_ch), "ds against the chain rule on the GPU's gX, gW"
+    if with_mx:
+        tol_cha = float(np.sum(tol_ch * lam) + np.sum(np.abs(ch["ds"]) * lam) * 2.0 ** -20 + 1e-300)
+        print(f"   chain: ds {ratio(np.abs(got['ds'] - ch['ds']), tol_ch):.3g}, dalpha "
+              f"{abs(got['da'][0] - ch['dalpha']) / tol_cha:.3g} (bound {tol_cha:.3g} of {abs(ch['dalpha']):.3g})",
+              flush=True)
+        assert abs(got["da"][0] - ch["dalpha"]) <= tol_cha
+        assert abs(got["da"][1] - ch["deta"]) <= tol_cha * a * (1 - a) + 2.0 ** -50 * abs(ch["deta"])
+    return ref
+
+
+SHAPES = [(16, 128, 256), (3, 5, 32), (17, 33, 272), (130, 260, 528), (257, 300, 1040), (70, 40, 4096)]
+
+
+def _id(s):
+    return "x".join(map(str, s))
+
+
+@pytest.mark.parametrize("eta", [0.0, 0.4], ids=lambda e: f"eta{e}")
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+def test_ste_backward(orc, shape, dtype, eta):
+    m, n, k = shape
+    c = inputs.small(m, n, k, seed=41 + m + n + k, dtype=dtype, bias=True)
+    dyt = _dy(m, n, 7 + m * n, dtype)
+    alpha, dev, host = _forward(c, eta, orc)
+    got = _backward(c, dyt, alpha, dev)
+    _check_grads(c, dyt, alpha, host, got, orc)
+    # the same inputs give the same bits
+    again = _backward(c, dyt, alpha, dev)
+    for key in ("dx", "dw", "db", "ds", "da"):
+        assert np.array_equal(got[key].view(np.uint8), again[key].view(np.uint8)), key
+
+
+def test_ste_backward_tiny_config(orc):
+    """The tiny fp32 layer (16 x 256 -> 128, outlier channels {3, 77, 200},
+    bias, alpha = 1/2 from eta = 0)."""
+    c = inputs.tiny()
+    dyt = _dy(c.m, c.n, 3, "f32")
+    alpha, dev, host = _forward(c, 0.0, orc)
+    got = _backward(c, dyt, alpha, dev)
+    _check_grads(c, dyt, alpha, host, got, orc)
+
+
+def test_ste_backward_floored_channel(orc):
+    """A channel whose s_raw falls below the floor (tiny activations, huge
+    weights): s is the floor there and that channel passes nothing to
+    alpha, on the GPU as in the oracle."""
+    m, n, k = 24, 40, 272
+    c = inputs.small(m, n, k, seed=5, dtype="f32", bias=False)
+    xf, wf = c.x.f32.copy(), c.w.f32.copy()
+    rng = np.random.default_rng(9)
+    xf[:, 7] = (rng.standard_normal(m) * 1e-6).astype(np.float32)
+    wf[:, 7] = (rng.standard_normal(n) * 1e12).astype(np.float32)
+    c2 = inputs.LinearCase(c.name, "f32", inputs.Tensor(xf, None), inputs.Tensor(wf, None), None)
+    dyt = _dy(m, n, 11, "f32")
+    alpha, dev, host = _forward(c2, -0.3, orc)
+    assert host["s"][7] == np.float32(1e-8)
+    got = _backward(c2, dyt, alpha, dev, bias=False)
+    ref = _check_grads(c2, dyt, alpha, host, got, orc)
+    assert abs(ref["ds"][7]) > 1.0
+
+
+def test_ste_backward_uncalibrated(orc):
+    """Never calibrated (s = 1, which does not depend on alpha): the
+    gradients at X, W and the bias as for s = 1, no alpha gradient, and the
+    warning status."""
+    m, n, k = 33, 20, 96
+    c = inputs.small(m, n, k, seed=13, dtype="bf16", bias=True)
+    dyt = _dy(m, n, 17, "bf16")
+    alpha, dev, host = _forward(c, 0.0, orc)
+    ones = torch.ones(k, dtype=torch.float32, device=DEV)
+    B.sq_quantize_weight(dev["w"], ones, dev["wq"], dev["sw"])
+    B.sq_quantize_act(dev["x"], ones, dev["xq"], dev["sx"])
+    dev["s"] = ones
+    torch.cuda.synchronize()
+    host = dict(host, s=np.ones(k, np.float32), wq=down(dev["wq"]), sw=down(dev["sw"]), xq=down(dev["xq"]),
+                sx=down(dev["sx"]))
+    got = _backward(c, dyt, alpha, dev, with_mx=False)
+    _check_grads(c, dyt, alpha, host, got, orc, with_mx=False)
+
+
+@pytest.mark.slow
+def test_ste_backward_prefill(orc):
+    """The prefill shape (2048 x 4096 -> 4096, bf16 activations and
+    upstream gradient, 1% outlier channels x 50), every gradient element
+    against the oracle."""
+    c = inputs.prefill()
+    dyt = _dy(c.m, c.n, 2024, "bf16")
+    print("prefill straight-through backward: GPU", flush=True)
+    alpha, dev, host = _forward(c, 0.0, orc)
+    got = _backward(c, dyt, alpha, dev, bias=False)
+    print("prefill straight-through backward: oracle", flush=True)
+    _check_grads(c, dyt, alpha, host, got, orc)
+
+
+@pytest.mark.parametrize("count", [1, 7, 4096, 3 * (1 << 20) + 5])
+def test_aux_loss_grad(orc, count):
+    """The auxiliary relative squared error and its gradient at y_q."""
+    rng = np.random.default_rng(count)
+    yfp = rng.standard_normal(count, dtype=np.float32)
+    yq = (yfp + rng.standard_normal(count, dtype=np.float32) * np.float32(0.01)).astype(np.float32)
+    dyq = _zeros(count, torch.float32)
+    loss = _zeros(1, torch.float64)
+    ws = torch.empty(B.sq_aux_loss_grad_workspace_bytes(count), dtype=torch.uint8, device=DEV)
+    assert B.sq_aux_loss_grad(up(yfp), up(yq), dyq, loss, ws) == B.SQ_OK
+    torch.cuda.synchronize()
+    ref_loss, ref_g = orc.aux_loss_grad(yfp.astype(np.float64), yq.astype(np.float64))
+    tol = (count + 64) * 2.0 ** -52
+    assert abs(float(down(loss)[0]) - ref_loss) <= 3 * tol * ref_loss
+    g = down(dyq).astype(np.float64)
+    assert np.all(np.abs(g - ref_g) <= U * np.abs(ref_g) + 2 * tol * np.abs(ref_g))
+
+
+def test_layer_training_step(orc):
+    """The layer's learnable alpha: eta from the initial alpha, the weights
+    re-quantised at sigmoid(eta), train_forward and backward equal to the
+    oracle's training step (forward bit-exact, gradients within the bars
+    above), then a new eta re-quantises the weights for its alpha."""
+    m, n, k = 40, 72, 528
+    c = inputs.small(m, n, k, seed=77, dtype="bf16", bias=True)
+    layer = B.SmoothQuantLinear(up(c.w), up(c.bias), alpha=0.4, layout="row", learnable_alpha=True)
+    assert np.float32(layer.eta) == orc.eta_from_alpha(0.4)
+    layer.calibrate(up(c.x))
+    layer.freeze()
+    y = layer.train_forward(up(c.x))
+    dyt = _dy(m, n, 5, "f32")
+    g = layer.backward(up(dyt))
+    torch.cuda.synchronize()
+    mx = orc.calibrate(c.x.f32)
+    r = orc.training_step(c.x.f32, c.w.f32, c.bias.f32, mx, float(np.float32(layer.eta)), dyt.f32)
+    s_h = down(layer.smooth)
+    assert np.abs(s_h.view(np.int32).astype(np.int64) - r["s"].view(np.int32)).max() <= 1
+    host = dict(mx=mx, mw=r["mw"], s=s_h, wq=down(layer.weight_int8), sw=down(layer.weight_scale))
+    host["xq"], host["sx"] = orc.quantize_act(c.x.f32, s_h)
+    got = dict(dx=down(g["dx"]), dw=down(g["dw"]), db=down(g["dbias"]), ds=down(g["dsmooth"]),
+               da=np.array([g["dalpha"], g["deta"]]))
+    _check_grads(c, dyt, np.float32(layer.alpha), host, got, orc)
+    xq_r, sx_r, acc, yref = orc.linear(c.x.f32, s_h, host["wq"], host["sw"], c.bias.f32)
+    scale = np.abs(acc.astype(np.float64) * sx_r[:, None] * host["sw"][None, :]) + np.abs(c.bias.f32)[None, :]
+    assert np.all(np.abs(down(y).astype(np.float64) - yref) <= 1e-6 * scale)
+    layer.set_eta(layer.eta - 0.5)
+    torch.cuda.synchronize()
+    a2 = orc.alpha_from_eta(layer.eta)
+    assert np.float32(layer.alpha) == a2
+    s2, wq2, sw2 = orc.prepare_weight(c.w.f32, mx, a2)
+    s_h2 = down(layer.smooth)
+    assert np.abs(s_h2.view(np.int32).astype(np.int64) - s2.view(np.int32)).max() <= 1
+    wq_r, sw_r = orc.quantize_rows(orc.smooth_weight(c.w.f32, s_h2))
+    assert_equal(down(layer.weight_int8), wq_r, "w_q after the new eta")

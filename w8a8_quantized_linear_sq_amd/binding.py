@@ -28,6 +28,7 @@ SQ_MAX_ROWS = 1 << 30
 SQ_MAX_TILES = (1 << 23) - 1
 SQ_NOALLOC_MAX_CODES = 1 << 24
 SQ_NOALLOC_MAX_TOKENS = 1 << 14
+SQ_STE_MAX_ROWS = 1 << 24
 
 
 class SQError(RuntimeError):
@@ -46,6 +47,13 @@ _SIGNATURES = {
     "sq_w8a8_linear": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P, _SZ, _P], _E),
     "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
     "sq_w8a8_linear_noalloc": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P], _E),
+    "sq_alpha_from_eta": ([_F], _F),
+    "sq_eta_from_alpha": ([ctypes.c_double], _F),
+    "sq_ste_backward_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "sq_ste_backward": ([_P, _E, _I64, _I64, _I64, _P, _E, _P, _E, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
+                         _P, _P, _P, _SZ, _P], _E),
+    "sq_aux_loss_grad_workspace_bytes": ([_I64], _SZ),
+    "sq_aux_loss_grad": ([_P, _P, _I64, _P, _P, _P, _SZ, _P], _E),
     "sq_status_string": ([_E], ctypes.c_char_p),
     "sq_abi_version": ([], _E),
     "sq_quantize_tensor": ([_P, _E, _I64, _P, _P, _P], _E),
@@ -470,6 +478,63 @@ def sq_w8a8_linear_noalloc(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Ten
                    _ptr(w_scale), n, _ptr(bias), _ptr(y), _dtype_code(y), _stream(stream, x))
 
 
+def sq_alpha_from_eta(eta: float) -> float:
+    """alpha = sigmoid(eta) (binary64, rounded to binary32)."""
+    return float(lib().sq_alpha_from_eta(float(eta)))
+
+
+def sq_eta_from_alpha(alpha: float) -> float:
+    """The page's initial eta for an initial alpha: log(a / max(1e-6, 1 - a))."""
+    return float(lib().sq_eta_from_alpha(float(alpha)))
+
+
+def sq_ste_backward_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().sq_ste_backward_workspace_bytes(m, n, k))
+
+
+def sq_ste_backward(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, smooth: torch.Tensor, x_q: torch.Tensor,
+                    x_scale: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, x_max_abs: torch.Tensor | None,
+                    w_max_abs: torch.Tensor | None, alpha: float, dx: torch.Tensor, dw: torch.Tensor,
+                    dbias: torch.Tensor | None, dsmooth: torch.Tensor | None, dalpha_deta: torch.Tensor,
+                    workspace: torch.Tensor, stream=None) -> int:
+    """The straight-through backward: dx, dw, dbias, dsmooth and
+    (dalpha, deta) for the upstream gradient dy (SQ_WARN_UNCALIBRATED when
+    x_max_abs is None: no alpha gradient)."""
+    m, n = dy.shape
+    k = x.shape[1]
+    for t, nm in ((dx, "dx"), (dw, "dw"), (smooth, "smooth"), (x_scale, "x_scale"), (w_scale, "w_scale")):
+        _need_dtype(t, torch.float32, nm)
+    for t, nm in ((dbias, "dbias"), (dsmooth, "dsmooth"), (x_max_abs, "x_max_abs"), (w_max_abs, "w_max_abs")):
+        if t is not None:
+            _need_dtype(t, torch.float32, nm)
+    _need_dtype(dalpha_deta, torch.float64, "dalpha_deta")
+    if x.shape != (m, k) or w.shape != (n, k) or x_q.shape != (m, k) or w_q.shape != (n, k):
+        raise ValueError("x [m][k], w [n][k] and their codes must match dy [m][n]")
+    nbytes = workspace.numel() * workspace.element_size()
+    return _invoke("sq_ste_backward", _ptr(dy), _dtype_code(dy), m, n, k, _ptr(x), _dtype_code(x), _ptr(w),
+                   _dtype_code(w), _ptr(smooth), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                   _ptr(x_max_abs), _ptr(w_max_abs), float(alpha), _ptr(dx), _ptr(dw), _ptr(dbias), _ptr(dsmooth),
+                   _ptr(dalpha_deta), _ptr(workspace), nbytes, _stream(stream, dy))
+
+
+def sq_aux_loss_grad_workspace_bytes(count: int) -> int:
+    return int(lib().sq_aux_loss_grad_workspace_bytes(count))
+
+
+def sq_aux_loss_grad(y_fp: torch.Tensor, y_q: torch.Tensor, dy_q: torch.Tensor, loss: torch.Tensor,
+                     workspace: torch.Tensor, stream=None) -> int:
+    """loss = ||y_fp - y_q||^2 / ||y_fp||^2 (binary64, device) and its
+    gradient at y_q (fp32)."""
+    for t, nm in ((y_fp, "y_fp"), (y_q, "y_q"), (dy_q, "dy_q")):
+        _need_dtype(t, torch.float32, nm)
+    _need_dtype(loss, torch.float64, "loss")
+    if y_fp.numel() != y_q.numel() or dy_q.numel() != y_q.numel():
+        raise ValueError("y_fp, y_q and dy_q must have one size")
+    nbytes = workspace.numel() * workspace.element_size()
+    return _invoke("sq_aux_loss_grad", _ptr(y_fp), _ptr(y_q), y_q.numel(), _ptr(dy_q), _ptr(loss), _ptr(workspace),
+                   nbytes, _stream(stream, y_q))
+
+
 # ---------------------------------------------------------------------------
 # The page's layer lifecycle on top of the ABI: calibrate -> freeze -> forward
 # (SmoothQuantW8A8 in "w8a8_smoothquant.py"). Buffers only; no arithmetic.
@@ -486,7 +551,7 @@ class SmoothQuantLinear:
     the faster ones."""
 
     def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, alpha: float = 0.5,
-                 layout: str = "row"):
+                 layout: str = "row", learnable_alpha: bool = False):
         if not weight.is_cuda:
             raise ValueError("weight must be a device tensor")
         if layout not in ("row", "tiled"):
@@ -507,6 +572,13 @@ class SmoothQuantLinear:
         self.weight_scale = torch.ones(n, dtype=torch.float32, device=dev)
         self.weight_max_abs = torch.empty(k, dtype=torch.float32, device=dev)
         self.is_quantized = False
+        # the page's learnable alpha: alpha = sigmoid(eta), eta initialised
+        # from the given alpha (then alpha is eta's sigmoid, not exactly it)
+        self.learnable_alpha = bool(learnable_alpha)
+        self.eta = sq_eta_from_alpha(alpha) if learnable_alpha else None
+        if learnable_alpha:
+            self.alpha = sq_alpha_from_eta(self.eta)
+        self._saved = None
 
     def calibrate(self, x: torch.Tensor) -> None:
         if self.is_quantized:
@@ -540,6 +612,56 @@ class SmoothQuantLinear:
             raise RuntimeError("recompute before freeze")
         self.alpha = float(alpha)
         return self._quantize_weight()
+
+    def set_eta(self, eta: float) -> int:
+        """The learnable alpha's parameter: alpha = sigmoid(eta); the weights
+        are re-smoothed and re-quantised for it (one pass over W)."""
+        if not self.learnable_alpha:
+            raise RuntimeError("alpha is not learnable for this layer")
+        self.eta = float(eta)
+        return self.recompute(sq_alpha_from_eta(self.eta))
+
+    def train_forward(self, x: torch.Tensor) -> torch.Tensor:
+        """The quantized forward in fp32 (as the page's training forward),
+        keeping what the straight-through backward needs (row layout)."""
+        if not self.is_quantized:
+            raise RuntimeError("forward before freeze")
+        if self.layout != "row":
+            raise RuntimeError("the straight-through backward takes row-major codes (layout='row')")
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        m, k = x2.shape
+        n = self.weight_scale.shape[0]
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+        sq_quantize_act(x2, self.smooth, x_q, x_scale)
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        sq_w8a8_gemm(x_q, x_scale, self.weight_int8, self.weight_scale, self.bias, y)
+        self._saved = (x2, x_q, x_scale, x.shape)
+        return y.reshape(*x.shape[:-1], n)
+
+    def backward(self, dy: torch.Tensor) -> dict:
+        """The straight-through backward of the last train_forward for the
+        upstream gradient dy: dict with dx, dw, dbias (None without a
+        bias), dsmooth (device tensors), dalpha and deta (floats; zero when
+        the layer was never calibrated)."""
+        if self._saved is None:
+            raise RuntimeError("backward before train_forward")
+        x2, x_q, x_scale, xshape = self._saved
+        m, k = x2.shape
+        n = self.weight_scale.shape[0]
+        dy2 = dy.reshape(m, n).contiguous()
+        dev = x2.device
+        dx = torch.empty((m, k), dtype=torch.float32, device=dev)
+        dw = torch.empty((n, k), dtype=torch.float32, device=dev)
+        db = torch.empty(n, dtype=torch.float32, device=dev) if self.bias is not None else None
+        ds = torch.empty(k, dtype=torch.float32, device=dev)
+        da = torch.empty(2, dtype=torch.float64, device=dev)
+        ws = torch.empty(max(sq_ste_backward_workspace_bytes(m, n, k), 256), dtype=torch.uint8, device=dev)
+        mx = self.calib_max_abs if self.calib_count else None
+        sq_ste_backward(dy2, x2, self.weight, self.smooth, x_q, x_scale, self.weight_int8, self.weight_scale, mx,
+                        self.weight_max_abs, self.alpha, dx, dw, db, ds, da, ws)
+        dah = da.cpu()
+        return dict(dx=dx.reshape(xshape), dw=dw, dbias=db, dsmooth=ds, dalpha=float(dah[0]), deta=float(dah[1]))
 
     def quantization_error(self, x: torch.Tensor) -> float:
         """||Y_fp - Y_q||_F / max(||Y_fp||_F, 1e-12): the unquantised linear

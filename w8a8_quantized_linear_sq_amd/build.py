@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsq.so")
-SOURCES = ["sq_api.hip", "sq_quant.hip", "sq_gemm.hip", "sq_wo.hip", "sq_error.hip"]
+SOURCES = ["sq_api.hip", "sq_quant.hip", "sq_gemm.hip", "sq_wo.hip", "sq_error.hip", "sq_ste.hip"]
 ARCH = os.environ.get("SQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

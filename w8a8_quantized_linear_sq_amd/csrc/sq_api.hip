@@ -400,6 +400,68 @@ sq_status sq_w8a8_linear(const void* x, sq_dtype xt, int64_t m, int64_t k, const
     return launched(e);
 }
 
+// ---------------------------------------------------------------------------
+// The learnable alpha and the straight-through backward
+// ---------------------------------------------------------------------------
+float sq_alpha_from_eta(float eta) { return (float)(1.0 / (1.0 + exp(-(double)eta))); }
+
+float sq_eta_from_alpha(double alpha) {
+    const double d = 1.0 - alpha;
+    return (float)log(alpha / (d > 1e-6 ? d : 1e-6));
+}
+
+size_t sq_ste_backward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m <= 0 || n <= 0 || k <= 0 || m > SQ_STE_MAX_ROWS || n > SQ_STE_MAX_ROWS || k > SQ_MAX_K) return 0;
+    return sq_ste_layout(m, n, k).bytes;
+}
+
+sq_status sq_ste_backward(const void* dy, sq_dtype dyt, int64_t m, int64_t n, int64_t k, const void* x, sq_dtype xt,
+                          const void* w, sq_dtype wt, const float* smooth, const int8_t* x_q, const float* x_scale,
+                          const int8_t* w_q, const float* w_scale, const float* x_max_abs, const float* w_max_abs,
+                          float alpha, float* dx, float* dw, float* dbias, float* dsmooth, double* dalpha_deta,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!fp_in(dyt) || !fp_in(xt) || !fp_in(wt)) return SQ_ERR_DTYPE;
+    if (m <= 0 || n <= 0 || m > SQ_STE_MAX_ROWS || n > SQ_STE_MAX_ROWS) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    // the products' tile grids and the transposes' grids (64 x 64 tiles)
+    if (!tiles_fit(m, k) || !tiles_fit(n, k)) return SQ_ERR_SHAPE;
+    if (((m + 63) / 64) * ((n + 63) / 64) > kMaxTiles || ((m + 63) / 64 + (n + 63) / 64) * ((k + 63) / 64) > kMaxTiles)
+        return SQ_ERR_SHAPE;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;
+    if (!dy || !x || !w || !smooth || !x_q || !x_scale || !w_q || !w_scale || !dx || !dw || !dalpha_deta)
+        return SQ_ERR_ARG;
+    if (x_max_abs && !w_max_abs) return SQ_ERR_ARG;
+    if (!workspace || workspace_bytes < sq_ste_backward_workspace_bytes(m, n, k)) return SQ_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(x_q) || !aligned16(w_q) || !aligned16(dx) || !aligned16(dw))
+        return SQ_ERR_ALIGN;
+    if (((uintptr_t)dy & (dyt == SQ_BF16 ? 1u : 3u)) != 0 || ((uintptr_t)workspace & 255u) != 0 ||
+        ((uintptr_t)dalpha_deta & 7u) != 0)
+        return SQ_ERR_ALIGN;
+    hipError_t e = sq_launch_ste_backward(dy, dyt == SQ_BF16, m, n, k, x, xt == SQ_BF16, w, wt == SQ_BF16, smooth,
+                                          x_q, x_scale, w_q, w_scale, x_max_abs, w_max_abs, (double)alpha, dx, dw,
+                                          dbias, dsmooth, dalpha_deta, workspace, as_stream(stream));
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    return x_max_abs ? SQ_OK : SQ_WARN_UNCALIBRATED;
+}
+
+size_t sq_aux_loss_grad_workspace_bytes(int64_t count) {
+    return count <= 0 ? 0 : sq_relative_error_workspace_bytes(count) + 256;
+}
+
+sq_status sq_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, float* dy_q, double* loss,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (count <= 0) return SQ_ERR_SHAPE;
+    if (!y_fp || !y_q || !dy_q || !loss) return SQ_ERR_ARG;
+    if (!workspace || workspace_bytes < sq_aux_loss_grad_workspace_bytes(count)) return SQ_ERR_WORKSPACE;
+    if (!aligned16(y_fp) || !aligned16(y_q) || ((uintptr_t)dy_q & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0 ||
+        ((uintptr_t)loss & 7u) != 0)
+        return SQ_ERR_ALIGN;
+    double* norms = (double*)workspace;  // [3], then the partial sums
+    double* partial = (double*)((char*)workspace + 256);
+    return launched(sq_launch_aux_loss_grad(y_fp, y_q, count, partial, norms, dy_q, loss, as_stream(stream)));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace sq {
 
 // The floor of the method, the binary32 value nearest to 1e-8 (0x322BCC77).
@@ -25,6 +27,18 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     return v;
+}
+
+// P(x, a) = x^a through binary64 (the smoothing factor's powers): exact
+// forms built from correctly rounded sqrt for a in {0, 1/4, 1/2, 3/4, 1},
+// pow otherwise.
+__device__ __forceinline__ double pow64(double x, double a) {
+    if (a == 0.0) return 1.0;
+    if (a == 1.0) return x;
+    if (a == 0.5) return __builtin_sqrt(x);
+    if (a == 0.25) return __builtin_sqrt(__builtin_sqrt(x));
+    if (a == 0.75) return __builtin_sqrt(x) * __builtin_sqrt(__builtin_sqrt(x));
+    return pow(x, a);
 }
 
 }  // namespace sq
@@ -110,3 +124,30 @@ hipError_t sq_launch_gemm_stream(const int8_t* xq, const float* sx, int64_t m, c
 hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_t m, const int8_t* wq,
                                        const float* sw, int64_t n, int64_t k, const void* bias, int bias_kind,
                                        void* y, int out_kind, int scalar_scales, hipStream_t st);
+// y [m][n] fp32 = a [m][kbytes/2] (bf16) times b [n][ldb/2] (bf16) summed
+// over kbytes/2 terms with b's columns repeating every ldb/2 (kbytes and ldb
+// multiples of 64 bytes, kbytes a multiple of ldb)
+hipError_t sq_launch_gemm_bf16_periodic(const void* a, const void* b, int64_t m, int64_t n, int64_t kbytes,
+                                        int64_t ldb, float* y, hipStream_t st);
+
+// The straight-through backward (learnable alpha): workspace regions (byte
+// offsets, 256-aligned) for m tokens, n output channels, k input channels.
+struct SteLayout {
+    int64_t m64, n64;          // m, n rounded up to 64 (the packed contraction)
+    int64_t gx, gw, gb;        // row groups of the three column-sum passes
+    size_t a1, bw, a2, bx;     // packed factors and transposed codes (bf16)
+    size_t px, pw, pb, term;   // binary64 partial sums and per-channel terms
+    size_t bytes;              // total
+};
+SteLayout sq_ste_layout(int64_t m, int64_t n, int64_t k);
+// dx [m][k], dw [n][k] (fp32; also the products' outputs), db [n] (or
+// NULL), ds [k] (or NULL), dalpha_deta [2]; mx NULL: no alpha gradient
+hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_t n, int64_t k, const void* x,
+                                  int x_bf16, const void* w, int w_bf16, const float* s, const int8_t* xq,
+                                  const float* sx, const int8_t* wq, const float* sw, const float* mx,
+                                  const float* mw, double alpha, float* dx, float* dw, float* db, float* ds,
+                                  double* dalpha_deta, void* workspace, hipStream_t st);
+// dy_q = 2 (y_q - y_fp) / max(||y_fp||^2, 1e-24) and the loss ||y_fp -
+// y_q||^2 / that; partial: sq_relative_error_blocks(count) pairs, norms [3]
+hipError_t sq_launch_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, double* partial,
+                                   double* norms, float* dy_q, double* loss, hipStream_t st);

@@ -139,11 +139,16 @@ constexpr int kI8 = 0, kBf16 = 1, kF32 = 2;
 // chunks, tile (g, c) at (g * k / 64 + c) * 1 KiB, each tile row-major; k is
 // then the padded row length, a multiple of 64, and the padding is zero):
 // every DMA load reads one whole tile, 1 KiB contiguous.
-template <int ET, int BM, int BN, int WGM, int WGN, int OUT, bool TILED>
+// BPER (row-major only): B's rows are ldb bytes long (a multiple of 64) and
+// repeat along k, so B's byte at k offset c is the one at c mod ldb: one
+// product sums several A planes against the same B (the straight-through
+// backward splits an fp32 operand into three bf16 planes side by side).
+template <int ET, int BM, int BN, int WGM, int WGN, int OUT, bool TILED, bool BPER = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
-    int bias_kind, void* __restrict__ Y, int grid_m, int grid_n, int scalar_scales) {
+    int bias_kind, void* __restrict__ Y, int grid_m, int grid_n, int scalar_scales, int ldb) {
+    static_assert(!(BPER && TILED), "a periodic B is row-major");
     constexpr int NW = WGM * WGN;                 // wavefronts (WGM x WGN grid)
     constexpr int kStages = NW == 8 ? kStagesPingPong : kStagesInterleaved;
     static_assert(kStages >= 3 && kStages <= 5, "the prologue's wait covers up to three later stages");
@@ -183,6 +188,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const int8_t* gbase[LOADS]; // the block's first byte (uniform)
     int voff[LOADS];
     int dst[LOADS];
+    bool per[LOADS];            // BPER: the block holds B rows (offsets wrap at ldb)
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
         const int blk = wave + NW * q;
@@ -202,9 +208,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
             // every lane's row is at or after the block's clamped first row
             const int r0 = in_a ? min(m0 + blk * kBlockRows, m - 1) : min(n0 + blk * kBlockRows - BM, n - 1);
             const int r = in_a ? min(m0 + row, m - 1) : min(n0 + row - BM, n - 1);
-            g = (in_a ? A : B) + (int64_t)r0 * k;
-            voff[q] = (r - r0) * k + chunk * 16;
+            const int ld = (BPER && !in_a) ? ldb : k;
+            g = (in_a ? A : B) + (int64_t)r0 * ld;
+            voff[q] = (r - r0) * ld + chunk * 16;
         }
+        per[q] = BPER && !in_a;
         src[q] = g + voff[q];
         gbase[q] = g;
         dst[q] = blk * 1024;
@@ -212,10 +220,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     auto issue_stage = [&](int kt, int buf) {
         const int kb = TILED ? kt * 1024 : kt * kBK;
 #pragma unroll
-        for (int q = 0; q < LOADS; ++q)
-            // 16 rows of k bytes from the block's first byte: every offset
-            // a stage adds stays below that record count
-            dma_load16(gbase[q], 16 * k, voff[q] + kb, (lds_ptr_t)(smem + buf * STAGE + dst[q]));
+        for (int q = 0; q < LOADS; ++q) {
+            if constexpr (BPER) {
+                // 16 rows of ldb bytes for a B block, the offset wrapped
+                const int kq = per[q] ? kb % ldb : kb;
+                dma_load16(gbase[q], 16 * (per[q] ? ldb : k), voff[q] + kq, (lds_ptr_t)(smem + buf * STAGE + dst[q]));
+            } else {
+                // 16 rows of k bytes from the block's first byte: every offset
+                // a stage adds stays below that record count
+                dma_load16(gbase[q], 16 * k, voff[q] + kb, (lds_ptr_t)(smem + buf * STAGE + dst[q]));
+            }
+        }
     };
     // a last partial step: the same layout through registers, chunks past k
     // zero-filled
@@ -390,7 +405,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
             mfmas(ga, gb);
         }
     }
-    if (!TILED && k % kBK) {
+    if (!TILED && !BPER && k % kBK) {
         // a last partial step through registers: its buffer was last read
         // kStages steps ago
         __syncthreads();
@@ -519,21 +534,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     }
 }
 
-template <int ET, bool TILED, int BM, int BN, int WGM, int WGN>
+template <int ET, bool TILED, int BM, int BN, int WGM, int WGN, bool BPER = false>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
                        int n, int kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
-                       hipStream_t st) {
+                       hipStream_t st, int ldb = 0) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
     dim3 grid(gm * gn), block(64 * WGM * WGN);
     if (out_kind == 0)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
-                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
-    else if (out_kind == 1)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
-                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
-    else if constexpr (ET == kI8)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 2, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
-                           sx, sw, bias, bias_kind, y, gm, gn, scalar_scales);
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0, TILED, BPER>), grid, block, 0, st, xq, wq, m, n,
+                           kbytes, sx, sw, bias, bias_kind, y, gm, gn, scalar_scales, ldb);
+    else if constexpr (!BPER) {
+        if (out_kind == 1)
+            hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
+                               sx, sw, bias, bias_kind, y, gm, gn, scalar_scales, 0);
+        else if constexpr (ET == kI8)
+            hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 2, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
+                               sx, sw, bias, bias_kind, y, gm, gn, scalar_scales, 0);
+    }
     return hipGetLastError();
 }
 
@@ -542,10 +559,10 @@ hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* w
 // area over the configuration's measured speed per unit area on MI355X
 // (256 x 256: 1.0, 128 x 256: 0.80, 128 x 128: 0.73, from full-wave runs of
 // the int8 product).
-template <int ET, bool TILED = false>
+template <int ET, bool TILED = false, bool BPER = false>
 hipError_t launch_tiled(const int8_t* a, const float* sx, int64_t m, const int8_t* b, const float* sw, int64_t n,
                         int64_t kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
-                        hipStream_t st) {
+                        hipStream_t st, int64_t ldb = 0) {
     struct Cfg { int bm, bn; double speed; };
     const Cfg cfgs[] = {{256, 256, 1.0}, {128, 256, 0.80}, {128, 128, 0.73}};
     int best = 0;
@@ -559,11 +576,11 @@ hipError_t launch_tiled(const int8_t* a, const float* sx, int64_t m, const int8_
             best = i;
         }
     }
-    const int mi = (int)m, ni = (int)n, ki = (int)kbytes;
+    const int mi = (int)m, ni = (int)n, ki = (int)kbytes, lb = (int)ldb;
     switch (best) {
-        case 0: return launch_tile<ET, TILED, 256, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        case 1: return launch_tile<ET, TILED, 128, 256, 2, 4>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
-        default: return launch_tile<ET, TILED, 128, 128, 2, 2>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 0: return launch_tile<ET, TILED, 256, 256, 2, 4, BPER>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st, lb);
+        case 1: return launch_tile<ET, TILED, 128, 256, 2, 4, BPER>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st, lb);
+        default: return launch_tile<ET, TILED, 128, 128, 2, 2, BPER>(a, sx, mi, b, sw, ni, ki, bias, bias_kind, y, out_kind, scalar_scales, st, lb);
     }
 }
 
@@ -599,4 +616,14 @@ hipError_t sq_launch_reference_gemm(const void* x, const void* w, int bf16, int6
     const int8_t* b = (const int8_t*)w;
     if (bf16) return launch_tiled<kBf16>(a, nullptr, m, b, nullptr, n, 2 * k, bias, bias_kind, y, out_kind, 0, st);
     return launch_tiled<kF32>(a, nullptr, m, b, nullptr, n, 4 * k, bias, bias_kind, y, out_kind, 0, st);
+}
+
+// The straight-through backward's products: y[i][j] = sum_c a[i][c] b[j][c mod
+// (ldb / 2)] with bf16 a [m][kbytes / 2] and bf16 b [n][ldb / 2] (kbytes and
+// ldb multiples of 64, kbytes a multiple of ldb), fp32 sums, fp32 out.
+hipError_t sq_launch_gemm_bf16_periodic(const void* a, const void* b, int64_t m, int64_t n, int64_t kbytes,
+                                        int64_t ldb, float* y, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    return launch_tiled<kBf16, false, true>((const int8_t*)a, nullptr, m, (const int8_t*)b, nullptr, n, kbytes,
+                                            nullptr, 0, y, 0, 0, st, ldb);
 }

@@ -199,15 +199,6 @@ hipError_t sq_launch_colmax_partial(const void* x, int bf16, int64_t rows, int64
 // A block owns 64 channels; its 4 wavefronts split the row groups (8 loads
 // in flight each) and meet in LDS.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double pow64(double x, double a) {
-    if (a == 0.0) return 1.0;
-    if (a == 1.0) return x;
-    if (a == 0.5) return __builtin_sqrt(x);
-    if (a == 0.25) return __builtin_sqrt(__builtin_sqrt(x));
-    if (a == 0.75) return __builtin_sqrt(x) * __builtin_sqrt(__builtin_sqrt(x));
-    return pow(x, a);
-}
-
 __global__ __launch_bounds__(256) void smooth_factor_kernel(const float* __restrict__ x_max,
                                                             const unsigned* partial, int64_t groups, double a_x,
                                                             double a_w, int64_t k, float* s) {

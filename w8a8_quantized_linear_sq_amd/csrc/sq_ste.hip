@@ -1,0 +1,416 @@
+// sq_ste.hip -- the straight-through backward of the quantized forward and
+// the gradient of the learnable alpha, for gfx950.
+//
+// Page "w8a8_smoothquant.py" (BiGRU_T_version): the module docstring's notes
+// on the learnable alpha (alpha = sigmoid(eta), round and clamp passed
+// through by a straight-through estimator, a relative squared error as an
+// auxiliary loss), STEQuantize / ste_quantize (the gradient of the
+// dequantised value goes to the quantiser's input unchanged, none to its
+// scale) and SmoothQuantW8A8.forward (s recomputed from alpha, X~ = X / s,
+// W~ = W * s, both quantised, Y = Xd Wd^T + bias). With Xd = xq * sx (per
+// token) and Wd = wq * sw (per output channel):
+//   gX[t][j] = sum_o dy[t][o] wq[o][j] sw[o]     dx = gX / s_j
+//   gW[o][j] = sum_t dy[t][o] xq[t][j] sx[t]     dw = gW * s_j
+//   db[o]    = sum_t dy[t][o]
+//   ds_j     = sum_o gW[o][j] w[o][j] - sum_t gX[t][j] x[t][j] / s_j^2
+//   dalpha   = sum_j [s_raw_j >= 1e-8] ds_j s_raw_j (ln mx_j + ln mw_j)
+//   deta     = dalpha alpha (1 - alpha)
+//
+// Design:
+//   * both products contract over the rows of their int8 operand, so the
+//     operands are first rearranged so that the contraction is contiguous
+//     (the form the MFMA tile kernel reads): the fp32 factor
+//     v = RN32(dy * scale) is split exactly into three bf16 planes,
+//     v = a1 + a2 + a3 (8 significant bits each), laid side by side along
+//     the contraction; the int8 codes are transposed into bf16 (exact).
+//     The tile kernel's periodic-B form then sums the three planes against
+//     the same codes in one launch: every product is exact in fp32 and only
+//     the fp32 accumulation rounds, as in the page's fp32 autograd;
+//   * the two products write gX and gW into dx and dw; one column-sum pass
+//     per output folds the smoothing (dx = gX / s with IEEE division,
+//     dw = gW * s) and accumulates sum gX x and sum gW w in binary64 per
+//     row group (a fixed order: the same inputs give the same bits);
+//   * ds_j, its share of dalpha, the bias gradient and the final sums run
+//     in small kernels over k and n, fixed-order trees.
+#include "sq_device.h"
+
+using namespace sq;
+
+namespace {
+
+// bf16 round-to-nearest-even of a finite binary32 value (the bit pattern)
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// v = a1 + a2 + a3 exactly, each a bf16: a1 = RN_bf16(v) leaves a remainder
+// of at most 16 significant bits (exact in fp32), a2 = RN_bf16 of that
+// leaves at most 8, which a3 holds exactly (as long as no piece falls below
+// bf16's normal range, i.e. |v| >= 2^-110; below that the lost part is
+// under 2^-133 in magnitude).
+__device__ __forceinline__ void split3(float v, uint32_t& a1, uint32_t& a2, uint32_t& a3) {
+    a1 = bf16_rne(v);
+    const float r1 = v - bf16_val(a1);
+    a2 = bf16_rne(r1);
+    const float r2 = r1 - bf16_val(a2);
+    a3 = bf16_rne(r2);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_val(const void* p, int64_t i) {
+    if constexpr (BF16) return bf16_val(((const uint16_t*)p)[i]);
+    else return ((const float*)p)[i];
+}
+
+// a[t][p * ld + o] = plane p of RN32(dy[t][o] * sc[o]) for o < n, zero for
+// n <= o < ld (ld a multiple of 64). Thread: 4 consecutive o of one row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void ste_pack_rows_kernel(const void* __restrict__ dy, const float* __restrict__ sc,
+                                                            int64_t m, int64_t n, int64_t ld, uint16_t* __restrict__ a) {
+    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (o0 >= ld) return;
+    for (int64_t t = blockIdx.y; t < m; t += gridDim.y) {
+        uint32_t h[3][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t o = o0 + e;
+            const float v = o < n ? load_val<BF16>(dy, t * n + o) * sc[o] : 0.0f;
+            split3(v, h[0][e], h[1][e], h[2][e]);
+        }
+        uint16_t* row = a + t * 3 * ld + o0;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            const u32x2 w = {h[p][0] | (h[p][1] << 16), h[p][2] | (h[p][3] << 16)};
+            *(u32x2*)(row + p * ld) = w;
+        }
+    }
+}
+
+// a[o][p * ld + t] = plane p of RN32(dy[t][o] * sc[t]) for t < m, zero for
+// m <= t < ld; rows o < n. 64 x 64 tiles through LDS (tile (ti, oi) with
+// ti = blockIdx.x % (ld / 64)).
+constexpr int kTP = 72;  // LDS row pitch in bf16 (16-byte aligned rows)
+template <bool BF16>
+__global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restrict__ dy, const float* __restrict__ sc,
+                                                            int64_t m, int64_t n, int64_t ld, uint16_t* __restrict__ a) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[3][64][kTP];  // [plane][o][t]
+    const int64_t tiles_t = ld / 64;
+    const int64_t t0 = (blockIdx.x % tiles_t) * 64, o0 = (blockIdx.x / tiles_t) * 64;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tt = ty + 16 * r;
+        const int64_t t = t0 + tt;
+        const float f = t < m ? sc[t] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int oo = tx * 4 + e;
+            const int64_t o = o0 + oo;
+            const float v = (t < m && o < n) ? load_val<BF16>(dy, t * n + o) * f : 0.0f;
+            uint32_t h1, h2, h3;
+            split3(v, h1, h2, h3);
+            tile[0][oo][tt] = (uint16_t)h1;
+            tile[1][oo][tt] = (uint16_t)h2;
+            tile[2][oo][tt] = (uint16_t)h3;
+        }
+    }
+    __syncthreads();
+    // 64 rows o x 3 planes x 8 pieces of 16 bytes (8 t each)
+    for (int c = threadIdx.x; c < 64 * 3 * 8; c += 256) {
+        const int oo = c / 24, p = (c / 8) % 3, piece = c % 8;
+        const int64_t o = o0 + oo;
+        if (o >= n) continue;
+        const u32x4 v = *(const u32x4*)&tile[p][oo][piece * 8];
+        *(u32x4*)(a + o * 3 * ld + p * ld + t0 + piece * 8) = v;
+    }
+}
+
+// b[j][o] = bf16(q[o][j]) (exact) for o < rows, zero for rows <= o < ld;
+// j < k. q is [rows][k] int8 row-major; 64 x 64 tiles through LDS.
+constexpr int kQP = 68;  // LDS row pitch in bytes
+__global__ __launch_bounds__(256) void ste_transpose_codes_kernel(const int8_t* __restrict__ q, int64_t rows,
+                                                                  int64_t k, int64_t ld, uint16_t* __restrict__ b) {
+    __shared__ __attribute__((aligned(16))) int8_t tile[64][kQP];  // [o][j]
+    const int64_t tiles_o = ld / 64;
+    const int64_t o0 = (blockIdx.x % tiles_o) * 64, j0 = (blockIdx.x / tiles_o) * 64;
+    {
+        const int oo = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const int64_t o = o0 + oo, j = j0 + part * 16;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (o < rows && j < k) v = *(const u32x4*)(q + o * k + j);  // k % 16 == 0: whole pieces
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *(uint32_t*)&tile[oo][part * 16 + 4 * e] = v[e];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 64 * 8; c += 256) {
+        const int jj = c >> 3, piece = c & 7;
+        const int64_t j = j0 + jj;
+        if (j >= k) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = (float)tile[piece * 8 + 2 * e][jj];
+            const float hi = (float)tile[piece * 8 + 2 * e + 1][jj];
+            w[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);  // |code| <= 128: exact
+        }
+        const u32x4 v = {w[0], w[1], w[2], w[3]};
+        *(u32x4*)(b + j * ld + o0 + piece * 8) = v;
+    }
+}
+
+// Column sums over row groups, with an optional elementwise factor and an
+// optional in-place fold of s:
+//   part[g][c] = sum over rows r of group g of y[r][c] * z[r][c] (binary64,
+//                rows in order; z = 1 when ZK == 0)
+//   OP 1: y[r][c] = y[r][c] / s[c] (IEEE);  OP 2: y[r][c] = y[r][c] * s[c]
+// y is fp32 when OP != 0 (else YBF16 selects its type); z is fp32 (ZK 1)
+// or bf16 (ZK 2). VEC: cols % 4 == 0 and rows 16-byte aligned, 4 columns
+// per thread as one vector; otherwise 4 scalar columns.
+template <int ZK, int OP, bool YBF16, bool VEC>
+__global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, const void* __restrict__ z,
+                                                         const float* __restrict__ s, int64_t rows, int64_t cols,
+                                                         int64_t rpg, double* __restrict__ part) {
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c0 >= cols) return;
+    const int64_t g = blockIdx.y;
+    const int64_t r0 = g * rpg, r1 = min(rows, r0 + rpg);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (OP != 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = c0 + e < cols ? s[c0 + e] : 1.0f;
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        float yv[4], zv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        const int64_t base = r * cols + c0;
+        if constexpr (VEC && !YBF16) {
+            const float4 v = *(const float4*)((const float*)y + base);
+            yv[0] = v.x; yv[1] = v.y; yv[2] = v.z; yv[3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yv[e] = c0 + e < cols ? load_val<YBF16>(y, base + e) : 0.0f;
+        }
+        if constexpr (ZK == 1 && VEC) {
+            const float4 v = *(const float4*)((const float*)z + base);
+            zv[0] = v.x; zv[1] = v.y; zv[2] = v.z; zv[3] = v.w;
+        } else if constexpr (ZK == 2 && VEC) {
+            const u32x2 v = *(const u32x2*)((const uint16_t*)z + base);
+            zv[0] = bf16_lo(v.x); zv[1] = bf16_hi(v.x); zv[2] = bf16_lo(v.y); zv[3] = bf16_hi(v.y);
+        } else if constexpr (ZK != 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zv[e] = c0 + e < cols ? load_val<ZK == 2>(z, base + e) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += (double)yv[e] * (double)zv[e];
+        if constexpr (OP != 0) {
+            float out[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = OP == 1 ? yv[e] / sc[e] : yv[e] * sc[e];
+            if constexpr (VEC) {
+                *(float4*)((float*)y + base) = make_float4(out[0], out[1], out[2], out[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < cols) ((float*)y)[base + e] = out[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (c0 + e < cols) part[g * cols + c0 + e] = acc[e];
+}
+
+// ds_j and its term of dalpha:
+//   ds_j   = sum_g pw[g][j] - (sum_g px[g][j]) / s_j^2
+//   term_j = ds_j * s_raw_j * (ln mx_j + ln mw_j) where s_raw_j >= 1e-8,
+//            else 0 (the floor of s passes no gradient); 0 without mx
+__global__ __launch_bounds__(256) void ste_ds_kernel(const double* __restrict__ px, int64_t gx,
+                                                     const double* __restrict__ pw, int64_t gw,
+                                                     const float* __restrict__ s, const float* __restrict__ mx,
+                                                     const float* __restrict__ mw, double a_x, double a_w, int64_t k,
+                                                     float* __restrict__ ds_out, double* __restrict__ term) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= k) return;
+    double sw_ = 0.0, sx_ = 0.0;
+    for (int64_t g = 0; g < gw; ++g) sw_ += pw[g * k + j];
+    for (int64_t g = 0; g < gx; ++g) sx_ += px[g * k + j];
+    const double sj = (double)s[j];
+    const double ds = sw_ - sx_ / (sj * sj);
+    if (ds_out) ds_out[j] = (float)ds;
+    double tj = 0.0;
+    if (mx) {
+        const float mxj = fmaxf(mx[j], kFloor);
+        const float num = (float)pow64((double)mxj, a_x);
+        const float den = (float)pow64((double)mw[j], a_w);
+        const float raw = num / den;
+        if (raw >= kFloor) tj = ds * (double)raw * (log((double)mxj) + log((double)mw[j]));
+    }
+    term[j] = tj;
+}
+
+// out[0] = dalpha = sum_j term[j], out[1] = deta = dalpha alpha (1 - alpha):
+// one block, each thread a strided range in order, then a fixed tree.
+__global__ __launch_bounds__(256) void ste_alpha_kernel(const double* __restrict__ term, int64_t k, double alpha,
+                                                        double* __restrict__ out) {
+    __shared__ double red[256];
+    double acc = 0.0;
+    for (int64_t j = threadIdx.x; j < k; j += 256) acc += term[j];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out[0] = red[0];
+        out[1] = red[0] * alpha * (1.0 - alpha);
+    }
+}
+
+// db[o] = sum_g pb[g][o] (binary64 in group order, then fp32)
+__global__ __launch_bounds__(256) void ste_bias_kernel(const double* __restrict__ pb, int64_t groups, int64_t n,
+                                                       float* __restrict__ db) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= n) return;
+    double acc = 0.0;
+    for (int64_t g = 0; g < groups; ++g) acc += pb[g * n + o];
+    db[o] = (float)acc;
+}
+
+// dy_q[i] = 2 (y_q[i] - y_fp[i]) / den and loss = ||y_fp - y_q||^2 / den with
+// den = max(||y_fp||^2, 1e-24), from the two norms in norms[0], norms[1]
+__global__ __launch_bounds__(256) void ste_aux_grad_kernel(const float* __restrict__ y_fp, const float* __restrict__ y_q,
+                                                           int64_t count, const double* __restrict__ norms,
+                                                           float* __restrict__ dy_q, double* __restrict__ loss) {
+    const double f = norms[1], d = norms[0];
+    const double den = fmax(f * f, 1e-24);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride)
+        dy_q[i] = (float)(2.0 * ((double)y_q[i] - (double)y_fp[i]) / den);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *loss = d * d / den;
+}
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// row groups of a column-sum pass: about 2048 blocks in all, at least 8
+// rows per group, at most 1024 groups
+int64_t colsum_groups(int64_t rows, int64_t cols) {
+    const int64_t gx = (cols + 1023) / 1024;
+    int64_t g = 2048 / gx;
+    g = std::max<int64_t>(1, std::min<int64_t>(g, (rows + 7) / 8));
+    return std::min<int64_t>(g, 1024);
+}
+
+template <int ZK, int OP, bool YBF16>
+hipError_t launch_colsum(void* y, const void* z, const float* s, int64_t rows, int64_t cols, int64_t groups,
+                         double* part, bool vec, hipStream_t st) {
+    const int64_t rpg = (rows + groups - 1) / groups;
+    const dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)groups);
+    if (vec)
+        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, true>), grid, dim3(256), 0, st, y, z, s, rows, cols, rpg,
+                           part);
+    else
+        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, false>), grid, dim3(256), 0, st, y, z, s, rows, cols,
+                           rpg, part);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace layout of the straight-through backward (each region 256-byte
+// aligned): the two packed factors, the two transposed codes, the column
+// partial sums of the three passes and the per-channel terms of dalpha.
+SteLayout sq_ste_layout(int64_t m, int64_t n, int64_t k) {
+    SteLayout L{};
+    const int64_t m64 = pad64(m), n64 = pad64(n);
+    L.m64 = m64;
+    L.n64 = n64;
+    L.gx = colsum_groups(m, k);
+    L.gw = colsum_groups(n, k);
+    L.gb = colsum_groups(m, n);
+    size_t off = 0;
+    L.a1 = off; off = align256(off + (size_t)m * 3 * n64 * 2);
+    L.bw = off; off = align256(off + (size_t)k * n64 * 2);
+    L.a2 = off; off = align256(off + (size_t)n * 3 * m64 * 2);
+    L.bx = off; off = align256(off + (size_t)k * m64 * 2);
+    L.px = off; off = align256(off + (size_t)L.gx * k * 8);
+    L.pw = off; off = align256(off + (size_t)L.gw * k * 8);
+    L.pb = off; off = align256(off + (size_t)L.gb * n * 8);
+    L.term = off; off = align256(off + (size_t)k * 8);
+    L.bytes = off;
+    return L;
+}
+
+hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_t n, int64_t k, const void* x,
+                                  int x_bf16, const void* w, int w_bf16, const float* s, const int8_t* xq,
+                                  const float* sx, const int8_t* wq, const float* sw, const float* mx,
+                                  const float* mw, double alpha, float* dx, float* dw, float* db, float* ds,
+                                  double* dalpha_deta, void* workspace, hipStream_t st) {
+    const SteLayout L = sq_ste_layout(m, n, k);
+    char* base = (char*)workspace;
+    uint16_t* a1 = (uint16_t*)(base + L.a1);
+    uint16_t* bw = (uint16_t*)(base + L.bw);
+    uint16_t* a2 = (uint16_t*)(base + L.a2);
+    uint16_t* bx = (uint16_t*)(base + L.bx);
+    double* px = (double*)(base + L.px);
+    double* pw = (double*)(base + L.pw);
+    double* pb = (double*)(base + L.pb);
+    double* term = (double*)(base + L.term);
+    hipError_t e;
+    // gX: a1 = RN32(dy * sw) in three planes [m][3 n64], bw = wq^T [k][n64]
+    {
+        const dim3 grid((unsigned)((L.n64 + 1023) / 1024), (unsigned)std::min<int64_t>(m, 65535));
+        if (dy_bf16) hipLaunchKernelGGL(ste_pack_rows_kernel<true>, grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+        else hipLaunchKernelGGL(ste_pack_rows_kernel<false>, grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+        hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.n64 / 64) * ((k + 63) / 64))), dim3(256), 0,
+                           st, wq, n, k, L.n64, bw);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = sq_launch_gemm_bf16_periodic(a1, bw, m, k, 3 * L.n64 * 2, L.n64 * 2, dx, st);
+        if (e != hipSuccess) return e;
+    }
+    // gW: a2 = RN32(dy^T * sx) in three planes [n][3 m64], bx = xq^T [k][m64]
+    {
+        const dim3 grid((unsigned)((L.m64 / 64) * ((n + 63) / 64)));
+        if (dy_bf16) hipLaunchKernelGGL(ste_pack_cols_kernel<true>, grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+        else hipLaunchKernelGGL(ste_pack_cols_kernel<false>, grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+        hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.m64 / 64) * ((k + 63) / 64))), dim3(256), 0,
+                           st, xq, m, k, L.m64, bx);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = sq_launch_gemm_bf16_periodic(a2, bx, n, k, 3 * L.m64 * 2, L.m64 * 2, dw, st);
+        if (e != hipSuccess) return e;
+    }
+    // dx = gX / s with sum_t gX x;  dw = gW * s with sum_o gW w
+    e = x_bf16 ? launch_colsum<2, 1, false>(dx, x, s, m, k, L.gx, px, true, st)
+               : launch_colsum<1, 1, false>(dx, x, s, m, k, L.gx, px, true, st);
+    if (e != hipSuccess) return e;
+    e = w_bf16 ? launch_colsum<2, 2, false>(dw, w, s, n, k, L.gw, pw, true, st)
+               : launch_colsum<1, 2, false>(dw, w, s, n, k, L.gw, pw, true, st);
+    if (e != hipSuccess) return e;
+    // ds, dalpha, deta
+    hipLaunchKernelGGL(ste_ds_kernel, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, st, px, L.gx, pw, L.gw, s, mx,
+                       mw, alpha, 1.0 - alpha, k, ds, term);
+    hipLaunchKernelGGL(ste_alpha_kernel, dim3(1), dim3(256), 0, st, term, k, alpha, dalpha_deta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // db = sum_t dy
+    if (db) {
+        e = dy_bf16 ? launch_colsum<0, 0, true>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st)
+                    : launch_colsum<0, 0, false>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(ste_bias_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb, L.gb, n, db);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t sq_launch_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, double* partial,
+                                   double* norms, float* dy_q, double* loss, hipStream_t st) {
+    hipError_t e = sq_launch_relative_error(y_fp, y_q, count, partial, norms, st);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
+    hipLaunchKernelGGL(ste_aux_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, st, y_fp, y_q, count, norms, dy_q,
+                       loss);
+    return hipGetLastError();
+}
