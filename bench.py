@@ -7,7 +7,7 @@ Default workload (the headline): the transformer block's O projection
 (M = N = K = 4096, bf16 in and out, alpha = 0.5, calibrated on 512 separate
 tokens fed as 4 batches of 128). One step is one pass of the whole path
 over one batch of synthetic input:
-  reset the running max -> 4 x sq_calibrate -> sq_prepare_weight_tiled ->
+  sq_calibrate_first + 3 x sq_calibrate -> sq_prepare_weight_tiled ->
   sq_quantize_act_tiled -> sq_w8a8_gemm_tiled (int8 GEMM + fused dequant),
 the int8 codes kept in 16 x 64 tiles (--layout row: the row-major calls
 sq_prepare_weight, sq_quantize_act and sq_w8a8_gemm instead).
@@ -404,7 +404,7 @@ def main():
     elif mode == "per_tensor":
         stage_names = ["quantize_weight", "quantize_act", "gemm"]
     else:
-        stage_names = ["reset+calibrate", "prepare_weight", "quantize_act", "gemm"]
+        stage_names = ["calibrate", "prepare_weight", "quantize_act", "gemm"]
 
     # every call of a step marshalled once per buffer set (binding.prepared):
     # the timed loop then only repeats the C calls
@@ -429,7 +429,8 @@ def main():
                 s["call_gemm"] = B.prepared(B.sq_wo_linear, s["x"], s["wq"], s["ws"], s["bias"], s["y"], stream)
             continue
         if mode == "full":
-            s["calls_calib"] = [B.prepared(B.sq_calibrate, cb, s["run"], stream) for cb in s["calib"]]
+            s["calls_calib"] = [B.prepared(B.sq_calibrate_first if i == 0 else B.sq_calibrate, cb, s["run"], stream)
+                                for i, cb in enumerate(s["calib"])]
         if tiled:
             if mode == "full":
                 s["call_prep"] = B.prepared(B.sq_prepare_weight_tiled, s["w"], s["run"], alpha, s["smooth"],
@@ -454,7 +455,8 @@ def main():
 
         mark()
         if mode == "full":
-            s["run"].zero_()
+            # the first batch starts the running max (sq_calibrate_first:
+            # no zero fill), the others fold into it
             for call in s["calls_calib"]:
                 call()
             mark()
@@ -522,6 +524,24 @@ def main():
     torch.cuda.synchronize()
     gemm_warm_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
+    # the per-call linear (SURVEY's second figure): activation codes + the
+    # product, as a forward runs them on prepared weights, GEMM_LAUNCHES
+    # calls in one graph over the rotated sets, replayed between events
+    per_call_ms = None
+    if mode in ("full", "per_call"):
+        pc_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pc_graph, stream=stream):
+            for i in range(GEMM_LAUNCHES):
+                sets[i % rotate]["call_act"]()
+                sets[i % rotate]["call_gemm"]()
+        pc_graph.replay()
+        torch.cuda.synchronize()
+        gev[0].record(stream)
+        pc_graph.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize()
+        per_call_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
+
     # stage breakdown: a second pass of K steps with an event between stages
     # (every event adds a few microseconds between kernels, so this pass is
     # not the throughput figure)
@@ -538,8 +558,8 @@ def main():
     # per-launch floor between dependent kernels included, no event gaps);
     # these figures give the stages' rooflines
     def stage_calls(s, nm):
-        if nm == "reset+calibrate":
-            return [s["run"].zero_] + s["calls_calib"]
+        if nm == "calibrate":
+            return s["calls_calib"]
         if nm in ("prepare_weight", "quantize_weight"):
             return [s["call_prep"]]
         if nm == "quantize_act":
@@ -568,7 +588,6 @@ def main():
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     act_ms = stage_graph_ms.get("quantize_act", 0.0)
-    linear_tops = ops / ((act_ms + gemm_ms) * 1e-3) / 1e12
 
     def hbm(bytes_, ms):
         gbs = bytes_ / (ms * 1e-3) / 1e9
@@ -587,7 +606,7 @@ def main():
         stage_roof = {"quantize_act": hbm(m * k * 2 + m * k + 4 * m + 4 * k, act_ms)}
     if mode == "full":
         stage_roof["prepare_weight"] = hbm(2 * n * k * 2 + n * k + 4 * n + 8 * k, stage_graph_ms["prepare_weight"])
-        stage_roof["reset+calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_graph_ms["reset+calibrate"])
+        stage_roof["calibrate"] = hbm(calib_rows * k * 2 + 8 * k, stage_graph_ms["calibrate"])
     kernel_name = (("int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_per_tensor_tiled)" if tiled
                     else "int8 GEMM + fused dequant (sq_w8a8_gemm_per_tensor)") if mode == "per_tensor"
                    else "int8 GEMM + fused dequant on 16 x 64 tiles (sq_w8a8_gemm_tiled)" if tiled
@@ -649,10 +668,17 @@ def main():
         "stages_us": stages,
         "stages_us_graph": stages_graph,
         "stage_rooflines": stage_roof,
-        "linear_tops": round(linear_tops, 2),
         "gemm_tops": round(gemm_tops, 2),
         "wall_s_timed": round(t_wall, 4),
     }
+    if per_call_ms is not None:
+        line["per_call_linear_us"] = round(per_call_ms * 1e3, 2)
+        line["per_call_linear_tops"] = round(ops / (per_call_ms * 1e-3) / 1e12, 2)
+        line["per_call_note"] = ("activation codes + int8 product + dequant on prepared weights "
+                                 f"({'sq_quantize_act_tiled + sq_w8a8_gemm_tiled' if tiled else 'sq_quantize_act + sq_w8a8_gemm'}), "
+                                 f"{GEMM_LAUNCHES} calls in one graph over the rotated sets")
+    line["value_is"] = ("the whole step (calibration, weight preparation, activation codes, product) per "
+                        "unit time" if mode == "full" else "one call per unit time")
     if mode == "full" and len(case.alphas) > 1:
         line["alpha_sweep"] = alpha_sweep(torch, B, case, sets[0], stream)
     if not args.no_cpu_baseline:

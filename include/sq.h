@@ -93,6 +93,18 @@ sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k,
                        float* running_max_abs, void* stream);
 
 /*
+ * sq_calibrate_first -- the first batch of a calibration: the running max
+ * starts from this batch alone, whatever the buffer held,
+ *   running_max_abs[j] = max_r |x[r][j]|       (0 for rows == 0)
+ * i.e. sq_calibrate on a zero-filled buffer, without the caller's fill
+ * (one launch when the batch fits one row group of the column max, up to
+ * 128 rows). Later batches go through sq_calibrate. Arguments as
+ * sq_calibrate; x may be NULL when rows == 0.
+ */
+sq_status sq_calibrate_first(const void* x, sq_dtype xt, int64_t rows, int64_t k,
+                             float* running_max_abs, void* stream);
+
+/*
  * sq_prepare_weight -- the smoothing factor s and the int8 weights.
  * Follows calibrate_smoothquant + SmoothQuantW8A8.freeze_quantization
  * (page "w8a8_smoothquant.py"); calling it again with another alpha is

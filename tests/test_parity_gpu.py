@@ -67,6 +67,28 @@ def test_calibrate(orc, shape, dtype):
     assert_equal(down(run), orc.calibrate(c.x.f32), "running max")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,k", [(1, 16), (128, 4096), (129, 272), (2048, 4096), (5000, 1040), (64, 16384)],
+                         ids=lambda v: str(v))
+def test_calibrate_first(orc, rows, k, dtype):
+    """sq_calibrate_first starts the running max from its batch whatever the
+    buffer held (here values larger than any |x|), through the one-launch
+    path (one row group) and the fill-and-fold path (several); later
+    batches fold as usual."""
+    c = inputs.small(rows, 8, k, seed=rows + k, dtype=dtype, bias=False)
+    x = up(c.x)
+    run = torch.full((k,), 1e30, dtype=torch.float32, device=DEV)
+    half = rows // 2
+    B.sq_calibrate_first(x[half:], run)
+    B.sq_calibrate(x[:half], run)
+    torch.cuda.synchronize()
+    assert_equal(down(run), orc.calibrate(c.x.f32), "running max")
+    empty = torch.full((k,), 5.0, dtype=torch.float32, device=DEV)
+    B.sq_calibrate_first(x[:0], empty)
+    torch.cuda.synchronize()
+    assert not down(empty).any()
+
+
 # ---------------------------------------------------------------------------
 # a2-a5: s, int8 weights, weight scales
 # ---------------------------------------------------------------------------

@@ -41,6 +41,7 @@ _P, _I64, _SZ, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes
 
 _SIGNATURES = {
     "sq_calibrate": ([_P, _E, _I64, _I64, _P, _P], _E),
+    "sq_calibrate_first": ([_P, _E, _I64, _I64, _P, _P], _E),
     "sq_prepare_weight": ([_P, _E, _I64, _I64, _P, _F, _P, _P, _P, _P], _E),
     "sq_quantize_act": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
     "sq_w8a8_gemm": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
@@ -193,6 +194,15 @@ def sq_calibrate(x: torch.Tensor, running_max_abs: torch.Tensor, stream=None) ->
     _need_dtype(running_max_abs, torch.float32, "running_max_abs")
     return _invoke("sq_calibrate", _ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
                    _stream(stream, x))
+
+
+def sq_calibrate_first(x: torch.Tensor, running_max_abs: torch.Tensor, stream=None) -> int:
+    """running_max_abs[j] = max_r |x[r, j]| (a first batch; no zero fill needed)."""
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    _need_dtype(running_max_abs, torch.float32, "running_max_abs")
+    return _invoke("sq_calibrate_first", _ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
+                   _stream(stream, running_max_abs))
 
 
 def sq_prepare_weight(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: float, smooth: torch.Tensor,
@@ -584,7 +594,10 @@ class SmoothQuantLinear:
         if self.is_quantized:
             raise RuntimeError("calibration after freeze is not allowed")
         x2 = x.reshape(-1, x.shape[-1])
-        sq_calibrate(x2, self.calib_max_abs)
+        if self.calib_count == 0:
+            sq_calibrate_first(x2, self.calib_max_abs)
+        else:
+            sq_calibrate(x2, self.calib_max_abs)
         self.calib_count += x2.shape[0]
 
     def freeze(self) -> int:

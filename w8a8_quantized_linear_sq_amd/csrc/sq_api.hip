@@ -70,6 +70,17 @@ sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k, floa
     return launched(sq_launch_colmax(x, xt == SQ_BF16, rows, k, running_max_abs, as_stream(stream)));
 }
 
+sq_status sq_calibrate_first(const void* x, sq_dtype xt, int64_t rows, int64_t k, float* running_max_abs,
+                             void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (rows < 0 || rows > kMaxRows) return SQ_ERR_SHAPE;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    if (!running_max_abs || (rows > 0 && !x)) return SQ_ERR_ARG;
+    if ((rows > 0 && !aligned16(x)) || !aligned16(running_max_abs)) return SQ_ERR_ALIGN;
+    return launched(sq_launch_colmax_first(x, xt == SQ_BF16, rows, k, running_max_abs, as_stream(stream)));
+}
+
 sq_status sq_prepare_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* x_max_abs,
                             float alpha, float* smooth, int8_t* w_q, float* w_scale, void* stream) {
     if (!fp_in(wt)) return SQ_ERR_DTYPE;

@@ -49,6 +49,10 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st);
 // running column max of |x| folded into running_max (calibration)
 hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
                             hipStream_t st);
+// the same for a first batch: running_max = the batch's column max, whatever
+// it held (one launch when the batch fits one row group)
+hipError_t sq_launch_colmax_first(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
+                                  hipStream_t st);
 // row groups for a partial column max whose [groups][k] uint32 result must
 // fit in scratch_bytes (at least 1)
 int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes);

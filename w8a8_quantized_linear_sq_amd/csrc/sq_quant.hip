@@ -45,14 +45,16 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 // patterns as unsigned integers is the order of the values: every max is an
 // exact integer max, independent of order.
 //   FOLD:    out[j] = max(out[j], max) -- one row group: the owning thread
-//            updates in place; several: integer atomicMax (the running max of
-//            calibration keeps its value across calls);
+//            updates in place (or, with `overwrite`, writes the max without
+//            reading out: a first calibration batch); several: integer
+//            atomicMax (the running max of calibration keeps its value
+//            across calls);
 //   PARTIAL: out[g * k + j] = max over row group g (plain stores).
 // ---------------------------------------------------------------------------
 template <bool BF16, bool FOLD, int L>
 __global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
                                                      int64_t rows_per_group, int64_t k,
-                                                     unsigned* __restrict__ out) {
+                                                     unsigned* __restrict__ out, int overwrite) {
     constexpr int U = 8;
     constexpr int W = 64 / L;  // chunks per strip
     __shared__ u32x4 red[4][64];
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x
     if constexpr (FOLD) {
         if (gridDim.y == 1) {
 #pragma unroll
-            for (int i = 0; i < NC; ++i) out[col0 + i] = max(out[col0 + i], val[i]);
+            for (int i = 0; i < NC; ++i) out[col0 + i] = overwrite ? val[i] : max(out[col0 + i], val[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < NC; ++i) atomicMax(out + col0 + i, val[i]);
@@ -144,23 +146,23 @@ static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups
 
 template <bool FOLD, int L>
 static void launch_colmax_l(const void* x, int bf16, int64_t rows, int64_t kvec, int64_t k, unsigned* out,
-                            int64_t groups, int64_t rpg, hipStream_t st) {
+                            int64_t groups, int64_t rpg, int overwrite, hipStream_t st) {
     dim3 grid((unsigned)((kvec + 64 / L - 1) / (64 / L)), (unsigned)groups);
     if (bf16)
         hipLaunchKernelGGL((colmax_kernel<true, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
-                           k, out);
+                           k, out, overwrite);
     else
         hipLaunchKernelGGL((colmax_kernel<false, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
-                           k, out);
+                           k, out, overwrite);
 }
 
 template <bool FOLD>
 static hipError_t launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, unsigned* out, int64_t groups,
-                                int64_t rpg, hipStream_t st) {
+                                int64_t rpg, hipStream_t st, int overwrite = 0) {
     const int64_t kvec = bf16 ? k / 8 : k / 4;
     switch (colmax_l(rows)) {
-        case 1: launch_colmax_l<FOLD, 1>(x, bf16, rows, kvec, k, out, groups, rpg, st); break;
-        default: launch_colmax_l<FOLD, 4>(x, bf16, rows, kvec, k, out, groups, rpg, st); break;
+        case 1: launch_colmax_l<FOLD, 1>(x, bf16, rows, kvec, k, out, groups, rpg, overwrite, st); break;
+        default: launch_colmax_l<FOLD, 4>(x, bf16, rows, kvec, k, out, groups, rpg, overwrite, st); break;
     }
     return hipGetLastError();
 }
@@ -170,6 +172,19 @@ hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, fl
     if (rows <= 0) return hipSuccess;
     int64_t gx, groups, rpg;
     colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg);
+    return launch_colmax<true>(x, bf16, rows, k, (unsigned*)running_max, groups, rpg, st);
+}
+
+hipError_t sq_launch_colmax_first(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
+                                  hipStream_t st) {
+    if (rows <= 0) return sq_launch_fill(running_max, 0.0f, k, st);
+    int64_t gx, groups, rpg;
+    colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg);
+    if (groups == 1)  // one row group: its owners write the max directly
+        return launch_colmax<true>(x, bf16, rows, k, (unsigned*)running_max, 1, rpg, st, 1);
+    // several row groups fold with atomics into a zeroed buffer
+    hipError_t e = sq_launch_fill(running_max, 0.0f, k, st);
+    if (e != hipSuccess) return e;
     return launch_colmax<true>(x, bf16, rows, k, (unsigned*)running_max, groups, rpg, st);
 }
 
