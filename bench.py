@@ -438,6 +438,12 @@ def main():
             s["call_act"] = B.prepared(B.sq_quantize_act_tiled, s["x"], s["smooth"], s["xq"], s["xs"], stream)
             s["call_gemm"] = B.prepared(B.sq_w8a8_gemm_tiled, s["xq"], s["xs"], m, s["wq"], s["ws"], n, k,
                                         s["bias"], s["y"], stream)
+            if mode == "per_call" and m <= 64:
+                # the same forward as one kernel (sq_w8a8_linear_tiled_fused:
+                # the weight stream quantises the activations itself)
+                s["fws"] = B.linear_tiled_workspace(m, k, dev, fused=True)
+                s["call_fused"] = B.prepared(B.sq_w8a8_linear_tiled_fused, s["x"], s["smooth"], s["wq"], s["ws"],
+                                             n, s["bias"], s["y"], s["fws"], stream)
             continue
         if mode == "full":
             s["call_prep"] = B.prepared(B.sq_prepare_weight, s["w"], s["run"], alpha, s["smooth"], s["wq"],
@@ -541,6 +547,19 @@ def main():
         gev[1].record(stream)
         torch.cuda.synchronize()
         per_call_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
+    fused_ms = None
+    if "call_fused" in sets[0]:
+        f_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(f_graph, stream=stream):
+            for i in range(GEMM_LAUNCHES):
+                sets[i % rotate]["call_fused"]()
+        f_graph.replay()
+        torch.cuda.synchronize()
+        gev[0].record(stream)
+        f_graph.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize()
+        fused_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
     # stage breakdown: a second pass of K steps with an event between stages
     # (every event adds a few microseconds between kernels, so this pass is
@@ -677,6 +696,13 @@ def main():
         line["per_call_note"] = ("activation codes + int8 product + dequant on prepared weights "
                                  f"({'sq_quantize_act_tiled + sq_w8a8_gemm_tiled' if tiled else 'sq_quantize_act + sq_w8a8_gemm'}), "
                                  f"{GEMM_LAUNCHES} calls in one graph over the rotated sets")
+    if fused_ms is not None:
+        line["per_call_fused_us"] = round(fused_ms * 1e3, 2)
+        line["per_call_fused_tops"] = round(ops / (fused_ms * 1e-3) / 1e12, 2)
+        line["per_call_fused_note"] = ("the same forward as one kernel, sq_w8a8_linear_tiled_fused (the weight "
+                                       f"stream quantises the activations itself), {GEMM_LAUNCHES} calls in one "
+                                       "graph over the rotated sets")
+        line["per_call_fused_fallbacks"] = sum(B.linear_tiled_fallbacks(s["fws"]) for s in sets)
     line["value_is"] = ("the whole step (calibration, weight preparation, activation codes, product) per "
                         "unit time" if mode == "full" else "one call per unit time")
     if mode == "full" and len(case.alphas) > 1:

@@ -516,6 +516,55 @@ size_t sq_aux_loss_grad_workspace_bytes(int64_t count);
 sq_status sq_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, float* dy_q,
                            double* loss, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sq_w8a8_linear_tiled -- one frozen forward on weights in the tiled layout
+ * (SmoothQuantW8A8.forward, quantized branch, page "w8a8_smoothquant.py"):
+ * sq_quantize_act_tiled then sq_w8a8_gemm_tiled (the same codes, scales and
+ * output bits), the codes in the caller's workspace.
+ *   x         [m][k] in xt; smooth [k]; w_q in 16 x 64 tiles (from
+ *             sq_prepare_weight_tiled), w_scale [n]
+ *   bias      [n] in bias_t (F32 or BF16), or NULL; y [m][n] in yt
+ *   workspace sq_w8a8_linear_tiled_workspace_bytes(m, k) bytes, 256-byte
+ *             aligned: the tiled x_q at byte 0, then x_scale [m] at the
+ *             next 256-byte boundary
+ */
+size_t sq_w8a8_linear_tiled_workspace_bytes(int64_t m, int64_t k);
+sq_status sq_w8a8_linear_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                               const float* smooth, const int8_t* w_q, const float* w_scale,
+                               int64_t n, const void* bias, sq_dtype bias_t, void* y,
+                               sq_dtype yt, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * sq_w8a8_linear_tiled_fused -- sq_w8a8_linear_tiled for up to 64 tokens as
+ * ONE kernel, the activation quantisation fused into the weight-streaming
+ * product's prologue: workgroup b quantises tokens b, b + grid, ... and
+ * publishes each (a flag per token); every workgroup waits, bounded, for
+ * the tokens, and one whose wait runs out quantises the missing tokens
+ * itself (the same bytes). The same codes, scales and output bits as
+ * sq_w8a8_linear_tiled. Measured slower on the decode shape (16 x 4096 ->
+ * 11008: 22.5 us against 14.5 us for the two launches): the publication
+ * puts several dependent memory round trips ahead of the first multiply.
+ *   m         1 to 64 (SQ_ERR_SHAPE beyond)
+ *   workspace sq_w8a8_linear_tiled_fused_workspace_bytes(m, k) bytes,
+ *             256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE: its first
+ *             1 KiB holds synchronisation words that every call leaves
+ *             consistent for the next; then the tiled x_q (byte 1024) and
+ *             x_scale [m]. Calls that share a workspace must not overlap.
+ * The other arguments as sq_w8a8_linear_tiled.
+ */
+size_t sq_w8a8_linear_tiled_fused_workspace_bytes(int64_t m, int64_t k);
+sq_status sq_w8a8_linear_tiled_fused(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                                     const float* smooth, const int8_t* w_q, const float* w_scale,
+                                     int64_t n, const void* bias, sq_dtype bias_t, void* y,
+                                     sq_dtype yt, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+/* Test hook of sq_w8a8_linear_tiled_fused: the polls (about 60 ns each) a
+ * workgroup waits for the other workgroups' tokens before it quantises them
+ * itself (default 4096; 0 makes every workgroup quantise every token
+ * itself). Process-wide; not for concurrent use with calls. */
+void sq_set_fused_wait_polls(int polls);
+
 /* Workspace bytes sq_w8a8_linear needs for m tokens of k channels. */
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k);
 

@@ -446,3 +446,30 @@ def test_aux_loss_grad_errors(L):
     assert f(None, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need, None) == B.SQ_ERR_ARG
     assert f(OK_PTR, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need - 1, None) == B.SQ_ERR_WORKSPACE
     assert f(BAD, OK_PTR, 100, OK_PTR, OK_PTR, OK_PTR, need, None) == B.SQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_linear_tiled_errors(L, fused):
+    f = L.sq_w8a8_linear_tiled_fused if fused else L.sq_w8a8_linear_tiled
+    need = (L.sq_w8a8_linear_tiled_fused_workspace_bytes if fused else L.sq_w8a8_linear_tiled_workspace_bytes)(4, 64)
+    assert need >= (1024 if fused else 0) + 16 * 64 + 16
+    assert L.sq_w8a8_linear_tiled_workspace_bytes(0, 64) == 0
+    if fused:
+        big = L.sq_w8a8_linear_tiled_fused_workspace_bytes(65, 64)
+        assert f(OK_PTR, B.SQ_BF16, 65, 64, OK_PTR, OK_PTR, OK_PTR, 8, None, B.SQ_F32, OK_PTR, B.SQ_BF16, OK_PTR,
+                 big, None) == B.SQ_ERR_SHAPE
+
+    def call(x=OK_PTR, xt=B.SQ_BF16, m=4, k=64, s=OK_PTR, wq=OK_PTR, sw=OK_PTR, n=8, bias=None, bt=B.SQ_F32,
+             y=OK_PTR, yt=B.SQ_BF16, ws=OK_PTR, wsb=need):
+        return f(x, xt, m, k, s, wq, sw, n, bias, bt, y, yt, ws, wsb, None)
+
+    assert call(xt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(bias=OK_PTR, bt=9) == B.SQ_ERR_DTYPE
+    assert call(n=0) == B.SQ_ERR_SHAPE
+    assert call(k=40) == B.SQ_ERR_ALIGN
+    assert call(x=None) == B.SQ_ERR_ARG
+    assert call(s=None) == B.SQ_ERR_ARG
+    assert call(ws=None) == B.SQ_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.SQ_ERR_WORKSPACE
+    assert call(ws=OK_PTR + 16) == B.SQ_ERR_ALIGN
+    assert call(m=0, x=None, y=None) == B.SQ_OK

@@ -48,6 +48,11 @@ _SIGNATURES = {
     "sq_w8a8_linear": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P, _SZ, _P], _E),
     "sq_w8a8_linear_workspace_bytes": ([_I64, _I64], _SZ),
     "sq_w8a8_linear_noalloc": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _P, _E, _P], _E),
+    "sq_w8a8_linear_tiled_workspace_bytes": ([_I64, _I64], _SZ),
+    "sq_w8a8_linear_tiled": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _E, _P, _E, _P, _SZ, _P], _E),
+    "sq_w8a8_linear_tiled_fused_workspace_bytes": ([_I64, _I64], _SZ),
+    "sq_w8a8_linear_tiled_fused": ([_P, _E, _I64, _I64, _P, _P, _P, _I64, _P, _E, _P, _E, _P, _SZ, _P], _E),
+    "sq_set_fused_wait_polls": ([ctypes.c_int], None),
     "sq_alpha_from_eta": ([_F], _F),
     "sq_eta_from_alpha": ([ctypes.c_double], _F),
     "sq_ste_backward_workspace_bytes": ([_I64, _I64, _I64], _SZ),
@@ -475,6 +480,68 @@ def sq_w8a8_linear(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_s
                    _ptr(bias), _ptr(y), _dtype_code(y), _ptr(workspace), nbytes, _stream(stream, x))
 
 
+def sq_w8a8_linear_tiled_workspace_bytes(m: int, k: int) -> int:
+    return int(lib().sq_w8a8_linear_tiled_workspace_bytes(m, k))
+
+
+def sq_w8a8_linear_tiled_fused_workspace_bytes(m: int, k: int) -> int:
+    return int(lib().sq_w8a8_linear_tiled_fused_workspace_bytes(m, k))
+
+
+def linear_tiled_workspace(m: int, k: int, device, fused: bool = False) -> torch.Tensor:
+    """A workspace for sq_w8a8_linear_tiled, or zero-filled for
+    sq_w8a8_linear_tiled_fused (the zeros are the initial state of its
+    synchronisation words)."""
+    nbytes = (sq_w8a8_linear_tiled_fused_workspace_bytes if fused else sq_w8a8_linear_tiled_workspace_bytes)(m, k)
+    return torch.zeros(max(nbytes, 1024 if fused else 256), dtype=torch.uint8, device=device)
+
+
+def linear_tiled_views(workspace: torch.Tensor, m: int, k: int, fused: bool = False):
+    """(x_q in tiles (flat int8), x_scale [m] fp32) views of a
+    sq_w8a8_linear_tiled(_fused) workspace."""
+    base = 1024 if fused else 0
+    tb = sq_tiled_bytes(m, k)
+    off = base + (tb + 255) // 256 * 256
+    return workspace[base: base + tb].view(torch.int8), workspace[off: off + 4 * m].view(torch.float32)
+
+
+def linear_tiled_fallbacks(workspace: torch.Tensor) -> int:
+    """How many workgroups of sq_w8a8_linear_tiled_fused have run out of
+    polls and quantised the tokens themselves, over every call on this
+    workspace (a statistic the synchronisation words keep)."""
+    return int(workspace[16:24].view(torch.int64).item())
+
+
+def sq_w8a8_linear_tiled(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor, n: int,
+                         bias: torch.Tensor | None, y: torch.Tensor, workspace: torch.Tensor, stream=None) -> int:
+    """One forward on tiled int8 weights (activation codes into the
+    workspace, then the product)."""
+    m, k = x.shape
+    _need_tiled(w_q, n, k, "w_q")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    nbytes = workspace.numel() * workspace.element_size()
+    return _invoke("sq_w8a8_linear_tiled", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q), _ptr(w_scale), n,
+                   _ptr(bias), bt, _ptr(y), _dtype_code(y), _ptr(workspace), nbytes, _stream(stream, x))
+
+
+def sq_w8a8_linear_tiled_fused(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                               n: int, bias: torch.Tensor | None, y: torch.Tensor, workspace: torch.Tensor,
+                               stream=None) -> int:
+    """The same forward as one kernel (up to 64 tokens); the workspace
+    (linear_tiled_workspace(..., fused=True)) must have been zero-filled once."""
+    m, k = x.shape
+    _need_tiled(w_q, n, k, "w_q")
+    bt = _dtype_code(bias) if bias is not None else SQ_F32
+    nbytes = workspace.numel() * workspace.element_size()
+    return _invoke("sq_w8a8_linear_tiled_fused", _ptr(x), _dtype_code(x), m, k, _ptr(smooth), _ptr(w_q),
+                   _ptr(w_scale), n, _ptr(bias), bt, _ptr(y), _dtype_code(y), _ptr(workspace), nbytes,
+                   _stream(stream, x))
+
+
+def sq_set_fused_wait_polls(polls: int) -> None:
+    lib().sq_set_fused_wait_polls(int(polls))
+
+
 def sq_w8a8_linear_noalloc(x: torch.Tensor, smooth: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
                            bias: torch.Tensor | None, y: torch.Tensor, stream=None) -> int:
     """sq_w8a8_linear with the activation codes in the library's own fixed
@@ -555,8 +622,8 @@ class SmoothQuantLinear:
     layout "row" keeps the int8 weights as [n][k] row-major and runs the
     forward as one sq_w8a8_linear call (sq_quantize_act + sq_w8a8_gemm when
     the bias type differs from x's); "tiled" keeps them in 16 x 64 tiles
-    (flat, sq_tiled_bytes(n, k)) and runs the forward as
-    sq_quantize_act_tiled + sq_w8a8_gemm_tiled. Both give the same smoothing
+    (flat, sq_tiled_bytes(n, k)) and runs the forward as one
+    sq_w8a8_linear_tiled call. Both give the same smoothing
     factor, scales, codes and outputs, bit for bit; the tiled products are
     the faster ones."""
 
@@ -707,10 +774,8 @@ class SmoothQuantLinear:
         y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
         if self.layout == "tiled":
             if m:
-                x_q = tiled_empty(m, k, x.device)
-                x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
-                sq_quantize_act_tiled(x2, self.smooth, x_q, x_scale)
-                sq_w8a8_gemm_tiled(x_q, x_scale, m, self.weight_int8, self.weight_scale, n, k, self.bias, y)
+                ws = torch.empty(sq_w8a8_linear_tiled_workspace_bytes(m, k), dtype=torch.uint8, device=x.device)
+                sq_w8a8_linear_tiled(x2, self.smooth, self.weight_int8, self.weight_scale, n, self.bias, y, ws)
         elif self.bias is not None and self.bias.dtype != x2.dtype:
             # sq_w8a8_linear takes the bias in x's type; another bias type
             # goes through the two calls it is made of, which take its type

@@ -4,6 +4,7 @@
 #include "../../include/sq.h"
 #include "sq_device.h"
 
+#include <atomic>
 #include <mutex>
 
 namespace {
@@ -383,6 +384,73 @@ sq_status sq_selfcheck_division(unsigned b_begin, unsigned b_end, unsigned long 
     if (((uintptr_t)mismatches & 7u) != 0) return SQ_ERR_ALIGN;
     if (b_begin > b_end || b_end > (1u << 23)) return SQ_ERR_SHAPE;
     return launched(sq_launch_selfcheck_division(b_begin, b_end, mismatches, as_stream(stream)));
+}
+
+// sq_w8a8_linear_tiled's workspace: the tiled codes, then the scales.
+// sq_w8a8_linear_tiled_fused's: its synchronisation words first (a fixed
+// place, whatever m), then the same.
+namespace {
+constexpr size_t kFusedSyncBytes = 1024;  // at least sq_stream_fused_sync_bytes()
+std::atomic<int> g_fused_wait_polls{4096};
+
+sq_status check_linear_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                             const int8_t* w_q, const float* w_scale, int64_t n, const void* bias, sq_dtype bias_t,
+                             const void* y, sq_dtype yt, const void* workspace, size_t workspace_bytes, size_t need) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    sq_status st = check_gemm(w_q, w_scale, m, w_q, w_scale, n, k, bias, bias_t, y, yt);
+    if (st != SQ_OK || m == 0) return st;
+    if (!x || !smooth) return SQ_ERR_ARG;
+    if (!workspace || workspace_bytes < need) return SQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return SQ_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(smooth)) return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+}  // namespace
+
+size_t sq_w8a8_linear_tiled_workspace_bytes(int64_t m, int64_t k) {
+    if (m <= 0 || k <= 0) return 0;
+    return round_up(sq_tiled_bytes(m, k), 256) + 4 * (size_t)m;
+}
+
+sq_status sq_w8a8_linear_tiled(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                               const int8_t* w_q, const float* w_scale, int64_t n, const void* bias, sq_dtype bias_t,
+                               void* y, sq_dtype yt, void* workspace, size_t workspace_bytes, void* stream) {
+    sq_status st = check_linear_tiled(x, xt, m, k, smooth, w_q, w_scale, n, bias, bias_t, y, yt, workspace,
+                                      workspace_bytes, sq_w8a8_linear_tiled_workspace_bytes(m, k));
+    if (st != SQ_OK || m == 0) return st;
+    int8_t* xq = (int8_t*)workspace;
+    float* xs = (float*)((char*)workspace + round_up(sq_tiled_bytes(m, k), 256));
+    hipStream_t s = as_stream(stream);
+    hipError_t e = sq_launch_quantize_act_tiled(x, xt == SQ_BF16, smooth, m, k, xq, xs, s);
+    if (e == hipSuccess)
+        e = sq_launch_gemm_tiled(xq, xs, m, w_q, w_scale, n, k, bias, bias_kind(bias, bias_t), y, out_kind(yt), 0, s);
+    return launched(e);
+}
+
+size_t sq_w8a8_linear_tiled_fused_workspace_bytes(int64_t m, int64_t k) {
+    if (m <= 0 || k <= 0) return 0;
+    return kFusedSyncBytes + sq_w8a8_linear_tiled_workspace_bytes(m, k);
+}
+
+void sq_set_fused_wait_polls(int polls) { g_fused_wait_polls.store(polls < 0 ? 0 : polls, std::memory_order_relaxed); }
+
+sq_status sq_w8a8_linear_tiled_fused(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* smooth,
+                                     const int8_t* w_q, const float* w_scale, int64_t n, const void* bias,
+                                     sq_dtype bias_t, void* y, sq_dtype yt, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    if (m > kStreamMaxM) return SQ_ERR_SHAPE;
+    sq_status st = check_linear_tiled(x, xt, m, k, smooth, w_q, w_scale, n, bias, bias_t, y, yt, workspace,
+                                      workspace_bytes, sq_w8a8_linear_tiled_fused_workspace_bytes(m, k));
+    if (st != SQ_OK || m == 0) return st;
+    static_assert(kFusedSyncBytes % 256 == 0, "the codes stay 256-byte aligned");
+    if (sq_stream_fused_sync_bytes() > kFusedSyncBytes) return SQ_ERR_HIP;
+    char* base = (char*)workspace;
+    int8_t* xq = (int8_t*)(base + kFusedSyncBytes);
+    float* xs = (float*)(base + kFusedSyncBytes + round_up(sq_tiled_bytes(m, k), 256));
+    return launched(sq_launch_linear_stream_fused(x, xt == SQ_BF16, smooth, m, k, xq, xs, w_q, w_scale, n, bias,
+                                                  bias_kind(bias, bias_t), y, out_kind(yt), base,
+                                                  g_fused_wait_polls.load(std::memory_order_relaxed),
+                                                  as_stream(stream)));
 }
 
 size_t sq_w8a8_linear_workspace_bytes(int64_t m, int64_t k) {

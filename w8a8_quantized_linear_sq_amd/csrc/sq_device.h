@@ -29,6 +29,32 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// The quantisers' exact division (Markstein's correction, see sq_quant.hip):
+// y = RN(1/b), q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0) = RN(a / b).
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: RN(q + kMagic)'s low byte is rint(q)
+
+// RN(1/s) for s in [2^-40, 2^40): the hardware reciprocal refined by one
+// Newton-Raphson step for 1/s in its fma form, r + r (1 - s r); on gfx950 it
+// equals the IEEE quotient 1/s for every binary32 s in [2^-100, 2^100)
+// (sq_selfcheck_reciprocal). Elsewhere NaN, which fails every guard.
+__device__ __forceinline__ float recip_rn(float s) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    return (s >= 0x1p-40f && s < 0x1p40f) ? y : __builtin_nanf("");
+}
+
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+    const float q0 = a * y;
+    return __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
+}
+
+// low bytes of four words -> one word
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // [a.b0, b.b0, 0, 0]
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // [a, b, c, d]
+}
+
 // P(x, a) = x^a through binary64 (the smoothing factor's powers): exact
 // forms built from correctly rounded sqrt for a in {0, 1/4, 1/2, 3/4, 1},
 // pow otherwise.
@@ -155,3 +181,13 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
 // y_q||^2 / that; partial: sq_relative_error_blocks(count) pairs, norms [3]
 hipError_t sq_launch_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, double* partial,
                                    double* norms, float* dy_q, double* loss, hipStream_t st);
+// the W8A8 linear for m <= kStreamMaxM in one launch: the weight stream
+// quantises the activations itself (codes to xq in 16 x 64 tiles, scales
+// to sx) before multiplying them; sync: sq_stream_fused_sync_bytes() bytes
+// of the caller's workspace, zero before the first call; wait_polls bounds
+// each workgroup's wait for the other workgroups' tokens
+hipError_t sq_launch_linear_stream_fused(const void* x, int bf16, const float* s, int64_t m, int64_t k,
+                                         int8_t* xq, float* sx, const int8_t* wq, const float* sw, int64_t n,
+                                         const void* bias, int bias_kind, void* y, int out_kind, void* sync,
+                                         int wait_polls, hipStream_t st);
+size_t sq_stream_fused_sync_bytes();

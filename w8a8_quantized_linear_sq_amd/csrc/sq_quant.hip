@@ -298,23 +298,6 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 // further row's loads are issued before the current row is finished. One
 // barrier per row (the block max goes through a double-buffered LDS slot).
 // ---------------------------------------------------------------------------
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-
-// RN(1/s) for s in [2^-40, 2^40): the hardware reciprocal refined by one
-// Newton-Raphson step for 1/s in its fma form, r + r (1 - s r); on gfx950 it
-// equals the IEEE quotient 1/s for every binary32
-// s in [2^-100, 2^100) (sq_selfcheck_reciprocal). Elsewhere NaN, which fails
-// every guard below.
-__device__ __forceinline__ float recip_rn(float s) {
-    const float r = __builtin_amdgcn_rcpf(s);
-    const float y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
-    return (s >= 0x1p-40f && s < 0x1p40f) ? y : __builtin_nanf("");
-}
-
-__device__ __forceinline__ float div_rn(float a, float b, float y) {
-    const float q0 = a * y;
-    return __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
-}
 
 __global__ __launch_bounds__(256) void selfcheck_reciprocal_kernel(unsigned long long* mismatches) {
     const unsigned long long idx = (unsigned long long)blockIdx.x * 256 + threadIdx.x;
@@ -355,12 +338,6 @@ hipError_t sq_launch_selfcheck_division(unsigned b_begin, unsigned b_end, unsign
     return hipGetLastError();
 }
 
-// low bytes of four words -> one word
-__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // [a.b0, b.b0, 0, 0]
-    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
-    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // [a, b, c, d]
-}
 
 // TILED: the codes go to 16 x 64 tiles (rows in groups of 16, K in 64-byte
 // chunks, tile (g, c) at (g * K64 / 64 + c) * 1 KiB, each tile row-major;

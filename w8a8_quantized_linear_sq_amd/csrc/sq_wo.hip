@@ -55,6 +55,20 @@
 //     l % 16, bytes 16 (l / 16) .. +16, the tile's own order). The int32
 //     sums are exact; the epilogue is the GEMM's, f32(acc) * sx[t] * sw[o]
 //     (+ bias[o]), or the raw int32 sums (OUT = 2).
+//   * FUSED (I8, TILED): the activation quantisation of the same call runs in
+//     this kernel (page "w8a8_smoothquant.py", SmoothQuantW8A8.forward:
+//     X / s, per-token int8, then the product). Workgroup b quantises tokens
+//     b, b + grid, ... (bit-identical to the row quantiser) into the
+//     caller's tiled code buffer, then publishes each with a per-token flag
+//     (release at agent scope). Every workgroup issues its first weight
+//     loads, then waits (acquire) until every token's flag holds this
+//     call's epoch; the wait is bounded, and a workgroup that runs out of
+//     polls quantises the missing tokens itself (the same bytes: the race
+//     between identical writes is benign), so no workgroup can hang on
+//     another. The epoch lives in the caller's workspace next to the
+//     flags: every workgroup reads it at its start, and the last workgroup
+//     to finish (a done counter) advances it and resets the counter, so
+//     successive calls and graph replays see fresh flags.
 #include <atomic>
 #include <type_traits>
 
@@ -83,20 +97,168 @@ __device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi) {
     return out;
 }
 
+// The fused path's synchronisation words in the caller's workspace (zero
+// before the first call): epoch, done counter, one flag per token.
+struct FuseSync {
+    unsigned long long epoch;
+    unsigned long long done;
+    unsigned long long fallbacks;  // workgroups that ran out of polls, ever (a statistic)
+    unsigned long long pad;
+    unsigned long long flag[64];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8]) {
+    if constexpr (BF16) {
+        const u32x4 r = *(const u32x4*)((const uint16_t*)x + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(r[i]);
+            v[2 * i + 1] = bf16_hi(r[i]);
+        }
+    } else {
+        const u32x4 a = *(const u32x4*)((const float*)x + off);
+        const u32x4 b = *(const u32x4*)((const float*)x + off + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    }
+}
+
+// One token row of the per-token activation quantiser, by the 512 threads
+// of a workgroup, bit-identical to the row quantiser's arithmetic (thread t
+// owns the 8-channel chunks t, t + 512, ..., at most kProdChunks of them,
+// held in registers: the row is read once):
+//   x~ = x / s (exact division; the IEEE division where the fast quotient
+//   leaves its proven range), scale = max(max |x~|, 1e-8) / 127,
+//   codes = round_half_even(x~ / scale) into the 16 x 64 tiles of q (padding
+//   columns zero).
+constexpr int kProdChunks = 4;  // 512 threads x 4 chunks x 8 = 16384 channels
+template <bool BF16>
+__device__ void produce_row(const void* x, const float* __restrict__ s, int64_t row, int64_t k, int8_t* q,
+                            float* scale_out, float* red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t k8 = k >> 3, k64 = (k + 63) & ~(int64_t)63;
+    auto in_range = [](float q0) {
+        const float a0 = __builtin_fabsf(q0);
+        return a0 >= 0x1p-50f && a0 <= 0x1p120f;
+    };
+    float v[kProdChunks][8], sv[kProdChunks][8];
+#pragma unroll
+    for (int c = 0; c < kProdChunks; ++c) {
+        const int64_t j8 = (int64_t)c * 64 * kWaves + tid;
+        if (j8 < k8) {
+            load8<BF16>(x, row * k + j8 * 8, v[c]);
+            load8<false>(s, j8 * 8, sv[c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[c][i] = 0.0f;
+                sv[c][i] = 1.0f;
+            }
+        }
+    }
+    // the quotients; the IEEE division where any of the thread's quotients
+    // leaves the fast range (as the row quantiser decides it)
+    float xs[kProdChunks][8], yv[kProdChunks][8];
+    float qmax = 0.0f;
+    bool y_bad = false;
+#pragma unroll
+    for (int c = 0; c < kProdChunks; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            yv[c][i] = recip_rn(sv[c][i]);
+            y_bad |= __builtin_isnan(yv[c][i]);
+            xs[c][i] = div_rn(v[c][i], sv[c][i], yv[c][i]);
+            qmax = fmaxf(qmax, __builtin_fabsf(v[c][i] * yv[c][i]));
+        }
+    if (y_bad || !(qmax <= 0x1p120f)) {
+#pragma unroll
+        for (int c = 0; c < kProdChunks; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float q0 = v[c][i] * yv[c][i];
+                if (!in_range(q0) && q0 != 0.0f) xs[c][i] = v[c][i] / sv[c][i];
+            }
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kProdChunks; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, __builtin_fabsf(xs[c][i]));
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w]);
+    __syncthreads();  // red is reused by the next row
+    const float scale = fmaxf(mx, kFloor) / kQmax;
+    const float rs = 1.0f / scale;
+#pragma unroll
+    for (int c = 0; c < kProdChunks; ++c) {
+        const int64_t j8 = (int64_t)c * 64 * kWaves + tid;
+        if (j8 >= (k64 >> 3)) continue;
+        u32x2 codes = {0u, 0u};
+        if (j8 < k8) {
+            uint32_t b[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(div_rn(xs[c][i], scale, rs) + kMagic);
+            codes = u32x2{pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7])};
+        }
+        *(u32x2*)(q + ((row >> 4) * (k64 >> 6) + (j8 >> 3)) * 1024 + (row & 15) * 64 + (j8 & 7) * 8) = codes;
+    }
+    if (tid == 0) scale_out[row] = scale;
+}
+
+// FUSE: 0 none; 1, 2: the activation quantisation of the call runs here
+// (FUSED above) from bf16 (1) or fp32 (2) activations xf with smoothing
+// factor sf; X and sa are then the tiled code and scale buffers it fills.
+struct FuseArgs {
+    const void* xf;
+    const float* sf;
+    FuseSync* sync;
+    int wait_polls;
+};
+
 // v_mfma_f32_16x16x32_bf16 operands: lane l holds 8 k-consecutive bf16 of
 // row (l % 16) at k offset 8 * (l / 16); result lane l, register r -> row
 // 4 * (l / 16) + r (token), column l % 16 (weight row).
-template <int TM, int G, int CB, int NB, int OUT, bool TILED, bool I8>
+template <int TM, int G, int CB, int NB, int OUT, bool TILED, bool I8, int FUSE = 0>
 __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const int8_t* Bw, int m, int n, int k,
                                                          int rows, const float* __restrict__ sa,
                                                          const float* __restrict__ sb, const void* __restrict__ bias,
-                                                         int bias_kind, void* __restrict__ Y, int scalar_scales) {
+                                                         int bias_kind, void* __restrict__ Y, int scalar_scales,
+                                                         FuseArgs fa) {
     static_assert(I8 || OUT != 2, "raw int32 sums only for the int8 product");
+    static_assert(FUSE == 0 || (I8 && TILED), "the fused quantisation writes tiled int8 codes");
     typedef typename std::conditional<I8, i32x4, f32x4>::type acc_t;
     constexpr int XV = I8 ? 1 : 2;  // 16-byte activation loads per token group and chunk
     __shared__ acc_t red[kWaves][TM * G][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned long long epoch = 0;
+    if constexpr (FUSE != 0) {
+        // this call's epoch (stable while the kernel runs: only the last
+        // workgroup to finish advances it)
+        // (the previous call's update is visible: kernels on a stream are
+        // ordered)
+        epoch = __hip_atomic_load(&fa.sync->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float* fred = (float*)&red[0][0][0];
+        for (int tok = blockIdx.x; tok < m; tok += gridDim.x) {
+            produce_row<FUSE == 1>(fa.xf, fa.sf, tok, k, (int8_t*)X, (float*)sa, fred);
+            // the workgroup's codes are complete (the barrier orders every
+            // thread's stores before thread 0's release, which makes them
+            // visible to every compute unit before the flag)
+            __syncthreads();
+            // system scope: the flag is written through to memory, where the
+            // other compute units' polls read it (each XCD's L2 would keep
+            // serving them a stale copy at agent scope)
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&fa.sync->flag[tok], epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
     const int r16 = lane & 15, grp = lane >> 4;
     const int nchunks = (k + kChunk - 1) / kChunk;
     int row0;
@@ -249,9 +411,75 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const in
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
+    if constexpr (FUSE != 0) {
+        // the first batches' weights stream while the tokens are quantised
 #pragma unroll
-    for (int i = 0; i < NB; ++i) load(bufs[i], i);
-    fence();
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int off = woff(i, j);
+#pragma unroll
+                for (int g = 0; g < G; ++g) bufs[i].w[g][j] = *(const u32x4*)(wrow[g] + off);
+            }
+        fence();
+        // wavefront 0 waits, bounded, for every token's flag of this epoch
+        // (relaxed polls from memory, system scope: an acquire per poll would
+        // invalidate the caches the producers work from; one acquire
+        // follows the wait)
+        __shared__ int missing;
+        if (wave == 0) {
+            bool ready = false;
+            for (int poll = 0;; ++poll) {
+                ready = true;
+                if (lane < m)
+                    ready = __hip_atomic_load(&fa.sync->flag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                            epoch + 1;
+                if (__builtin_amdgcn_ballot_w64(!ready) == 0 || poll >= fa.wait_polls) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            const unsigned long long late = __builtin_amdgcn_ballot_w64(!ready);
+            if (lane == 0) missing = late != 0;
+        }
+        __syncthreads();
+        if (missing) {
+            // out of polls: quantise every token not yet published here (the
+            // same bytes its producer writes) and publish it
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(&fa.sync->fallbacks, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float* fred = (float*)&red[0][0][0];
+            __shared__ int done_tok;
+            for (int tok = 0; tok < m; ++tok) {
+                if (threadIdx.x == 0)
+                    done_tok = __hip_atomic_load(&fa.sync->flag[tok], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                               epoch + 1;
+                __syncthreads();
+                const int skip = done_tok;
+                __syncthreads();
+                if (skip) continue;
+                produce_row<FUSE == 1>(fa.xf, fa.sf, tok, k, (int8_t*)X, (float*)sa, fred);
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&fa.sync->flag[tok], epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+        // acquire the published codes (the flags observed above) before any
+        // wavefront reads them
+        if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int off = woff(i, j);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) bufs[i].x[t][j][0] = *(const u32x4*)(xrow[t] + off);
+            }
+        fence();
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) load(bufs[i], i);
+        fence();
+    }
     int b = 0;
     for (; b + NB < nb; b += NB) {
 #pragma unroll
@@ -303,38 +531,51 @@ __global__ __launch_bounds__(64 * kWaves) void wo_kernel(const void* X, const in
             }
         }
     }
+    if constexpr (FUSE != 0) {
+        // the last workgroup to finish advances the epoch (every workgroup
+        // has read it by then) and resets the counter for the next call
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned long long prev =
+                __hip_atomic_fetch_add(&fa.sync->done, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == gridDim.x - 1) {
+                __hip_atomic_store(&fa.sync->done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&fa.sync->epoch, epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 // grid: row-major weights, ceil(n / rows) workgroups of `rows` rows; tiled
 // weights, `rows` is the workgroup count (the groups spread over them)
-template <int TM, int G, int CB, int NB, bool TILED, bool I8>
+template <int TM, int G, int CB, int NB, bool TILED, bool I8, int FUSE = 0>
 hipError_t launch_wo(const void* x, const float* sx, int m, const int8_t* wq, const float* sw, int n, int k,
                      int rows, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
-                     hipStream_t st) {
+                     hipStream_t st, FuseArgs fa = FuseArgs{}) {
     const dim3 grid(TILED ? rows : (n + rows - 1) / rows), block(64 * kWaves);
     if (out_kind == 0)
-        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 0, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
-                           sw, bias, bias_kind, y, scalar_scales);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 0, TILED, I8, FUSE>), grid, block, 0, st, x, wq, m, n, k, rows,
+                           sx, sw, bias, bias_kind, y, scalar_scales, fa);
     else if (out_kind == 1)
-        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 1, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
-                           sw, bias, bias_kind, y, scalar_scales);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 1, TILED, I8, FUSE>), grid, block, 0, st, x, wq, m, n, k, rows,
+                           sx, sw, bias, bias_kind, y, scalar_scales, fa);
     else if constexpr (I8)
-        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 2, TILED, I8>), grid, block, 0, st, x, wq, m, n, k, rows, sx,
-                           sw, bias, bias_kind, y, scalar_scales);
+        hipLaunchKernelGGL((wo_kernel<TM, G, CB, NB, 2, TILED, I8, FUSE>), grid, block, 0, st, x, wq, m, n, k, rows,
+                           sx, sw, bias, bias_kind, y, scalar_scales, fa);
     return hipGetLastError();
 }
 
 // One chunk per batch, two register buffers: measured on the decode shapes,
 // larger batches leave more compute after the last bytes arrive and more
 // buffers only lengthen the queues (both slower).
-template <int TM, bool TILED, bool I8>
+template <int TM, bool TILED, bool I8, int FUSE = 0>
 hipError_t launch_wo_t(int groups, const void* x, const float* sx, int m, const int8_t* wq, const float* sw, int n,
                        int k, int rows, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
-                       hipStream_t st) {
+                       hipStream_t st, FuseArgs fa = FuseArgs{}) {
     switch (groups) {
-        case 1: return launch_wo<TM, 1, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
-        case 2: return launch_wo<TM, 2, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
-        default: return launch_wo<TM, 3, 1, 2, TILED, I8>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st);
+        case 1: return launch_wo<TM, 1, 1, 2, TILED, I8, FUSE>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st, fa);
+        case 2: return launch_wo<TM, 2, 1, 2, TILED, I8, FUSE>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st, fa);
+        default: return launch_wo<TM, 3, 1, 2, TILED, I8, FUSE>(x, sx, m, wq, sw, n, k, rows, bias, bias_kind, y, out_kind, scalar_scales, st, fa);
     }
 }
 
@@ -438,3 +679,43 @@ hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_
     return wo_chunks<true, true>(xq, sx, m, k, wq, sw, n, wgs, groups, bias, bias_kind, y, out_kind, scalar_scales,
                                  st);
 }
+
+// The W8A8 linear for m <= 64 in one launch (FUSED above): the activation
+// codes and scales of x are written to xq (tiled) and sx by the kernel
+// itself, then the weight stream multiplies them. sync: the workspace's
+// synchronisation words (zero before the first call).
+hipError_t sq_launch_linear_stream_fused(const void* x, int bf16, const float* s, int64_t m, int64_t k,
+                                         int8_t* xq, float* sx, const int8_t* wq, const float* sw, int64_t n,
+                                         const void* bias, int bias_kind, void* y, int out_kind, void* sync,
+                                         int wait_polls, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    if (m > kStreamMaxM) return hipErrorInvalidValue;
+    int wgs, groups;
+    tiled_grid(n, wgs, groups);
+    const FuseArgs fa{x, s, (FuseSync*)sync, wait_polls};
+    const int mi = (int)m, ni = (int)n, ki = (int)k;
+    switch ((mi + 15) / 16) {
+        case 1:
+            return bf16 ? launch_wo_t<1, true, true, 1>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa)
+                        : launch_wo_t<1, true, true, 2>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa);
+        case 2:
+            return bf16 ? launch_wo_t<2, true, true, 1>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa)
+                        : launch_wo_t<2, true, true, 2>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa);
+        case 3:
+            return bf16 ? launch_wo_t<3, true, true, 1>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa)
+                        : launch_wo_t<3, true, true, 2>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa);
+        default:
+            return bf16 ? launch_wo_t<4, true, true, 1>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa)
+                        : launch_wo_t<4, true, true, 2>(groups, xq, sx, mi, wq, sw, ni, ki, wgs, bias, bias_kind, y,
+                                                        out_kind, 0, st, fa);
+    }
+}
+
+size_t sq_stream_fused_sync_bytes() { return sizeof(FuseSync); }
