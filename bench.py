@@ -97,7 +97,56 @@ def _args():
     p.add_argument("--counter-pass", action="store_true",
                    help="run only a 256 MiB fp32 copy (known bytes) and the GEMM, 3 times each, for "
                         "rocprofv3 --pmc passes; prints no JSON line")
+    p.add_argument("--sweep-k", action="store_true",
+                   help="time the tiled int8 product at M = N = 4096 for K = 64 ... 8192 (graphs of 64 "
+                        "launches over 8 rotated operand sets, quantised N(0,1) codes, bf16 out): one JSON "
+                        "line per K; the intercept is the launch's fixed cost")
     return p.parse_args()
+
+
+def sweep_k(torch, B, dev):
+    """The product's time against K at M = N = 4096: fixed cost and per-step
+    cost of the tiled int8 product (each launch the real kernel)."""
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    m = n = 4096
+    for k in (64, 128, 256, 512, 1024, 2048, 4096, 8192):
+        sets = 8
+        ones = torch.ones(k, device=dev)
+        # the prepared launches hold raw device pointers only: every set's
+        # codes, scales and output stay referenced here until the graph is gone
+        bufs, ops = [], []
+        for i in range(sets):
+            pair = []
+            for rows in (m, n):
+                x = torch.randn(rows, k, device=dev, generator=gen).to(torch.bfloat16)
+                q = B.tiled_empty(rows, k, dev)
+                sc = torch.empty(rows, device=dev)
+                B.sq_quantize_act_tiled(x, ones, q, sc, stream)
+                pair.append((q, sc))
+            y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            bufs.append((pair, y))
+            ops.append(B.prepared(B.sq_w8a8_gemm_tiled, pair[0][0], pair[0][1], m, pair[1][0], pair[1][1], n, k,
+                                  None, y, stream))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(GEMM_LAUNCHES):
+                ops[r % sets]()
+        g.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / GEMM_LAUNCHES
+        print(json.dumps({"sweep": "tiled int8 product, M = N = 4096, bf16 out", "k": k, "us": round(us, 2),
+                          "tops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
+        del g, ops, bufs, ones
+        torch.cuda.empty_cache()
 
 
 def _gemm_traffic(layout: str):
@@ -335,6 +384,9 @@ def main():
     B.lib()  # fail loudly if libsq.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep_k:
+        sweep_k(torch, B, dev)
+        return
 
     desc, spec, mode = WORKLOADS[args.workload]
     case = _make_case(inputs, spec)

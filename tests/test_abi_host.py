@@ -144,6 +144,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         B.lib()
 
 
+def test_prepared_call_keeps_its_buffers_alive(L):
+    """A prepared call holds only raw pointers for the C call, so it must keep
+    the tensors behind them referenced: freed and returned to the device, they
+    would leave a captured launch pointing at unmapped memory. Marshalled
+    only, never invoked here."""
+    import gc
+    import weakref
+
+    import torch
+
+    x = torch.zeros(4, 64)
+    run = torch.zeros(64)
+    refs = [weakref.ref(x), weakref.ref(run)]
+    call = B.prepared(B.sq_calibrate, x, run)
+    del x, run
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del call
+    gc.collect()
+    assert all(r() is None for r in refs)
+
+
 def test_quantize_tensor_errors(L):
     f = L.sq_quantize_tensor
     assert f(OK_PTR, B.SQ_I32, 64, OK_PTR, OK_PTR, None) == B.SQ_ERR_DTYPE

@@ -139,7 +139,9 @@ def prepared(fn, *args, **kwargs):
     """Marshals one call of a wrapper below once and returns a zero-argument
     callable that repeats exactly that C call (same pointers, sizes and
     stream) and checks its status: for launch loops where the per-call
-    Python work would otherwise be paced against the GPU."""
+    Python work would otherwise be paced against the GPU. The callable holds
+    references to the arguments, so the buffers behind those pointers live as
+    long as it does (a graph captured from it needs the callable kept too)."""
     _capture.on = True
     try:
         fn(*args, **kwargs)
@@ -155,6 +157,7 @@ def prepared(fn, *args, **kwargs):
             raise SQError(name, status, status_string(status))
         return status
 
+    call.args = (args, kwargs)
     return call
 
 
