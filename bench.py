@@ -430,8 +430,10 @@ def main():
             tsx=torch.empty(1, dtype=torch.float32, device=dev),
             tsw=torch.empty(1, dtype=torch.float32, device=dev)))
     del x0, w0, c0
-    # one stream of our own (default priority) for every call, so that the
-    # steps can be captured into a graph on it
+    # the copies and fills above ran on the default stream; every call below
+    # runs on a stream of our own (default priority, so that the steps can be
+    # captured into a graph on it), which must not start before them
+    torch.cuda.synchronize()
     stream = torch.cuda.Stream(dev)
     torch.cuda.set_stream(stream)
     if args.counter_pass:

@@ -821,6 +821,8 @@ def test_split_prepare(orc, shape, dtype, alpha):
     mx = orc.calibrate(c.x.f32)
     side = torch.cuda.Stream()
     mw = _zeros(c.k, torch.float32)
+    # the side stream starts after the inputs and the zero fill are done
+    side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         B.sq_weight_col_max(w, mw)
     torch.cuda.current_stream().wait_stream(side)
