@@ -29,6 +29,24 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Max over the 64 lanes of a wavefront for non-negative binary32 values (no
+// NaN), taken on the bit patterns as unsigned integers (their order is the
+// values' order): within each row of 16 lanes by DPP (swaps inside quads,
+// then rotations of the row by 4 and 8), then across the four rows from one
+// lane of each. Every lane must be active; the result is uniform.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    uint32_t u = __float_as_uint(v);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, false));  // row_ror 4
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));  // row_ror 8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)u, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 // The quantisers' exact division (Markstein's correction, see sq_quant.hip):
 // y = RN(1/b), q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0) = RN(a / b).
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: RN(q + kMagic)'s low byte is rint(q)
@@ -46,6 +64,26 @@ __device__ __forceinline__ float recip_rn(float s) {
 __device__ __forceinline__ float div_rn(float a, float b, float y) {
     const float q0 = a * y;
     return __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
+}
+
+// The per-row scale RN(a / 127) for a >= the floor (a may be +inf): the
+// same correction with y = RN(1/127). The largest finite a keeps every step
+// in the normal range, so it equals the IEEE quotient (the significand pairs
+// are all checked by sq_selfcheck_division); +inf passes through.
+__device__ __forceinline__ float row_scale(float a) {
+    constexpr float y = 1.0f / kQmax;
+    return __builtin_isinf(a) ? a : div_rn(a, kQmax, y);
+}
+
+// RN(1/s) for a row scale s >= floor / 127 (about 2^-33.6): the Newton-refined
+// reciprocal of recip_rn where it is checked equal to the IEEE quotient
+// (below 2^100), the IEEE division above (scales reach 2^121, and inf).
+__device__ __forceinline__ float row_scale_recip(float s) {
+    if (__builtin_expect(s < 0x1p100f, 1)) {
+        const float r = __builtin_amdgcn_rcpf(s);
+        return __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    }
+    return 1.0f / s;
 }
 
 // low bytes of four words -> one word

@@ -283,6 +283,10 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 //     |q0| (an infinite x gives q0 = inf): above 2^120, or where a y is
 //     NaN, the thread's out-of-range quotients are recomputed with the IEEE
 //     division. A NaN x gives NaN on both routes.
+//   * scale = RN(max / 127) by the same correction with y = RN(1/127) (an
+//     infinite max passes through), and rs = RN(1 / scale) by the refined
+//     reciprocal below 2^100, the IEEE quotient above: both equal the IEEE
+//     results, so the scale is the binary32 quotient the method defines.
 //   * v / scale: scale is in [2^-34, 2^122] (floor / 127 up to max / 127)
 //     and |v / scale| <= 127.00002, so no step overflows; a step can only
 //     underflow when |v| < 2^-90, where the quotient is below 2^-50 and its
@@ -296,7 +300,10 @@ hipError_t sq_launch_smooth_factor(const float* x_max, const unsigned* partial, 
 // of them) and keeps their s (and y) in registers; the row stays in
 // registers between the max and the codes, so the input is read once; a
 // further row's loads are issued before the current row is finished. One
-// barrier per row (the block max goes through a double-buffered LDS slot).
+// barrier per row (the block max goes through a double-buffered LDS slot);
+// the wavefront max is taken by DPP and lane reads, not through LDS. The
+// per-row work is done by every thread: done with the IEEE divisions and an
+// LDS shuffle it made the activation quantiser 9% slower at 4096 x 4096.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void selfcheck_reciprocal_kernel(unsigned long long* mismatches) {
@@ -456,13 +463,13 @@ __global__ __launch_bounds__(T) void quantize_rows_kernel(const void* __restrict
             for (int i = 0; i < 8; ++i) mx = fmaxf(mx, __builtin_fabsf(xs[c][i]));
         // the next row's loads are in flight while this row finishes
         load_row(row + gridDim.x);
-        mx = wave_max(mx);
+        mx = wave_max_nonneg(mx);
         if (lane == 0) red[parity][wave] = mx;
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[parity][w]);
-        const float scale = fmaxf(mx, kFloor) / kQmax;
-        const float rs = 1.0f / scale;
+        const float scale = row_scale(fmaxf(mx, kFloor));
+        const float rs = row_scale_recip(scale);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int64_t j8 = (int64_t)c * T + tid;

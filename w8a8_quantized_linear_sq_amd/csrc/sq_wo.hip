@@ -188,14 +188,14 @@ __device__ void produce_row(const void* x, const float* __restrict__ s, int64_t 
     for (int c = 0; c < kProdChunks; ++c)
 #pragma unroll
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, __builtin_fabsf(xs[c][i]));
-    mx = wave_max(mx);
+    mx = wave_max_nonneg(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w]);
     __syncthreads();  // red is reused by the next row
-    const float scale = fmaxf(mx, kFloor) / kQmax;
-    const float rs = 1.0f / scale;
+    const float scale = row_scale(fmaxf(mx, kFloor));
+    const float rs = row_scale_recip(scale);
 #pragma unroll
     for (int c = 0; c < kProdChunks; ++c) {
         const int64_t j8 = (int64_t)c * 64 * kWaves + tid;
