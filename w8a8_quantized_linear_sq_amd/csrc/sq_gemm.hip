@@ -450,20 +450,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const bool whole = (m0 + BM <= m) && (n0 + BN <= n) && (n % (16 / OB) == 0) &&
                        (scalar_scales || ((uintptr_t)sa & 15) == 0) && (((uintptr_t)Y & 15) == 0);
     if (whole) {
+        // The row scales of a slab are loaded one slab ahead: the first
+        // slab's before the barrier, the next slab's before this slab's
+        // stores. Loaded just before their use, behind the scalar-scale
+        // branch, each load was waited for in turn, and on this chip that
+        // wait also drains the previous slab's stores (the memory counter
+        // counts both).
+        float sar_all[TM][4][4] = {};
+        auto load_slab = [&](int i) {
+            if constexpr (OUT != 2 && ET == kI8) {
+                if (scalar_scales) {
+                    const float v = sa[0];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sar_all[i][q][e] = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = *(const float4*)(sa + m0 + wm * WM + i * 32 + q * 8 + erow);
+                        sar_all[i][q][0] = v.x; sar_all[i][q][1] = v.y; sar_all[i][q][2] = v.z; sar_all[i][q][3] = v.w;
+                    }
+                }
+            }
+        };
+        load_slab(0);
         __syncthreads();  // every wavefront is done with the operand buffers
         int8_t* stage = smem + wave * 32 * PITCH;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int rbase = m0 + wm * WM + i * 32;
-            float sar[4][4] = {};
-            if constexpr (OUT != 2 && ET == kI8) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = scalar_scales ? make_float4(sa[0], sa[0], sa[0], sa[0])
-                                                   : *(const float4*)(sa + rbase + q * 8 + erow);
-                    sar[q][0] = v.x; sar[q][1] = v.y; sar[q][2] = v.z; sar[q][3] = v.w;
-                }
-            }
+            if (i + 1 < TM) load_slab(i + 1);
+            const float (&sar)[4][4] = sar_all[i];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 if constexpr (OUT == 1) {
