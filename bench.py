@@ -77,6 +77,9 @@ WORKLOADS = {
     "o_proj_per_tensor": ("per-tensor variant on the O projection shape, M=N=K=4096, bf16 in/out: per call the "
                           "weight and the input quantised with one scale each, then the int8 product",
                           ("block_linear", 1), "per_tensor"),
+    "ste_prefill": ("straight-through backward of the prefill linear, 2048 tokens x 4096 -> 4096, bf16, "
+                    "alpha=0.5 calibrated on the same tokens, upstream gradient N(0, 1) bf16 (seed 2010); per "
+                    "call: sq_ste_backward (dx, dw, db, ds and the alpha / eta gradient)", ("prefill",), "ste"),
     "decode_weight_only": ("weight-only int8 linear on the decode shape, 16 tokens x 4096 -> 11008, bf16 "
                            "activations and output, per-channel int8 weights prepared once (never calibrated, "
                            "s = 1); per call: the bf16 x int8 product + scale", ("decode",), "weight_only"),
@@ -289,6 +292,136 @@ def cpu_baseline(case, mode: str, budget_s: float):
     }
 
 
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def cpu_baseline_ste(case, dy, budget_s: float):
+    """The oracle's straight-through backward (binary64) on the first tokens
+    of the batch: its own calibration and weight preparation first (not
+    timed), then the backward of as many tokens as fit the budget."""
+    import oracle
+
+    o = oracle.get()
+    m, n, k = case.m, case.n, case.k
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    x, w = case.x.f32, case.w.f32
+    mx = o.calibrate(x)
+    mw = o.weight_col_max(w)
+    s, wq, sw = o.prepare_weight(w, mx, 0.5)
+
+    def run(rows):
+        xq, sx = o.quantize_act(x[:rows], s)
+        tp = time.perf_counter()
+        o.ste_backward(dy.f32[:rows], x[:rows], w, s, xq, sx, wq, sw, mx, mw, 0.5)
+        return time.perf_counter() - tp
+
+    probe = 4
+    per_row = run(probe) / probe
+    rows = int(min(m, max(probe, budget_s / per_row)))
+    t = run(rows)
+    return {"value": round(4.0 * rows * n * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the oracle's straight-through backward (binary64) on the first {rows} of {m} tokens "
+                       f"against the whole {n}x{k} weight (the two products' 4*{rows}*N*K flops, the column, "
+                       f"bias and alpha terms included), after its own calibration and weight preparation "
+                       f"(not timed): {t:.2f} s"),
+            "seconds_measured": round(t, 3)}
+
+
+def ste_bench(args, torch, np, B, inputs, case, desc, dev):
+    """One step = one straight-through backward call (sq_ste_backward) on a
+    quantised forward's state prepared beforehand (calibration on the same
+    tokens, weight preparation, activation codes: not timed)."""
+    m, n, k = case.m, case.n, case.k
+    alpha = 0.5
+    dy_t = inputs.upstream_grad(m, n, seed=2010)
+
+    def bf16(t):
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0, w0, dy0 = bf16(case.x), bf16(case.w), bf16(dy_t)
+    ws_bytes = B.sq_ste_backward_workspace_bytes(m, n, k)
+    set_bytes = m * n * 2 + (m + n) * k * (2 + 1 + 4) + ws_bytes
+    rotate = max(2, min(12, math.ceil(ROTATE_BYTES / set_bytes)))
+    sets = []
+    for _ in range(rotate):
+        sets.append(dict(
+            dy=dy0.clone(), x=x0.clone(), w=w0.clone(),
+            run=torch.empty(k, dtype=torch.float32, device=dev), mw=torch.empty(k, dtype=torch.float32, device=dev),
+            smooth=torch.empty(k, dtype=torch.float32, device=dev),
+            wq=torch.empty((n, k), dtype=torch.int8, device=dev), ws=torch.empty(n, dtype=torch.float32, device=dev),
+            xq=torch.empty((m, k), dtype=torch.int8, device=dev), xs=torch.empty(m, dtype=torch.float32, device=dev),
+            dx=torch.empty((m, k), dtype=torch.float32, device=dev),
+            dw=torch.empty((n, k), dtype=torch.float32, device=dev),
+            db=torch.empty(n, dtype=torch.float32, device=dev), ds=torch.empty(k, dtype=torch.float32, device=dev),
+            da=torch.empty(2, dtype=torch.float64, device=dev),
+            wsp=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)))
+    del x0, w0, dy0
+    # the copies above ran on the default stream; the calls below run on a
+    # stream of our own, which must not start before them
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    for s in sets:
+        B.sq_calibrate_first(s["x"], s["run"], stream)
+        B.sq_weight_col_max(s["w"], s["mw"], stream)
+        B.sq_prepare_weight(s["w"], s["run"], alpha, s["smooth"], s["wq"], s["ws"], stream)
+        B.sq_quantize_act(s["x"], s["smooth"], s["xq"], s["xs"], stream)
+        s["call"] = B.prepared(B.sq_ste_backward, s["dy"], s["x"], s["w"], s["smooth"], s["xq"], s["xs"], s["wq"],
+                               s["ws"], s["run"], s["mw"], alpha, s["dx"], s["dw"], s["db"], s["ds"], s["da"],
+                               s["wsp"], stream)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        sets[i % rotate]["call"]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(args.steps):
+            sets[i % rotate]["call"]()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ev[0].record(stream)
+    g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = ev[0].elapsed_time(ev[1]) / args.steps
+    flops = 4.0 * m * n * k            # the backward's two products, 2*M*N*K each
+    mfma_flops = 12.0 * m * n * k      # as run: each fp32 factor split into three exact bf16 planes
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = mfma_flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": f"straight-through backward TFLOP/s at M={m} N={n} K={k} (two products of 2*M*N*K)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; outlier input channels, W ~ N(0, sigma), upstream gradient N(0, 1), bf16)",
+        "config": {"workload": desc, "m": m, "n": n, "k": k, "alpha": alpha, "in_dtype": "bf16",
+                   "grad_dtype": "fp32", "rotated_buffer_sets": rotate, "int8_layout": "row-major"},
+        "roofline": {"bound": "mfma",
+                     "kernel": ("the straight-through backward call: its two products as three exact bf16 "
+                                "planes each on bf16 MFMA (gemm_kernel<bf16, .., periodic B>), with the packing "
+                                "and column passes; achieved counts the products' 12*M*N*K bf16 MFMA flops over "
+                                "the whole call"),
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "call_us": round(ms_per_step * 1e3, 2),
+        "wall_s_timed": round(t_wall, 4),
+        "value_is": "one backward call per unit time, counting the two products' 4*M*N*K flops",
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_ste(case, dy_t, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
 def alpha_sweep(torch, B, case, s, stream):
     """The workload's alpha sweep after the timed region (page
     "w8a8_smoothquant.py": recompute_smooth_scale, then quantization_error):
@@ -390,6 +523,9 @@ def main():
 
     desc, spec, mode = WORKLOADS[args.workload]
     case = _make_case(inputs, spec)
+    if mode == "ste":
+        ste_bench(args, torch, np, B, inputs, case, desc, dev)
+        return
     m, n, k = case.m, case.n, case.k
     alpha = 0.5
     # the int8 codes in 16 x 64 tiles unless asked not to

@@ -44,7 +44,25 @@ def test_cpu_baseline_object(mode):
         assert "whole steps" in cb["sample"] and cb["seconds_measured"] >= 0.2 or "50 whole steps" in cb["sample"]
 
 
+def test_cpu_baseline_ste_object():
+    case = inputs.tiny()
+    dy = inputs.upstream_grad(case.m, case.n, seed=3, dtype="f32")
+    cb = bench.cpu_baseline_ste(case, dy, 0.2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s"
+    assert cb["value"] > 0 and cb["cores"] >= 1
+    assert f"of {case.m} tokens" in cb["sample"]
+    assert cb["seconds_measured"] >= 0
+
+
+def test_upstream_grad_is_seeded_and_bf16_exact():
+    a = inputs.upstream_grad(5, 7, seed=11)
+    b = inputs.upstream_grad(5, 7, seed=11)
+    assert a.shape == (5, 7) and a.bits is not None
+    assert (a.bits == b.bits).all()
+    assert (inputs.bf16_to_f32(a.bits) == a.f32).all()
+
+
 def test_every_workload_names_a_case_and_mode():
     for name, (desc, spec, mode) in bench.WORKLOADS.items():
-        assert desc and mode in ("full", "per_call", "per_tensor", "weight_only"), name
+        assert desc and mode in ("full", "per_call", "per_tensor", "weight_only", "ste"), name
         assert hasattr(inputs, spec[0]), name

@@ -222,20 +222,57 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
         if (c0 + e < cols) part[g * cols + c0 + e] = acc[e];
 }
 
-// ds_j and its term of dalpha:
-//   ds_j   = sum_g pw[g][j] - (sum_g px[g][j]) / s_j^2
-//   term_j = ds_j * s_raw_j * (ln mx_j + ln mw_j) where s_raw_j >= 1e-8,
-//            else 0 (the floor of s passes no gradient); 0 without mx
-__global__ __launch_bounds__(256) void ste_ds_kernel(const double* __restrict__ px, int64_t gx,
-                                                     const double* __restrict__ pw, int64_t gw,
-                                                     const float* __restrict__ s, const float* __restrict__ mx,
-                                                     const float* __restrict__ mw, double a_x, double a_w, int64_t k,
-                                                     float* __restrict__ ds_out, double* __restrict__ term) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= k) return;
+// Sums of row-group partials for one column per lane: wavefront `wave` of
+// kSumWaves takes the groups wave, wave + kSumWaves, ... in that order with
+// eight loads in flight, and the callers add the wavefronts' sums in
+// wavefront order through LDS, so every call sums in the same order.
+constexpr int kSumWaves = 8;
+
+__device__ __forceinline__ double sum_groups(const double* __restrict__ p, int64_t groups, int64_t stride,
+                                             int64_t j, int wave) {
+    double acc = 0.0;
+    int64_t g = wave;
+    for (; g + kSumWaves * 7 < groups; g += kSumWaves * 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(g + kSumWaves * u) * stride + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; g < groups; g += kSumWaves) acc += p[g * stride + j];
+    return acc;
+}
+
+// ds[j] = sum_o gW[o][j] w[o][j] - sum_t gX[t][j] x[t][j] / s_j^2 from the
+// column passes' partials, and the per-channel term of dalpha,
+//   term[j] = [s_raw_j >= floor] ds_j s_raw_j (ln mx_j + ln mw_j)
+// (0 without calibration). A block owns 64 channels.
+__global__ __launch_bounds__(64 * kSumWaves) void ste_ds_kernel(const double* __restrict__ px, int64_t gx,
+                                                                const double* __restrict__ pw, int64_t gw,
+                                                                const float* __restrict__ s,
+                                                                const float* __restrict__ mx,
+                                                                const float* __restrict__ mw, double a_x, double a_w,
+                                                                int64_t k, float* __restrict__ ds_out,
+                                                                double* __restrict__ term) {
+    __shared__ double red[2][kSumWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
     double sw_ = 0.0, sx_ = 0.0;
-    for (int64_t g = 0; g < gw; ++g) sw_ += pw[g * k + j];
-    for (int64_t g = 0; g < gx; ++g) sx_ += px[g * k + j];
+    if (j < k) {
+        sw_ = sum_groups(pw, gw, k, j, wave);
+        sx_ = sum_groups(px, gx, k, j, wave);
+    }
+    red[0][wave][lane] = sw_;
+    red[1][wave][lane] = sx_;
+    __syncthreads();
+    if (wave != 0 || j >= k) return;
+    sw_ = 0.0;
+    sx_ = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSumWaves; ++w) {
+        sw_ += red[0][w][lane];
+        sx_ += red[1][w][lane];
+    }
     const double sj = (double)s[j];
     const double ds = sw_ - sx_ / (sj * sj);
     if (ds_out) ds_out[j] = (float)ds;
@@ -269,13 +306,19 @@ __global__ __launch_bounds__(256) void ste_alpha_kernel(const double* __restrict
     }
 }
 
-// db[o] = sum_g pb[g][o] (binary64 in group order, then fp32)
-__global__ __launch_bounds__(256) void ste_bias_kernel(const double* __restrict__ pb, int64_t groups, int64_t n,
-                                                       float* __restrict__ db) {
-    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (o >= n) return;
+// db[o] = sum_g pb[g][o] (binary64 in the fixed order of sum_groups, then
+// fp32); a block owns 64 outputs
+__global__ __launch_bounds__(64 * kSumWaves) void ste_bias_kernel(const double* __restrict__ pb, int64_t groups,
+                                                                  int64_t n, float* __restrict__ db) {
+    __shared__ double red[kSumWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t o = (int64_t)blockIdx.x * 64 + lane;
+    red[wave][lane] = o < n ? sum_groups(pb, groups, n, o, wave) : 0.0;
+    __syncthreads();
+    if (wave != 0 || o >= n) return;
     double acc = 0.0;
-    for (int64_t g = 0; g < groups; ++g) acc += pb[g * n + o];
+#pragma unroll
+    for (int w = 0; w < kSumWaves; ++w) acc += red[w][lane];
     db[o] = (float)acc;
 }
 
@@ -390,7 +433,7 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
                : launch_colsum<1, 2, false>(dw, w, s, n, k, L.gw, pw, true, st);
     if (e != hipSuccess) return e;
     // ds, dalpha, deta
-    hipLaunchKernelGGL(ste_ds_kernel, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, st, px, L.gx, pw, L.gw, s, mx,
+    hipLaunchKernelGGL(ste_ds_kernel, dim3((unsigned)((k + 63) / 64)), dim3(64 * kSumWaves), 0, st, px, L.gx, pw, L.gw, s, mx,
                        mw, alpha, 1.0 - alpha, k, ds, term);
     hipLaunchKernelGGL(ste_alpha_kernel, dim3(1), dim3(256), 0, st, term, k, alpha, dalpha_deta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -399,7 +442,7 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
         e = dy_bf16 ? launch_colsum<0, 0, true>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st)
                     : launch_colsum<0, 0, false>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(ste_bias_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb, L.gb, n, db);
+        hipLaunchKernelGGL(ste_bias_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, st, pb, L.gb, n, db);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

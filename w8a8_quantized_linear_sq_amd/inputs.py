@@ -175,6 +175,12 @@ def o_proj() -> LinearCase:
     return block_linear(1)
 
 
+def upstream_grad(m, n, *, seed, dtype="bf16") -> Tensor:
+    """An upstream gradient dL/dY for the backward: m x n standard normals
+    drawn in float32 (seed ``seed``), stored as ``dtype``."""
+    return _store(np.random.default_rng(seed).standard_normal((m, n), dtype=np.float32), dtype)
+
+
 def small(m, n, k, *, seed=7, dtype="bf16", bias=True, out_frac=0.01, out_mult=50.0,
           calib_rows=None, calib_batches=1) -> LinearCase:
     """A small case of the same structure for parity tests (ragged sizes)."""
