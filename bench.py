@@ -387,6 +387,33 @@ def ste_bench(args, torch, np, B, inputs, case, desc, dev):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms_per_step = ev[0].elapsed_time(ev[1]) / args.steps
+    # the auxiliary loss and its gradient at Y_q (after the timed region):
+    # the two norms need a whole pass over Y_fp and Y_q before the first
+    # gradient element, so 2 reads of each and one write of M x N fp32
+    aux_ws = B.sq_aux_loss_grad_workspace_bytes(m * n)
+    for i, s in enumerate(sets):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2020 + i)
+        s["y_fp"] = torch.randn(m, n, device=dev, generator=gen)
+        s["y_q"] = s["y_fp"] + 0.01 * torch.randn(m, n, device=dev, generator=gen)
+        s["dy_q"] = torch.empty(m, n, dtype=torch.float32, device=dev)
+        s["loss"] = torch.empty(1, dtype=torch.float64, device=dev)
+        s["aux_ws"] = torch.empty(max(aux_ws, 16), dtype=torch.uint8, device=dev)
+        s["aux"] = B.prepared(B.sq_aux_loss_grad, s["y_fp"], s["y_q"], s["dy_q"], s["loss"], s["aux_ws"], stream)
+    torch.cuda.synchronize()
+    ag = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ag, stream=stream):
+        for i in range(STAGE_LAUNCHES):
+            sets[i % rotate]["aux"]()
+    ag.replay()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    ag.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    aux_ms = ev[0].elapsed_time(ev[1]) / STAGE_LAUNCHES
+    aux_bytes = 5 * m * n * 4
+    aux_gbs = aux_bytes / (aux_ms * 1e-3) / 1e9
     flops = 4.0 * m * n * k            # the backward's two products, 2*M*N*K each
     mfma_flops = 12.0 * m * n * k      # as run: each fp32 factor split into three exact bf16 planes
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -414,6 +441,12 @@ def ste_bench(args, torch, np, B, inputs, case, desc, dev):
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "call_us": round(ms_per_step * 1e3, 2),
+        "aux_loss_grad": {"us": round(aux_ms * 1e3, 2), "bound": "hbm", "achieved": round(aux_gbs, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(aux_gbs / PEAK_HBM_GBS, 4),
+                          "note": (f"sq_aux_loss_grad on {m}x{n} fp32 Y_fp / Y_q: two passes over both (the "
+                                   f"norms first) and the gradient written, {aux_bytes} bytes per call; "
+                                   f"{STAGE_LAUNCHES} calls in one graph over the rotated sets, after the "
+                                   "timed region")},
         "wall_s_timed": round(t_wall, 4),
         "value_is": "one backward call per unit time, counting the two products' 4*M*N*K flops",
     }
