@@ -41,7 +41,8 @@
 //     hardware deals workgroups round-robin over the 8 XCDs) form a compact
 //     block sharing A rows and B columns in that XCD's L2;
 //   * the epilogue stages each 32-row slab through LDS and writes whole
-//     16-byte row chunks with streaming (non-temporal) stores;
+//     16-byte row chunks with streaming (non-temporal) stores, each slab's
+//     row scales loaded one slab ahead;
 //   * the same kernel, with the operands' element type as a parameter (K
 //     counted in bytes, so the LDS layout and the DMA are unchanged), is the
 //     full-precision reference of quantization_error (page
