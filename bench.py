@@ -753,7 +753,7 @@ def main():
     torch.cuda.synchronize()
     gemm_warm_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
-    # the per-call linear (SURVEY's second figure): activation codes + the
+    # the per-call linear (the second throughput figure): activation codes + the
     # product, as a forward runs them on prepared weights, GEMM_LAUNCHES
     # calls in one graph over the rotated sets, replayed between events
     per_call_ms = None
