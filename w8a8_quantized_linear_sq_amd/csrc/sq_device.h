@@ -47,6 +47,46 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
     return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
+// Eight consecutive elements at `off` of a bf16 or fp32 array as fp32
+// (exact widening): one 16-byte load for bf16, two for fp32; the address
+// must be 16-byte aligned.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8]) {
+    if constexpr (BF16) {
+        const u32x4 r = *(const u32x4*)((const uint16_t*)x + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(r[i]);
+            v[2 * i + 1] = bf16_hi(r[i]);
+        }
+    } else {
+        const u32x4 a = *(const u32x4*)((const float*)x + off);
+        const u32x4 b = *(const u32x4*)((const float*)x + off + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    }
+}
+
+// Four consecutive elements likewise: 8 bytes for bf16, 16 for fp32 (the
+// address aligned to that size).
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* x, int64_t off, float (&v)[4]) {
+    if constexpr (BF16) {
+        const u32x2 r = *(const u32x2*)((const uint16_t*)x + off);
+        v[0] = bf16_lo(r[0]);
+        v[1] = bf16_hi(r[0]);
+        v[2] = bf16_lo(r[1]);
+        v[3] = bf16_hi(r[1]);
+    } else {
+        const u32x4 r = *(const u32x4*)((const float*)x + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+    }
+}
+
 // The quantisers' exact division (Markstein's correction, see sq_quant.hip):
 // y = RN(1/b), q0 = RN(a y), q1 = fma(fma(-q0, b, a), y, q0) = RN(a / b).
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: RN(q + kMagic)'s low byte is rint(q)

@@ -65,25 +65,40 @@ __device__ __forceinline__ float load_val(const void* p, int64_t i) {
 }
 
 // a[t][p * ld + o] = plane p of RN32(dy[t][o] * sc[o]) for o < n, zero for
-// n <= o < ld (ld a multiple of 64). Thread: 4 consecutive o of one row.
-template <bool BF16>
+// n <= o < ld (ld a multiple of 64). Thread: 8 consecutive o of every row it
+// visits. VEC (dy and sc 16-byte aligned, n a multiple of 8): dy and sc read
+// 16 bytes at a time; else, and past n, element by element. The planes are
+// written 16 bytes at a time.
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void ste_pack_rows_kernel(const void* __restrict__ dy, const float* __restrict__ sc,
                                                             int64_t m, int64_t n, int64_t ld, uint16_t* __restrict__ a) {
-    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (o0 >= ld) return;
-    for (int64_t t = blockIdx.y; t < m; t += gridDim.y) {
-        uint32_t h[3][4];
+    const bool whole = VEC && o0 + 8 <= n;
+    float f[8];
+    if (whole) {
+        load8<false>(sc, o0, f);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t o = o0 + e;
-            const float v = o < n ? load_val<BF16>(dy, t * n + o) * sc[o] : 0.0f;
-            split3(v, h[0][e], h[1][e], h[2][e]);
+        for (int e = 0; e < 8; ++e) f[e] = o0 + e < n ? sc[o0 + e] : 0.0f;
+    }
+    for (int64_t t = blockIdx.y; t < m; t += gridDim.y) {
+        float v[8];
+        if (whole) {
+            load8<BF16>(dy, t * n + o0, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = o0 + e < n ? load_val<BF16>(dy, t * n + o0 + e) : 0.0f;
         }
+        uint32_t h[3][8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split3(v[e] * f[e], h[0][e], h[1][e], h[2][e]);
         uint16_t* row = a + t * 3 * ld + o0;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-            const u32x2 w = {h[p][0] | (h[p][1] << 16), h[p][2] | (h[p][3] << 16)};
-            *(u32x2*)(row + p * ld) = w;
+            const u32x4 w = {h[p][0] | (h[p][1] << 16), h[p][2] | (h[p][3] << 16), h[p][4] | (h[p][5] << 16),
+                             h[p][6] | (h[p][7] << 16)};
+            *(u32x4*)(row + p * ld) = w;
         }
     }
 }
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(256) void ste_pack_rows_kernel(const void* __restri
 // m <= t < ld; rows o < n. 64 x 64 tiles through LDS (tile (ti, oi) with
 // ti = blockIdx.x % (ld / 64)).
 constexpr int kTP = 72;  // LDS row pitch in bf16 (16-byte aligned rows)
-template <bool BF16>
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restrict__ dy, const float* __restrict__ sc,
                                                             int64_t m, int64_t n, int64_t ld, uint16_t* __restrict__ a) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][64][kTP];  // [plane][o][t]
@@ -104,11 +119,23 @@ __global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restri
         const int tt = ty + 16 * r;
         const int64_t t = t0 + tt;
         const float f = t < m ? sc[t] : 0.0f;
+        // four consecutive o of row t: one load when VEC (dy 16-byte aligned,
+        // n a multiple of 4) and all four lie below n
+        float d[4];
+        if (VEC && t < m && o0 + tx * 4 + 4 <= n) {
+            load4<BF16>(dy, t * n + o0 + tx * 4, d);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t o = o0 + tx * 4 + e;
+                d[e] = (t < m && o < n) ? load_val<BF16>(dy, t * n + o) : 0.0f;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int oo = tx * 4 + e;
             const int64_t o = o0 + oo;
-            const float v = (t < m && o < n) ? load_val<BF16>(dy, t * n + o) * f : 0.0f;
+            const float v = (t < m && o < n) ? d[e] * f : 0.0f;
             uint32_t h1, h2, h3;
             split3(v, h1, h2, h3);
             tile[0][oo][tt] = (uint16_t)h1;
@@ -336,6 +363,7 @@ __global__ __launch_bounds__(256) void ste_aux_grad_kernel(const float* __restri
 }
 
 int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+bool aligned16_ptr(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // row groups of a column-sum pass: about 2048 blocks in all, at least 8
@@ -405,9 +433,15 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
     hipError_t e;
     // gX: a1 = RN32(dy * sw) in three planes [m][3 n64], bw = wq^T [k][n64]
     {
-        const dim3 grid((unsigned)((L.n64 + 1023) / 1024), (unsigned)std::min<int64_t>(m, 65535));
-        if (dy_bf16) hipLaunchKernelGGL(ste_pack_rows_kernel<true>, grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
-        else hipLaunchKernelGGL(ste_pack_rows_kernel<false>, grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+        const dim3 grid((unsigned)((L.n64 + 2047) / 2048), (unsigned)std::min<int64_t>(m, 65535));
+        const bool vec = aligned16_ptr(dy) && aligned16_ptr(sw) && n % 8 == 0;
+        if (dy_bf16) {
+            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<true, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+            else hipLaunchKernelGGL((ste_pack_rows_kernel<true, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+        } else {
+            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<false, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+            else hipLaunchKernelGGL((ste_pack_rows_kernel<false, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+        }
         hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.n64 / 64) * ((k + 63) / 64))), dim3(256), 0,
                            st, wq, n, k, L.n64, bw);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -417,8 +451,14 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
     // gW: a2 = RN32(dy^T * sx) in three planes [n][3 m64], bx = xq^T [k][m64]
     {
         const dim3 grid((unsigned)((L.m64 / 64) * ((n + 63) / 64)));
-        if (dy_bf16) hipLaunchKernelGGL(ste_pack_cols_kernel<true>, grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
-        else hipLaunchKernelGGL(ste_pack_cols_kernel<false>, grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+        const bool vec = aligned16_ptr(dy) && n % 4 == 0;
+        if (dy_bf16) {
+            if (vec) hipLaunchKernelGGL((ste_pack_cols_kernel<true, true>), grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+            else hipLaunchKernelGGL((ste_pack_cols_kernel<true, false>), grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+        } else {
+            if (vec) hipLaunchKernelGGL((ste_pack_cols_kernel<false, true>), grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+            else hipLaunchKernelGGL((ste_pack_cols_kernel<false, false>), grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
+        }
         hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.m64 / 64) * ((k + 63) / 64))), dim3(256), 0,
                            st, xq, m, k, L.m64, bx);
         if ((e = hipGetLastError()) != hipSuccess) return e;

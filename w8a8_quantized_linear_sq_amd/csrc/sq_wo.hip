@@ -107,26 +107,6 @@ struct FuseSync {
     unsigned long long flag[64];
 };
 
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8]) {
-    if constexpr (BF16) {
-        const u32x4 r = *(const u32x4*)((const uint16_t*)x + off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_lo(r[i]);
-            v[2 * i + 1] = bf16_hi(r[i]);
-        }
-    } else {
-        const u32x4 a = *(const u32x4*)((const float*)x + off);
-        const u32x4 b = *(const u32x4*)((const float*)x + off + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(a[i]);
-            v[4 + i] = __uint_as_float(b[i]);
-        }
-    }
-}
-
 // One token row of the per-token activation quantiser, by the 512 threads
 // of a workgroup, bit-identical to the row quantiser's arithmetic (thread t
 // owns the 8-channel chunks t, t + 512, ..., at most kProdChunks of them,
