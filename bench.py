@@ -7,7 +7,8 @@ Default workload (the headline): the transformer block's O projection
 (M = N = K = 4096, bf16 in and out, alpha = 0.5, calibrated on 512 separate
 tokens fed as 4 batches of 128). One step is one pass of the whole path
 over one batch of synthetic input:
-  sq_calibrate_first + 3 x sq_calibrate -> sq_prepare_weight_tiled ->
+  sq_calibrate_batches (the 4 batches in one launch, starting the running
+  max) -> sq_prepare_weight_tiled ->
   sq_quantize_act_tiled -> sq_w8a8_gemm_tiled (int8 GEMM + fused dequant),
 the int8 codes kept in 16 x 64 tiles (--layout row: the row-major calls
 sq_prepare_weight, sq_quantize_act and sq_w8a8_gemm instead).
@@ -652,8 +653,11 @@ def main():
                 s["call_gemm"] = B.prepared(B.sq_wo_linear, s["x"], s["wq"], s["ws"], s["bias"], s["y"], stream)
             continue
         if mode == "full":
-            s["calls_calib"] = [B.prepared(B.sq_calibrate_first if i == 0 else B.sq_calibrate, cb, s["run"], stream)
-                                for i, cb in enumerate(s["calib"])]
+            s["calls_calib"] = [B.prepared(B.sq_calibrate_batches, s["calib"], s["run"], True, stream)]
+            # the same calibration a batch at a time (timed as a stage of
+            # its own, beside the step)
+            s["calls_calib_each"] = [B.prepared(B.sq_calibrate_first if i == 0 else B.sq_calibrate, cb, s["run"],
+                                                stream) for i, cb in enumerate(s["calib"])]
         if tiled:
             if mode == "full":
                 s["call_prep"] = B.prepared(B.sq_prepare_weight_tiled, s["w"], s["run"], alpha, s["smooth"],
@@ -684,8 +688,8 @@ def main():
 
         mark()
         if mode == "full":
-            # the first batch starts the running max (sq_calibrate_first:
-            # no zero fill), the others fold into it
+            # every calibration batch in one call, which starts the running
+            # max (no zero fill)
             for call in s["calls_calib"]:
                 call()
             mark()
@@ -802,6 +806,8 @@ def main():
     def stage_calls(s, nm):
         if nm == "calibrate":
             return s["calls_calib"]
+        if nm == "calibrate_each_batch":
+            return s["calls_calib_each"]
         if nm in ("prepare_weight", "quantize_weight"):
             return [s["call_prep"]]
         if nm == "quantize_act":
@@ -809,7 +815,7 @@ def main():
         return [s["call_gemm"]]
 
     stage_graph_ms = {}
-    for nm in stage_names:
+    for nm in stage_names + (["calibrate_each_batch"] if mode == "full" else []):
         if nm == "gemm":
             stage_graph_ms[nm] = gemm_ms
             continue
@@ -886,7 +892,9 @@ def main():
     stages["note"] = "second pass of the same K steps with an event between stages"
     stages_graph = {nm: round(v * 1e3, 2) for nm, v in stage_graph_ms.items()}
     stages_graph["note"] = (f"each stage alone: a graph of {STAGE_LAUNCHES} repetitions over the rotated sets "
-                            "(the product: its own graph); the stage rooflines use these")
+                            "(the product: its own graph); the stage rooflines use these"
+                            + ("; calibrate is the step's one sq_calibrate_batches call, calibrate_each_batch the "
+                               "same batches a call each (not in the step)" if mode == "full" else ""))
     line = {
         "metric": (METRIC if args.workload == "o_proj" else
                    f"weight-only int8 linear TOPS at M={m} N={n} K={k}" if mode == "weight_only" else

@@ -78,6 +78,8 @@ typedef enum {
 #define SQ_MAX_ROWS (1LL << 30)
 /* Largest number of 128 x 128 output tiles of one product. */
 #define SQ_MAX_TILES ((1LL << 23) - 1)
+/* Most calibration batches one sq_calibrate_batches call takes. */
+#define SQ_MAX_CALIB_BATCHES 8
 
 /*
  * sq_calibrate -- running per-input-channel max of |X| over calibration rows.
@@ -103,6 +105,31 @@ sq_status sq_calibrate(const void* x, sq_dtype xt, int64_t rows, int64_t k,
  */
 sq_status sq_calibrate_first(const void* x, sq_dtype xt, int64_t rows, int64_t k,
                              float* running_max_abs, void* stream);
+
+/*
+ * sq_calibrate_batches -- several calibration batches at once. The running
+ * max of SmoothQuantW8A8.calibrate (page "w8a8_smoothquant.py") is a max
+ * over every calibration row, so batches already resident on the device can
+ * be folded in together, with the same result bits as one sq_calibrate per
+ * batch in any order:
+ *   running_max_abs[j] = max(start_j, max_b max_r |x[b][r][j]|)
+ * where start_j is the buffer's value (first == 0, as sq_calibrate) or 0
+ * (first != 0, as sq_calibrate_first on the first batch: no zero fill).
+ *   x               HOST array of nbatch DEVICE pointers, batch b [rows[b]][k]
+ *                   in xt, each 16-byte aligned (may be NULL where rows[b] == 0)
+ *   rows            HOST array of nbatch row counts, each >= 0, summing to at
+ *                   most SQ_MAX_ROWS
+ *   nbatch          1 .. SQ_MAX_CALIB_BATCHES
+ *   running_max_abs [k] fp32, in/out as in sq_calibrate
+ * Both host arrays are read before the call returns. One launch over all
+ * the rows (the row groups of a column max over that many rows), after a
+ * zero fill when first != 0 and the rows make more than one row group (more
+ * than 128 rows).
+ * Returns SQ_OK, or SQ_ERR_* before launching. No rows at all: a no-op, or
+ * the buffer set to 0 when first != 0.
+ */
+sq_status sq_calibrate_batches(const void* const* x, const int64_t* rows, int nbatch, sq_dtype xt,
+                               int64_t k, float* running_max_abs, int first, void* stream);
 
 /*
  * sq_prepare_weight -- the smoothing factor s and the int8 weights.

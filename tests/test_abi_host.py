@@ -60,6 +60,52 @@ def test_calibrate_errors(L):
     assert f(None, B.SQ_BF16, 0, 64, None, None) == B.SQ_OK
 
 
+def test_calibrate_batches_errors(L):
+    f = L.sq_calibrate_batches
+
+    def call(ptrs, rows, nbatch=None, xt=B.SQ_BF16, k=64, run=OK_PTR, first=0):
+        n = len(rows) if nbatch is None else nbatch
+        pa = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+        ra = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+        return f(pa, ra, n, xt, k, run, first, None)
+
+    two = [OK_PTR, OK_PTR + 4096]
+    assert call(two, [4, 4], xt=B.SQ_I32) == B.SQ_ERR_DTYPE
+    assert call(two, [4, 4], nbatch=0) == B.SQ_ERR_SHAPE
+    assert call(two, [4, 4], nbatch=B.SQ_MAX_CALIB_BATCHES + 1) == B.SQ_ERR_SHAPE
+    assert call(two, [4, -1]) == B.SQ_ERR_SHAPE
+    assert call(two, [4, 4], k=0) == B.SQ_ERR_SHAPE
+    assert call(two, [4, 4], k=B.SQ_MAX_K + 16) == B.SQ_ERR_SHAPE
+    assert call(two, [4, 4], k=24) == B.SQ_ERR_ALIGN
+    assert call([OK_PTR, 0], [4, 4]) == B.SQ_ERR_ARG
+    assert call([OK_PTR, BAD], [4, 4]) == B.SQ_ERR_ALIGN
+    assert call(two, [4, 4], run=None) == B.SQ_ERR_ARG
+    assert call(two, [4, 4], run=BAD) == B.SQ_ERR_ALIGN
+    # rows past the limit, alone or only in sum
+    assert call(two, [B.SQ_MAX_ROWS + 1, 0]) == B.SQ_ERR_SHAPE
+    assert call(two, [B.SQ_MAX_ROWS, 1]) == B.SQ_ERR_SHAPE
+    assert call(two, [1 << 62, 1 << 62]) == B.SQ_ERR_SHAPE
+    # null host arrays
+    assert f(None, (ctypes.c_int64 * 1)(4), 1, B.SQ_BF16, 64, OK_PTR, 0, None) == B.SQ_ERR_ARG
+    assert f((ctypes.c_void_p * 1)(OK_PTR), None, 1, B.SQ_BF16, 64, OK_PTR, 0, None) == B.SQ_ERR_ARG
+    # empty batches need no pointer; with no rows at all and first == 0 the
+    # call is a no-op
+    assert call([0, 0, 0], [0, 0, 0]) == B.SQ_OK
+
+
+def test_calibrate_batches_binding_checks():
+    import torch
+    run = torch.zeros(64)
+    with pytest.raises(ValueError):
+        B.sq_calibrate_batches([], run)
+    with pytest.raises(ValueError):
+        B.sq_calibrate_batches([torch.zeros(2, 64), torch.zeros(2, 32)], run)
+    with pytest.raises(ValueError):
+        B.sq_calibrate_batches([torch.zeros(2, 64), torch.zeros(2, 64, dtype=torch.bfloat16)], run)
+    with pytest.raises(TypeError):
+        B.sq_calibrate_batches([torch.zeros(2, 64)], run.double())
+
+
 def test_prepare_weight_errors(L):
     f = L.sq_prepare_weight
     args = dict(w=OK_PTR, wt=B.SQ_BF16, n=8, k=64, mx=OK_PTR, alpha=0.5, s=OK_PTR, wq=OK_PTR, ws=OK_PTR)

@@ -89,6 +89,40 @@ def test_calibrate_first(orc, rows, k, dtype):
     assert not down(empty).any()
 
 
+# batches (row counts) per call: the bench's four of 128 tokens, ragged runs
+# with empty batches, the one-launch limit (1024 rows in all) and just past
+# it (row groups folded with atomics), and long runs (one row per load)
+BATCHES = [([128, 128, 128, 128], 4096), ([1, 0, 37, 5, 200, 3, 0, 17], 272), ([1024], 1040),
+           ([600, 425], 4096), ([3000, 0, 2000, 100], 1040), ([2, 70], 16384), ([1], 16), ([0, 0], 64)]
+
+
+@pytest.mark.parametrize("first", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,k", BATCHES, ids=lambda v: "-".join(map(str, v)) if isinstance(v, list) else str(v))
+def test_calibrate_batches(orc, rows, k, dtype, first):
+    """sq_calibrate_batches: every batch (separate buffers) folded at once,
+    into a buffer that already holds the max of earlier rows (first == 0),
+    or starting from these batches alone whatever the buffer held
+    (first == 1); bit-exact against the oracle's running max over the same
+    rows."""
+    total = sum(rows)
+    c = inputs.small(total + 9, 8, k, seed=total + k + 11, dtype=dtype, bias=False)
+    x = up(c.x)
+    cuts = np.cumsum([0] + rows)
+    batches = [x[a:b].clone() for a, b in zip(cuts[:-1], cuts[1:])]
+    prior = c.x.f32[total:]  # 9 rows calibrated before the call
+    if first:
+        run = torch.full((k,), 1e30, dtype=torch.float32, device=DEV)
+        want = orc.calibrate(c.x.f32[:total]) if total else np.zeros(k, np.float32)
+    else:
+        run = up(orc.calibrate(prior))
+        want = orc.calibrate(c.x.f32)
+    torch.cuda.synchronize()
+    B.sq_calibrate_batches(batches, run, first=bool(first))
+    torch.cuda.synchronize()
+    assert_equal(down(run), want, "running max")
+
+
 # ---------------------------------------------------------------------------
 # a2-a5: s, int8 weights, weight scales
 # ---------------------------------------------------------------------------
@@ -447,6 +481,30 @@ def test_layer_lifecycle():
     fresh = B.SmoothQuantLinear(up(c.w), None)
     assert fresh.freeze() == B.SQ_WARN_UNCALIBRATED
     assert torch.all(fresh.smooth == 1.0)
+
+
+def test_layer_calibrate_batches(orc):
+    """SmoothQuantLinear.calibrate_batches: eleven batches (two calls of
+    sq_calibrate_batches, the first starting the running max, one batch
+    empty) give the oracle's running max over all their rows, and then the
+    same smoothing factor and codes as the layer calibrated batch by batch."""
+    c = _case((300, 24, 272), "bf16")
+    x = up(c.x)
+    cuts = [0, 1, 30, 30, 64, 100, 128, 160, 200, 233, 260, 300]
+    batches = [x[a:b] for a, b in zip(cuts[:-1], cuts[1:])]
+    many = B.SmoothQuantLinear(up(c.w), None, alpha=0.5)
+    many.calibrate(x[:0])  # an empty first batch starts nothing
+    many.calibrate_batches(batches)
+    one = B.SmoothQuantLinear(up(c.w), None, alpha=0.5)
+    for b in batches:
+        one.calibrate(b)
+    torch.cuda.synchronize()
+    assert many.calib_count == one.calib_count == 300
+    assert_equal(down(many.calib_max_abs), orc.calibrate(c.x.f32), "running max")
+    many.freeze()
+    one.freeze()
+    torch.cuda.synchronize()
+    assert torch.equal(many.smooth, one.smooth) and torch.equal(many.weight_int8, one.weight_int8)
 
 
 @pytest.mark.parametrize("layout", ["row", "tiled"])

@@ -26,6 +26,7 @@ SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
 SQ_MAX_K = 16384
 SQ_MAX_ROWS = 1 << 30
 SQ_MAX_TILES = (1 << 23) - 1
+SQ_MAX_CALIB_BATCHES = 8
 SQ_NOALLOC_MAX_CODES = 1 << 24
 SQ_NOALLOC_MAX_TOKENS = 1 << 14
 SQ_STE_MAX_ROWS = 1 << 24
@@ -42,6 +43,7 @@ _P, _I64, _SZ, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes
 _SIGNATURES = {
     "sq_calibrate": ([_P, _E, _I64, _I64, _P, _P], _E),
     "sq_calibrate_first": ([_P, _E, _I64, _I64, _P, _P], _E),
+    "sq_calibrate_batches": ([_P, _P, _E, _E, _I64, _P, _E, _P], _E),
     "sq_prepare_weight": ([_P, _E, _I64, _I64, _P, _F, _P, _P, _P, _P], _E),
     "sq_quantize_act": ([_P, _E, _I64, _I64, _P, _P, _P, _P], _E),
     "sq_w8a8_gemm": ([_P, _P, _I64, _P, _P, _I64, _I64, _P, _E, _P, _E, _P], _E),
@@ -211,6 +213,25 @@ def sq_calibrate_first(x: torch.Tensor, running_max_abs: torch.Tensor, stream=No
     _need_dtype(running_max_abs, torch.float32, "running_max_abs")
     return _invoke("sq_calibrate_first", _ptr(x), _dtype_code(x), rows, k, _ptr(running_max_abs),
                    _stream(stream, running_max_abs))
+
+
+def sq_calibrate_batches(xs, running_max_abs: torch.Tensor, first: bool = False, stream=None) -> int:
+    """Every batch of ``xs`` (a sequence of tensors of one dtype and last
+    dimension k) folded into running_max_abs at once; with ``first`` the
+    running max starts from these batches alone (no zero fill needed)."""
+    xs = list(xs)
+    if not xs:
+        raise ValueError("sq_calibrate_batches needs at least one batch")
+    k = xs[0].shape[-1]
+    for x in xs:
+        if x.shape[-1] != k or x.dtype != xs[0].dtype:
+            raise ValueError("calibration batches must share their dtype and last dimension")
+    _need_dtype(running_max_abs, torch.float32, "running_max_abs")
+    rows = [x.numel() // k if k else 0 for x in xs]
+    ptrs = (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+    counts = (ctypes.c_int64 * len(xs))(*rows)
+    return _invoke("sq_calibrate_batches", ptrs, counts, len(xs), _dtype_code(xs[0]), k, _ptr(running_max_abs),
+                   1 if first else 0, _stream(stream, running_max_abs))
 
 
 def sq_prepare_weight(w: torch.Tensor, x_max_abs: torch.Tensor | None, alpha: float, smooth: torch.Tensor,
@@ -669,6 +690,18 @@ class SmoothQuantLinear:
         else:
             sq_calibrate(x2, self.calib_max_abs)
         self.calib_count += x2.shape[0]
+
+    def calibrate_batches(self, xs) -> None:
+        """Several device-resident calibration batches at once, up to
+        SQ_MAX_CALIB_BATCHES per call of sq_calibrate_batches: the same running
+        max as calibrate on each batch in turn."""
+        if self.is_quantized:
+            raise RuntimeError("calibration after freeze is not allowed")
+        xs = [x.reshape(-1, x.shape[-1]) for x in xs]
+        for i in range(0, len(xs), SQ_MAX_CALIB_BATCHES):
+            chunk = xs[i:i + SQ_MAX_CALIB_BATCHES]
+            sq_calibrate_batches(chunk, self.calib_max_abs, first=self.calib_count == 0)
+            self.calib_count += sum(x.shape[0] for x in chunk)
 
     def freeze(self) -> int:
         """Returns SQ_OK, or SQ_WARN_UNCALIBRATED when no batch was seen. The

@@ -82,6 +82,27 @@ sq_status sq_calibrate_first(const void* x, sq_dtype xt, int64_t rows, int64_t k
     return launched(sq_launch_colmax_first(x, xt == SQ_BF16, rows, k, running_max_abs, as_stream(stream)));
 }
 
+sq_status sq_calibrate_batches(const void* const* x, const int64_t* rows, int nbatch, sq_dtype xt, int64_t k,
+                               float* running_max_abs, int first, void* stream) {
+    if (!fp_in(xt)) return SQ_ERR_DTYPE;
+    if (nbatch < 1 || nbatch > SQ_MAX_CALIB_BATCHES) return SQ_ERR_SHAPE;
+    if (!x || !rows || !running_max_abs) return SQ_ERR_ARG;
+    sq_status st = check_k(k);
+    if (st != SQ_OK) return st;
+    int64_t total = 0;
+    for (int b = 0; b < nbatch; ++b) {
+        if (rows[b] < 0 || rows[b] > kMaxRows) return SQ_ERR_SHAPE;
+        total += rows[b];
+        if (total > kMaxRows) return SQ_ERR_SHAPE;
+        if (rows[b] > 0 && !x[b]) return SQ_ERR_ARG;
+        if (rows[b] > 0 && !aligned16(x[b])) return SQ_ERR_ALIGN;
+    }
+    if (!aligned16(running_max_abs)) return SQ_ERR_ALIGN;
+    if (total == 0 && !first) return SQ_OK;
+    return launched(sq_launch_colmax_batches(x, rows, nbatch, xt == SQ_BF16, k, running_max_abs, first,
+                                             as_stream(stream)));
+}
+
 sq_status sq_prepare_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* x_max_abs,
                             float alpha, float* smooth, int8_t* w_q, float* w_scale, void* stream) {
     if (!fp_in(wt)) return SQ_ERR_DTYPE;

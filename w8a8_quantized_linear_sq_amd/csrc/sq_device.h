@@ -157,6 +157,11 @@ hipError_t sq_launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, fl
 // it held (one launch when the batch fits one row group)
 hipError_t sq_launch_colmax_first(const void* x, int bf16, int64_t rows, int64_t k, float* running_max,
                                   hipStream_t st);
+// several calibration batches (x[b], rows[b], b < nbatch <= 8) folded into
+// running_max in one launch (after a zero fill when first and the rows make
+// several row groups); first: running_max starts from these batches alone
+hipError_t sq_launch_colmax_batches(const void* const* x, const int64_t* rows, int nbatch, int bf16, int64_t k,
+                                    float* running_max, int first, hipStream_t st);
 // row groups for a partial column max whose [groups][k] uint32 result must
 // fit in scratch_bytes (at least 1)
 int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes);

@@ -8,6 +8,7 @@
 //     output channel (freeze_quantization -> quantize_per_channel_symmetric)
 //     and activations X / s with one scale per token (forward ->
 //     quantize_per_token_symmetric).
+#include "../../include/sq.h"
 #include "sq_device.h"
 
 using namespace sq;
@@ -36,11 +37,47 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// The rows of a column max's input, handed out as runs of consecutive rows
+// of one buffer: runs(r0, r1, f) calls f(p, count) for each run within rows
+// [r0, r1), p pointing at the run's first row (kvec u32x4 chunks per row).
+// One matrix is a single run; several calibration batches are taken as one
+// sequence of rows, a run per batch that the row range meets.
+// ---------------------------------------------------------------------------
+struct OneMatrix {
+    const u32x4* x;
+    int64_t kvec;
+    template <class F>
+    __device__ __forceinline__ void runs(int64_t r0, int64_t r1, F&& f) const {
+        f(x + r0 * kvec, r1 - r0);
+    }
+};
+
+struct BatchRows {
+    const u32x4* x[SQ_MAX_CALIB_BATCHES];
+    // one past batch b's last row in the sequence; entries past the last
+    // batch hold the total, so they make no run
+    int64_t end[SQ_MAX_CALIB_BATCHES];
+    int64_t kvec;
+    // the bounds are the same for the whole block (scalar registers), and
+    // the loop is unrolled so that the table is never indexed at run time
+    template <class F>
+    __device__ __forceinline__ void runs(int64_t r0, int64_t r1, F&& f) const {
+        int64_t start = 0;
+#pragma unroll
+        for (int b = 0; b < SQ_MAX_CALIB_BATCHES; ++b) {
+            const int64_t lo = max(r0, start), hi = min(r1, end[b]);
+            if (lo < hi) f(x[b] + (lo - start) * kvec, hi - lo);
+            start = end[b];
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // Column max of |x| over a group of rows.
 // Block = 4 wavefronts over one strip of 64 / L 16-byte column chunks; a
 // load instruction of a wavefront covers L rows of the strip (64 / L lanes
-// per row), and wavefront w takes row steps w, w+4, ... of the group with 8
-// loads in flight (L > 1 spreads a short batch over more blocks); the
+// per row), and wavefront w takes row steps w, w+4, ... of each run of the
+// group's rows with 8 loads in flight (L > 1 spreads a short batch over more blocks); the
 // partial maxima meet in LDS. |x| >= 0, so the order of the binary32 bit
 // patterns as unsigned integers is the order of the values: every max is an
 // exact integer max, independent of order.
@@ -51,8 +88,8 @@ hipError_t sq_launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 //            across calls);
 //   PARTIAL: out[g * k + j] = max over row group g (plain stores).
 // ---------------------------------------------------------------------------
-template <bool BF16, bool FOLD, int L>
-__global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
+template <bool BF16, bool FOLD, int L, class Src>
+__global__ __launch_bounds__(256) void colmax_kernel(Src src, int64_t rows, int64_t kvec,
                                                      int64_t rows_per_group, int64_t k,
                                                      unsigned* __restrict__ out, int overwrite) {
     constexpr int U = 8;
@@ -79,15 +116,17 @@ __global__ __launch_bounds__(256) void colmax_kernel(const u32x4* __restrict__ x
     };
     if (c < kvec) {
         constexpr int STEP = 4 * L;  // rows per round of the 4 wavefronts
-        int64_t r = r0 + wave * L + sub;
-        for (; r + STEP * (U - 1) < r1; r += STEP * U) {
-            u32x4 v[U];
+        src.runs(r0, r1, [&](const u32x4* p, int64_t count) {
+            int64_t r = wave * L + sub;
+            for (; r + STEP * (U - 1) < count; r += STEP * U) {
+                u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = x[(r + STEP * u) * kvec + c];
+                for (int u = 0; u < U; ++u) v[u] = p[(r + STEP * u) * kvec + c];
 #pragma unroll
-            for (int u = 0; u < U; ++u) fold(v[u]);
-        }
-        for (; r < r1; r += STEP) fold(x[r * kvec + c]);
+                for (int u = 0; u < U; ++u) fold(v[u]);
+            }
+            for (; r < count; r += STEP) fold(p[r * kvec + c]);
+        });
     }
     red[wave][lane] = m;
     __syncthreads();
@@ -148,11 +187,12 @@ template <bool FOLD, int L>
 static void launch_colmax_l(const void* x, int bf16, int64_t rows, int64_t kvec, int64_t k, unsigned* out,
                             int64_t groups, int64_t rpg, int overwrite, hipStream_t st) {
     dim3 grid((unsigned)((kvec + 64 / L - 1) / (64 / L)), (unsigned)groups);
+    const OneMatrix src{(const u32x4*)x, kvec};
     if (bf16)
-        hipLaunchKernelGGL((colmax_kernel<true, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
+        hipLaunchKernelGGL((colmax_kernel<true, FOLD, L, OneMatrix>), grid, dim3(256), 0, st, src, rows, kvec, rpg,
                            k, out, overwrite);
     else
-        hipLaunchKernelGGL((colmax_kernel<false, FOLD, L>), grid, dim3(256), 0, st, (const u32x4*)x, rows, kvec, rpg,
+        hipLaunchKernelGGL((colmax_kernel<false, FOLD, L, OneMatrix>), grid, dim3(256), 0, st, src, rows, kvec, rpg,
                            k, out, overwrite);
 }
 
@@ -186,6 +226,64 @@ hipError_t sq_launch_colmax_first(const void* x, int bf16, int64_t rows, int64_t
     hipError_t e = sq_launch_fill(running_max, 0.0f, k, st);
     if (e != hipSuccess) return e;
     return launch_colmax<true>(x, bf16, rows, k, (unsigned*)running_max, groups, rpg, st);
+}
+
+// Several calibration batches in one launch, read as one run of rows with
+// the row groups of one matrix of that many rows (a group may span
+// batches). When the run starts the max and has several row groups, a zero
+// fill comes first and the groups fold with atomics. (One row group of
+// narrow strips, or wider blocks over all rows, would need no fill; both
+// measured slower on four batches of 128 tokens.)
+template <int L>
+static void launch_colmax_batches_l(const BatchRows& src, int bf16, int64_t total, int64_t kvec, int64_t rpg,
+                                    int64_t groups, int64_t k, unsigned* out, int overwrite, hipStream_t st) {
+    dim3 grid((unsigned)((kvec + 64 / L - 1) / (64 / L)), (unsigned)groups);
+    if (bf16)
+        hipLaunchKernelGGL((colmax_kernel<true, true, L, BatchRows>), grid, dim3(256), 0, st, src, total, kvec, rpg,
+                           k, out, overwrite);
+    else
+        hipLaunchKernelGGL((colmax_kernel<false, true, L, BatchRows>), grid, dim3(256), 0, st, src, total, kvec,
+                           rpg, k, out, overwrite);
+}
+
+hipError_t sq_launch_colmax_batches(const void* const* x, const int64_t* rows, int nbatch, int bf16, int64_t k,
+                                    float* running_max, int first, hipStream_t st) {
+    const int64_t kvec = bf16 ? k / 8 : k / 4;
+    BatchRows src{};
+    src.kvec = kvec;
+    int64_t total = 0;
+    for (int b = 0; b < SQ_MAX_CALIB_BATCHES; ++b) {
+        if (b < nbatch) {
+            src.x[b] = (const u32x4*)x[b];
+            total += rows[b];
+        }
+        src.end[b] = total;
+    }
+    if (total == 0) return first ? sq_launch_fill(running_max, 0.0f, k, st) : hipSuccess;
+    // a single batch with rows: the one-matrix kernel (a smaller argument
+    // block, the same grid)
+    for (int b = 0; b < nbatch; ++b) {
+        if (rows[b] == total)
+            return first ? sq_launch_colmax_first(x[b], bf16, total, k, running_max, st)
+                         : sq_launch_colmax(x[b], bf16, total, k, running_max, st);
+    }
+    int64_t gx, groups, rpg;
+    colmax_grid(total, kvec, gx, groups, rpg);
+    int overwrite = 0;
+    if (first) {
+        if (groups == 1) {
+            overwrite = 1;  // its owners write each column's max directly
+        } else {
+            hipError_t e = sq_launch_fill(running_max, 0.0f, k, st);
+            if (e != hipSuccess) return e;
+        }
+    }
+    unsigned* out = (unsigned*)running_max;
+    if (colmax_l(total) == 4)
+        launch_colmax_batches_l<4>(src, bf16, total, kvec, rpg, groups, k, out, overwrite, st);
+    else
+        launch_colmax_batches_l<1>(src, bf16, total, kvec, rpg, groups, k, out, overwrite, st);
+    return hipGetLastError();
 }
 
 int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes) {
