@@ -45,6 +45,7 @@ import math
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -151,6 +152,52 @@ def sweep_k(torch, B, dev):
                           "tops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
         del g, ops, bufs, ones
         torch.cuda.empty_cache()
+
+
+def _read_sclk_mhz(path: str):
+    """The current shader clock the driver reports in pp_dpm_sclk (the line
+    marked with '*'), in MHz, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+                    return int(m.group(1)) if m else None
+    except OSError:
+        return None
+    return None
+
+
+def sample_sclk(load, period_s: float = 0.01):
+    """Shader clock while `load()` keeps the GPU busy (it enqueues work and
+    waits for it): the driver's current-clock file read every period_s from
+    a thread of its own; the first fifth of the samples (the clock's ramp)
+    is dropped. None where no single such file is readable."""
+    import glob
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(files) != 1 or _read_sclk_mhz(files[0]) is None:
+        load()
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = _read_sclk_mhz(files[0])
+            if v is not None:
+                samples.append(v)
+            time.sleep(period_s)
+
+    t = threading.Thread(target=sampler, daemon=True)
+    t.start()
+    try:
+        load()
+    finally:
+        stop.set()
+        t.join()
+    kept = sorted(samples[len(samples) // 5:])
+    if not kept:
+        return None
+    return {"median": kept[len(kept) // 2], "min": kept[0], "max": kept[-1], "samples": len(kept)}
 
 
 def _gemm_traffic(layout: str):
@@ -757,6 +804,27 @@ def main():
     torch.cuda.synchronize()
     gemm_warm_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
+    # the shader clock under the product: the rotated-set product graph
+    # replayed back to back for about half a second while the driver's
+    # current-clock reading is sampled
+    replays = max(1, int(0.5 / max(gemm_ms * 1e-3 * GEMM_LAUNCHES, 1e-6)))
+
+    def product_load():
+        for _ in range(replays):
+            gemm_graph.replay()
+        torch.cuda.synchronize()
+
+    sclk = sample_sclk(product_load)
+    if sclk is not None:
+        sclk["source"] = (f"pp_dpm_sclk read every 10 ms over {replays} replays of the {GEMM_LAUNCHES}-launch "
+                          "product graph (rotated sets)")
+        if m > 64 and mode != "weight_only":
+            # the product's fraction of the peak scaled to that clock (the
+            # rated peak assumes 2.4 GHz)
+            at_clock = PEAK_INT8_TOPS * sclk["median"] / 2400.0
+            sclk["gemm_frac_of_peak_at_median_clock"] = round(2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12 / at_clock,
+                                                              4)
+
     # the per-call linear (the second throughput figure): activation codes + the
     # product, as a forward runs them on prepared weights, GEMM_LAUNCHES
     # calls in one graph over the rotated sets, replayed between events
@@ -915,6 +983,7 @@ def main():
         "gemm_us": round(gemm_ms * 1e3, 2),
         "gemm_launches_timed": GEMM_LAUNCHES,
         "gemm_us_warm": round(gemm_warm_ms * 1e3, 2),
+        "sclk_mhz_under_gemm": sclk,
         "stages_us": stages,
         "stages_us_graph": stages_graph,
         "stage_rooflines": stage_roof,

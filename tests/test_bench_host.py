@@ -66,3 +66,16 @@ def test_every_workload_names_a_case_and_mode():
     for name, (desc, spec, mode) in bench.WORKLOADS.items():
         assert desc and mode in ("full", "per_call", "per_tensor", "weight_only", "ste"), name
         assert hasattr(inputs, spec[0]), name
+
+
+def test_sclk_reading(tmp_path):
+    """The driver's current-clock file: the line marked '*' gives the clock
+    (deep sleep and numbered levels alike); missing or unmarked: None."""
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("S: 96Mhz\n0: 500Mhz\n1: 1712Mhz *\n2: 2400Mhz\n")
+    assert bench._read_sclk_mhz(str(f)) == 1712
+    f.write_text("S: 96Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench._read_sclk_mhz(str(f)) == 96
+    f.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench._read_sclk_mhz(str(f)) is None
+    assert bench._read_sclk_mhz(str(tmp_path / "missing")) is None
