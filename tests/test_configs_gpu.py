@@ -331,3 +331,29 @@ def test_int32_product_matches_vendor_library_4096(tiled):
     ref = torch._int_mm(xr, wr.t())  # (k x n): the transposed view of W_q
     torch.cuda.synchronize()
     assert torch.equal(y, ref), int((y != ref).sum())
+
+
+VENDOR_CASES = {"prefill": inputs.prefill, "qkv": lambda: inputs.block_linear(0), "up": lambda: inputs.block_linear(2),
+                "down": lambda: inputs.block_linear(3), "mlp_up": inputs.mlp_up}
+
+
+@pytest.mark.parametrize("name", list(VENDOR_CASES))
+def test_int32_product_matches_vendor_library_full_size(name):
+    """The exact int32 product of every other full-size workload (tiled
+    codes, alpha 0.5), every element, against the vendor library's int8
+    GEMM on the same codes (untiled): where the output checks against the
+    oracle are sampled (the MLP up-projection: 1 row in 16), this covers
+    every accumulator, including the 8192 x 28672 ones."""
+    case = VENDOR_CASES[name]()
+    m, n, k = case.m, case.n, case.k
+    print(f"[{name}] {m}x{n}x{k}", flush=True)
+    run = _calibrate(case)
+    s, sx, sw = _empty(k, torch.float32), _empty(m, torch.float32), _empty(n, torch.float32)
+    xq, wq = B.tiled_empty(m, k, DEV), B.tiled_empty(n, k, DEV)
+    B.sq_prepare_weight_tiled(up(case.w), run, 0.5, s, wq, sw)
+    B.sq_quantize_act_tiled(up(case.x), s, xq, sx)
+    y = _empty((m, n), torch.int32)
+    B.sq_w8a8_gemm_tiled(xq, None, m, wq, None, n, k, None, y)
+    ref = torch._int_mm(B.untile(xq, m, k), B.untile(wq, n, k).t())
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref), int((y != ref).sum())
