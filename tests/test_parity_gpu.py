@@ -483,6 +483,40 @@ def test_layer_lifecycle():
     assert torch.all(fresh.smooth == 1.0)
 
 
+@pytest.mark.parametrize("rows", [[128, 128, 128, 128], [3, 0, 90]], ids=["4x128", "ragged"])
+def test_calibrate_batches_graph_replays(orc, rows):
+    """sq_calibrate_batches captured in a HIP graph (its zero fill is a
+    kernel, not a memset) and replayed four times, the buffer refilled with
+    values above every |x| and other work run eagerly between replays:
+    every replay gives the oracle's running max."""
+    k = 4096
+    total = sum(rows)
+    c = inputs.small(total, 8, k, seed=total + 5, dtype="bf16", bias=False)
+    x = up(c.x)
+    cuts = np.cumsum([0] + rows)
+    batches = [x[a:b].clone() for a, b in zip(cuts[:-1], cuts[1:])]
+    want = orc.calibrate(c.x.f32)
+    run = torch.full((k,), 1e30, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(DEV)
+    stream.wait_stream(torch.cuda.current_stream())
+    call = B.prepared(B.sq_calibrate_batches, batches, run, True, stream)
+    with torch.cuda.stream(stream):
+        call()  # eager once before capture
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call()
+    other = torch.zeros(k, dtype=torch.float32, device=DEV)
+    for i in range(4):
+        run.fill_(1e30 + i)
+        other += 1.0  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_equal(down(run), want, f"running max, replay {i}")
+
+
 def test_layer_calibrate_batches(orc):
     """SmoothQuantLinear.calibrate_batches: eleven batches (two calls of
     sq_calibrate_batches, the first starting the running max, one batch
