@@ -171,7 +171,10 @@ def _check_grads(c, dyt, alpha, host, got, orc, with_mx=True):
     return ref
 
 
-SHAPES = [(16, 128, 256), (3, 5, 32), (17, 33, 272), (130, 260, 528), (257, 300, 1040), (70, 40, 4096)]
+# the last two: at least 1024 tokens and few 256 x 256 tiles of gX, so gX
+# runs with its contraction split in two halves (ragged n and k)
+SHAPES = [(16, 128, 256), (3, 5, 32), (17, 33, 272), (130, 260, 528), (257, 300, 1040), (70, 40, 4096),
+          (1040, 300, 272), (1100, 17, 48)]
 
 
 def _id(s):

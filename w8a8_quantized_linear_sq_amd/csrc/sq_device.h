@@ -242,6 +242,11 @@ hipError_t sq_launch_gemm_stream_tiled(const int8_t* xq, const float* sx, int64_
 // multiples of 64 bytes, kbytes a multiple of ldb)
 hipError_t sq_launch_gemm_bf16_periodic(const void* a, const void* b, int64_t m, int64_t n, int64_t kbytes,
                                         int64_t ldb, float* y, hipStream_t st);
+// the same with the contraction split in two halves, one launch: y[h] =
+// a[h] b[h], a[h] at h * m * kbytes bytes, b[h] at h * n * ldb bytes, y[h]
+// at h * m * n floats
+hipError_t sq_launch_gemm_bf16_periodic_split2(const void* a, const void* b, int64_t m, int64_t n, int64_t kbytes,
+                                               int64_t ldb, float* y, hipStream_t st);
 
 // The straight-through backward (learnable alpha): workspace regions (byte
 // offsets, 256-aligned) for m tokens, n output channels, k input channels.
@@ -250,6 +255,9 @@ struct SteLayout {
     int64_t gx, gw, gb;        // row groups of the three column-sum passes
     size_t a1, bw, a2, bx;     // packed factors and transposed codes (bf16)
     size_t px, pw, pb, term;   // binary64 partial sums and per-channel terms
+    bool split;                // gX's contraction split in two halves (one launch)
+    int64_t nh;                // n64 / 2 when split, else n64
+    size_t gxh;                // the two halves of gX, fp32 [2][m][k] (split only)
     size_t bytes;              // total
 };
 SteLayout sq_ste_layout(int64_t m, int64_t n, int64_t k);

@@ -144,12 +144,22 @@ constexpr int kI8 = 0, kBf16 = 1, kF32 = 2;
 // repeat along k, so B's byte at k offset c is the one at c mod ldb: one
 // product sums several A planes against the same B (the straight-through
 // backward splits an fp32 operand into three bf16 planes side by side).
-template <int ET, int BM, int BN, int WGM, int WGN, int OUT, bool TILED, bool BPER = false>
+// NSPLIT (BPER, fp32 out): gridDim.y independent products of the same shape
+// in one launch, product h with A at h * m * k bytes, B at h * n * ldb bytes
+// and Y at h * m * n floats (the halves of a contraction split in two).
+template <int ET, int BM, int BN, int WGM, int WGN, int OUT, bool TILED, bool BPER = false, int NSPLIT = 1>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, int m, int n, int k,
     const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
     int bias_kind, void* __restrict__ Y, int grid_m, int grid_n, int scalar_scales, int ldb) {
     static_assert(!(BPER && TILED), "a periodic B is row-major");
+    static_assert(NSPLIT == 1 || (BPER && OUT == 0), "split products: periodic B, fp32 out");
+    if constexpr (NSPLIT > 1) {
+        const int64_t h = blockIdx.y;
+        A += h * m * k;
+        B += h * n * ldb;
+        Y = (float*)Y + h * m * n;
+    }
     constexpr int NW = WGM * WGN;                 // wavefronts (WGM x WGN grid)
     constexpr int kStages = NW == 8 ? kStagesPingPong : kStagesInterleaved;
     static_assert(kStages >= 3 && kStages <= 5, "the prologue's wait covers up to three later stages");
@@ -553,15 +563,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(
     }
 }
 
-template <int ET, bool TILED, int BM, int BN, int WGM, int WGN, bool BPER = false>
+template <int ET, bool TILED, int BM, int BN, int WGM, int WGN, bool BPER = false, int NSPLIT = 1>
 hipError_t launch_tile(const int8_t* xq, const float* sx, int m, const int8_t* wq, const float* sw,
                        int n, int kbytes, const void* bias, int bias_kind, void* y, int out_kind, int scalar_scales,
                        hipStream_t st, int ldb = 0) {
     const int gm = (m + BM - 1) / BM, gn = (n + BN - 1) / BN;
-    dim3 grid(gm * gn), block(64 * WGM * WGN);
+    dim3 grid(gm * gn, NSPLIT), block(64 * WGM * WGN);
     if (out_kind == 0)
-        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0, TILED, BPER>), grid, block, 0, st, xq, wq, m, n,
-                           kbytes, sx, sw, bias, bias_kind, y, gm, gn, scalar_scales, ldb);
+        hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 0, TILED, BPER, NSPLIT>), grid, block, 0, st, xq, wq, m,
+                           n, kbytes, sx, sw, bias, bias_kind, y, gm, gn, scalar_scales, ldb);
     else if constexpr (!BPER) {
         if (out_kind == 1)
             hipLaunchKernelGGL((gemm_kernel<ET, BM, BN, WGM, WGN, 1, TILED>), grid, block, 0, st, xq, wq, m, n, kbytes,
@@ -645,4 +655,17 @@ hipError_t sq_launch_gemm_bf16_periodic(const void* a, const void* b, int64_t m,
     if (m <= 0 || n <= 0) return hipSuccess;
     return launch_tiled<kBf16, false, true>((const int8_t*)a, nullptr, m, (const int8_t*)b, nullptr, n, kbytes,
                                             nullptr, 0, y, 0, 0, st, ldb);
+}
+
+// The same product with its contraction split in two halves, both in one
+// launch of 256 x 256 tiles (the halves fill the compute units where the
+// output alone has too few such tiles): y[h] = a[h] b[h] for h = 0, 1, with
+// a[h] [m][kbytes / 2] at h * m * kbytes bytes, b[h] [n][ldb / 2] at
+// h * n * ldb bytes and y[h] [m][n] at h * m * n floats.
+hipError_t sq_launch_gemm_bf16_periodic_split2(const void* a, const void* b, int64_t m, int64_t n, int64_t kbytes,
+                                               int64_t ldb, float* y, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    return launch_tile<kBf16, false, 256, 256, 2, 4, true, 2>((const int8_t*)a, nullptr, (int)m, (const int8_t*)b,
+                                                              nullptr, (int)n, (int)kbytes, nullptr, 0, y, 0, 0, st,
+                                                              (int)ldb);
 }

@@ -64,16 +64,21 @@ __device__ __forceinline__ float load_val(const void* p, int64_t i) {
     else return ((const float*)p)[i];
 }
 
-// a[t][p * ld + o] = plane p of RN32(dy[t][o] * sc[o]) for o < n, zero for
-// n <= o < ld (ld a multiple of 64). Thread: 8 consecutive o of every row it
-// visits. VEC (dy and sc 16-byte aligned, n a multiple of 8): dy and sc read
-// 16 bytes at a time; else, and past n, element by element. The planes are
-// written 16 bytes at a time.
+// Plane p of RN32(dy[t][o] * sc[o]) for o < n, zero for n <= o < ld (ld a
+// multiple of 64), with the columns in parts of nh (nh divides ld, a
+// multiple of 32): part h = o / nh is a matrix [m][3 nh] of its own at
+// h * m * 3 nh, row t holding the three planes of its nh columns side by
+// side, a[h][t][p * nh + o % nh] (nh = ld: one part). Thread: 8
+// consecutive o of every row it visits. VEC (dy and sc 16-byte aligned, n a
+// multiple of 8): dy and sc read 16 bytes at a time; else, and past n,
+// element by element. The planes are written 16 bytes at a time.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void ste_pack_rows_kernel(const void* __restrict__ dy, const float* __restrict__ sc,
-                                                            int64_t m, int64_t n, int64_t ld, uint16_t* __restrict__ a) {
+                                                            int64_t m, int64_t n, int64_t ld, int64_t nh,
+                                                            uint16_t* __restrict__ a) {
     const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (o0 >= ld) return;
+    uint16_t* part = a + (o0 / nh) * m * 3 * nh + o0 % nh;
     const bool whole = VEC && o0 + 8 <= n;
     float f[8];
     if (whole) {
@@ -93,12 +98,12 @@ __global__ __launch_bounds__(256) void ste_pack_rows_kernel(const void* __restri
         uint32_t h[3][8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) split3(v[e] * f[e], h[0][e], h[1][e], h[2][e]);
-        uint16_t* row = a + t * 3 * ld + o0;
+        uint16_t* row = part + t * 3 * nh;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             const u32x4 w = {h[p][0] | (h[p][1] << 16), h[p][2] | (h[p][3] << 16), h[p][4] | (h[p][5] << 16),
                              h[p][6] | (h[p][7] << 16)};
-            *(u32x4*)(row + p * ld) = w;
+            *(u32x4*)(row + p * nh) = w;
         }
     }
 }
@@ -154,11 +159,14 @@ __global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restri
     }
 }
 
-// b[j][o] = bf16(q[o][j]) (exact) for o < rows, zero for rows <= o < ld;
-// j < k. q is [rows][k] int8 row-major; 64 x 64 tiles through LDS.
+// bf16(q[o][j]) (exact) for o < rows, zero for rows <= o < ld; j < k, with
+// the o in parts of nh (nh divides ld, a multiple of 8): part h = o / nh is
+// a matrix [k][nh] of its own at h * k * nh, b[h][j][o % nh] (nh = ld: one
+// part, b[j][o]). q is [rows][k] int8 row-major; 64 x 64 tiles through LDS.
 constexpr int kQP = 68;  // LDS row pitch in bytes
 __global__ __launch_bounds__(256) void ste_transpose_codes_kernel(const int8_t* __restrict__ q, int64_t rows,
-                                                                  int64_t k, int64_t ld, uint16_t* __restrict__ b) {
+                                                                  int64_t k, int64_t ld, int64_t nh,
+                                                                  uint16_t* __restrict__ b) {
     __shared__ __attribute__((aligned(16))) int8_t tile[64][kQP];  // [o][j]
     const int64_t tiles_o = ld / 64;
     const int64_t o0 = (blockIdx.x % tiles_o) * 64, j0 = (blockIdx.x / tiles_o) * 64;
@@ -183,22 +191,28 @@ __global__ __launch_bounds__(256) void ste_transpose_codes_kernel(const int8_t* 
             w[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);  // |code| <= 128: exact
         }
         const u32x4 v = {w[0], w[1], w[2], w[3]};
-        *(u32x4*)(b + j * ld + o0 + piece * 8) = v;
+        const int64_t o = o0 + piece * 8;  // 8 o in one part
+        *(u32x4*)(b + (o / nh) * k * nh + j * nh + o % nh) = v;
     }
 }
 
 // Column sums over row groups, with an optional elementwise factor and an
-// optional in-place fold of s:
+// optional fold of s:
 //   part[g][c] = sum over rows r of group g of y[r][c] * z[r][c] (binary64,
 //                rows in order; z = 1 when ZK == 0)
-//   OP 1: y[r][c] = y[r][c] / s[c] (IEEE);  OP 2: y[r][c] = y[r][c] * s[c]
+//   OP 1: out[r][c] = y[r][c] / s[c] (IEEE);  OP 2: out[r][c] = y[r][c] * s[c]
+// with out = y (in place) unless TWO: then y holds two fp32 partial
+// matrices, the second at y + rows * cols, and y[r][c] stands for their
+// sum RN32(y0 + y1) (the halves of a split product), written to out.
 // y is fp32 when OP != 0 (else YBF16 selects its type); z is fp32 (ZK 1)
 // or bf16 (ZK 2). VEC: cols % 4 == 0 and rows 16-byte aligned, 4 columns
 // per thread as one vector; otherwise 4 scalar columns.
-template <int ZK, int OP, bool YBF16, bool VEC>
+template <int ZK, int OP, bool YBF16, bool VEC, bool TWO = false>
 __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, const void* __restrict__ z,
                                                          const float* __restrict__ s, int64_t rows, int64_t cols,
-                                                         int64_t rpg, double* __restrict__ part) {
+                                                         int64_t rpg, double* __restrict__ part,
+                                                         float* __restrict__ out) {
+    static_assert(!TWO || (OP != 0 && !YBF16), "two partials: fp32, folded into out");
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (c0 >= cols) return;
     const int64_t g = blockIdx.y;
@@ -215,9 +229,16 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
         if constexpr (VEC && !YBF16) {
             const float4 v = *(const float4*)((const float*)y + base);
             yv[0] = v.x; yv[1] = v.y; yv[2] = v.z; yv[3] = v.w;
+            if constexpr (TWO) {
+                const float4 u = *(const float4*)((const float*)y + rows * cols + base);
+                yv[0] += u.x; yv[1] += u.y; yv[2] += u.z; yv[3] += u.w;
+            }
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) yv[e] = c0 + e < cols ? load_val<YBF16>(y, base + e) : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                yv[e] = c0 + e < cols ? load_val<YBF16>(y, base + e) : 0.0f;
+                if constexpr (TWO) yv[e] += c0 + e < cols ? ((const float*)y)[rows * cols + base + e] : 0.0f;
+            }
         }
         if constexpr (ZK == 1 && VEC) {
             const float4 v = *(const float4*)((const float*)z + base);
@@ -232,15 +253,16 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += (double)yv[e] * (double)zv[e];
         if constexpr (OP != 0) {
-            float out[4];
+            float o4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = OP == 1 ? yv[e] / sc[e] : yv[e] * sc[e];
+            for (int e = 0; e < 4; ++e) o4[e] = OP == 1 ? yv[e] / sc[e] : yv[e] * sc[e];
+            float* dst = TWO ? out : (float*)y;
             if constexpr (VEC) {
-                *(float4*)((float*)y + base) = make_float4(out[0], out[1], out[2], out[3]);
+                *(float4*)(dst + base) = make_float4(o4[0], o4[1], o4[2], o4[3]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (c0 + e < cols) ((float*)y)[base + e] = out[e];
+                    if (c0 + e < cols) dst[base + e] = o4[e];
             }
         }
     }
@@ -375,19 +397,26 @@ int64_t colsum_groups(int64_t rows, int64_t cols) {
     return std::min<int64_t>(g, 1024);
 }
 
-template <int ZK, int OP, bool YBF16>
+template <int ZK, int OP, bool YBF16, bool TWO = false>
 hipError_t launch_colsum(void* y, const void* z, const float* s, int64_t rows, int64_t cols, int64_t groups,
-                         double* part, bool vec, hipStream_t st) {
+                         double* part, bool vec, hipStream_t st, float* out = nullptr) {
     const int64_t rpg = (rows + groups - 1) / groups;
     const dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)groups);
     if (vec)
-        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, true>), grid, dim3(256), 0, st, y, z, s, rows, cols, rpg,
-                           part);
+        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, true, TWO>), grid, dim3(256), 0, st, y, z, s, rows, cols,
+                           rpg, part, out);
     else
-        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, false>), grid, dim3(256), 0, st, y, z, s, rows, cols,
-                           rpg, part);
+        hipLaunchKernelGGL((ste_colsum_kernel<ZK, OP, YBF16, false, TWO>), grid, dim3(256), 0, st, y, z, s, rows,
+                           cols, rpg, part, out);
     return hipGetLastError();
 }
+
+// gX with its contraction (the n output channels, three planes each) split
+// in two halves run side by side in one launch of 256 x 256 tiles, where
+// gX [m][k] alone has at most half as many such tiles as the chip has
+// compute units and m is large enough for the product to dominate; the
+// halves' fp32 results are added in a fixed order by the column pass.
+bool ste_split_gx(int64_t m, int64_t k) { return m >= 1024 && ((m + 255) / 256) * ((k + 255) / 256) <= 128; }
 
 }  // namespace
 
@@ -403,6 +432,8 @@ SteLayout sq_ste_layout(int64_t m, int64_t n, int64_t k) {
     L.gw = colsum_groups(n, k);
     L.gb = colsum_groups(m, n);
     size_t off = 0;
+    L.split = ste_split_gx(m, k);
+    L.nh = L.split ? n64 / 2 : n64;
     L.a1 = off; off = align256(off + (size_t)m * 3 * n64 * 2);
     L.bw = off; off = align256(off + (size_t)k * n64 * 2);
     L.a2 = off; off = align256(off + (size_t)n * 3 * m64 * 2);
@@ -411,6 +442,7 @@ SteLayout sq_ste_layout(int64_t m, int64_t n, int64_t k) {
     L.pw = off; off = align256(off + (size_t)L.gw * k * 8);
     L.pb = off; off = align256(off + (size_t)L.gb * n * 8);
     L.term = off; off = align256(off + (size_t)k * 8);
+    L.gxh = off; off = align256(off + (L.split ? (size_t)2 * m * k * 4 : 0));
     L.bytes = off;
     return L;
 }
@@ -430,22 +462,26 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
     double* pw = (double*)(base + L.pw);
     double* pb = (double*)(base + L.pb);
     double* term = (double*)(base + L.term);
+    float* gxh = (float*)(base + L.gxh);
     hipError_t e;
-    // gX: a1 = RN32(dy * sw) in three planes [m][3 n64], bw = wq^T [k][n64]
+    // gX: a1 = RN32(dy * sw) in three planes [m][3 n64], bw = wq^T [k][n64];
+    // split: each in two parts over the n (a1 [2][m][3 nh], bw [2][k][nh]),
+    // the two halves of gX to gxh [2][m][k]
     {
         const dim3 grid((unsigned)((L.n64 + 2047) / 2048), (unsigned)std::min<int64_t>(m, 65535));
         const bool vec = aligned16_ptr(dy) && aligned16_ptr(sw) && n % 8 == 0;
         if (dy_bf16) {
-            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<true, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
-            else hipLaunchKernelGGL((ste_pack_rows_kernel<true, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<true, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, L.nh, a1);
+            else hipLaunchKernelGGL((ste_pack_rows_kernel<true, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, L.nh, a1);
         } else {
-            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<false, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
-            else hipLaunchKernelGGL((ste_pack_rows_kernel<false, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, a1);
+            if (vec) hipLaunchKernelGGL((ste_pack_rows_kernel<false, true>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, L.nh, a1);
+            else hipLaunchKernelGGL((ste_pack_rows_kernel<false, false>), grid, dim3(256), 0, st, dy, sw, m, n, L.n64, L.nh, a1);
         }
         hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.n64 / 64) * ((k + 63) / 64))), dim3(256), 0,
-                           st, wq, n, k, L.n64, bw);
+                           st, wq, n, k, L.n64, L.nh, bw);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = sq_launch_gemm_bf16_periodic(a1, bw, m, k, 3 * L.n64 * 2, L.n64 * 2, dx, st);
+        e = L.split ? sq_launch_gemm_bf16_periodic_split2(a1, bw, m, k, 3 * L.nh * 2, L.nh * 2, gxh, st)
+                    : sq_launch_gemm_bf16_periodic(a1, bw, m, k, 3 * L.n64 * 2, L.n64 * 2, dx, st);
         if (e != hipSuccess) return e;
     }
     // gW: a2 = RN32(dy^T * sx) in three planes [n][3 m64], bx = xq^T [k][m64]
@@ -460,14 +496,18 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
             else hipLaunchKernelGGL((ste_pack_cols_kernel<false, false>), grid, dim3(256), 0, st, dy, sx, m, n, L.m64, a2);
         }
         hipLaunchKernelGGL(ste_transpose_codes_kernel, dim3((unsigned)((L.m64 / 64) * ((k + 63) / 64))), dim3(256), 0,
-                           st, xq, m, k, L.m64, bx);
+                           st, xq, m, k, L.m64, L.m64, bx);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         e = sq_launch_gemm_bf16_periodic(a2, bx, n, k, 3 * L.m64 * 2, L.m64 * 2, dw, st);
         if (e != hipSuccess) return e;
     }
     // dx = gX / s with sum_t gX x;  dw = gW * s with sum_o gW w
-    e = x_bf16 ? launch_colsum<2, 1, false>(dx, x, s, m, k, L.gx, px, true, st)
-               : launch_colsum<1, 1, false>(dx, x, s, m, k, L.gx, px, true, st);
+    if (L.split)
+        e = x_bf16 ? launch_colsum<2, 1, false, true>(gxh, x, s, m, k, L.gx, px, true, st, dx)
+                   : launch_colsum<1, 1, false, true>(gxh, x, s, m, k, L.gx, px, true, st, dx);
+    else
+        e = x_bf16 ? launch_colsum<2, 1, false>(dx, x, s, m, k, L.gx, px, true, st)
+                   : launch_colsum<1, 1, false>(dx, x, s, m, k, L.gx, px, true, st);
     if (e != hipSuccess) return e;
     e = w_bf16 ? launch_colsum<2, 2, false>(dw, w, s, n, k, L.gw, pw, true, st)
                : launch_colsum<1, 2, false>(dw, w, s, n, k, L.gw, pw, true, st);
