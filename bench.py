@@ -804,27 +804,6 @@ def main():
     torch.cuda.synchronize()
     gemm_warm_ms = gev[0].elapsed_time(gev[1]) / GEMM_LAUNCHES
 
-    # the shader clock under the product: the rotated-set product graph
-    # replayed back to back for about half a second while the driver's
-    # current-clock reading is sampled
-    replays = max(1, int(0.5 / max(gemm_ms * 1e-3 * GEMM_LAUNCHES, 1e-6)))
-
-    def product_load():
-        for _ in range(replays):
-            gemm_graph.replay()
-        torch.cuda.synchronize()
-
-    sclk = sample_sclk(product_load)
-    if sclk is not None:
-        sclk["source"] = (f"pp_dpm_sclk read every 10 ms over {replays} replays of the {GEMM_LAUNCHES}-launch "
-                          "product graph (rotated sets)")
-        if m > 64 and mode != "weight_only":
-            # the product's fraction of the peak scaled to that clock (the
-            # rated peak assumes 2.4 GHz)
-            at_clock = PEAK_INT8_TOPS * sclk["median"] / 2400.0
-            sclk["gemm_frac_of_peak_at_median_clock"] = round(2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12 / at_clock,
-                                                              4)
-
     # the per-call linear (the second throughput figure): activation codes + the
     # product, as a forward runs them on prepared weights, GEMM_LAUNCHES
     # calls in one graph over the rotated sets, replayed between events
@@ -899,6 +878,28 @@ def main():
         gev[1].record(stream)
         torch.cuda.synchronize()
         stage_graph_ms[nm] = gev[0].elapsed_time(gev[1]) / STAGE_LAUNCHES
+
+    # the shader clock under the product: the rotated-set product graph
+    # replayed back to back for about half a second while the driver's
+    # current-clock reading is sampled (after every timed figure: the
+    # sustained load heats the chip and lowers the clock of what follows)
+    replays = max(1, int(0.5 / max(gemm_ms * 1e-3 * GEMM_LAUNCHES, 1e-6)))
+
+    def product_load():
+        for _ in range(replays):
+            gemm_graph.replay()
+        torch.cuda.synchronize()
+
+    sclk = sample_sclk(product_load)
+    if sclk is not None:
+        sclk["source"] = (f"pp_dpm_sclk read every 10 ms over {replays} replays of the {GEMM_LAUNCHES}-launch "
+                          "product graph (rotated sets)")
+        if m > 64 and mode != "weight_only":
+            # the product's fraction of the peak scaled to that clock (the
+            # rated peak assumes 2.4 GHz)
+            at_clock = PEAK_INT8_TOPS * sclk["median"] / 2400.0
+            sclk["gemm_frac_of_peak_at_median_clock"] = round(2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12 / at_clock,
+                                                              4)
 
     ops = 2.0 * m * n * k
     value = ops / (ms_per_step * 1e-3) / 1e12
