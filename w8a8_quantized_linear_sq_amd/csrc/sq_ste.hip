@@ -205,8 +205,8 @@ __global__ __launch_bounds__(256) void ste_transpose_codes_kernel(const int8_t* 
 // matrices, the second at y + rows * cols, and y[r][c] stands for their
 // sum RN32(y0 + y1) (the halves of a split product), written to out.
 // y is fp32 when OP != 0 (else YBF16 selects its type); z is fp32 (ZK 1)
-// or bf16 (ZK 2). VEC: cols % 4 == 0 and rows 16-byte aligned, 4 columns
-// per thread as one vector; otherwise 4 scalar columns.
+// or bf16 (ZK 2). VEC: cols % 4 == 0 and y and z 16-byte aligned (8 for a
+// bf16 y), 4 columns per thread as one vector; otherwise 4 scalar columns.
 template <int ZK, int OP, bool YBF16, bool VEC, bool TWO = false>
 __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, const void* __restrict__ z,
                                                          const float* __restrict__ s, int64_t rows, int64_t cols,
@@ -223,9 +223,10 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[e] = c0 + e < cols ? s[c0 + e] : 1.0f;
     }
-    for (int64_t r = r0; r < r1; ++r) {
-        float yv[4], zv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    auto load_row = [&](int64_t r, float (&yv)[4], float (&zv)[4]) {
         const int64_t base = r * cols + c0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[e] = 1.0f;
         if constexpr (VEC && !YBF16) {
             const float4 v = *(const float4*)((const float*)y + base);
             yv[0] = v.x; yv[1] = v.y; yv[2] = v.z; yv[3] = v.w;
@@ -233,6 +234,9 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
                 const float4 u = *(const float4*)((const float*)y + rows * cols + base);
                 yv[0] += u.x; yv[1] += u.y; yv[2] += u.z; yv[3] += u.w;
             }
+        } else if constexpr (VEC) {
+            const u32x2 v = *(const u32x2*)((const uint16_t*)y + base);
+            yv[0] = bf16_lo(v.x); yv[1] = bf16_hi(v.x); yv[2] = bf16_lo(v.y); yv[3] = bf16_hi(v.y);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -250,6 +254,9 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
 #pragma unroll
             for (int e = 0; e < 4; ++e) zv[e] = c0 + e < cols ? load_val<ZK == 2>(z, base + e) : 0.0f;
         }
+    };
+    auto finish_row = [&](int64_t r, const float (&yv)[4], const float (&zv)[4]) {
+        const int64_t base = r * cols + c0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += (double)yv[e] * (double)zv[e];
         if constexpr (OP != 0) {
@@ -265,6 +272,21 @@ __global__ __launch_bounds__(256) void ste_colsum_kernel(void* __restrict__ y, c
                     if (c0 + e < cols) dst[base + e] = o4[e];
             }
         }
+    };
+    // rows in order (the binary64 sums' order), four rows' loads in flight
+    constexpr int U = 4;
+    int64_t r = r0;
+    for (; r + U <= r1; r += U) {
+        float yv[U][4], zv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_row(r + u, yv[u], zv[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) finish_row(r + u, yv[u], zv[u]);
+    }
+    for (; r < r1; ++r) {
+        float yv[4], zv[4];
+        load_row(r, yv, zv);
+        finish_row(r, yv, zv);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -519,8 +541,9 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // db = sum_t dy
     if (db) {
-        e = dy_bf16 ? launch_colsum<0, 0, true>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st)
-                    : launch_colsum<0, 0, false>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, false, st);
+        const bool vec = n % 4 == 0 && ((uintptr_t)dy & (dy_bf16 ? 7 : 15)) == 0;
+        e = dy_bf16 ? launch_colsum<0, 0, true>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, vec, st)
+                    : launch_colsum<0, 0, false>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, vec, st);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(ste_bias_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, st, pb, L.gb, n, db);
         if ((e = hipGetLastError()) != hipSuccess) return e;
