@@ -95,6 +95,9 @@ def _args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="o_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sclk", action="store_true",
+                   help="skip sampling the shader clock (for profiler runs: its half second of product "
+                        "launches would outnumber the benchmark's own in a kernel trace)")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--layout", choices=("tiled", "row"), default="tiled",
                    help="int8 code layout: 16 x 64 tiles (default) or row-major (the per-tensor workload "
@@ -890,7 +893,7 @@ def main():
             gemm_graph.replay()
         torch.cuda.synchronize()
 
-    sclk = sample_sclk(product_load)
+    sclk = None if args.no_sclk else sample_sclk(product_load)
     if sclk is not None:
         sclk["source"] = (f"pp_dpm_sclk read every 10 ms over {replays} replays of the {GEMM_LAUNCHES}-launch "
                           "product graph (rotated sets)")
