@@ -954,6 +954,11 @@ def main():
                 "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                 "traffic": None if traffic is None else round(traffic)}
+        if sclk is not None and "gemm_frac_of_peak_at_median_clock" in sclk:
+            # the same against the peak at the clock the chip held under the
+            # product (the rated peak assumes 2.4 GHz)
+            roof["sclk_mhz"] = sclk["median"]
+            roof["frac_at_sclk"] = sclk["gemm_frac_of_peak_at_median_clock"]
 
     config = {"workload": desc, "m": m, "n": n, "k": k, "alpha": alpha, "in_dtype": "bf16",
               "out_dtype": "bf16", "bias": case.bias is not None, "rotated_buffer_sets": rotate}
