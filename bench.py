@@ -109,7 +109,55 @@ def _args():
                    help="time the tiled int8 product at M = N = 4096 for K = 64 ... 8192 (graphs of 64 "
                         "launches over 8 rotated operand sets, quantised N(0,1) codes, bf16 out): one JSON "
                         "line per K; the intercept is the launch's fixed cost")
+    p.add_argument("--hbm-reference", action="store_true",
+                   help="time torch's own device copy, fill and column amax at 48 MiB, 192 MiB and 1 GiB "
+                        "(graphs of 16 over rotated buffers): the HBM rates plain kernels reach on this box, "
+                        "one JSON line")
     return p.parse_args()
+
+
+def hbm_reference(torch, dev):
+    """Reference HBM rates of torch's own kernels (not this library's) on
+    the box: a device copy (read + write), a fill (write only) and a column
+    amax of a bf16 [rows][4096] matrix (read only), each as a graph of 16
+    launches over enough rotated buffers that every cycle covers at least
+    1 GiB (so no launch finds its data in the 256 MB Infinity Cache),
+    replayed once untimed and once between events."""
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    out = {"metric": "reference HBM rates of plain torch kernels (GB/s)", "unit": "GB/s", "sizes_mib": {}}
+
+    def timed(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(16):
+                calls[i % len(calls)]()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / 16
+
+    for mib in (48, 192, 1024):
+        nbytes = mib << 20
+        sets = max(2, -(-(1 << 30) // nbytes))
+        src = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_() for _ in range(sets)]
+        dst = [torch.empty_like(t) for t in src]
+        cols = 4096
+        red = [torch.empty(cols, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        torch.cuda.synchronize()
+        t_copy = timed([lambda i=i: dst[i].copy_(src[i]) for i in range(sets)])
+        t_fill = timed([lambda i=i: dst[i].fill_(1.0) for i in range(sets)])
+        t_amax = timed([lambda i=i: torch.amax(src[i].view(-1, cols), dim=0, out=red[i]) for i in range(sets)])
+        out["sizes_mib"][str(mib)] = {"copy": round(2 * nbytes / t_copy / 1e9, 1),
+                                      "fill": round(nbytes / t_fill / 1e9, 1),
+                                      "column_amax": round(nbytes / t_amax / 1e9, 1), "rotated_sets": sets}
+        del src, dst, red
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 def sweep_k(torch, B, dev):
@@ -603,6 +651,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.sweep_k:
         sweep_k(torch, B, dev)
+        return
+    if args.hbm_reference:
+        hbm_reference(torch, dev)
         return
 
     desc, spec, mode = WORKLOADS[args.workload]
