@@ -113,7 +113,81 @@ def _args():
                    help="time torch's own device copy, fill and column amax at 48 MiB, 192 MiB and 1 GiB "
                         "(graphs of 16 over rotated buffers): the HBM rates plain kernels reach on this box, "
                         "one JSON line")
+    p.add_argument("--vendor-reference", action="store_true",
+                   help="the vendor library's int8 GEMM (torch._int_mm, int32 out) against this library's "
+                        "product (int32 and bf16 out, row-major and tiled) on the O projection's quantised "
+                        "codes, 32 launches over 8 rotated sets; one JSON line")
     return p.parse_args()
+
+
+def vendor_reference(torch, B, dev):
+    """Paired timing, one process: torch._int_mm (the vendor int8 GEMM,
+    int32 out) and this library's product on the same codes (the O
+    projection's activations and weights quantised by this library), each as
+    32 launches over 8 rotated sets; the int32 results compared element for
+    element."""
+    import numpy as np
+
+    from w8a8_quantized_linear_sq_amd import inputs
+
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    case = inputs.o_proj()
+    m, n, k = case.m, case.n, case.k
+    x0 = torch.from_numpy(case.x.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w0 = torch.from_numpy(case.w.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    run = torch.zeros(k, dtype=torch.float32, device=dev)
+    for cb in case.calib:
+        B.sq_calibrate(torch.from_numpy(cb.bits.view(np.int16)).to(dev).view(torch.bfloat16), run, stream)
+    sets = []
+    for i in range(8):
+        s_ = torch.empty(k, device=dev)
+        xq, wq = torch.empty((m, k), dtype=torch.int8, device=dev), torch.empty((n, k), dtype=torch.int8, device=dev)
+        sx, sw = torch.empty(m, device=dev), torch.empty(n, device=dev)
+        B.sq_prepare_weight(w0, run, 0.5, s_, wq, sw, stream)
+        B.sq_quantize_act(x0, s_, xq, sx, stream)
+        xt, wt = B.tiled_empty(m, k, dev), B.tiled_empty(n, k, dev)
+        B.sq_prepare_weight_tiled(w0, run, 0.5, s_, wt, sw, stream)
+        B.sq_quantize_act_tiled(x0, s_, xt, sx, stream)
+        sets.append(dict(xq=xq, wq=wq, xt=xt, wt=wt, sx=sx, sw=sw,
+                         y32=torch.empty((m, n), dtype=torch.int32, device=dev),
+                         y16=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
+    del x0, w0
+    torch.cuda.synchronize()
+
+    # eager launches (the vendor library refuses stream capture): a pass
+    # of 32 untimed, then 32 between events; at ~60 us per launch the host
+    # enqueues far ahead of the GPU, so the events time the kernels
+    def timed(fn):
+        for i in range(32):
+            fn(sets[i % 8])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(32):
+            fn(sets[i % 8])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / 32
+
+    us = {
+        "vendor_int_mm_int32": timed(lambda st: torch._int_mm(st["xq"], st["wq"].t())),
+        "sq_w8a8_gemm_int32": timed(lambda st: B.sq_w8a8_gemm(st["xq"], None, st["wq"], None, None, st["y32"],
+                                                               stream)),
+        "sq_w8a8_gemm_tiled_int32": timed(lambda st: B.sq_w8a8_gemm_tiled(st["xt"], None, m, st["wt"], None, n, k,
+                                                                          None, st["y32"], stream)),
+        "sq_w8a8_gemm_tiled_bf16": timed(lambda st: B.sq_w8a8_gemm_tiled(st["xt"], st["sx"], m, st["wt"], st["sw"],
+                                                                         n, k, None, st["y16"], stream)),
+    }
+    st = sets[0]
+    ref = torch._int_mm(st["xq"], st["wq"].t())
+    B.sq_w8a8_gemm_tiled(st["xt"], None, m, st["wt"], None, n, k, None, st["y32"], stream)
+    torch.cuda.synchronize()
+    ops = 2.0 * m * n * k
+    print(json.dumps({"metric": "int8 GEMM at M=N=K=4096 on the O projection's codes (us per launch)",
+                      "us": {key: round(v, 2) for key, v in us.items()},
+                      "tops": {key: round(ops / (v * 1e-6) / 1e12, 1) for key, v in us.items()},
+                      "int32_identical": bool(torch.equal(ref, st["y32"]))}), flush=True)
 
 
 def hbm_reference(torch, dev):
@@ -654,6 +728,9 @@ def main():
         return
     if args.hbm_reference:
         hbm_reference(torch, dev)
+        return
+    if args.vendor_reference:
+        vendor_reference(torch, B, dev)
         return
 
     desc, spec, mode = WORKLOADS[args.workload]
