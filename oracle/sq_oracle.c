@@ -27,8 +27,7 @@
  * (quantize_tensor, QuantizedLinear); for the weight-only linear, the
  * torchao page "quantization/subclass.py" (Int8WeightOnlyQuantizedLinearWeight).
  *
- * Readings where the page is silent or garbled (each one also listed in
- * the design notes of the repository):
+ * Readings where the page is silent or garbled:
  *   R1  codes are clamped to [-128, 127]; with a max-abs scale no code
  *       below -127 can arise, so the page's [-127, 127] gives the same codes.
  *   R2  round() is round-half-to-even of the fp32 quotient.
