@@ -118,10 +118,13 @@ __global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restri
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][64][kTP];  // [plane][o][t]
     const int64_t tiles_t = ld / 64;
     const int64_t t0 = (blockIdx.x % tiles_t) * 64, o0 = (blockIdx.x / tiles_t) * 64;
+    // thread: four consecutive o (tx) of four consecutive t (ty), so that
+    // each plane's four t of one o go to LDS as one 8-byte store
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    uint32_t h[3][4][4];  // [plane][o][t]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int tt = ty + 16 * r;
+        const int tt = 4 * ty + r;
         const int64_t t = t0 + tt;
         const float f = t < m ? sc[t] : 0.0f;
         // four consecutive o of row t: one load when VEC (dy 16-byte aligned,
@@ -138,16 +141,17 @@ __global__ __launch_bounds__(256) void ste_pack_cols_kernel(const void* __restri
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int oo = tx * 4 + e;
-            const int64_t o = o0 + oo;
+            const int64_t o = o0 + tx * 4 + e;
             const float v = (t < m && o < n) ? d[e] * f : 0.0f;
-            uint32_t h1, h2, h3;
-            split3(v, h1, h2, h3);
-            tile[0][oo][tt] = (uint16_t)h1;
-            tile[1][oo][tt] = (uint16_t)h2;
-            tile[2][oo][tt] = (uint16_t)h3;
+            split3(v, h[0][e][r], h[1][e][r], h[2][e][r]);
         }
     }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *(u32x2*)&tile[p][tx * 4 + e][4 * ty] =
+                u32x2{h[p][e][0] | (h[p][e][1] << 16), h[p][e][2] | (h[p][e][3] << 16)};
     __syncthreads();
     // 64 rows o x 3 planes x 8 pieces of 16 bytes (8 t each)
     for (int c = threadIdx.x; c < 64 * 3 * 8; c += 256) {
