@@ -183,20 +183,29 @@ __global__ __launch_bounds__(256) void ste_transpose_codes_kernel(const int8_t* 
         for (int e = 0; e < 4; ++e) *(uint32_t*)&tile[oo][part * 16 + 4 * e] = v[e];
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < 64 * 8; c += 256) {
-        const int jj = c >> 3, piece = c & 7;
-        const int64_t j = j0 + jj;
-        if (j >= k) continue;
-        uint32_t w[4];
+    // thread c < 128: 4 consecutive j (jq) x 8 consecutive o (piece), read
+    // as one 4-byte word per o (the 4 j of that o), written as 4 rows of 8 o
+    if (threadIdx.x < 128) {
+        const int piece = threadIdx.x & 7, jq = threadIdx.x >> 3;
+        uint32_t word[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = (float)tile[piece * 8 + 2 * e][jj];
-            const float hi = (float)tile[piece * 8 + 2 * e + 1][jj];
-            w[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);  // |code| <= 128: exact
-        }
-        const u32x4 v = {w[0], w[1], w[2], w[3]};
+        for (int r = 0; r < 8; ++r) word[r] = *(const uint32_t*)&tile[piece * 8 + r][jq * 4];
         const int64_t o = o0 + piece * 8;  // 8 o in one part
-        *(u32x4*)(b + (o / nh) * k * nh + j * nh + o % nh) = v;
+        uint16_t* dst = b + (o / nh) * k * nh + o % nh;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t j = j0 + jq * 4 + q;
+            if (j >= k) break;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // |code| <= 128: exact in bf16
+                const float lo = (float)(int8_t)(word[2 * e] >> (8 * q));
+                const float hi = (float)(int8_t)(word[2 * e + 1] >> (8 * q));
+                w[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+            }
+            *(u32x4*)(dst + j * nh) = u32x4{w[0], w[1], w[2], w[3]};
+        }
     }
 }
 
