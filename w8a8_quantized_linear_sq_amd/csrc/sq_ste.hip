@@ -331,16 +331,14 @@ __device__ __forceinline__ double sum_groups(const double* __restrict__ p, int64
 // column passes' partials, and the per-channel term of dalpha,
 //   term[j] = [s_raw_j >= floor] ds_j s_raw_j (ln mx_j + ln mw_j)
 // (0 without calibration). A block owns 64 channels.
-__global__ __launch_bounds__(64 * kSumWaves) void ste_ds_kernel(const double* __restrict__ px, int64_t gx,
-                                                                const double* __restrict__ pw, int64_t gw,
-                                                                const float* __restrict__ s,
-                                                                const float* __restrict__ mx,
-                                                                const float* __restrict__ mw, double a_x, double a_w,
-                                                                int64_t k, float* __restrict__ ds_out,
-                                                                double* __restrict__ term) {
-    __shared__ double red[2][kSumWaves][64];
+__device__ __forceinline__ void ste_ds_block(int64_t blk, double (&red)[2][kSumWaves][64],
+                                             const double* __restrict__ px, int64_t gx,
+                                             const double* __restrict__ pw, int64_t gw, const float* __restrict__ s,
+                                             const float* __restrict__ mx, const float* __restrict__ mw, double a_x,
+                                             double a_w, int64_t k, float* __restrict__ ds_out,
+                                             double* __restrict__ term) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t j = blk * 64 + lane;
     double sw_ = 0.0, sx_ = 0.0;
     if (j < k) {
         sw_ = sum_groups(pw, gw, k, j, wave);
@@ -392,11 +390,11 @@ __global__ __launch_bounds__(256) void ste_alpha_kernel(const double* __restrict
 
 // db[o] = sum_g pb[g][o] (binary64 in the fixed order of sum_groups, then
 // fp32); a block owns 64 outputs
-__global__ __launch_bounds__(64 * kSumWaves) void ste_bias_kernel(const double* __restrict__ pb, int64_t groups,
-                                                                  int64_t n, float* __restrict__ db) {
-    __shared__ double red[kSumWaves][64];
+__device__ __forceinline__ void ste_bias_block(int64_t blk, double (&red)[kSumWaves][64],
+                                               const double* __restrict__ pb, int64_t groups, int64_t n,
+                                               float* __restrict__ db) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t o = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t o = blk * 64 + lane;
     red[wave][lane] = o < n ? sum_groups(pb, groups, n, o, wave) : 0.0;
     __syncthreads();
     if (wave != 0 || o >= n) return;
@@ -404,6 +402,22 @@ __global__ __launch_bounds__(64 * kSumWaves) void ste_bias_kernel(const double* 
 #pragma unroll
     for (int w = 0; w < kSumWaves; ++w) acc += red[w][lane];
     db[o] = (float)acc;
+}
+
+// ds (blocks below kblocks, 64 channels each) and db (the blocks after
+// them, 64 outputs each) in one launch: both only read the column passes'
+// partials, so their blocks are independent.
+__global__ __launch_bounds__(64 * kSumWaves) void ste_finish_kernel(
+    const double* __restrict__ px, int64_t gx, const double* __restrict__ pw, int64_t gw,
+    const float* __restrict__ s, const float* __restrict__ mx, const float* __restrict__ mw, double a_x, double a_w,
+    int64_t k, float* __restrict__ ds_out, double* __restrict__ term, int64_t kblocks,
+    const double* __restrict__ pb, int64_t gb, int64_t n, float* __restrict__ db) {
+    __shared__ double red[2][kSumWaves][64];
+    const int64_t blk = blockIdx.x;
+    if (blk < kblocks)
+        ste_ds_block(blk, red, px, gx, pw, gw, s, mx, mw, a_x, a_w, k, ds_out, term);
+    else
+        ste_bias_block(blk - kblocks, red[0], pb, gb, n, db);
 }
 
 // dy_q[i] = 2 (y_q[i] - y_fp[i]) / den and loss = ||y_fp - y_q||^2 / den with
@@ -550,21 +564,20 @@ hipError_t sq_launch_ste_backward(const void* dy, int dy_bf16, int64_t m, int64_
     e = w_bf16 ? launch_colsum<2, 2, false>(dw, w, s, n, k, L.gw, pw, true, st)
                : launch_colsum<1, 2, false>(dw, w, s, n, k, L.gw, pw, true, st);
     if (e != hipSuccess) return e;
-    // ds, dalpha, deta
-    hipLaunchKernelGGL(ste_ds_kernel, dim3((unsigned)((k + 63) / 64)), dim3(64 * kSumWaves), 0, st, px, L.gx, pw, L.gw, s, mx,
-                       mw, alpha, 1.0 - alpha, k, ds, term);
-    hipLaunchKernelGGL(ste_alpha_kernel, dim3(1), dim3(256), 0, st, term, k, alpha, dalpha_deta);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // db = sum_t dy
+    // db's column sums of dy
     if (db) {
         const bool vec = n % 4 == 0 && ((uintptr_t)dy & (dy_bf16 ? 7 : 15)) == 0;
         e = dy_bf16 ? launch_colsum<0, 0, true>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, vec, st)
                     : launch_colsum<0, 0, false>((void*)dy, nullptr, nullptr, m, n, L.gb, pb, vec, st);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(ste_bias_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, st, pb, L.gb, n, db);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return hipSuccess;
+    // ds and the per-channel terms of dalpha, and db, in one launch; then
+    // dalpha, deta
+    const int64_t kblocks = (k + 63) / 64, nblocks = db ? (n + 63) / 64 : 0;
+    hipLaunchKernelGGL(ste_finish_kernel, dim3((unsigned)(kblocks + nblocks)), dim3(64 * kSumWaves), 0, st, px, L.gx,
+                       pw, L.gw, s, mx, mw, alpha, 1.0 - alpha, k, ds, term, kblocks, pb, L.gb, n, db);
+    hipLaunchKernelGGL(ste_alpha_kernel, dim3(1), dim3(256), 0, st, term, k, alpha, dalpha_deta);
+    return hipGetLastError();
 }
 
 hipError_t sq_launch_aux_loss_grad(const float* y_fp, const float* y_q, int64_t count, double* partial,
