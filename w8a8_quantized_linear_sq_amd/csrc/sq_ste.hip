@@ -375,6 +375,9 @@ __global__ __launch_bounds__(256) void ste_alpha_kernel(const double* __restrict
                                                         double* __restrict__ out) {
     __shared__ double red[256];
     double acc = 0.0;
+    // unrolled so that the loads are issued together; the adds keep their
+    // order
+#pragma unroll 8
     for (int64_t j = threadIdx.x; j < k; j += 256) acc += term[j];
     red[threadIdx.x] = acc;
     __syncthreads();
