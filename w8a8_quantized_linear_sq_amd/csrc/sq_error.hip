@@ -80,6 +80,9 @@ __global__ __launch_bounds__(kThreads) void sqerr_final_kernel(const double* __r
                                                                double* __restrict__ out) {
     __shared__ double red[kThreads / 64];
     double d2 = 0.0, f2 = 0.0;
+    // at most kMaxBlocks / kThreads = 4 rounds, unrolled so that their loads
+    // are issued together (the adds keep their order)
+#pragma unroll 4
     for (int i = threadIdx.x; i < blocks; i += kThreads) {
         d2 += partial[2 * i];
         f2 += partial[2 * i + 1];
