@@ -716,6 +716,8 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(const unsigned* __res
                                                            float* __restrict__ scale) {
     __shared__ float red[4];
     unsigned m = 0;
+    // at most 4 rounds (1024 block maxima), their loads issued together
+#pragma unroll 4
     for (int i = threadIdx.x; i < blocks; i += 256) m = max(m, partial[i]);
     float mx = wave_max(__uint_as_float(m));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
