@@ -26,12 +26,17 @@
 //     The tile kernel's periodic-B form then sums the three planes against
 //     the same codes in one launch: every product is exact in fp32 and only
 //     the fp32 accumulation rounds, as in the page's fp32 autograd;
-//   * the two products write gX and gW into dx and dw; one column-sum pass
-//     per output folds the smoothing (dx = gX / s with IEEE division,
-//     dw = gW * s) and accumulates sum gX x and sum gW w in binary64 per
-//     row group (a fixed order: the same inputs give the same bits);
-//   * ds_j, its share of dalpha, the bias gradient and the final sums run
-//     in small kernels over k and n, fixed-order trees.
+//   * the two products write gX and gW into dx and dw; where gX's output
+//     has few 256 x 256 tiles (the prefill shape), its contraction is split
+//     over the output channels in two halves that run side by side in one
+//     launch of 256 x 256 tiles, each half a matrix of its own, and the
+//     column pass adds them (half 0 + half 1) before the fold;
+//   * one column-sum pass per output folds the smoothing (dx = gX / s with
+//     IEEE division, dw = gW * s) and accumulates sum gX x and sum gW w in
+//     binary64 per row group (a fixed order: the same inputs give the same
+//     bits);
+//   * ds_j with its share of dalpha and the bias gradient share one launch
+//     (independent blocks); the alpha sum follows; all fixed-order trees.
 #include "sq_device.h"
 
 using namespace sq;
