@@ -280,7 +280,7 @@ def sweep_k(torch, B, dev):
 
 
 def _read_sclk_mhz(path: str):
-    """The current shader clock the driver reports in pp_dpm_sclk (the line
+    """The current shader clock the amdgpu kernel driver reports in pp_dpm_sclk (the line
     marked with '*'), in MHz, or None."""
     try:
         with open(path) as f:
@@ -295,7 +295,7 @@ def _read_sclk_mhz(path: str):
 
 def sample_sclk(load, period_s: float = 0.01):
     """Shader clock while `load()` keeps the GPU busy (it enqueues work and
-    waits for it): the driver's current-clock file read every period_s from
+    waits for it): the amdgpu current-clock file read every period_s from
     a thread of its own; the first fifth of the samples (the clock's ramp)
     is dropped. None where no single such file is readable."""
     import glob
@@ -1011,7 +1011,7 @@ def main():
         stage_graph_ms[nm] = gev[0].elapsed_time(gev[1]) / STAGE_LAUNCHES
 
     # the shader clock under the product: the rotated-set product graph
-    # replayed back to back for about half a second while the driver's
+    # replayed back to back for about half a second while the amdgpu
     # current-clock reading is sampled (after every timed figure: the
     # sustained load heats the chip and lowers the clock of what follows)
     replays = max(1, int(0.5 / max(gemm_ms * 1e-3 * GEMM_LAUNCHES, 1e-6)))

@@ -69,7 +69,7 @@ def test_every_workload_names_a_case_and_mode():
 
 
 def test_sclk_reading(tmp_path):
-    """The driver's current-clock file: the line marked '*' gives the clock
+    """The amdgpu current-clock file (pp_dpm_sclk): the line marked '*' gives the clock
     (deep sleep and numbered levels alike); missing or unmarked: None."""
     f = tmp_path / "pp_dpm_sclk"
     f.write_text("S: 96Mhz\n0: 500Mhz\n1: 1712Mhz *\n2: 2400Mhz\n")
