@@ -605,10 +605,12 @@ static hipError_t launch_rows(const void* x, const float* s, int64_t m, int64_t 
     }
     else if (k8 <= 1024) { T = 512; C = 2; }
     else if (k8 <= 1408) {
-        // many rows: 6 wavefronts with 4 chunks each beat 11 with 2 (paired
-        // runs, 4096 x 11008 bf16: 34.1 -> 29.9 us); few rows: the wider
-        // block's shorter chain per row wins (256 rows: 5.3 against 5.8 us)
-        if (m >= 1024) { T = 384; C = 4; }
+        // many rows: 8 wavefronts with 3 chunks each beat 6 with 4 and 11
+        // with 2 (paired runs over rotated sets, 11008 channels, tiled
+        // activation codes: 4096 rows 28.0 -> 25.9 us, 1024 rows 15.8 ->
+        // 13.9 us; weights level or better); few rows: the wider block's
+        // shorter chain per row wins (256 rows: 6.2 against 6.3 and 7.5 us)
+        if (m >= 1024) { T = 512; C = 3; }
         else { T = 704; C = 2; }
     }
     else if (k8 <= 1536) { T = 512; C = 3; }
