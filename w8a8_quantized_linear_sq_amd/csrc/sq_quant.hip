@@ -168,11 +168,19 @@ __global__ __launch_bounds__(256) void colmax_kernel(Src src, int64_t rows, int6
 // busy (about 1024) but at least 128 rows per group, so that a column gets
 // few partial maxima (atomics when folding, partials when reducing).
 // rows per load instruction: 4 for a batch of up to 2048 rows (four times
-// the blocks, a short batch in flight at once), 1 otherwise (measured best)
-static int colmax_l(int64_t rows) { return rows <= 2048 ? 4 : 1; }
+// the blocks, a short batch in flight at once), and for the partial maxima
+// (the weights) of rows of at most 512 chunks, which L = 1 splits into only
+// 8 strips (256 blocks of 4096 rows, one per CU; paired runs of the whole
+// tiled weight preparation, same outputs: 4096 x 4096 29.8 -> 27.9 us,
+// 12288 x 4096 91.5 -> 89.2 us, 11008 x 4096 76.5 -> 74.3 us, while longer
+// rows measured slower with it); 1 otherwise (measured best)
+static int colmax_l(int64_t rows, int64_t kvec, bool partial) {
+    return rows <= 2048 || (partial && kvec <= 512) ? 4 : 1;
+}
 
-static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups, int64_t& rpg) {
-    const int L = colmax_l(rows);
+static void colmax_grid(int64_t rows, int64_t kvec, int64_t& gx, int64_t& groups, int64_t& rpg,
+                        bool partial = false) {
+    const int L = colmax_l(rows, kvec, partial);
     gx = (kvec + 64 / L - 1) / (64 / L);
     int64_t want = 1024 / gx;
     if (want < 1) want = 1;
@@ -200,7 +208,7 @@ template <bool FOLD>
 static hipError_t launch_colmax(const void* x, int bf16, int64_t rows, int64_t k, unsigned* out, int64_t groups,
                                 int64_t rpg, hipStream_t st, int overwrite = 0) {
     const int64_t kvec = bf16 ? k / 8 : k / 4;
-    switch (colmax_l(rows)) {
+    switch (colmax_l(rows, kvec, !FOLD)) {
         case 1: launch_colmax_l<FOLD, 1>(x, bf16, rows, kvec, k, out, groups, rpg, overwrite, st); break;
         default: launch_colmax_l<FOLD, 4>(x, bf16, rows, kvec, k, out, groups, rpg, overwrite, st); break;
     }
@@ -279,7 +287,7 @@ hipError_t sq_launch_colmax_batches(const void* const* x, const int64_t* rows, i
         }
     }
     unsigned* out = (unsigned*)running_max;
-    if (colmax_l(total) == 4)
+    if (colmax_l(total, kvec, false) == 4)
         launch_colmax_batches_l<4>(src, bf16, total, kvec, rpg, groups, k, out, overwrite, st);
     else
         launch_colmax_batches_l<1>(src, bf16, total, kvec, rpg, groups, k, out, overwrite, st);
@@ -288,7 +296,7 @@ hipError_t sq_launch_colmax_batches(const void* const* x, const int64_t* rows, i
 
 int64_t sq_colmax_partial_groups(int64_t rows, int64_t k, int bf16, int64_t scratch_bytes) {
     int64_t gx, groups, rpg;
-    colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg);
+    colmax_grid(rows, bf16 ? k / 8 : k / 4, gx, groups, rpg, true);
     const int64_t fit = scratch_bytes / (4 * k);
     if (groups > fit) groups = fit < 1 ? 1 : fit;
     return groups;
