@@ -117,6 +117,11 @@ def _args():
                    help="the vendor library's int8 GEMM (torch._int_mm, int32 out) against this library's "
                         "product (int32 and bf16 out, row-major and tiled) on the O projection's quantised "
                         "codes, 32 launches over 8 rotated sets; one JSON line")
+    p.add_argument("--mfma-reference", action="store_true",
+                   help="the int8 matrix units' ceiling on this box: the product's own MFMA instructions at "
+                        "4096^3 with no memory work (libsq_probe.so), beside the tiled product on the same "
+                        "codes, graphs of 64 launches; shader clock per workgroup from s_memtime over "
+                        "s_memrealtime; one JSON line")
     return p.parse_args()
 
 
@@ -232,6 +237,126 @@ def hbm_reference(torch, dev):
         del src, dst, red
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
+
+
+def mfma_reference(torch, B, dev):
+    """The ceiling of an int8 product at 4096^3 on this part: the probe
+    kernel (csrc/sq_probe.hip) issues the product's MFMA instructions, 16
+    per wavefront per 64-byte K step on 256 x 256 tiles, on operands held in
+    registers (the codes of the O projection) with no memory work at all.
+    Timed as a graph of 64 launches between events, beside the tiled product
+    on the same codes: on one operand set (warm, as the probe's own few
+    loads are) and over 8 rotated sets (cold, as the default run times it).
+    The probe's workgroups report shader cycles and 100 MHz ticks of their
+    loop (barrier to barrier), so the clock the chip held and the matrix
+    units' busy fraction (32 cycles per instruction per SIMD at the rated
+    peak, 2 wavefronts x 16 instructions per step on each SIMD) follow, and
+    when the loops started and ended over the grid."""
+    import ctypes
+
+    import numpy as np
+
+    from w8a8_quantized_linear_sq_amd import build as hip_build
+    from w8a8_quantized_linear_sq_amd import inputs
+
+    if not os.path.exists(hip_build.PROBE_LIB):
+        raise RuntimeError(f"{hip_build.PROBE_LIB} is missing: build first (python -m w8a8_quantized_linear_sq_amd.build)")
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    P.sqp_mfma_ceiling.restype = ctypes.c_int
+    P.sqp_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    case = inputs.o_proj()
+    m, n, k = case.m, case.n, case.k
+    x0 = torch.from_numpy(case.x.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w0 = torch.from_numpy(case.w.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    run = torch.zeros(k, dtype=torch.float32, device=dev)
+    for cb in case.calib:
+        B.sq_calibrate(torch.from_numpy(cb.bits.view(np.int16)).to(dev).view(torch.bfloat16), run, stream)
+    s_ = torch.empty(k, device=dev)
+    xq, wq = torch.empty((m, k), dtype=torch.int8, device=dev), torch.empty((n, k), dtype=torch.int8, device=dev)
+    sx, sw = torch.empty(m, device=dev), torch.empty(n, device=dev)
+    B.sq_prepare_weight(w0, run, 0.5, s_, wq, sw, stream)
+    B.sq_quantize_act(x0, s_, xq, sx, stream)
+    sets = []
+    for i in range(8):
+        xt, wt = B.tiled_empty(m, k, dev), B.tiled_empty(n, k, dev)
+        B.sq_prepare_weight_tiled(w0, run, 0.5, s_, wt, sw, stream)
+        B.sq_quantize_act_tiled(x0, s_, xt, sx, stream)
+        sets.append((xt, wt, torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
+    del x0, w0
+    tiles = (m // 256) * (n // 256)
+    sink = torch.empty(tiles * 512, dtype=torch.int32, device=dev)
+    # two clock buffers, written by alternate launches: the last two launches
+    # of a graph give the gap between one launch's end and the next's start
+    clocks = [torch.zeros(5 * tiles, dtype=torch.int64, device=dev) for _ in range(2)]
+    torch.cuda.synchronize()
+
+    def probe(c, kk=k):
+        # kk < k: the same buffers read as kk-byte rows (a prefix of each)
+        rc = P.sqp_mfma_ceiling(xq.data_ptr(), wq.data_ptr(), m, n, kk, sink.data_ptr(), c.data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"sqp_mfma_ceiling returned {rc}")
+
+    prods = [B.prepared(B.sq_w8a8_gemm_tiled, xt, sx, m, wt, sw, n, k, None, y, stream) for xt, wt, y in sets]
+
+    def timed(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(GEMM_LAUNCHES):
+                calls[r % len(calls)]()
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / GEMM_LAUNCHES
+
+    us_probe = timed([lambda: probe(clocks[0]), lambda: probe(clocks[1])])
+    prev, cyc = (c.view(tiles, 5).cpu().numpy() for c in clocks)  # the last two launches
+    t0 = cyc[:, 2].min()  # the last launch's first wavefront start
+
+    def rel(v):
+        return (v - t0) / 100.0
+
+    entry_us, starts_us, ends_us = rel(cyc[:, 2]), rel(cyc[:, 3]), rel(cyc[:, 4])
+    gap_us = (t0 - prev[:, 4].max()) / 100.0
+    cyc = cyc[:, :2].astype(np.float64)
+    us_probe_k64 = timed([lambda: probe(clocks[0], 64)])
+    us_warm = timed(prods[:1])
+    us_cold = timed(prods)
+    mhz = cyc[:, 0] / (cyc[:, 1] / 100.0)
+    busy = (2 * 16 * (k // 64) * 32) / cyc[:, 0]
+    ops = 2.0 * m * n * k
+
+    def tops(us):
+        return round(ops / (us * 1e-6) / 1e12, 1)
+
+    print(json.dumps({
+        "metric": "int8 MFMA ceiling at M=N=K=4096 (the product's instructions, no memory work) beside the product",
+        "probe_us": round(us_probe, 2), "probe_tops": tops(us_probe),
+        "probe_frac_of_rated_peak": round(ops / (us_probe * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+        "probe_shader_cycles_median": int(np.median(cyc[:, 0])),
+        "probe_clock_mhz_median": round(float(np.median(mhz)), 1),
+        "probe_clock_mhz_range": [round(float(mhz.min()), 1), round(float(mhz.max()), 1)],
+        "probe_mfma_busy_median": round(float(np.median(busy)), 3),
+        "probe_loop_us_median": round(float(np.median(cyc[:, 1])) / 100.0, 2),
+        "probe_us_after_first_wave_start": {
+            key: [round(float(v.min()), 2), round(float(np.median(v)), 2), round(float(v.max()), 2)]
+            for key, v in (("workgroup_start", entry_us), ("loop_start", starts_us), ("end", ends_us))},
+        "probe_gap_us_previous_end_to_first_start": round(float(gap_us), 2),
+        "probe_us_at_k64": round(us_probe_k64, 2),
+        "product_us_warm": round(us_warm, 2), "product_tops_warm": tops(us_warm),
+        "product_us_cold": round(us_cold, 2), "product_tops_cold": tops(us_cold),
+        "product_over_probe_time_cold": round(us_cold / us_probe, 3),
+        "rated_peak_tops": PEAK_INT8_TOPS,
+        "note": "graphs of 64 launches; probe clocks from its last launch (min, median, max over workgroups), "
+                "the gap from the launch before it; product bf16 out, tiled codes, warm = one operand set, "
+                "cold = 8 rotated sets"}), flush=True)
 
 
 def sweep_k(torch, B, dev):
@@ -731,6 +856,9 @@ def main():
         return
     if args.vendor_reference:
         vendor_reference(torch, B, dev)
+        return
+    if args.mfma_reference:
+        mfma_reference(torch, B, dev)
         return
 
     desc, spec, mode = WORKLOADS[args.workload]

@@ -541,3 +541,16 @@ def test_linear_tiled_errors(L, fused):
     assert call(wsb=need - 1) == B.SQ_ERR_WORKSPACE
     assert call(ws=OK_PTR + 16) == B.SQ_ERR_ALIGN
     assert call(m=0, x=None, y=None) == B.SQ_OK
+
+
+def test_mfma_probe_rejects_shapes_before_launch():
+    """The measurement probe (libsq_probe.so, the benchmark's MFMA-ceiling
+    reference) refuses shapes its grid does not cover, with no launch."""
+    from w8a8_quantized_linear_sq_amd import build as hip_build
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    P.sqp_mfma_ceiling.restype = ctypes.c_int
+    P.sqp_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for m, n, k in ((255, 256, 64), (256, 300, 64), (256, 256, 32), (256, 256, 96), (0, 256, 64),
+                    (1 << 40, 256, 64), (256, 256, 1 << 31)):
+        assert P.sqp_mfma_ceiling(OK_PTR, OK_PTR, m, n, k, OK_PTR, OK_PTR, None) == -1, (m, n, k)
