@@ -96,8 +96,9 @@ def _args():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="o_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sclk", action="store_true",
-                   help="skip sampling the shader clock (for profiler runs: its half second of product "
-                        "launches would outnumber the benchmark's own in a kernel trace)")
+                   help="skip sampling the shader clock and the MFMA-ceiling probe after the timed figures "
+                        "(for profiler runs: their launches would outnumber the benchmark's own in a kernel "
+                        "trace)")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--layout", choices=("tiled", "row"), default="tiled",
                    help="int8 code layout: 16 x 64 tiles (default) or row-major (the per-tensor workload "
@@ -239,6 +240,69 @@ def hbm_reference(torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def _probe_lib():
+    """libsq_probe.so (the MFMA-ceiling probe), loaded on first use."""
+    import ctypes
+
+    from w8a8_quantized_linear_sq_amd import build as hip_build
+
+    if not os.path.exists(hip_build.PROBE_LIB):
+        raise RuntimeError(f"{hip_build.PROBE_LIB} is missing: build first (python -m w8a8_quantized_linear_sq_amd.build)")
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    P.sqp_mfma_ceiling.restype = ctypes.c_int
+    P.sqp_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return P
+
+
+def mfma_ceiling(torch, dev, stream, xq, wq, m, n, k):
+    """The matrix units' ceiling for an m x n x k int8 product on this machine,
+    measured beside the product: the probe kernel (csrc/sq_probe.hip) issues
+    the product's 256 x 256-tile MFMA instructions with no memory work, as a
+    graph of 64 launches replayed once untimed and once between events. Its
+    operands are bytes of the int8 code buffers xq (m x k) and wq (n x k),
+    row-major or in 16 x 64 tiles (the same size when k is a multiple of 64;
+    only their values matter). None where the shape does not fit the probe's
+    grid (m and n multiples of 256, k of 64)."""
+    import ctypes
+
+    import numpy as np
+
+    if m % 256 or n % 256 or k % 64 or m < 256 or n < 256:
+        return None
+    P = _probe_lib()
+    tiles = (m // 256) * (n // 256)
+    sink = torch.empty(tiles * 512, dtype=torch.int32, device=dev)
+    clocks = torch.zeros(5 * tiles, dtype=torch.int64, device=dev)
+
+    def probe():
+        rc = P.sqp_mfma_ceiling(xq.data_ptr(), wq.data_ptr(), m, n, k, sink.data_ptr(), clocks.data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"sqp_mfma_ceiling returned {rc}")
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(GEMM_LAUNCHES):
+            probe()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / GEMM_LAUNCHES
+    cyc = clocks.view(tiles, 5).cpu().numpy()[:, :2].astype(np.float64)
+    tops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+    del g
+    return {"us": round(us, 2), "tops": round(tops, 1), "frac_of_rated_peak": round(tops / PEAK_INT8_TOPS, 4),
+            "clock_mhz_median": round(float(np.median(cyc[:, 0] / (cyc[:, 1] / 100.0))), 1),
+            "source": "probe kernel (csrc/sq_probe.hip): the product's MFMA instructions with no memory work, "
+                      f"graph of {GEMM_LAUNCHES} launches after every timed figure"}
+
+
 def mfma_reference(torch, B, dev):
     """The ceiling of an int8 product at 4096^3 on this part: the probe
     kernel (csrc/sq_probe.hip) issues the product's MFMA instructions, 16
@@ -259,12 +323,7 @@ def mfma_reference(torch, B, dev):
     from w8a8_quantized_linear_sq_amd import build as hip_build
     from w8a8_quantized_linear_sq_amd import inputs
 
-    if not os.path.exists(hip_build.PROBE_LIB):
-        raise RuntimeError(f"{hip_build.PROBE_LIB} is missing: build first (python -m w8a8_quantized_linear_sq_amd.build)")
-    P = ctypes.CDLL(hip_build.PROBE_LIB)
-    P.sqp_mfma_ceiling.restype = ctypes.c_int
-    P.sqp_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P = _probe_lib()
     stream = torch.cuda.Stream(dev)
     torch.cuda.set_stream(stream)
     case = inputs.o_proj()
@@ -1215,6 +1274,12 @@ def main():
             # product (the rated peak assumes 2.4 GHz)
             roof["sclk_mhz"] = sclk["median"]
             roof["frac_at_sclk"] = sclk["gemm_frac_of_peak_at_median_clock"]
+        if not args.no_sclk:
+            # what the matrix units deliver here with no memory work at all
+            ceil = mfma_ceiling(torch, dev, stream, sets[0]["xq"], sets[0]["wq"], m, n, k)
+            if ceil is not None:
+                roof["mfma_ceiling"] = ceil
+                roof["frac_of_ceiling"] = round(ceil["us"] / (gemm_ms * 1e3), 4)
 
     config = {"workload": desc, "m": m, "n": n, "k": k, "alpha": alpha, "in_dtype": "bf16",
               "out_dtype": "bf16", "bias": case.bias is not None, "rotated_buffer_sets": rotate}
