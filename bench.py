@@ -252,6 +252,9 @@ def _probe_lib():
     P.sqp_mfma_ceiling.restype = ctypes.c_int
     P.sqp_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P.sqp_stream_probe.restype = ctypes.c_int
+    P.sqp_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return P
 
 
@@ -386,6 +389,23 @@ def mfma_reference(torch, B, dev):
     gap_us = (t0 - prev[:, 4].max()) / 100.0
     cyc = cyc[:, :2].astype(np.float64)
     us_probe_k64 = timed([lambda: probe(clocks[0], 64)])
+
+    # the product's operand stream (tiled codes, direct-to-LDS buffer loads,
+    # three steps ahead) alone and with the matrix instructions
+    def operand_stream(mfma):
+        xt, wt, _ = sets[0]
+        rc = P.sqp_stream_probe(xt.data_ptr(), wt.data_ptr(), m, n, k, mfma, sink.data_ptr(), clocks[0].data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"sqp_stream_probe returned {rc}")
+
+    halves = {}
+    for name, mfma in (("loads_only", 0), ("loads_and_mfma", 1)):
+        us_h = timed([lambda mf=mfma: operand_stream(mf)])
+        cy = clocks[0].view(tiles, 5).cpu().numpy()[:, :2].astype(np.float64)
+        halves[name] = {"us": round(us_h, 2), "shader_cycles_median": int(np.median(cy[:, 0])),
+                        "loop_us_median": round(float(np.median(cy[:, 1])) / 100.0, 2),
+                        "clock_mhz_median": round(float(np.median(cy[:, 0] / (cy[:, 1] / 100.0))), 1)}
     us_warm = timed(prods[:1])
     us_cold = timed(prods)
     mhz = cyc[:, 0] / (cyc[:, 1] / 100.0)
@@ -409,6 +429,7 @@ def mfma_reference(torch, B, dev):
             for key, v in (("workgroup_start", entry_us), ("loop_start", starts_us), ("end", ends_us))},
         "probe_gap_us_previous_end_to_first_start": round(float(gap_us), 2),
         "probe_us_at_k64": round(us_probe_k64, 2),
+        "operand_stream_probe": halves,
         "product_us_warm": round(us_warm, 2), "product_tops_warm": tops(us_warm),
         "product_us_cold": round(us_cold, 2), "product_tops_cold": tops(us_cold),
         "product_over_probe_time_cold": round(us_cold / us_probe, 3),

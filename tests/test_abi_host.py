@@ -554,3 +554,10 @@ def test_mfma_probe_rejects_shapes_before_launch():
     for m, n, k in ((255, 256, 64), (256, 300, 64), (256, 256, 32), (256, 256, 96), (0, 256, 64),
                     (1 << 40, 256, 64), (256, 256, 1 << 31)):
         assert P.sqp_mfma_ceiling(OK_PTR, OK_PTR, m, n, k, OK_PTR, OK_PTR, None) == -1, (m, n, k)
+    P.sqp_stream_probe.restype = ctypes.c_int
+    P.sqp_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for m, n, k in ((255, 256, 64), (256, 300, 64), (256, 256, 32), (256, 256, 96), (0, 256, 64),
+                    (1 << 40, 256, 64), (256, 256, 1 << 28)):
+        for mfma in (0, 1):
+            assert P.sqp_stream_probe(OK_PTR, OK_PTR, m, n, k, mfma, OK_PTR, OK_PTR, None) == -1, (m, n, k)

@@ -115,7 +115,148 @@ __global__ __launch_bounds__(512) void mfma_ceiling_kernel(const int8_t* __restr
     }
 }
 
+// The product's operand stream, with or without its matrix instructions:
+// per 64-byte K step each workgroup brings its tile's 32 KiB of operand
+// tiles (16 row groups of A and 16 of B, one 1 KiB tile each, tiled codes)
+// into a 4-stage LDS ring with direct-to-LDS buffer loads, three steps
+// ahead, 4 loads per wavefront per step, in the product's tile order
+// (XCD-compact, groups of 4 along m). With MFMA, each wavefront also runs
+// the ceiling kernel's 16 instructions per step on operands held in
+// registers. Nothing reads the LDS and there is no barrier inside the loop:
+// the two halves of the product's loop, alone and together.
+constexpr int kStage = 32768;
+constexpr int kXcds = 8;
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, stride 0
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma_load16(const int8_t* base, int bytes, int voff, lds_ptr_t dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferFlags),
+                                             dst, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector memory operations outstanding
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+template <bool MFMA>
+__global__ __launch_bounds__(512, 1) void stream_probe_kernel(const int8_t* __restrict__ A,
+                                                              const int8_t* __restrict__ B, int k64, int grid_m,
+                                                              int grid_n, int steps, int* __restrict__ sink,
+                                                              uint64_t* __restrict__ clocks) {
+    __shared__ __attribute__((aligned(1024))) int8_t smem[4 * kStage];
+    uint64_t entry;
+    asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(entry) : : "memory");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // the product's tile order
+    const int total = grid_m * grid_n;
+    int pid = blockIdx.x;
+    if (total % kXcds == 0) pid = (pid % kXcds) * (total / kXcds) + pid / kXcds;
+    const int group_size = 4 * grid_n;
+    const int first_m = (pid / group_size) * 4;
+    const int gm = min(grid_m - first_m, 4);
+    const int tile_m = first_m + (pid % group_size) % gm;
+    const int tile_n = (pid % group_size) / gm;
+
+    // wavefront w fills blocks w, w + 8, w + 16, w + 24 of a stage (0-15:
+    // A's row groups, 16-31: B's); a block is one row group's tile of the
+    // step, 1 KiB contiguous, lane i its bytes 16 i .. 16 i + 15
+    const int8_t* g[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int blk = wave + 8 * q;
+        g[q] = blk < 16 ? A + (int64_t)(tile_m * 16 + blk) * k64 * 16 : B + (int64_t)(tile_n * 16 + blk - 16) * k64 * 16;
+    }
+    auto issue = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dma_load16(g[q], 16 * k64, lane * 16 + kt * 1024,
+                       (lds_ptr_t)(smem + (kt & 3) * kStage + (wave + 8 * q) * 1024));
+    };
+
+    i32x4 a[2][4], b[2][2];
+    i32x16 acc[4][2];
+    if constexpr (MFMA) {
+        // register operands: bytes of the tile's own first code tiles
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[s][i] = *(const i32x4*)(g[0] + (int64_t)(2 * i + s) * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[s][j] = *(const i32x4*)(g[2] + (int64_t)(2 * j + s) * 1024 + lane * 16);
+            asm volatile("" ::"v"(a[s][0]), "v"(a[s][1]), "v"(a[s][2]), "v"(a[s][3]), "v"(b[s][0]), "v"(b[s][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = i32x16{};
+    }
+    uint64_t c0, r0, c1, r1;
+    __syncthreads();
+    read_clocks(c0, r0);
+    for (int kt = 0; kt < 3 && kt < steps; ++kt) issue(kt);
+    for (int kt = 0; kt < steps; ++kt) {
+        // stage kt has landed (the product waits here before its LDS reads)
+        if (kt + 2 < steps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        else if (kt + 1 < steps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if constexpr (MFMA) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 3 < steps) issue(kt + 3);
+    }
+    int fold = (int)smem[threadIdx.x * 16];  // a byte of the first stage
+    if constexpr (MFMA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) fold ^= acc[i][j][e];
+    }
+    sink[(int64_t)blockIdx.x * 512 + threadIdx.x] = fold;
+    __syncthreads();
+    read_clocks(c1, r1);
+    if (threadIdx.x == 0) {
+        clocks[5 * blockIdx.x] = c1 - c0;
+        clocks[5 * blockIdx.x + 1] = r1 - r0;
+        clocks[5 * blockIdx.x + 2] = entry;
+        clocks[5 * blockIdx.x + 3] = r0;
+        clocks[5 * blockIdx.x + 4] = r1;
+    }
+}
+
 }  // namespace
+
+// The operand-stream probe (stream_probe_kernel above) for an m x n x k
+// product: a and b are m x k and n x k int8 codes on the device in 16 x 64
+// tiles (row groups of 16, K in 64-byte chunks, tile (g, c) at
+// (g k / 64 + c) KiB); m and n multiples of 256, k a multiple of 64, at
+// least 64. mfma: 0 the loads alone, 1 the loads and the matrix
+// instructions. sink and clocks as for sqp_mfma_ceiling. Returns 0, -1 for
+// a shape outside these limits, or the HIP error of the launch.
+extern "C" int sqp_stream_probe(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k, int mfma,
+                                int* sink, uint64_t* clocks, void* stream) {
+    if (m < kTile || n < kTile || k < 64 || m % kTile || n % kTile || k % 64) return -1;
+    const int64_t tiles = (m / kTile) * (n / kTile);
+    // a row group's record (16 k bytes) must fit the descriptor's 32-bit count
+    if (tiles > (1 << 20) || 16 * k > (int64_t)INT32_MAX) return -1;
+    const int gm = (int)(m / kTile), gn = (int)(n / kTile), steps = (int)(k / 64);
+    if (mfma)
+        hipLaunchKernelGGL(stream_probe_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, (hipStream_t)stream, a, b,
+                           (int)k, gm, gn, steps, sink, clocks);
+    else
+        hipLaunchKernelGGL(stream_probe_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, (hipStream_t)stream, a, b,
+                           (int)k, gm, gn, steps, sink, clocks);
+    return (int)hipGetLastError();
+}
 
 // m x n x k int8 product's matrix instructions with no memory work (see
 // above). xq: m x k and wq: n x k row-major int8 codes on the device (only
