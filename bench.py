@@ -266,12 +266,14 @@ def mfma_ceiling(torch, dev, stream, xq, wq, m, n, k):
     operands are bytes of the int8 code buffers xq (m x k) and wq (n x k),
     row-major or in 16 x 64 tiles (the same size when k is a multiple of 64;
     only their values matter). None where the shape does not fit the probe's
-    grid (m and n multiples of 256, k of 64)."""
+    grid (m and n multiples of 256, k of 64) or its 256 x 256 tiles do not
+    fill the chip's 256 compute units (the product then runs smaller tiles,
+    and the probe's figure would not be its ceiling)."""
     import ctypes
 
     import numpy as np
 
-    if m % 256 or n % 256 or k % 64 or m < 256 or n < 256:
+    if m % 256 or n % 256 or k % 64 or (m // 256) * (n // 256) < 256:
         return None
     P = _probe_lib()
     tiles = (m // 256) * (n // 256)
