@@ -1297,7 +1297,11 @@ def main():
             # product (the rated peak assumes 2.4 GHz)
             roof["sclk_mhz"] = sclk["median"]
             roof["frac_at_sclk"] = sclk["gemm_frac_of_peak_at_median_clock"]
-        if not args.no_sclk:
+        from w8a8_quantized_linear_sq_amd import build as hip_build
+        if not args.no_sclk and not os.path.exists(hip_build.PROBE_LIB):
+            # a measurement aid, not the product: its absence is reported
+            roof["mfma_ceiling"] = {"skipped": f"{hip_build.PROBE_LIB} not built"}
+        elif not args.no_sclk:
             # what the matrix units deliver here with no memory work at all
             ceil = mfma_ceiling(torch, dev, stream, sets[0]["xq"], sets[0]["wq"], m, n, k)
             if ceil is not None:
