@@ -1,10 +1,11 @@
-// sq_probe.hip -- measurement probe, not part of the library's ABI: the
+// sq_probe.hip -- measurement probes, not part of the library's ABI: the
 // rate the int8 matrix units of this part sustain with no memory work at
-// all, the ceiling any int8 product of the same size can reach here. Built
-// into its own shared library (libsq_probe.so), loaded only by the
-// benchmark's reference mode.
+// all, the ceiling any int8 product of the same size can reach here
+// (mfma_ceiling_kernel), and the product's operand stream alone and beside
+// those instructions (stream_probe_kernel, below). Built into their own
+// shared library (libsq_probe.so), loaded only by the benchmark.
 //
-// The kernel issues exactly the matrix instructions of the int8 product's
+// The ceiling kernel issues exactly the matrix instructions of the int8 product's
 // 256 x 256 tiles (gemm_kernel in sq_gemm.hip) for an m x n x k product:
 // one workgroup of 8 wavefronts per output tile, wavefronts in a 2 x 4 grid
 // of 128 x 64 blocks, per 64-byte K step 16 v_mfma_i32_32x32x32_i8 per
