@@ -391,6 +391,22 @@ def mfma_reference(torch, B, dev):
     gap_us = (t0 - prev[:, 4].max()) / 100.0
     cyc = cyc[:, :2].astype(np.float64)
     us_probe_k64 = timed([lambda: probe(clocks[0], 64)])
+    # the same grid with twice the K (longer launches): codes of 2k bytes a
+    # row, the first k bytes of each the O projection's
+    xq2 = torch.cat([xq, xq], dim=1)
+    wq2 = torch.cat([wq, wq], dim=1)
+
+    def probe_2k():
+        rc = P.sqp_mfma_ceiling(xq2.data_ptr(), wq2.data_ptr(), m, n, 2 * k, sink.data_ptr(), clocks[1].data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"sqp_mfma_ceiling returned {rc}")
+
+    us_probe_2k = timed([probe_2k])
+    cy2 = clocks[1].view(tiles, 5).cpu().numpy()[:, :2].astype(np.float64)
+    probe_2k_line = {"k": 2 * k, "us": round(us_probe_2k, 2),
+                     "frac_of_rated_peak": round(4.0 * m * n * k / (us_probe_2k * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+                     "clock_mhz_median": round(float(np.median(cy2[:, 0] / (cy2[:, 1] / 100.0))), 1)}
 
     # the product's operand stream (tiled codes, direct-to-LDS buffer loads,
     # three steps ahead) alone and with the matrix instructions
@@ -431,6 +447,7 @@ def mfma_reference(torch, B, dev):
             for key, v in (("workgroup_start", entry_us), ("loop_start", starts_us), ("end", ends_us))},
         "probe_gap_us_previous_end_to_first_start": round(float(gap_us), 2),
         "probe_us_at_k64": round(us_probe_k64, 2),
+        "probe_at_twice_k": probe_2k_line,
         "operand_stream_probe": halves,
         "product_us_warm": round(us_warm, 2), "product_tops_warm": tops(us_warm),
         "product_us_cold": round(us_cold, 2), "product_tops_cold": tops(us_cold),
